@@ -1,0 +1,290 @@
+/*
+ * swimba_oracle.c -- plain, slow, fp64 CPU oracle for the Swimba
+ * (Switch Mamba) parameter-space mixture-of-experts selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file or the library built from it; only the test-suite, the smoke
+ * check and the benchmark's CPU-baseline leg do.  It shares no code, header,
+ * table or helper with the HIP library.
+ *
+ * Pages cited (by title and section):
+ *   [SW] "Swimba: Switch Mamba Model Scales State Space Models"
+ *        (gist.science summaries in Spanish, Dutch and French).  The Dutch
+ *        technical summary, section "Kernmechanisme van Swimba", writes the
+ *        mixed recurrence; the French summary, "Fondements Théoriques", states
+ *        Theorems 1-4.
+ *   [MB] "Mamba y las SSMs: el retorno del estado persistente", sections
+ *        "SSMs - Modelos de espacios de estados" (the linear state/output
+ *        equations with the D feed-through) and "Mamba" (selective B_t, C_t,
+ *        the zero-order-hold transition exp(Delta_t A), Figure 2: Delta as the
+ *        forgetting factor).
+ *
+ * What is computed (one channel d of one sequence b; N state entries):
+ *   router     l_e = sum_d x_d Wr[d,e]; the k largest (ties: lower e first);
+ *              gates = softmax over the k selected logits (convex weights).
+ *   mixing     Abar[n] = sum_j g_j A[e_j,d,n], beta = sum_j g_j bias[e_j,d],
+ *              delta = sum_j g_j Dskip[e_j,d]      (parameters mixed, [SW])
+ *   discretise Delta = softplus(dt_raw + beta); a[n] = exp(Delta Abar[n])
+ *              ([MB] "Mamba": transition exp(Delta A)); injection
+ *              Delta * B[t,n] * x (Euler form of the input term)
+ *   recurrence h[n] <- a[n] h[n] + Delta B[t,n] x      ([MB], [SW])
+ *   readout    y = sum_n C[t,n] h[n] + delta x          (after the update)
+ * The separate design keeps one state per expert and advances only the
+ * selected ones ([SW] the two MoE-SSM designs; Theorem 4).
+ *
+ * Readings where the pages are silent are listed in the design document:
+ * Euler injection, bias mixed before softplus, gates = softmax over the top
+ * k, equal logits broken towards the lower expert index, zero initial state.
+ *
+ * Every loop is the definition written out, in fp64, in the order the
+ * definition states it.  OpenMP runs independent (b,d) channels (and
+ * independent tokens in the router) in parallel; that changes no result.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* Stable softplus, log(1 + exp(z)) = max(z,0) + log1p(exp(-|z|)). */
+static double softplus(double z) {
+  return (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z)));
+}
+
+/* ---------------------------------------------------------------- router */
+/*
+ * ref_route: per token t of T, logits over E experts, the top k and their
+ * gates ([SW] Dutch summary "Kernmechanisme": a router computes per-token
+ * weights pi_t over the active experts, e.g. top-1 or top-k).
+ *   x      [T, D]   token features (the scanned input)
+ *   Wr     [D, E]   router weights
+ *   idx    [T, k]   out: selected experts, largest logit first
+ *   gate   [T, k]   out: softmax over the selected logits
+ *   logits [T, E]   out (may be NULL): the fp64 logits
+ *   absdot [T, E]   out (may be NULL): sum_d |x_d Wr[d,e]|, the magnitude
+ *                   that bounds the rounding error of any float summation
+ */
+void ref_route(int64_t T, int D, int E, int k, const double* x,
+               const double* Wr, int32_t* idx, double* gate, double* logits,
+               double* absdot) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* l = (double*)malloc(sizeof(double) * (size_t)E);
+    int* taken = (int*)calloc((size_t)E, sizeof(int));
+    for (int e = 0; e < E; ++e) {
+      double s = 0.0, sa = 0.0;
+      for (int d = 0; d < D; ++d) {
+        double p = x[t * D + d] * Wr[(int64_t)d * E + e];
+        s += p;
+        sa += fabs(p);
+      }
+      l[e] = s;
+      if (logits) logits[t * E + e] = s;
+      if (absdot) absdot[t * E + e] = sa;
+    }
+    /* top-k by (logit descending, index ascending) */
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || l[e] > l[best]) best = e;
+      }
+      taken[best] = 1;
+      idx[t * k + j] = best;
+    }
+    /* softmax restricted to the selected experts */
+    double m = l[idx[t * k + 0]];
+    double z = 0.0;
+    for (int j = 0; j < k; ++j) z += exp(l[idx[t * k + j]] - m);
+    for (int j = 0; j < k; ++j) gate[t * k + j] = exp(l[idx[t * k + j]] - m) / z;
+    free(l);
+    free(taken);
+  }
+}
+
+/* ----------------------------------------------------------- mixed scan */
+/*
+ * ref_scan: the parameter-space-mixed selective scan, one state trajectory
+ * per (b,d) ([SW] "Kernmechanisme van Swimba"; Theorem 1: one selective SSM).
+ *   x, dt_raw [B, L, D]     inputs and pre-activation step sizes
+ *   Bm, Cm    [B, L, N]     selective input / output vectors B_t, C_t
+ *   idx, gate [B, L, k]     routing (from ref_route or forced)
+ *   A         [E, D, N]     per-expert diagonal transitions (negative)
+ *   dt_bias   [E, D]        per-expert step-size bias
+ *   Dskip     [E, D]        per-expert feed-through D
+ *   h0        [B, D, N]     initial state, or NULL for zeros
+ *   y         [B, L, D]     out
+ *   h_final   [B, D, N]     out, or NULL
+ */
+void ref_scan(int B, int L, int D, int N, int E, int k, const double* x,
+              const double* dt_raw, const double* Bm, const double* Cm,
+              const int32_t* idx, const double* gate, const double* A,
+              const double* dt_bias, const double* Dskip, const double* h0,
+              double* y, double* h_final) {
+  (void)E;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int d = 0; d < D; ++d) {
+      double* h = (double*)malloc(sizeof(double) * (size_t)N);
+      for (int n = 0; n < N; ++n)
+        h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.0;
+      for (int t = 0; t < L; ++t) {
+        int64_t bt = (int64_t)b * L + t;
+        const int32_t* e = idx + bt * k;
+        const double* g = gate + bt * k;
+        double xv = x[bt * D + d];
+        /* mixed per-token parameters */
+        double beta = 0.0, delta = 0.0;
+        for (int j = 0; j < k; ++j) {
+          beta += g[j] * dt_bias[(int64_t)e[j] * D + d];
+          delta += g[j] * Dskip[(int64_t)e[j] * D + d];
+        }
+        double Dt = softplus(dt_raw[bt * D + d] + beta);
+        double yv = 0.0;
+        for (int n = 0; n < N; ++n) {
+          double Abar = 0.0;
+          for (int j = 0; j < k; ++j)
+            Abar += g[j] * A[((int64_t)e[j] * D + d) * N + n];
+          double a = exp(Dt * Abar);
+          double bb = Dt * Bm[bt * N + n] * xv;
+          h[n] = a * h[n] + bb;
+          yv += Cm[bt * N + n] * h[n];
+        }
+        y[bt * D + d] = yv + delta * xv;
+      }
+      if (h_final)
+        for (int n = 0; n < N; ++n) h_final[((int64_t)b * D + d) * N + n] = h[n];
+      free(h);
+    }
+  }
+}
+
+/* -------------------------------------------------------- separate scan */
+/*
+ * ref_scan_separate: the "MoE of separate SSMs" design: one state trajectory
+ * per expert.  At token t, for each slot j (in slot order) the selected
+ * expert e = idx[t,j] advances its own state with its own (unmixed)
+ * parameters and emits y_e; the token's output is sum_j g_j y_e.  Experts
+ * not selected at t keep their state unchanged ([SW] Spanish summary
+ * "Distinción de Diseños", French "Distinction des deux designs";
+ * Theorem 4: the two designs differ once routing varies over time).
+ *   h0, h_final [B, E, D, N] (NULL allowed); other arrays as ref_scan.
+ */
+void ref_scan_separate(int B, int L, int D, int N, int E, int k,
+                       const double* x, const double* dt_raw,
+                       const double* Bm, const double* Cm, const int32_t* idx,
+                       const double* gate, const double* A,
+                       const double* dt_bias, const double* Dskip,
+                       const double* h0, double* y, double* h_final) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int d = 0; d < D; ++d) {
+      double* H = (double*)malloc(sizeof(double) * (size_t)E * N);
+      for (int e = 0; e < E; ++e)
+        for (int n = 0; n < N; ++n)
+          H[e * N + n] = h0 ? h0[(((int64_t)b * E + e) * D + d) * N + n] : 0.0;
+      for (int t = 0; t < L; ++t) {
+        int64_t bt = (int64_t)b * L + t;
+        double xv = x[bt * D + d];
+        double yv = 0.0;
+        for (int j = 0; j < k; ++j) {
+          int e = idx[bt * k + j];
+          double Dt = softplus(dt_raw[bt * D + d] + dt_bias[(int64_t)e * D + d]);
+          double ye = 0.0;
+          for (int n = 0; n < N; ++n) {
+            double a = exp(Dt * A[((int64_t)e * D + d) * N + n]);
+            H[e * N + n] = a * H[e * N + n] + Dt * Bm[bt * N + n] * xv;
+            ye += Cm[bt * N + n] * H[e * N + n];
+          }
+          ye += Dskip[(int64_t)e * D + d] * xv;
+          yv += gate[bt * k + j] * ye;
+        }
+        y[bt * D + d] = yv;
+      }
+      if (h_final)
+        for (int e = 0; e < E; ++e)
+          for (int n = 0; n < N; ++n)
+            h_final[(((int64_t)b * E + e) * D + d) * N + n] = H[e * N + n];
+      free(H);
+    }
+  }
+}
+
+/* ------------------------------------------------------ plain Mamba scan */
+/*
+ * ref_mamba_scan: the single-expert selective scan ([MB] "Mamba": state
+ * update with exp(Delta_t A) and selective B_t, C_t; "SSMs": D feed-through).
+ * Written independently of ref_scan so that the E = 1 and identical-expert
+ * reductions (Theorem 1) compare two different pieces of code.
+ *   A [D, N], dt_bias [D], Dskip [D]; h0, h_final [B, D, N] (NULL allowed).
+ */
+void ref_mamba_scan(int B, int L, int D, int N, const double* x,
+                    const double* dt_raw, const double* Bm, const double* Cm,
+                    const double* A, const double* dt_bias,
+                    const double* Dskip, const double* h0, double* y,
+                    double* h_final) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int d = 0; d < D; ++d) {
+      double* h = (double*)malloc(sizeof(double) * (size_t)N);
+      for (int n = 0; n < N; ++n)
+        h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.0;
+      for (int t = 0; t < L; ++t) {
+        int64_t bt = (int64_t)b * L + t;
+        double u = x[bt * D + d];
+        double Dt = softplus(dt_raw[bt * D + d] + dt_bias[d]);
+        double out = Dskip[d] * u;
+        for (int n = 0; n < N; ++n) {
+          h[n] = exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * Bm[bt * N + n] * u;
+          out += Cm[bt * N + n] * h[n];
+        }
+        y[bt * D + d] = out;
+      }
+      if (h_final)
+        for (int n = 0; n < N; ++n) h_final[((int64_t)b * D + d) * N + n] = h[n];
+      free(h);
+    }
+  }
+}
+
+/* ------------------------------------------------------------ decode step */
+/*
+ * ref_step: one decoding step on a persistent state ([MB] Figure 2: the
+ * state lives on and is updated once per token).  Routing comes from the
+ * router on this token's x (when idx_in is NULL) or is forced.
+ *   x, dt_raw [B, D]; Bm, Cm [B, N]; Wr [D, E]; idx_in, gate_in [B, k] or NULL
+ *   state [B, D, N] in/out; y [B, D] out; idx_out, gate_out [B, k] out
+ *   (may be NULL).
+ */
+void ref_step(int B, int D, int N, int E, int k, const double* x,
+              const double* dt_raw, const double* Bm, const double* Cm,
+              const double* Wr, const int32_t* idx_in, const double* gate_in,
+              const double* A, const double* dt_bias, const double* Dskip,
+              double* state, double* y, int32_t* idx_out, double* gate_out) {
+  int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)B * k);
+  double* gate = (double*)malloc(sizeof(double) * (size_t)B * k);
+  if (idx_in) {
+    for (int64_t i = 0; i < (int64_t)B * k; ++i) {
+      idx[i] = idx_in[i];
+      gate[i] = gate_in[i];
+    }
+  } else {
+    ref_route(B, D, E, k, x, Wr, idx, gate, NULL, NULL);
+  }
+  /* a step is the scan over a sequence of length one, state carried */
+  ref_scan(B, 1, D, N, E, k, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip,
+           state, y, state);
+  if (idx_out)
+    for (int64_t i = 0; i < (int64_t)B * k; ++i) idx_out[i] = idx[i];
+  if (gate_out)
+    for (int64_t i = 0; i < (int64_t)B * k; ++i) gate_out[i] = gate[i];
+  free(idx);
+  free(gate);
+}
+
+/* Threads the parallel loops above use (for reporting the CPU baseline). */
+#ifdef _OPENMP
+#include <omp.h>
+int ref_num_threads(void) { return omp_get_max_threads(); }
+#else
+int ref_num_threads(void) { return 1; }
+#endif

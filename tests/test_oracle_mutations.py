@@ -1,0 +1,65 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+the pins catch every one of them: a pin that no mistake can trip pins nothing."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = open(oracle._SRC).read()
+
+# (name, original text, planted mistake)
+MUTATIONS = [
+    ("drop_D_term", "y[bt * D + d] = yv + delta * xv;", "y[bt * D + d] = yv;"),
+    ("readout_before_update",
+     "          h[n] = a * h[n] + bb;\n          yv += Cm[bt * N + n] * h[n];",
+     "          yv += Cm[bt * N + n] * h[n];\n          h[n] = a * h[n] + bb;"),
+    ("exp_sign", "double a = exp(Dt * Abar);", "double a = exp(-Dt * Abar);"),
+    ("softplus_sign", "log1p(exp(-fabs(z)))", "log1p(exp(fabs(z)))"),
+    ("softplus_drop_relu", "return (z > 0.0 ? z : 0.0) + log1p", "return log1p"),
+    ("bias_unmixed", "beta += g[j] * dt_bias", "beta += dt_bias"),
+    ("D_unmixed", "delta += g[j] * Dskip", "delta += Dskip"),
+    ("A_first_gate_only", "Abar += g[j] * A[", "Abar += g[0] * A["),
+    ("A_transposed", "Abar += g[j] * A[((int64_t)e[j] * D + d) * N + n];",
+     "Abar += g[j] * A[((int64_t)e[j] * N + n) * D + d];"),
+    ("injection_no_delta", "double bb = Dt * Bm[bt * N + n] * xv;", "double bb = Bm[bt * N + n] * xv;"),
+    ("B_C_swapped", "yv += Cm[bt * N + n] * h[n];", "yv += Bm[bt * N + n] * h[n];"),
+    ("h0_ignored", "h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.0;\n      for (int t = 0; t < L; ++t) {\n        int64_t bt = (int64_t)b * L + t;\n        const int32_t* e",
+     "h[n] = 0.0;\n      for (int t = 0; t < L; ++t) {\n        int64_t bt = (int64_t)b * L + t;\n        const int32_t* e"),
+    ("route_tie_to_higher", "if (best < 0 || l[e] > l[best]) best = e;", "if (best < 0 || l[e] >= l[best]) best = e;"),
+    ("route_softmax_all", "for (int j = 0; j < k; ++j) z += exp(l[idx[t * k + j]] - m);",
+     "for (int j = 0; j < E; ++j) z += exp(l[j] - m);"),
+    ("route_absdot_signed", "sa += fabs(p);", "sa += p;"),
+    ("separate_wrong_expert_A", "double a = exp(Dt * A[((int64_t)e * D + d) * N + n]);",
+     "double a = exp(Dt * A[((int64_t)0 * D + d) * N + n]);"),
+    ("separate_ungated", "yv += gate[bt * k + j] * ye;", "yv += ye;"),
+    ("separate_bias_of_slot0", "softplus(dt_raw[bt * D + d] + dt_bias[(int64_t)e * D + d]);",
+     "softplus(dt_raw[bt * D + d] + dt_bias[(int64_t)idx[bt * k] * D + d]);"),
+    ("separate_decays_all",
+     "          ye += Dskip[(int64_t)e * D + d] * xv;",
+     "          for (int o = 0; o < E; ++o) if (o != e) for (int n = 0; n < N; ++n) H[o * N + n] *= 0.5;\n          ye += Dskip[(int64_t)e * D + d] * xv;"),
+    ("mamba_wrong_A_index", "exp(Dt * A[(int64_t)d * N + n])", "exp(Dt * A[(int64_t)n])"),
+    ("mamba_no_D", "double out = Dskip[d] * u;", "double out = 0.0;"),
+    ("step_routes_first_token_only", "ref_route(B, D, E, k, x, Wr, idx, gate, NULL, NULL);",
+     "ref_route(1, D, E, k, x, Wr, idx, gate, NULL, NULL);\n    for (int64_t i = k; i < (int64_t)B * k; ++i) { idx[i] = idx[i % k]; gate[i] = gate[i % k]; }"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(name, old, new, tmp_path):
+    assert SRC.count(old) == 1, "mutation anchor for %s not unique/present" % name
+    src = tmp_path / ("mut_%s.c" % name)
+    src.write_text(SRC.replace(old, new))
+    so = str(tmp_path / ("libmut_%s.so" % name))
+    oracle.build(force=True, src=str(src), out=so)
+    lib = oracle.load(so)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, "no pin caught mutation %s" % name
