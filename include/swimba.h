@@ -1,0 +1,182 @@
+/*
+ * swimba.h -- C ABI of libswimba.so: the Swimba (Switch Mamba)
+ * parameter-space mixture-of-experts selective scan on MI355X (gfx950).
+ *
+ * Pages cited by title and section:
+ *   [SW] "Swimba: Switch Mamba Model Scales State Space Models" (gist.science
+ *        summaries; Dutch "Kernmechanisme van Swimba": router weights per token,
+ *        parameters of the active experts mixed, one recurrence; Spanish
+ *        "Distinción de Diseños" / French "Distinction des deux designs": the
+ *        separate design with one state trajectory per expert; French
+ *        "Fondements Théoriques": Theorems 1-4).
+ *   [MB] "Mamba y las SSMs: el retorno del estado persistente" (section "SSMs":
+ *        h_t = A h_{t-1} + B x_t, y_t = C h_t + D x_t; section "Mamba":
+ *        selective B_t, C_t and transition exp(Delta_t A); Figure 2: the state
+ *        kept on chip, inputs and outputs streamed from HBM).
+ *
+ * What the library computes, per sequence b and channel d (N = 16 states):
+ *   router:  l_e = sum_d x_d Wr[d,e]; top k by (logit desc, expert asc);
+ *            gates = softmax over the k selected logits.
+ *   mixed:   Abar = sum_j g_j A[e_j,d,:], beta = sum_j g_j dt_bias[e_j,d],
+ *            delta = sum_j g_j Dskip[e_j,d]; Delta = softplus(dt_raw + beta);
+ *            h <- exp(Delta Abar) * h + Delta * B_t * x;  y = C_t . h + delta x
+ *            (y reads the updated state).
+ *   separate: each expert keeps its own state; at token t each selected
+ *            expert e_j advances with its own A, bias, Dskip and emits y_j;
+ *            y = sum_j g_j y_j; unselected experts' states do not change.
+ *
+ * Conventions (all entry points):
+ *   - Every tensor argument is a DEVICE pointer owned by the caller, dense and
+ *     row-major (last index fastest), and must stay valid until the work
+ *     enqueued on `stream` has finished.  The library allocates no memory,
+ *     keeps no global state and never synchronises the stream; calls on
+ *     different streams may run concurrently.
+ *   - Work is enqueued on `stream` (NULL = the null stream).  A return of
+ *     SWIMBA_OK means the kernels were launched; execution errors surface in
+ *     later HIP calls on that stream.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     negative return nothing was enqueued.  Values are not inspected:
+ *     NaN/Inf propagate.  The scans assume A < 0 and gates >= 0 (contractive
+ *     transitions, [SW] Theorem 3); when the kernels see otherwise they fall
+ *     back to an exact but slower carry between chunks.
+ *   - bf16 tensors hold raw bfloat16 bits (uint16).  Arithmetic is fp32.
+ */
+#ifndef SWIMBA_H
+#define SWIMBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SWIMBA_F32 = 0, SWIMBA_BF16 = 1 } swimba_dtype;
+
+enum {
+  SWIMBA_OK = 0,
+  SWIMBA_EINVAL = -1,       /* a null pointer, a negative size, k > E, ...   */
+  SWIMBA_EUNSUPPORTED = -2, /* valid but not built: N != 16, E > 64, ...     */
+  SWIMBA_EWORKSPACE = -3,   /* workspace smaller than the query, or unaligned */
+  SWIMBA_EHIP = -4          /* a kernel launch failed                         */
+};
+
+/* Largest expert count and the only state size this build supports. */
+#define SWIMBA_MAX_EXPERTS 64
+#define SWIMBA_STATE_N 16
+
+/*
+ * swimba_route -- router logits, top-k and gates for T tokens ([SW] Dutch
+ * summary "Kernmechanisme van Swimba": per-token weights pi_t over the
+ * active experts, top-1 or top-k).
+ *   x      [T, D]  token features, dtype x_dtype
+ *   Wr     [D, E]  fp32 router weights
+ *   idx    [T, k]  out, int32: selected experts, largest logit first; equal
+ *                  logits are taken in ascending expert order
+ *   gate   [T, k]  out, fp32: softmax over the selected logits (top-1: 1.0)
+ * Logits are fp32 sums; a token whose logits tie to within fp32 rounding may
+ * order those experts either way.  Constraints: T >= 0, D >= 1,
+ * 1 <= k <= E <= SWIMBA_MAX_EXPERTS.  T == 0 launches nothing.
+ */
+int swimba_route(const void* x, swimba_dtype x_dtype, const float* Wr, int64_t T, int D, int E,
+                 int k, int32_t* idx, float* gate, hipStream_t stream);
+
+/* How the scans join chunks of one sequence. */
+typedef enum {
+  SWIMBA_CARRY_AUTO = 0,   /* library's choice (the decay-bounded fix-up)    */
+  SWIMBA_CARRY_REWALK = 1, /* recompute every chunk from its carried state   */
+  SWIMBA_CARRY_FIXUP = 2   /* recompute only until the carried state has
+                              decayed below fp32 resolution (needs A < 0)    */
+} swimba_carry;
+
+typedef struct {
+  int B, L, D, N, E, k;         /* batch, length, channels, states (16), experts, active */
+  swimba_dtype in_dtype;        /* dtype of x, dt_raw, Bm, Cm                            */
+  swimba_dtype y_dtype;         /* dtype of y                                            */
+  const void* x;                /* [B, L, D]                                             */
+  const void* dt_raw;           /* [B, L, D]  step size before bias and softplus          */
+  const void* Bm;               /* [B, L, N]  selective input vector B_t                  */
+  const void* Cm;               /* [B, L, N]  selective output vector C_t                 */
+  const int32_t* idx;           /* [B, L, k]  routing, 0 <= idx < E                       */
+  const float* gate;            /* [B, L, k]  routing weights                             */
+  const float* A;               /* [E, D, N]  per-expert diagonal transition (< 0)        */
+  const float* dt_bias;         /* [E, D]                                                 */
+  const float* Dskip;           /* [E, D]     per-expert feed-through D                   */
+  const float* h0;              /* NULL = zeros; [B, D, N] (separate: [B, E, D, N])       */
+  void* y;                      /* [B, L, D]  out                                         */
+  float* h_final;               /* NULL = not written; [B, D, N] (separate: [B, E, D, N]) */
+  int chunk;                    /* tokens per chunk; 0 = library's choice                 */
+  swimba_carry carry;           /* chunk join method                                      */
+  hipEvent_t* phase_events;     /* NULL, or 4 events recorded on `stream`: before the
+                                   chunk pass, before the carry pass, before the fix-up
+                                   pass, after the fix-up pass (timing only)              */
+} swimba_scan_args;
+
+/*
+ * swimba_scan_workspace_size -- bytes of device workspace the scan needs for
+ * these arguments (0 when the sequence is one chunk).  `separate` selects
+ * swimba_scan_separate's layout.  Returns 0 as well for invalid arguments;
+ * the scan call itself reports those.
+ */
+size_t swimba_scan_workspace_size(const swimba_scan_args* a, int separate);
+
+/*
+ * swimba_scan -- the parameter-space-mixed selective scan: one state
+ * trajectory per (b, d), the selected experts' A, dt_bias and Dskip mixed by
+ * the gates at every token ([SW] "Kernmechanisme van Swimba"; Theorem 1; [MB]
+ * "Mamba": exp(Delta A) transition, Figure 2 on-chip state).
+ *   ws, ws_bytes: device workspace of at least swimba_scan_workspace_size(a,0)
+ *   bytes, 256-byte aligned; its contents on entry do not matter.
+ * Constraints: B, L >= 0; D >= 1; N == 16; 1 <= k <= E <= 64; chunk >= 0.
+ * L == 0 writes h_final = h0 (or zeros).
+ */
+int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * swimba_scan_separate -- the separate design ([SW] "MoE of separate SSMs"):
+ * one state per expert (h0/h_final [B, E, D, N]); each selected expert
+ * advances with its own parameters; y = sum_j g_j y_j.  An expert listed
+ * twice for one token advances twice.  Same constraints as swimba_scan, plus
+ * E <= 16.
+ */
+int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+typedef struct {
+  int B, D, N, E, k;
+  swimba_dtype in_dtype, y_dtype;
+  const void* x;                /* [B, D]                                        */
+  const void* dt_raw;           /* [B, D]                                        */
+  const void* Bm;               /* [B, N]                                        */
+  const void* Cm;               /* [B, N]                                        */
+  const float* Wr;              /* [D, E]: route this token when idx == NULL     */
+  const int32_t* idx;           /* NULL, or forced routing [B, k]                */
+  const float* gate;            /* [B, k] with idx                               */
+  int32_t* idx_out;             /* NULL, or [B, k]: routing used                 */
+  float* gate_out;              /* NULL, or [B, k]                               */
+  const float* A;               /* [E, D, N]                                     */
+  const float* dt_bias;         /* [E, D]                                        */
+  const float* Dskip;           /* [E, D]                                        */
+  float* state;                 /* [B, D, N] fp32, read and updated in place     */
+  void* y;                      /* [B, D] out                                    */
+} swimba_step_args;
+
+/*
+ * swimba_step -- one decoding step of the mixed scan on a persistent state
+ * ([MB] Figure 2: the state persists and is updated once per token): route
+ * (unless forced), mix, discretise, update `state` in place and emit y.
+ * Equal to swimba_scan over a length-1 sequence with h0 = h_final = state.
+ * Constraints: B >= 0, D >= 1, N == 16, 1 <= k <= E <= 64; Wr or idx/gate.
+ */
+int swimba_step(const swimba_step_args* a, hipStream_t stream);
+
+/* Static string for a status code. */
+const char* swimba_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIMBA_H */

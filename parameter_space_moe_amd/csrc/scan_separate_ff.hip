@@ -1,0 +1,8 @@
+// Instantiations of the separate design for x/dt_raw/B/C in float and y in float.
+#include "scan_separate.hpp"
+
+namespace swimba {
+int launch_sep_ff(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
+  return sep::launch_sep_e<float, float>(a, pl, ws, st);
+}
+}  // namespace swimba

@@ -1,0 +1,206 @@
+// C ABI of libswimba.so: argument validation, chunk planning and dispatch.
+// No allocation, no synchronisation; every error is reported before launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "swimba.h"
+#include "swimba_internal.hpp"
+
+namespace swimba {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0 = not yet queried
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool dtype_ok(swimba_dtype d) { return d == SWIMBA_F32 || d == SWIMBA_BF16; }
+
+// Sizes and options only (enough for the workspace query).
+int validate_scan(const swimba_scan_args* a, int separate) {
+  if (a == nullptr) return SWIMBA_EINVAL;
+  if (a->B < 0 || a->L < 0 || a->D < 1 || a->N < 1 || a->E < 1 || a->k < 1 || a->k > a->E ||
+      a->chunk < 0)
+    return SWIMBA_EINVAL;
+  if (!dtype_ok(a->in_dtype) || !dtype_ok(a->y_dtype)) return SWIMBA_EINVAL;
+  if (a->carry != SWIMBA_CARRY_AUTO && a->carry != SWIMBA_CARRY_REWALK &&
+      a->carry != SWIMBA_CARRY_FIXUP)
+    return SWIMBA_EINVAL;
+  if (a->N != SWIMBA_STATE_N) return SWIMBA_EUNSUPPORTED;
+  if (a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
+  if (separate && a->E > 16) return SWIMBA_EUNSUPPORTED;
+  // the mixed scan stages E tables of 4.5 KiB (plus per-wave sums) in LDS
+  if (!separate && a->E > 16) return SWIMBA_EUNSUPPORTED;
+  return SWIMBA_OK;
+}
+
+// Pointers the launch will dereference.
+int validate_scan_pointers(const swimba_scan_args* a) {
+  if (a->A == nullptr || a->dt_bias == nullptr || a->Dskip == nullptr) return SWIMBA_EINVAL;
+  if (a->B > 0 && a->L > 0) {
+    if (a->x == nullptr || a->dt_raw == nullptr || a->Bm == nullptr || a->Cm == nullptr ||
+        a->idx == nullptr || a->gate == nullptr || a->y == nullptr)
+      return SWIMBA_EINVAL;
+  }
+  return SWIMBA_OK;
+}
+
+}  // namespace
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = g_cus[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    g_cus[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p) {
+  int rc = validate_scan(a, separate);
+  if (rc != SWIMBA_OK) return rc;
+  *p = ScanPlan();
+  p->ntiles = (a->D + 63) / 64;
+  p->waves = (!separate && a->E > 8) ? 8 : 4;
+  if (a->L == 0 || a->B == 0) {
+    p->chunk = 0;
+    p->nchunks = 0;
+    return SWIMBA_OK;
+  }
+  int chunk = a->chunk;
+  if (chunk == 0) {
+    // Aim for about four resident waves per SIMD (16 per CU) from the
+    // independent (b, tile) recurrences, then cut sequences into chunks no
+    // shorter than a few fix-up horizons.
+    const long long cus = device_cus();
+    const long long target = 16 * cus / (separate ? 2 : 1);
+    const long long base = (long long)a->B * p->ntiles;
+    long long want = (target + base - 1) / base;
+    const int min_chunk = separate ? 256 : 128;
+    long long maxc = (a->L + min_chunk - 1) / min_chunk;
+    if (want > maxc) want = maxc;
+    if (want < 1) want = 1;
+    chunk = (int)((a->L + want - 1) / want);
+  }
+  if (chunk > a->L) chunk = a->L;
+  p->chunk = chunk;
+  p->nchunks = (int)(((long long)a->L + chunk - 1) / chunk);
+  if (p->nchunks > 1) {
+    const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N : SWIMBA_STATE_N;
+    const size_t arr = (size_t)a->B * p->nchunks * rows * a->D * sizeof(float);
+    p->off_P = 0;
+    p->off_H = align256(arr);
+    p->off_flags = p->off_H + align256(arr);
+    p->bytes = p->off_flags + align256((size_t)a->B * p->nchunks * p->ntiles * sizeof(int32_t));
+  }
+  return SWIMBA_OK;
+}
+
+namespace {
+
+__global__ void fill_initial_state(const float* h0, float* h, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) h[i] = h0 ? h0[i] : 0.f;
+}
+
+int empty_sequence(const swimba_scan_args* a, int separate, hipStream_t s) {
+  if (a->h_final == nullptr || a->B == 0) return SWIMBA_OK;
+  const size_t n = (size_t)a->B * (separate ? a->E : 1) * a->D * SWIMBA_STATE_N;
+  hipLaunchKernelGGL(fill_initial_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     a->h0, a->h_final, n);
+  return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
+}
+
+int run_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t s, int separate) {
+  ScanPlan p;
+  int rc = plan_scan(a, separate, &p);
+  if (rc != SWIMBA_OK) return rc;
+  rc = validate_scan_pointers(a);
+  if (rc != SWIMBA_OK) return rc;
+  if (p.bytes > 0) {
+    if (ws == nullptr || ws_bytes < p.bytes || (reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+      return SWIMBA_EWORKSPACE;
+  }
+  if (a->B == 0 || a->L == 0) {
+    if (a->phase_events)
+      for (int i = 0; i < 4; ++i) (void)hipEventRecord(a->phase_events[i], s);
+    return empty_sequence(a, separate, s);
+  }
+  return separate ? launch_scan_separate(a, p, ws, s) : launch_scan(a, p, ws, s);
+}
+
+}  // namespace
+}  // namespace swimba
+
+using namespace swimba;
+
+extern "C" {
+
+int swimba_route(const void* x, swimba_dtype x_dtype, const float* Wr, int64_t T, int D, int E,
+                 int k, int32_t* idx, float* gate, hipStream_t stream) {
+  if (T < 0 || D < 1 || E < 1 || k < 1 || k > E || !dtype_ok(x_dtype)) return SWIMBA_EINVAL;
+  if (E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
+  if (T == 0) return SWIMBA_OK;
+  if (x == nullptr || Wr == nullptr || idx == nullptr || gate == nullptr) return SWIMBA_EINVAL;
+  return launch_route(x, x_dtype, Wr, T, D, E, k, idx, gate, stream);
+}
+
+size_t swimba_scan_workspace_size(const swimba_scan_args* a, int separate) {
+  ScanPlan p;
+  if (plan_scan(a, separate ? 1 : 0, &p) != SWIMBA_OK) return 0;
+  return p.bytes;
+}
+
+int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_scan(a, ws, ws_bytes, stream, 0);
+}
+
+int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  return run_scan(a, ws, ws_bytes, stream, 1);
+}
+
+int swimba_step(const swimba_step_args* a, hipStream_t stream) {
+  if (a == nullptr) return SWIMBA_EINVAL;
+  if (a->B < 0 || a->D < 1 || a->N < 1 || a->E < 1 || a->k < 1 || a->k > a->E)
+    return SWIMBA_EINVAL;
+  if (!dtype_ok(a->in_dtype) || !dtype_ok(a->y_dtype)) return SWIMBA_EINVAL;
+  if (a->N != SWIMBA_STATE_N || a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
+  if (a->B == 0) return SWIMBA_OK;
+  if (a->x == nullptr || a->dt_raw == nullptr || a->Bm == nullptr || a->Cm == nullptr ||
+      a->A == nullptr || a->dt_bias == nullptr || a->Dskip == nullptr || a->state == nullptr ||
+      a->y == nullptr)
+    return SWIMBA_EINVAL;
+  if (a->idx == nullptr && a->Wr == nullptr) return SWIMBA_EINVAL;
+  if (a->idx != nullptr && a->gate == nullptr) return SWIMBA_EINVAL;
+  // state and A are read as 16-byte vectors
+  if ((reinterpret_cast<uintptr_t>(a->state) & 15) || (reinterpret_cast<uintptr_t>(a->A) & 15))
+    return SWIMBA_EINVAL;
+  return launch_step(a, stream);
+}
+
+const char* swimba_status_string(int status) {
+  switch (status) {
+    case SWIMBA_OK:
+      return "ok";
+    case SWIMBA_EINVAL:
+      return "invalid argument";
+    case SWIMBA_EUNSUPPORTED:
+      return "unsupported configuration";
+    case SWIMBA_EWORKSPACE:
+      return "workspace too small or not 256-byte aligned";
+    case SWIMBA_EHIP:
+      return "HIP launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Device-side helpers shared by the Swimba kernels (gfx950 / CDNA4).
+//
+// Transcendentals use the hardware's own base-2 instructions (v_exp_f32,
+// v_log_f32, about 1 ulp); natural-base constants are folded in by the
+// callers so that every exponential in a hot loop is a single v_exp_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swimba {
+
+constexpr int kN = 16;          // state entries per channel (the only size built)
+constexpr int kWave = 64;       // CDNA wavefront
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+using bf16_t = uint16_t;        // raw bfloat16 bits
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
+  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// softplus(z) = max(z, 0) + ln(1 + exp(-|z|)), in two hardware transcendentals.
+__device__ __forceinline__ float softplus_f32(float z) {
+  float e = hw_exp2(-fabsf(z) * kLog2e);
+  return fmaxf(z, 0.0f) + hw_log2(1.0f + e) * kLn2;
+}
+
+// Wave-uniform value into an SGPR (the argument must already be uniform).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+}  // namespace swimba

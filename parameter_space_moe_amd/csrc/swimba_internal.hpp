@@ -1,0 +1,48 @@
+// Host-side launch interfaces between the C ABI (swimba_api.cpp) and the
+// kernels.  Nothing here is exported.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "swimba.h"
+
+namespace swimba {
+
+// Chunk plan of one scan call.
+struct ScanPlan {
+  int ntiles = 0;       // 64-channel tiles: ceil(D / 64)
+  int chunk = 0;        // tokens per chunk
+  int nchunks = 0;      // ceil(L / chunk); <= 1 means a single pass
+  int waves = 4;        // waves per workgroup (chunks sharing one table)
+  size_t off_P = 0, off_H = 0, off_flags = 0, bytes = 0;  // workspace layout
+};
+
+// Fills `p` for these arguments; returns a status.  Pure host arithmetic.
+int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p);
+
+// Kernel launchers (validated arguments only).
+int launch_route(const void* x, swimba_dtype xd, const float* Wr, int64_t T, int D, int E,
+                 int k, int32_t* idx, float* gate, hipStream_t s);
+int launch_scan(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
+int launch_scan_separate(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
+int launch_step(const swimba_step_args* a, hipStream_t s);
+// Pass 2 of the chunked scans: carried-in state per chunk (rows = 16 or E*16).
+int launch_carry(int B, int C, int D, int E, const float* P, float* H, float* h_final,
+                 int separate, hipStream_t st);
+
+// Compute units of the current device (cached per device).
+int device_cus();
+
+// Kernels that stage more than 64 KiB of dynamic LDS must say so before launch
+// (gfx950 has 160 KiB per CU).
+template <typename Kernel>
+inline void allow_dynamic_lds(Kernel kernel, size_t bytes) {
+  if (bytes > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace swimba

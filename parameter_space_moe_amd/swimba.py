@@ -1,0 +1,267 @@
+"""Python binding of libswimba.so: the same entry points as include/swimba.h,
+taking torch tensors.  Argument marshalling only -- every step of the
+computation runs in the HIP kernels; torch provides device memory and the
+current stream.  There is no fallback: without the built library every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswimba.so")
+
+F32, BF16 = 0, 1
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+CARRY = {"auto": 0, "rewalk": 1, "fixup": 2}
+N_STATE = 16
+
+_vp = ctypes.c_void_p
+_ci = ctypes.c_int
+
+
+class ScanArgs(ctypes.Structure):
+    _fields_ = [("B", _ci), ("L", _ci), ("D", _ci), ("N", _ci), ("E", _ci), ("k", _ci),
+                ("in_dtype", _ci), ("y_dtype", _ci),
+                ("x", _vp), ("dt_raw", _vp), ("Bm", _vp), ("Cm", _vp),
+                ("idx", _vp), ("gate", _vp), ("A", _vp), ("dt_bias", _vp), ("Dskip", _vp),
+                ("h0", _vp), ("y", _vp), ("h_final", _vp),
+                ("chunk", _ci), ("carry", _ci), ("phase_events", _vp)]
+
+
+class StepArgs(ctypes.Structure):
+    _fields_ = [("B", _ci), ("D", _ci), ("N", _ci), ("E", _ci), ("k", _ci),
+                ("in_dtype", _ci), ("y_dtype", _ci),
+                ("x", _vp), ("dt_raw", _vp), ("Bm", _vp), ("Cm", _vp),
+                ("Wr", _vp), ("idx", _vp), ("gate", _vp), ("idx_out", _vp), ("gate_out", _vp),
+                ("A", _vp), ("dt_bias", _vp), ("Dskip", _vp), ("state", _vp), ("y", _vp)]
+
+
+class SwimbaError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libswimba.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    so = path or LIB_PATH
+    if not os.path.exists(so):
+        raise ImportError("libswimba.so is not built (%s); run __graft_entry__.build() or "
+                          "python parameter_space_moe_amd/build.py" % so)
+    lib = ctypes.CDLL(so)
+    lib.swimba_route.argtypes = [_vp, _ci, _vp, ctypes.c_int64, _ci, _ci, _ci, _vp, _vp, _vp]
+    lib.swimba_route.restype = _ci
+    lib.swimba_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs), _ci]
+    lib.swimba_scan_workspace_size.restype = ctypes.c_size_t
+    for fn in (lib.swimba_scan, lib.swimba_scan_separate):
+        fn.argtypes = [ctypes.POINTER(ScanArgs), _vp, ctypes.c_size_t, _vp]
+        fn.restype = _ci
+    lib.swimba_step.argtypes = [ctypes.POINTER(StepArgs), _vp]
+    lib.swimba_step.restype = _ci
+    lib.swimba_status_string.argtypes = [_ci]
+    lib.swimba_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().swimba_status_string(status).decode()
+
+
+def _check(fn, rc):
+    if rc != OK:
+        raise SwimbaError(fn, rc)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("expected float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def route(x: torch.Tensor, Wr: torch.Tensor, k: int, idx=None, gate=None, stream=None):
+    """Top-k router: x [..., D] (f32/bf16), Wr [D, E] f32 -> idx [..., k] int32,
+    gate [..., k] f32 (include/swimba.h: swimba_route)."""
+    _need(x, "x")
+    D = x.shape[-1]
+    E = Wr.shape[1] if Wr.dim() == 2 else -1
+    _need(Wr, "Wr", (D, E), torch.float32, x.device)
+    T = x.numel() // D if D else 0
+    lead = tuple(x.shape[:-1])
+    if idx is None:
+        idx = torch.empty(lead + (k,), dtype=torch.int32, device=x.device)
+    if gate is None:
+        gate = torch.empty(lead + (k,), dtype=torch.float32, device=x.device)
+    _need(idx, "idx", lead + (k,), torch.int32, x.device)
+    _need(gate, "gate", lead + (k,), torch.float32, x.device)
+    rc = load().swimba_route(_ptr(x), _dt(x), _ptr(Wr), T, D, E, k, _ptr(idx), _ptr(gate),
+                             _stream(stream))
+    _check("swimba_route", rc)
+    return idx, gate
+
+
+def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, chunk, carry,
+               separate, phase_events):
+    _need(x, "x")
+    if x.dim() != 3:
+        raise ValueError("x must be [B, L, D]")
+    B, L, D = x.shape
+    E = A.shape[0]
+    N = A.shape[2] if A.dim() == 3 else -1
+    k = idx.shape[2] if idx.dim() == 3 else -1
+    dev = x.device
+    _need(dt_raw, "dt_raw", (B, L, D), x.dtype, dev)
+    _need(Bm, "Bm", (B, L, N), x.dtype, dev)
+    _need(Cm, "Cm", (B, L, N), x.dtype, dev)
+    _need(idx, "idx", (B, L, k), torch.int32, dev)
+    _need(gate, "gate", (B, L, k), torch.float32, dev)
+    _need(A, "A", (E, D, N), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (E, D), torch.float32, dev)
+    _need(Dskip, "Dskip", (E, D), torch.float32, dev)
+    sshape = (B, E, D, N) if separate else (B, D, N)
+    if h0 is not None:
+        _need(h0, "h0", sshape, torch.float32, dev)
+    _need(y, "y", (B, L, D), None, dev)
+    if h_final is not None:
+        _need(h_final, "h_final", sshape, torch.float32, dev)
+    a = ScanArgs()
+    a.B, a.L, a.D, a.N, a.E, a.k = B, L, D, N, E, k
+    a.in_dtype, a.y_dtype = _dt(x), _dt(y)
+    a.x, a.dt_raw, a.Bm, a.Cm = _ptr(x), _ptr(dt_raw), _ptr(Bm), _ptr(Cm)
+    a.idx, a.gate, a.A, a.dt_bias, a.Dskip = _ptr(idx), _ptr(gate), _ptr(A), _ptr(dt_bias), \
+        _ptr(Dskip)
+    a.h0, a.y, a.h_final = _ptr(h0), _ptr(y), _ptr(h_final)
+    a.chunk = int(chunk)
+    a.carry = CARRY[carry] if isinstance(carry, str) else int(carry)
+    a.phase_events = phase_events
+    return a
+
+
+def workspace_size(args: ScanArgs, separate: bool) -> int:
+    return int(load().swimba_scan_workspace_size(ctypes.byref(args), 1 if separate else 0))
+
+
+def _scan(separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, y=None,
+          h_final=None, y_dtype=None, want_state=True, chunk=0, carry="auto", workspace=None,
+          stream=None, phase_events=None):
+    if y is None:
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
+    if h_final is None and want_state:
+        E = A.shape[0]
+        shape = (x.shape[0], E, x.shape[2], N_STATE) if separate else \
+            (x.shape[0], x.shape[2], N_STATE)
+        h_final = torch.empty(shape, dtype=torch.float32, device=x.device)
+    a = _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, chunk, carry,
+                   separate, phase_events)
+    lib = load()
+    need = workspace_size(a, separate)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    fn = lib.swimba_scan_separate if separate else lib.swimba_scan
+    rc = fn(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("swimba_scan_separate" if separate else "swimba_scan", rc)
+    return y, h_final
+
+
+def scan(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
+    """Parameter-space-mixed scan (include/swimba.h: swimba_scan).  Returns
+    (y [B,L,D], h_final [B,D,16] or None)."""
+    return _scan(False, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
+
+
+def scan_separate(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
+    """Separate design (include/swimba.h: swimba_scan_separate).  Returns
+    (y [B,L,D], h_final [B,E,D,16] or None)."""
+    return _scan(True, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
+
+
+def scan_workspace_bytes(x, A, idx, separate=False, chunk=0, y_dtype=None):
+    """Workspace bytes swimba_scan(_separate) needs for these shapes."""
+    B, L, D = x.shape
+    a = ScanArgs()
+    a.B, a.L, a.D, a.N, a.E, a.k = B, L, D, A.shape[2], A.shape[0], idx.shape[2]
+    a.in_dtype = _dt(x)
+    a.y_dtype = a.in_dtype if y_dtype is None else (BF16 if y_dtype == torch.bfloat16 else F32)
+    a.chunk = chunk
+    return workspace_size(a, separate)
+
+
+def step(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None, gate=None,
+         y=None, idx_out=None, gate_out=None, y_dtype=None, stream=None):
+    """One decode step (include/swimba.h: swimba_step).  x, dt_raw [B,D];
+    Bm, Cm [B,16]; state [B,D,16] f32 updated in place.  Routing from Wr [D,E]
+    with top-k, or forced idx/gate [B,k].  Returns y [B,D]."""
+    _need(x, "x")
+    B, D = x.shape
+    E, N = A.shape[0], A.shape[2]
+    dev = x.device
+    _need(dt_raw, "dt_raw", (B, D), x.dtype, dev)
+    _need(Bm, "Bm", (B, N), x.dtype, dev)
+    _need(Cm, "Cm", (B, N), x.dtype, dev)
+    _need(A, "A", (E, D, N), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (E, D), torch.float32, dev)
+    _need(Dskip, "Dskip", (E, D), torch.float32, dev)
+    _need(state, "state", (B, D, N), torch.float32, dev)
+    if idx is not None:
+        k = idx.shape[1]
+        _need(idx, "idx", (B, k), torch.int32, dev)
+        _need(gate, "gate", (B, k), torch.float32, dev)
+    else:
+        if Wr is None or k is None:
+            raise ValueError("step needs Wr and k, or idx and gate")
+        _need(Wr, "Wr", (D, E), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, D), dtype=y_dtype or x.dtype, device=dev)
+    _need(y, "y", (B, D), None, dev)
+    if idx_out is not None:
+        _need(idx_out, "idx_out", (B, k), torch.int32, dev)
+    if gate_out is not None:
+        _need(gate_out, "gate_out", (B, k), torch.float32, dev)
+    a = StepArgs()
+    a.B, a.D, a.N, a.E, a.k = B, D, N, E, k
+    a.in_dtype, a.y_dtype = _dt(x), _dt(y)
+    a.x, a.dt_raw, a.Bm, a.Cm = _ptr(x), _ptr(dt_raw), _ptr(Bm), _ptr(Cm)
+    a.Wr, a.idx, a.gate = _ptr(Wr), _ptr(idx), _ptr(gate)
+    a.idx_out, a.gate_out = _ptr(idx_out), _ptr(gate_out)
+    a.A, a.dt_bias, a.Dskip, a.state, a.y = _ptr(A), _ptr(dt_bias), _ptr(Dskip), _ptr(state), \
+        _ptr(y)
+    rc = load().swimba_step(ctypes.byref(a), _stream(stream))
+    _check("swimba_step", rc)
+    return y

@@ -1,0 +1,158 @@
+"""The C ABI on the CPU: the library loads, exports what include/swimba.h
+declares, the ctypes mirrors match the C structs, and invalid arguments are
+rejected before anything is launched (no GPU work is started here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from parameter_space_moe_amd import swimba as sw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swimba.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swimba_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sw.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert {"swimba_route", "swimba_scan", "swimba_scan_separate", "swimba_step",
+            "swimba_scan_workspace_size", "swimba_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_exports_nothing_but_the_abi():
+    out = subprocess.run(["nm", "-D", "--defined-only", sw.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    ours = {n for n in exported if n.startswith("swimba_")}
+    assert ours == set(header_functions())
+
+
+LAYOUT_SRC = r"""
+#include <cstddef>
+#include <cstdio>
+#include "swimba.h"
+#define F(S, m) std::printf(#S " " #m " %zu\n", offsetof(S, m));
+int main() {
+  std::printf("swimba_scan_args sizeof %zu\n", sizeof(swimba_scan_args));
+  std::printf("swimba_step_args sizeof %zu\n", sizeof(swimba_step_args));
+  %FIELDS%
+  return 0;
+}
+"""
+
+
+def test_ctypes_structs_match_header(tmp_path):
+    lines = []
+    for cname, cls in (("swimba_scan_args", sw.ScanArgs), ("swimba_step_args", sw.StepArgs)):
+        for f, _ in cls._fields_:
+            lines.append("F(%s, %s)" % (cname, f))
+    src = tmp_path / "layout.cpp"
+    src.write_text(LAYOUT_SRC.replace("%FIELDS%", "\n  ".join(lines)))
+    exe = tmp_path / "layout"
+    subprocess.run(["g++", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-I" + os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    got = {}
+    for l in out.splitlines():
+        s, m, v = l.split()
+        got[(s, m)] = int(v)
+    assert got[("swimba_scan_args", "sizeof")] == ctypes.sizeof(sw.ScanArgs)
+    assert got[("swimba_step_args", "sizeof")] == ctypes.sizeof(sw.StepArgs)
+    for cname, cls in (("swimba_scan_args", sw.ScanArgs), ("swimba_step_args", sw.StepArgs)):
+        for f, _ in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
+
+
+def scan_args(**kw):
+    a = sw.ScanArgs()
+    a.B, a.L, a.D, a.N, a.E, a.k = 1, 1024, 128, 16, 4, 2
+    a.in_dtype, a.y_dtype = sw.BF16, sw.BF16
+    fake = 0x100000  # never dereferenced: every call below fails validation first
+    for f in ("x", "dt_raw", "Bm", "Cm", "idx", "gate", "A", "dt_bias", "Dskip", "y"):
+        setattr(a, f, fake)
+    a.chunk = 0
+    a.carry = 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k", 0, sw.EINVAL), ("k", 5, sw.EINVAL), ("E", 0, sw.EINVAL), ("D", 0, sw.EINVAL),
+    ("B", -1, sw.EINVAL), ("L", -1, sw.EINVAL), ("chunk", -1, sw.EINVAL), ("carry", 7, sw.EINVAL),
+    ("in_dtype", 5, sw.EINVAL), ("N", 8, sw.EUNSUPPORTED), ("E", 65, sw.EUNSUPPORTED),
+    ("E", 17, sw.EUNSUPPORTED), ("x", None, sw.EINVAL), ("A", None, sw.EINVAL),
+    ("idx", None, sw.EINVAL),
+])
+def test_scan_rejects(lib, field, value, status):
+    a = scan_args(**{field: value})
+    assert lib.swimba_scan(ctypes.byref(a), None, 0, None) == status
+
+
+def test_separate_rejects_many_experts(lib):
+    a = scan_args(E=17)
+    assert lib.swimba_scan_separate(ctypes.byref(a), None, 0, None) == sw.EUNSUPPORTED
+
+
+def test_workspace_checked_before_launch(lib):
+    a = scan_args(chunk=256)
+    need = lib.swimba_scan_workspace_size(ctypes.byref(a), 0)
+    assert need > 0
+    assert lib.swimba_scan(ctypes.byref(a), None, 0, None) == sw.EWORKSPACE
+    assert lib.swimba_scan(ctypes.byref(a), 0x100000, need - 1, None) == sw.EWORKSPACE
+    assert lib.swimba_scan(ctypes.byref(a), 0x100010, need, None) == sw.EWORKSPACE  # unaligned
+
+
+def test_workspace_size_layout(lib):
+    # long-context workload with chunk 256: 256 chunks x 16 states x 2560 channels, two
+    # fp32 arrays (decays, states) and one int32 flag per (chunk, 64-channel tile)
+    a = scan_args(B=1, L=65536, D=2560, E=16, k=2, chunk=256)
+    arr = 256 * 16 * 2560 * 4
+    flags = 256 * 40 * 4
+    assert lib.swimba_scan_workspace_size(ctypes.byref(a), 0) == 2 * arr + flags
+    sep = 256 * 16 * 16 * 2560 * 4
+    assert lib.swimba_scan_workspace_size(ctypes.byref(a), 1) == 2 * sep + flags
+    # one chunk: no workspace
+    a = scan_args(L=100, chunk=100)
+    assert lib.swimba_scan_workspace_size(ctypes.byref(a), 0) == 0
+    # the query reads sizes only
+    a = scan_args(chunk=256, x=None, A=None)
+    assert lib.swimba_scan_workspace_size(ctypes.byref(a), 0) > 0
+
+
+def test_route_and_step_reject(lib):
+    assert lib.swimba_route(0x100000, sw.BF16, 0x100000, 10, 64, 4, 5, 0x100000, 0x100000,
+                            None) == sw.EINVAL
+    assert lib.swimba_route(0x100000, sw.BF16, 0x100000, 10, 64, 65, 2, 0x100000, 0x100000,
+                            None) == sw.EUNSUPPORTED
+    assert lib.swimba_route(None, sw.BF16, None, 0, 64, 4, 2, None, None, None) == sw.OK  # T = 0
+    s = sw.StepArgs()
+    s.B, s.D, s.N, s.E, s.k = 4, 128, 16, 8, 2
+    s.in_dtype = s.y_dtype = sw.BF16
+    for f in ("x", "dt_raw", "Bm", "Cm", "A", "dt_bias", "Dskip", "state", "y"):
+        setattr(s, f, 0x100000)
+    assert lib.swimba_step(ctypes.byref(s), None) == sw.EINVAL          # neither Wr nor idx
+    s.Wr = 0x100000
+    s.state = 0x100004
+    assert lib.swimba_step(ctypes.byref(s), None) == sw.EINVAL          # unaligned state
+    s.N = 8
+    assert lib.swimba_step(ctypes.byref(s), None) == sw.EUNSUPPORTED
+
+
+def test_status_strings(lib):
+    for st in (sw.OK, sw.EINVAL, sw.EUNSUPPORTED, sw.EWORKSPACE, sw.EHIP, 123):
+        assert isinstance(sw.status_string(st), str) and sw.status_string(st)

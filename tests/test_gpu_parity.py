@@ -1,0 +1,460 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Bars: router idx bit-exact wherever the fp32 ranking is certain (certified
+near-ties may order either way, and must be consistent with the tolerance);
+gates within the bound implied by the logit error; y and final state within
+rel 1e-4 (fp32 inputs) or 2e-3 (bf16 inputs, fp32 accumulation), bf16 y
+faithfully rounded.  The scan comparisons feed the GPU router's idx/gate to
+the oracle so that they do not depend on router rounding.  Full-size
+workloads run in the launch configuration the benchmark times and are
+compared on sampled channels (every (b, d) recurrence is independent)."""
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (TOL_BF16, TOL_F32, assert_faithful_bf16, check_route, dev_tensors,
+                         gate_bound, host, rel_err, route_tolerance)
+from parameter_space_moe_amd import swimba, workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@functools.lru_cache(maxsize=2)
+def workload(name):
+    w = workloads.BY_NAME[name]
+    inp = workloads.generate(w)
+    return w, inp, dev_tensors(inp, w.dtype, DEV)
+
+
+def small_case(B, L, D, N=16, E=4, k=2, dtype="f32", seed=0, h0=False):
+    w = workloads.Workload("case", B=B, L=L, D=D, N=N, E=E, k=k, dtype=dtype, seed=seed)
+    inp = workloads.generate(w)
+    if h0:
+        rng = np.random.default_rng(seed + 100)
+        inp["h0"] = rng.standard_normal((B, D, N)).astype(np.float32)
+    return w, inp, dev_tensors(inp, dtype, DEV)
+
+
+def route_on_gpu(t, w):
+    idx, gate = swimba.route(t["x"], t["Wr"], w.k)
+    return idx, gate
+
+
+def scan_args(t, idx, gate):
+    return (t["x"], t["dt_raw"], t["Bm"], t["Cm"], idx, gate, t["A"], t["dt_bias"], t["Dskip"])
+
+
+def oracle_scan(inp, idx, gate, dsel=None, h0=None, separate=False):
+    """Oracle on all channels or on the channel subset `dsel`."""
+    idx = host(idx).astype(np.int32) if isinstance(idx, torch.Tensor) else idx
+    gate = host(gate) if isinstance(gate, torch.Tensor) else gate
+    sl = slice(None) if dsel is None else dsel
+    args = (inp["x"][:, :, sl], inp["dt_raw"][:, :, sl], inp["Bm"], inp["Cm"], idx, gate,
+            inp["A"][:, sl], inp["dt_bias"][:, sl], inp["Dskip"][:, sl])
+    if h0 is not None:
+        h0 = h0[:, :, sl] if separate else h0[:, sl]
+    fn = oracle.scan_separate if separate else oracle.scan
+    return fn(*args, h0=h0)
+
+
+def tol_for(w):
+    return TOL_F32 if w.dtype == "f32" else TOL_BF16
+
+
+# ---------------------------------------------------------------- router
+@pytest.mark.parametrize("name", ["tiny", "mamba130m_layer", "mamba1p4b_layer", "long_context"])
+def test_route_workload(name):
+    w, inp, t = workload(name)
+    idx, gate = route_on_gpu(t, w)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy().reshape(-1, w.k)
+    gg = gate.cpu().numpy().reshape(-1, w.k).astype(np.float64)
+    T = gi.shape[0]
+    # properties of every token at full size
+    assert gi.min() >= 0 and gi.max() < w.E
+    assert np.all(np.sort(gi, axis=1)[:, 1:] != np.sort(gi, axis=1)[:, :-1]) if w.k > 1 else True
+    assert np.all(gg > 0) and np.max(np.abs(gg.sum(1) - 1)) < 1e-6
+    assert np.all(np.diff(gg, axis=1) <= 1e-7)
+    # oracle on sampled tokens
+    rng = np.random.default_rng(7)
+    sel = np.arange(T) if T <= 4096 else np.sort(rng.choice(T, 4096, replace=False))
+    xs = inp["x"].reshape(T, w.D)[sel]
+    ridx, rgate, logits, absdot = oracle.route(xs, inp["Wr"], w.k)
+    per_piece = 64 if w.dtype == "bf16" else 32
+    tol = route_tolerance(absdot, w.D, per_piece)
+    ties = check_route(gi[sel], logits, tol, w.k)
+    same = np.all(gi[sel] == ridx, axis=1)
+    gerr = np.abs(gg[sel] - rgate)
+    assert np.all(gerr[same] <= gate_bound(ridx, tol)[same]), float(gerr[same].max())
+    assert np.median(gerr[same]) < 1e-6
+    assert ties <= max(2, len(sel) // 200), ties
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,E,k", [(100, 1, 1), (100, 3, 2), (96, 5, 5), (64, 17, 3),
+                                   (72, 64, 4), (1, 8, 2), (513, 16, 16)])
+def test_route_shapes(dtype, D, E, k):
+    """Ragged D (scalar staging path), E not a kernel width, the wide-E path,
+    k = E, D = 1, and a token count that is not a multiple of 64."""
+    w, inp, t = small_case(B=3, L=45, D=D, E=E, k=k, dtype=dtype, seed=D + E)
+    idx, gate = route_on_gpu(t, w)
+    gi = idx.cpu().numpy().reshape(-1, k)
+    gg = gate.cpu().numpy().reshape(-1, k).astype(np.float64)
+    ridx, rgate, logits, absdot = oracle.route(inp["x"].reshape(-1, D), inp["Wr"], k)
+    tol = route_tolerance(absdot, D, 64 if dtype == "bf16" else 32)
+    check_route(gi, logits, tol, k)
+    same = np.all(gi == ridx, axis=1)
+    assert np.all(np.abs(gg - rgate)[same] <= gate_bound(ridx, tol)[same])
+
+
+def test_route_exact_ties_prefer_lower_expert():
+    w, inp, t = small_case(B=1, L=200, D=64, E=6, k=3, dtype="bf16", seed=3)
+    Wr = inp["Wr"].copy()
+    Wr[:, 4] = Wr[:, 1]
+    Wr[:, 5] = Wr[:, 2]
+    idx, gate = swimba.route(t["x"], torch.from_numpy(Wr).to(DEV), 3)
+    ridx, _, logits, _ = oracle.route(inp["x"].reshape(-1, 64), Wr, 3)
+    gi = idx.cpu().numpy().reshape(-1, 3)
+    for tk in range(gi.shape[0]):
+        s = list(gi[tk])
+        for a, b in ((1, 4), (2, 5)):
+            if a in s and b in s:
+                assert s.index(a) < s.index(b)
+
+
+def test_route_empty():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    Wr = torch.zeros((64, 4), dtype=torch.float32, device=DEV)
+    idx, gate = swimba.route(x, Wr, 2)
+    assert idx.shape == (0, 2)
+
+
+# ------------------------------------------------------------- mixed scan
+@pytest.mark.parametrize("carry", ["fixup", "rewalk"])
+@pytest.mark.parametrize("chunk", [0, 16, 64, 100, 256])
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_scan_tiny(chunk, carry, with_h0):
+    w, inp, t = workload("tiny")
+    idx, gate = route_on_gpu(t, w)
+    h0 = np.random.default_rng(5).standard_normal((w.B, w.D, 16)).astype(np.float32) \
+        if with_h0 else None
+    y, hf = swimba.scan(*scan_args(t, idx, gate), h0=None if h0 is None else
+                        torch.from_numpy(h0).to(DEV), chunk=chunk, carry=carry)
+    ry, rh = oracle_scan(inp, idx, gate, h0=h0)
+    assert rel_err(host(y), ry) < TOL_F32, rel_err(host(y), ry)
+    assert rel_err(host(hf), rh) < TOL_F32, rel_err(host(hf), rh)
+
+
+@pytest.mark.parametrize("chunk", [0, 77, 128, 700])
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+def test_scan_ragged_bf16(chunk, ydt):
+    """Several 64-channel tiles plus a ragged tail (D = 200), several chunks
+    plus a ragged last chunk, an initial state."""
+    w, inp, t = small_case(B=2, L=700, D=200, E=8, k=2, dtype="bf16", seed=11, h0=True)
+    idx, gate = route_on_gpu(t, w)
+    ydtype = torch.float32 if ydt == "f32" else torch.bfloat16
+    y, hf = swimba.scan(*scan_args(t, idx, gate), h0=t["h0"], chunk=chunk, y_dtype=ydtype)
+    ry, rh = oracle_scan(inp, idx, gate, h0=inp["h0"])
+    if ydt == "f32":
+        assert rel_err(host(y), ry) < TOL_BF16
+    else:
+        assert_faithful_bf16(y, ry, "y")
+    assert rel_err(host(hf), rh) < TOL_BF16
+
+
+@pytest.mark.parametrize("name", ["mamba130m_layer", "mamba1p4b_layer", "long_context"])
+def test_scan_workload_sampled(name):
+    """Full-size workload in the benchmark's launch configuration (chunk 0 =
+    the library's plan, 256 for the long context); sampled channels checked
+    against the oracle, bf16 y faithfully rounded and fp32 y within 2e-3."""
+    w, inp, t = workload(name)
+    idx, gate = route_on_gpu(t, w)
+    rng = np.random.default_rng(1)
+    dsel = np.sort(rng.choice(w.D, 24, replace=False))
+    ry, rh = oracle_scan(inp, idx, gate, dsel=dsel)
+    for ydtype in (torch.bfloat16, torch.float32):
+        y, hf = swimba.scan(*scan_args(t, idx, gate), chunk=w.chunk, y_dtype=ydtype)
+        ys = y[:, :, torch.from_numpy(dsel).to(DEV)]
+        if ydtype == torch.float32:
+            assert rel_err(host(ys), ry) < TOL_BF16, rel_err(host(ys), ry)
+        else:
+            assert_faithful_bf16(ys, ry, name)
+        assert rel_err(host(hf)[:, dsel], rh) < TOL_BF16, rel_err(host(hf)[:, dsel], rh)
+        del y, hf
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (8, 3), (8, 8), (16, 2), (16, 5), (2, 2)])
+def test_scan_expert_counts(E, k):
+    """Dense E = 1, runtime-k kernels (k = 3, 5, 8), the 8-wave workgroup for E > 8."""
+    w, inp, t = small_case(B=2, L=300, D=130, E=E, k=k, dtype="f32", seed=E * 10 + k)
+    idx, gate = route_on_gpu(t, w)
+    for chunk in (0, 64):
+        y, hf = swimba.scan(*scan_args(t, idx, gate), chunk=chunk)
+        ry, rh = oracle_scan(inp, idx, gate)
+        assert rel_err(host(y), ry) < TOL_F32, (chunk, rel_err(host(y), ry))
+        assert rel_err(host(hf), rh) < TOL_F32
+
+
+def test_scan_degenerate_shapes():
+    # L = 0: h_final = h0 (or zeros)
+    w, inp, t = small_case(B=2, L=0, D=70, E=4, k=2, h0=True)
+    idx = torch.zeros((2, 0, 2), dtype=torch.int32, device=DEV)
+    gate = torch.zeros((2, 0, 2), dtype=torch.float32, device=DEV)
+    y, hf = swimba.scan(*scan_args(t, idx, gate), h0=t["h0"])
+    assert torch.equal(hf, t["h0"])
+    y, hf = swimba.scan(*scan_args(t, idx, gate))
+    assert torch.count_nonzero(hf) == 0
+    # L = 1, D = 1
+    for (B, L, D) in ((1, 1, 64), (3, 5, 1), (1, 130, 1)):
+        w, inp, t = small_case(B=B, L=L, D=D, E=3, k=2, seed=B + L + D)
+        idx, gate = route_on_gpu(t, w)
+        for chunk in (0, 2):
+            y, hf = swimba.scan(*scan_args(t, idx, gate), chunk=chunk)
+            ry, rh = oracle_scan(inp, idx, gate)
+            assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
+
+
+def test_scan_chunking_and_carry_agree():
+    """Chunk size and the carry method change rounding only."""
+    w, inp, t = small_case(B=1, L=2048, D=128, E=8, k=2, dtype="bf16", seed=21)
+    idx, gate = route_on_gpu(t, w)
+    ref, rh = oracle_scan(inp, idx, gate)
+    outs = []
+    for chunk in (0, 32, 256, 2048):
+        for carry in ("fixup", "rewalk"):
+            y, hf = swimba.scan(*scan_args(t, idx, gate), chunk=chunk, carry=carry,
+                                y_dtype=torch.float32)
+            assert rel_err(host(y), ref) < TOL_BF16
+            outs.append(host(y))
+    for o in outs[1:]:
+        assert rel_err(o, outs[0]) < 1e-4
+
+
+def test_scan_deterministic():
+    w, inp, t = workload("mamba130m_layer")
+    idx, gate = route_on_gpu(t, w)
+    y1, h1 = swimba.scan(*scan_args(t, idx, gate))
+    y2, h2 = swimba.scan(*scan_args(t, idx, gate))
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    i2, g2 = route_on_gpu(t, w)
+    assert torch.equal(idx, i2) and torch.equal(gate, g2)
+
+
+def test_scan_split_composition():
+    w, inp, t = small_case(B=2, L=1000, D=96, E=4, k=2, dtype="bf16", seed=31)
+    idx, gate = route_on_gpu(t, w)
+    y, hf = swimba.scan(*scan_args(t, idx, gate), y_dtype=torch.float32)
+    cut = 377
+    a1 = [v[:, :cut].contiguous() for v in scan_args(t, idx, gate)[:6]] + list(
+        scan_args(t, idx, gate)[6:])
+    a2 = [v[:, cut:].contiguous() for v in scan_args(t, idx, gate)[:6]] + list(
+        scan_args(t, idx, gate)[6:])
+    y1, h1 = swimba.scan(*a1, y_dtype=torch.float32)
+    y2, h2 = swimba.scan(*a2, h0=h1, y_dtype=torch.float32)
+    assert rel_err(host(torch.cat([y1, y2], 1)), host(y)) < 1e-4
+    assert rel_err(host(h2), host(hf)) < 1e-4
+
+
+def test_scan_constant_inputs_closed_form_at_length():
+    """L = 65536 with constant inputs and routing: every chunk boundary of the
+    carry is pinned by h_t = b (1 - a^t) / (1 - a) without the oracle.  Slow
+    decay (1 - a ~ 1e-3) keeps the carry significant across all 256 chunks."""
+    B, L, D, N, E, k = 1, 65536, 64, 16, 2, 2
+    rng = np.random.default_rng(41)
+    xv = rng.uniform(0.5, 1.0, D).astype(np.float32)
+    rv = np.full(D, -6.0, np.float32)                       # Delta ~ 2.5e-3
+    Bv = rng.uniform(0.5, 1.0, N).astype(np.float32)
+    Cv = rng.uniform(-1.0, 1.0, N).astype(np.float32)
+    A = -rng.uniform(0.3, 0.6, (E, D, N)).astype(np.float32)
+    bias = np.zeros((E, D), np.float32)
+    Dsk = rng.standard_normal((E, D)).astype(np.float32)
+    g = np.array([0.7, 0.3], np.float32)
+    x = torch.from_numpy(np.broadcast_to(xv, (B, L, D)).copy()).to(DEV)
+    dt = torch.from_numpy(np.broadcast_to(rv, (B, L, D)).copy()).to(DEV)
+    Bm = torch.from_numpy(np.broadcast_to(Bv, (B, L, N)).copy()).to(DEV)
+    Cm = torch.from_numpy(np.broadcast_to(Cv, (B, L, N)).copy()).to(DEV)
+    idx = torch.from_numpy(np.broadcast_to(np.array([0, 1], np.int32), (B, L, k)).copy()).to(DEV)
+    gate = torch.from_numpy(np.broadcast_to(g, (B, L, k)).copy()).to(DEV)
+    y, hf = swimba.scan(x, dt, Bm, Cm, idx, gate, torch.from_numpy(A).to(DEV),
+                        torch.from_numpy(bias).to(DEV), torch.from_numpy(Dsk).to(DEV), chunk=256)
+    Dt = np.log1p(np.exp(rv.astype(np.float64)))
+    a = np.exp(Dt[:, None] * (g[0] * A[0].astype(np.float64) + g[1] * A[1]))  # [D, N]
+    b = Dt[:, None] * Bv[None].astype(np.float64) * xv[:, None]
+    ts = np.array([1, 255, 256, 257, 4096, 30000, 65535, 65536])
+    h = b[None] * (1 - a[None] ** ts[:, None, None]) / (1 - a[None])        # [T, D, N]
+    want = h @ Cv.astype(np.float64) + (g[0] * Dsk[0] + g[1] * Dsk[1]) * xv
+    got = host(y)[0, ts - 1]
+    # relative error of (1 - a) in fp32 is ~ 2^-24 / (Delta |Abar|) ~ 1e-4 here
+    assert rel_err(got, want) < 2e-3, rel_err(got, want)
+    assert rel_err(host(hf)[0], h[-1]) < 2e-3
+
+
+def test_scan_noncontractive_falls_back_to_rewalk():
+    """A > 0 somewhere (no contraction): the fix-up may not stop early; the
+    kernels detect it and recompute whole chunks, still matching the oracle."""
+    w, inp, t = small_case(B=1, L=600, D=64, E=4, k=2, dtype="f32", seed=51)
+    A = inp["A"].copy()
+    A[2, :, 3] = 0.02
+    inp["A"] = A
+    t["A"] = torch.from_numpy(A).to(DEV)
+    idx, gate = route_on_gpu(t, w)
+    y, hf = swimba.scan(*scan_args(t, idx, gate), chunk=64)
+    ry, rh = oracle_scan(inp, idx, gate)
+    assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
+
+
+# --------------------------------------------------------------- separate
+@pytest.mark.parametrize("chunk", [0, 32, 100, 256])
+def test_separate_tiny(chunk):
+    w, inp, t = workload("tiny")
+    idx, gate = route_on_gpu(t, w)
+    y, hf = swimba.scan_separate(*scan_args(t, idx, gate), chunk=chunk)
+    ry, rh = oracle_scan(inp, idx, gate, separate=True)
+    assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (4, 4), (16, 2), (3, 1)])
+@pytest.mark.parametrize("chunk", [0, 96])
+def test_separate_bf16(E, k, chunk):
+    w, inp, t = small_case(B=2, L=500, D=136, E=E, k=k, dtype="bf16", seed=E + k)
+    rng = np.random.default_rng(9)
+    H0 = rng.standard_normal((2, E, 136, 16)).astype(np.float32)
+    idx, gate = route_on_gpu(t, w)
+    y, hf = swimba.scan_separate(*scan_args(t, idx, gate), h0=torch.from_numpy(H0).to(DEV),
+                                 chunk=chunk, y_dtype=torch.float32)
+    ry, rh = oracle_scan(inp, idx, gate, h0=H0, separate=True)
+    assert rel_err(host(y), ry) < TOL_BF16 and rel_err(host(hf), rh) < TOL_BF16
+
+
+def test_separate_workload_sampled():
+    w, inp, t = workload("mamba1p4b_layer")
+    idx, gate = route_on_gpu(t, w)
+    dsel = np.sort(np.random.default_rng(2).choice(w.D, 16, replace=False))
+    ry, rh = oracle_scan(inp, idx, gate, dsel=dsel, separate=True)
+    y, hf = swimba.scan_separate(*scan_args(t, idx, gate))
+    assert_faithful_bf16(y[:, :, torch.from_numpy(dsel).to(DEV)], ry, "separate y")
+    assert rel_err(host(hf)[:, :, dsel], rh) < TOL_BF16
+
+
+def test_separate_constant_top1_equals_mixed():
+    w, inp, t = small_case(B=1, L=400, D=64, E=4, k=1, dtype="f32", seed=61)
+    idx = torch.full((1, 400, 1), 2, dtype=torch.int32, device=DEV)
+    gate = torch.ones((1, 400, 1), dtype=torch.float32, device=DEV)
+    ym, hm = swimba.scan(*scan_args(t, idx, gate), chunk=64)
+    ys, hs = swimba.scan_separate(*scan_args(t, idx, gate), chunk=64)
+    assert rel_err(host(ys), host(ym)) < 1e-5
+    assert rel_err(host(hs)[:, 2], host(hm)) < 1e-5
+    assert torch.count_nonzero(hs[:, [0, 1, 3]]) == 0
+
+
+# ------------------------------------------------------------------ step
+def step_tensors(s, dtype):
+    return dev_tensors(s, dtype, DEV)
+
+
+def test_step_decode_workload():
+    """Decode workload (B 256, D 5120, E 8, top-2): 8 routed steps, all
+    channels, against the oracle's step fed with the GPU's routing."""
+    w = workloads.BY_NAME["decode"]
+    p, steps = workloads.decode_steps(w, steps=8)
+    tp = dev_tensors(p, "f32", DEV)
+    state = torch.zeros((w.B, w.D, 16), dtype=torch.float32, device=DEV)
+    rstate = np.zeros((w.B, w.D, 16))
+    idx_out = torch.empty((w.B, w.k), dtype=torch.int32, device=DEV)
+    gate_out = torch.empty((w.B, w.k), dtype=torch.float32, device=DEV)
+    for s in steps:
+        ts = step_tensors(s, w.dtype)
+        y = swimba.step(ts["x"], ts["dt_raw"], ts["Bm"], ts["Cm"], tp["A"], tp["dt_bias"],
+                        tp["Dskip"], state, Wr=tp["Wr"], k=w.k, idx_out=idx_out,
+                        gate_out=gate_out, y_dtype=torch.float32)
+        gi = idx_out.cpu().numpy()
+        ridx, rgate, logits, absdot = oracle.route(s["x"], p["Wr"], w.k)
+        check_route(gi, logits, route_tolerance(absdot, w.D, 64), w.k)
+        ry, _, _ = oracle.step(s["x"], s["dt_raw"], s["Bm"], s["Cm"], p["A"], p["dt_bias"],
+                               p["Dskip"], rstate, idx=gi, gate=host(gate_out))
+        assert rel_err(host(y), ry) < TOL_BF16
+    assert rel_err(host(state), rstate) < TOL_BF16
+
+
+def test_step_128_steps_sampled_and_resume():
+    """128 steps on the decode workload: sampled channels against the oracle,
+    and a state saved to the host at step 64 and restored into a fresh buffer
+    continues bit-identically."""
+    w = workloads.BY_NAME["decode"]
+    p, steps = workloads.decode_steps(w)
+    tp = dev_tensors(p, "f32", DEV)
+    dsel = np.sort(np.random.default_rng(3).choice(w.D, 32, replace=False))
+    dsel_t = torch.from_numpy(dsel).to(DEV)
+    state = torch.zeros((w.B, w.D, 16), dtype=torch.float32, device=DEV)
+    rstate = np.zeros((w.B, len(dsel), 16))
+    Ap, bp, Dp = p["A"][:, dsel], p["dt_bias"][:, dsel], p["Dskip"][:, dsel]
+    idx_out = torch.empty((w.B, w.k), dtype=torch.int32, device=DEV)
+    gate_out = torch.empty((w.B, w.k), dtype=torch.float32, device=DEV)
+    saved = None
+    ys = []
+    all_steps = list(steps)
+    for i, s in enumerate(all_steps):
+        ts = step_tensors(s, w.dtype)
+        y = swimba.step(ts["x"], ts["dt_raw"], ts["Bm"], ts["Cm"], tp["A"], tp["dt_bias"],
+                        tp["Dskip"], state, Wr=tp["Wr"], k=w.k, idx_out=idx_out,
+                        gate_out=gate_out, y_dtype=torch.float32)
+        ys.append(y.clone())
+        ry, _, _ = oracle.step(s["x"][:, dsel], s["dt_raw"][:, dsel], s["Bm"], s["Cm"], Ap, bp,
+                               Dp, rstate, idx=idx_out.cpu().numpy(), gate=host(gate_out))
+        assert rel_err(host(y[:, dsel_t]), ry) < TOL_BF16, i
+        if i == 63:
+            saved = state.cpu().clone()
+    assert rel_err(host(state)[:, dsel], rstate) < TOL_BF16
+    final = state.clone()
+    # resume from the host copy taken after step 64
+    state2 = torch.empty_like(state)
+    state2.copy_(saved.to(DEV))
+    for i, s in enumerate(all_steps[64:]):
+        ts = step_tensors(s, w.dtype)
+        y = swimba.step(ts["x"], ts["dt_raw"], ts["Bm"], ts["Cm"], tp["A"], tp["dt_bias"],
+                        tp["Dskip"], state2, Wr=tp["Wr"], k=w.k, y_dtype=torch.float32)
+        assert torch.equal(y, ys[64 + i])
+    assert torch.equal(state2, final)
+
+
+def test_steps_equal_scan():
+    """128 forced-routing steps on a carried state equal one scan of L = 128."""
+    w, inp, t = small_case(B=4, L=128, D=200, E=8, k=2, dtype="bf16", seed=71, h0=True)
+    idx, gate = route_on_gpu(t, w)
+    y, hf = swimba.scan(*scan_args(t, idx, gate), h0=t["h0"], y_dtype=torch.float32)
+    state = t["h0"].clone()
+    for s in range(128):
+        ys = swimba.step(t["x"][:, s].contiguous(), t["dt_raw"][:, s].contiguous(),
+                         t["Bm"][:, s].contiguous(), t["Cm"][:, s].contiguous(), t["A"],
+                         t["dt_bias"], t["Dskip"], state, idx=idx[:, s].contiguous(),
+                         gate=gate[:, s].contiguous(), y_dtype=torch.float32)
+        assert rel_err(host(ys), host(y[:, s])) < 1e-4, s
+    assert rel_err(host(state), host(hf)) < 1e-4
+
+
+@pytest.mark.parametrize("B,D,E,k,dtype", [(1, 100, 4, 2, "f32"), (3, 64, 1, 1, "bf16"),
+                                           (5, 333, 16, 3, "bf16"), (2, 7, 64, 2, "f32")])
+def test_step_shapes(B, D, E, k, dtype):
+    w, inp, t = small_case(B=B, L=1, D=D, E=E, k=k, dtype=dtype, seed=B * D, h0=True)
+    state = t["h0"].clone()
+    rstate = inp["h0"].astype(np.float64).copy()
+    idx_out = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    gate_out = torch.empty((B, k), dtype=torch.float32, device=DEV)
+    y = swimba.step(t["x"][:, 0].contiguous(), t["dt_raw"][:, 0].contiguous(),
+                    t["Bm"][:, 0].contiguous(), t["Cm"][:, 0].contiguous(), t["A"], t["dt_bias"],
+                    t["Dskip"], state, Wr=t["Wr"], k=k, idx_out=idx_out, gate_out=gate_out,
+                    y_dtype=torch.float32)
+    ridx, rgate, logits, absdot = oracle.route(inp["x"][:, 0], inp["Wr"], k)
+    check_route(idx_out.cpu().numpy(), logits, route_tolerance(absdot, D, 64), k)
+    ry, _, _ = oracle.step(inp["x"][:, 0], inp["dt_raw"][:, 0], inp["Bm"][:, 0], inp["Cm"][:, 0],
+                           inp["A"], inp["dt_bias"], inp["Dskip"], rstate,
+                           idx=idx_out.cpu().numpy(), gate=host(gate_out))
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert rel_err(host(y), ry) < tol and rel_err(host(state), rstate) < tol
