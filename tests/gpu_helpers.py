@@ -62,13 +62,22 @@ def bf16_rne(v: np.ndarray) -> np.ndarray:
     return t.float().numpy().astype(np.float64)
 
 
-def assert_faithful_bf16(got_bf16: torch.Tensor, ref: np.ndarray, what=""):
-    """Every bf16 output lies within one bf16 ulp of the rounded reference."""
+def assert_faithful_bf16(got_bf16: torch.Tensor, ref: np.ndarray, what="", tol=TOL_F32):
+    """bf16 outputs are faithful roundings of values within the fp32 bar of
+    the reference: |got - ref| <= ulp_bf16 + tol * max(|ref|, rms(ref)).  The
+    second term is the fp32 arithmetic's own error, which scales with the
+    signal (rms), not with an output that happens to lie near zero."""
     got = host(got_bf16)
-    r = bf16_rne(ref)
-    bad = np.abs(got - r) > bf16_ulp(r) * (1 + 1e-9)
-    assert not bad.any(), "%s: %d bf16 outputs off by more than one ulp (max %.3g)" % (
-        what, int(bad.sum()), float(np.max(np.abs(got - r))))
+    ref = np.asarray(ref, np.float64)
+    rms = math.sqrt(float(np.mean(ref * ref))) if ref.size else 1.0
+    allow = bf16_ulp(np.maximum(np.abs(got), np.abs(ref))) + \
+        tol * np.maximum(np.abs(ref), rms)
+    err = np.abs(got - ref)
+    bad = ~(err <= allow)
+    if bad.any():
+        i = np.argsort((err / allow).ravel())[::-1][:5]
+        raise AssertionError("%s: %d bf16 outputs outside the bar; worst (got, ref): %s" % (
+            what, int(bad.sum()), list(zip(got.ravel()[i].tolist(), ref.ravel()[i].tolist()))))
 
 
 def route_tolerance(absdot: np.ndarray, D: int, per_piece: int, waves: int = 4) -> np.ndarray:
