@@ -1,0 +1,312 @@
+"""Benchmark of the Swimba hot path on one MI355X.
+
+One step = one pass of the path over one batch of the workload: the router
+(logits, top-k, gates) and the parameter-space-mixed scan with its chunk carry,
+inputs resident in HBM.  Printed as one JSON line (rank 0):
+  value    = tokens x channels per second of the whole step (G tc/s)
+  roofline = the dominant kernel (the scan's chunk pass) against the VALU issue
+             ceiling that bounds it, with its HBM rate against 8 TB/s beside it
+  modes    = the separate design, the dense single-expert scan (E = 1), the
+             scan alone, and the decode step, for the "mixed vs separate" and
+             "mixed vs dense" ratios
+  cpu_baseline = the fp64 oracle timed on this host on the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, public peak
+# VALU ceiling: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz issue slots per second;
+# a slot is one fp32 FMA (2 flops).  Packed fp32 is not used by this build, so
+# the non-packed FMA rate is the ceiling: 78.6 TFLOP/s.
+VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
+N_STATE = 16
+
+
+def slots_per_tc(k: int) -> float:
+    """Minimum VALU issue slots per token x channel of the mixed scan on this
+    ISA (v_exp_f32 and v_log_f32 issue at half rate: 2 slots each).
+    Per state entry: k for the mixed exponent, 2 for exp2, 1 for Delta*x*B,
+    1 for the state update, 1 for the readout.  Per (token, channel): softplus
+    (2 transcendentals = 4 slots, 5 VALU), beta and delta (2k), Delta*g_j (k),
+    Delta*x, the D term, and x/dt_raw/y conversions (3)."""
+    return N_STATE * (k + 5) + (4 + 5 + 3 * k + 2 + 3)
+
+
+# --------------------------------------------------------------- HIP events
+class Hip:
+    """HIP events through the runtime's C API (timing on a given stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        v = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(v), a, b) == 0
+        return float(v.value)
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+SCAN_SOURCES = ["parameter_space_moe_amd/csrc/scan_mixed.hpp",
+                "parameter_space_moe_amd/csrc/swimba_device.hpp"]
+
+
+def load_traffic(workload):
+    """HBM bytes per chunk-pass launch measured by rocprofv3 counters, if the
+    committed measurement was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "scan_chunk_%s_traffic.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest(SCAN_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp):
+    """The fp64 oracle on this host: router + mixed scan over the same workload."""
+    import numpy as np
+
+    import oracle
+    T = w.B * w.L
+    x = inp["x"].astype(np.float64)
+    reps = []
+    t_end = time.perf_counter() + 10.0
+    while True:
+        t0 = time.perf_counter()
+        idx, gate, _, _ = oracle.route(x.reshape(T, w.D), inp["Wr"], w.k)
+        oracle.scan(x, inp["dt_raw"], inp["Bm"], inp["Cm"], idx.reshape(w.B, w.L, w.k),
+                    gate.reshape(w.B, w.L, w.k), inp["A"], inp["dt_bias"], inp["Dskip"])
+        reps.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(reps) >= 5:
+            break
+    best = sorted(reps)[len(reps) // 2]
+    return {"value": round(w.tc / best / 1e9, 5), "unit": "G token*channel/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "whole workload (router + mixed scan, %d x %d x %d), median of %d runs"
+                      % (w.B, w.L, w.D, len(reps))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mamba130m_layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="time only the step (for profiler runs)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the Swimba scan has no multi-GPU path in this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from parameter_space_moe_amd import swimba, workloads
+
+    w = workloads.BY_NAME[args.workload]
+    assert w.steps == 0, "decode workload is reported under modes"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = workloads.generate(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def to(name, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(inp[name]))
+        return t.to(dtype).to(dev) if dtype is not None else t.to(dev)
+
+    x, dtr, Bm, Cm = to("x", dt), to("dt_raw", dt), to("Bm", dt), to("Cm", dt)
+    Wr, A, bias, Dsk = to("Wr"), to("A"), to("dt_bias"), to("Dskip")
+    B, L, D, E, k = w.B, w.L, w.D, w.E, w.k
+    idx = torch.empty((B, L, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((B, L, k), dtype=torch.float32, device=dev)
+    y = torch.empty((B, L, D), dtype=dt, device=dev)
+    hf = torch.empty((B, D, N_STATE), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = Hip()
+    K, W = args.steps, args.warmup
+    # marshalled once; the timed loop goes straight to the C ABI
+    route_call = swimba.PreparedRoute(x, Wr, k, idx, gate)
+    scan_call = swimba.PreparedScan(False, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y=y,
+                                    h_final=hf, chunk=w.chunk)
+    chunk_len, plan_chunks = swimba.scan_plan(x, A, idx, chunk=w.chunk)
+
+    # ------------------------------------------------------- the timed step
+    ev = [[hip.event() for _ in range(5)] for _ in range(K)]
+    ev_arrays = [(ctypes.c_void_p * 4)(e[1].value, e[2].value, e[3].value, e[4].value)
+                 for e in ev]
+
+    def step(i=None):
+        if i is None:
+            route_call()
+            scan_call()
+            return
+        hip.record(ev[i][0], stream)
+        route_call()
+        scan_call(ctypes.addressof(ev_arrays[i]))
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+    route_ms = sum(hip.ms(e[0], e[1]) for e in ev) / K
+    chunk_ms = sum(hip.ms(e[1], e[2]) for e in ev) / K
+    carry_ms = sum(hip.ms(e[2], e[3]) for e in ev) / K
+    fixup_ms = sum(hip.ms(e[3], e[4]) for e in ev) / K
+    scan_ms = chunk_ms + carry_ms + fixup_ms
+    tc = w.tc
+    value = tc / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the chunk pass.  Algorithmic bytes per launch: x, dt_raw
+    # read and y written once (2 B each in bf16), B_t, C_t, idx, gate per token,
+    # and the chunk records (decay and end state, fp32 x 16 per chunk/channel).
+    esz = 2 if w.dtype == "bf16" else 4
+    chunk_bytes = tc * 3 * esz + B * L * (2 * N_STATE * esz + 2 * k * 4)
+    if plan_chunks > 1:
+        chunk_bytes += 2 * B * plan_chunks * N_STATE * D * 4
+    achieved_gbs = chunk_bytes / (chunk_ms * 1e-3) / 1e9
+    flops = tc * slots_per_tc(k) * 2
+    achieved_tf = flops / (chunk_ms * 1e-3) / 1e12
+    traffic = load_traffic(w.name)
+
+    out = {
+        "metric": "scan throughput (G token*channel/s) + % of HBM roofline, mixed vs separate",
+        "value": round(value, 3), "unit": "G token*channel/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "L": L, "D": D, "N": N_STATE, "E": E, "k": k,
+                   "chunk": chunk_len, "chunks": plan_chunks, "parallelism": "single-gpu"},
+        "roofline": {"bound": "alu", "kernel": "mix_chunk_kernel",
+                     "achieved": round(achieved_tf, 3), "peak": round(VALU_PEAK_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved_tf / VALU_PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "note": "VALU issue slots as FMA-equivalent flops, %d slots/tc"
+                             % slots_per_tc(k)},
+        "roofline_hbm": {"bound": "hbm", "kernel": "mix_chunk_kernel",
+                         "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                         "step_frac": round(tc * 3 * esz / (ms_per_step * 1e-3) / 1e9
+                                            / HBM_PEAK_GBS, 4)},
+        "kernels_ms": {"route": round(route_ms, 4), "chunk_pass": round(chunk_ms, 4),
+                       "carry": round(carry_ms, 4), "fixup": round(fixup_ms, 4)},
+    }
+
+    if not args.no_modes:
+        out["modes"] = modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx,
+                             gate, y, hf)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+
+
+def _time(fn, reps, warm=2):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / reps
+
+
+def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gate, y, hf):
+    import numpy as np
+    import torch
+    dev = x.device
+    reps = max(5, args.steps // 2)
+    tc = w.tc
+    res = {}
+    # mixed scan alone (routing precomputed)
+    mixed = swimba.PreparedScan(False, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y=y, h_final=hf,
+                                chunk=w.chunk)
+    ms_mixed = _time(mixed, reps)
+    res["mixed_scan"] = {"ms": round(ms_mixed, 4), "G_tc_per_s": round(tc / ms_mixed / 1e6, 3)}
+    # separate design: route + per-expert scans
+    hfs = torch.empty((w.B, w.E, w.D, N_STATE), dtype=torch.float32, device=dev)
+    sep = swimba.PreparedScan(True, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y=y, h_final=hfs,
+                              chunk=w.chunk)
+    ms_sep = _time(sep, reps)
+    res["separate_scan"] = {"ms": round(ms_sep, 4), "G_tc_per_s": round(tc / ms_sep / 1e6, 3),
+                            "separate_over_mixed": round(ms_sep / ms_mixed, 3)}
+    del hfs, sep
+    # dense single-expert scan (E = 1): the plain Mamba scan on the same shapes
+    idx1 = torch.zeros((w.B, w.L, 1), dtype=torch.int32, device=dev)
+    gate1 = torch.ones((w.B, w.L, 1), dtype=torch.float32, device=dev)
+    A1, b1, D1 = A[:1].contiguous(), bias[:1].contiguous(), Dsk[:1].contiguous()
+    dense = swimba.PreparedScan(False, x, dtr, Bm, Cm, idx1, gate1, A1, b1, D1, y=y, h_final=hf,
+                                chunk=w.chunk)
+    ms_dense = _time(dense, reps)
+    res["dense_scan"] = {"ms": round(ms_dense, 4), "G_tc_per_s": round(tc / ms_dense / 1e6, 3),
+                         "mixed_over_dense": round(ms_mixed / ms_dense, 3)}
+    # decode workload: 128 routed steps on a persistent fp32 state
+    wd = workloads.BY_NAME["decode"]
+    p, steps = workloads.decode_steps(wd)
+    dd = torch.bfloat16 if wd.dtype == "bf16" else torch.float32
+    P = {kk: torch.from_numpy(v).to(dev) for kk, v in p.items()}
+    S = [{kk: torch.from_numpy(np.ascontiguousarray(v)).to(dd).to(dev) for kk, v in s.items()}
+         for s in steps]
+    state = torch.zeros((wd.B, wd.D, N_STATE), dtype=torch.float32, device=dev)
+    yd = torch.empty((wd.B, wd.D), dtype=dd, device=dev)
+
+    def run_decode():
+        for s in S:
+            swimba.step(s["x"], s["dt_raw"], s["Bm"], s["Cm"], P["A"], P["dt_bias"],
+                        P["Dskip"], state, Wr=P["Wr"], k=wd.k, y=yd)
+
+    ms_dec = _time(run_decode, 2, warm=1)
+    esz = 2 if wd.dtype == "bf16" else 4
+    per_step_bytes = wd.B * wd.D * (2 * N_STATE * 4 + 3 * esz)
+    gbs = per_step_bytes * len(S) / (ms_dec * 1e-3) / 1e9
+    res["decode"] = {"workload": wd.name, "steps": len(S), "ms": round(ms_dec, 4),
+                     "us_per_step": round(ms_dec * 1e3 / len(S), 2),
+                     "G_channel_steps_per_s": round(wd.B * wd.D * len(S) / ms_dec / 1e6, 3),
+                     "hbm_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "note": "state (84 MB) fits the 256 MB Infinity Cache in steady state"}
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -29,8 +29,9 @@
  *   - Every tensor argument is a DEVICE pointer owned by the caller, dense and
  *     row-major (last index fastest), and must stay valid until the work
  *     enqueued on `stream` has finished.  The library allocates no memory,
- *     keeps no global state and never synchronises the stream; calls on
- *     different streams may run concurrently.
+ *     keeps no state beyond a per-device cache of the compute-unit count, and
+ *     never synchronises the stream; calls on different streams may run
+ *     concurrently.
  *   - Work is enqueued on `stream` (NULL = the null stream).  A return of
  *     SWIMBA_OK means the kernels were launched; execution errors surface in
  *     later HIP calls on that stream.
@@ -97,8 +98,8 @@ typedef struct {
   swimba_dtype y_dtype;         /* dtype of y                                            */
   const void* x;                /* [B, L, D]                                             */
   const void* dt_raw;           /* [B, L, D]  step size before bias and softplus          */
-  const void* Bm;               /* [B, L, N]  selective input vector B_t                  */
-  const void* Cm;               /* [B, L, N]  selective output vector C_t                 */
+  const void* Bm;               /* [B, L, N]  selective input vector B_t (16-byte aligned)  */
+  const void* Cm;               /* [B, L, N]  selective output vector C_t (16-byte aligned) */
   const int32_t* idx;           /* [B, L, k]  routing, 0 <= idx < E                       */
   const float* gate;            /* [B, L, k]  routing weights                             */
   const float* A;               /* [E, D, N]  per-expert diagonal transition (< 0)        */
@@ -123,14 +124,23 @@ typedef struct {
 size_t swimba_scan_workspace_size(const swimba_scan_args* a, int separate);
 
 /*
+ * swimba_scan_plan -- the chunking the scan will use for these arguments:
+ * tokens per chunk and number of chunks (both 0 when B or L is 0).  Reads
+ * sizes and options only; returns the status the scan's size validation
+ * would return.
+ */
+int swimba_scan_plan(const swimba_scan_args* a, int separate, int* chunk, int* nchunks);
+
+/*
  * swimba_scan -- the parameter-space-mixed selective scan: one state
  * trajectory per (b, d), the selected experts' A, dt_bias and Dskip mixed by
  * the gates at every token ([SW] "Kernmechanisme van Swimba"; Theorem 1; [MB]
  * "Mamba": exp(Delta A) transition, Figure 2 on-chip state).
  *   ws, ws_bytes: device workspace of at least swimba_scan_workspace_size(a,0)
  *   bytes, 256-byte aligned; its contents on entry do not matter.
- * Constraints: B, L >= 0; D >= 1; N == 16; 1 <= k <= E <= 64; chunk >= 0.
- * L == 0 writes h_final = h0 (or zeros).
+ * Constraints: B, L >= 0; D >= 1; N == 16; 1 <= k <= E <= 16 (the selected
+ * experts' tables are staged in LDS); chunk >= 0.  L == 0 writes h_final = h0
+ * (or zeros).
  */
 int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const TIn* __re
   constexpr int kUnroll = EC <= 16 ? 8 : 1;
   __shared__ __align__(16) unsigned char smem[kSmem];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
   unsigned char* tile = smem + wave * 64 * kRowBytes;
   const int npieces = (D + CH - 1) / CH;

@@ -40,6 +40,7 @@ namespace mixed {
 
 constexpr float kFixupTol = 5.9604645e-08f;  // 2^-24
 constexpr float kTiny = 1e-30f;
+constexpr int kTB = 8;  // tokens per staging block
 
 struct MixParams {
   int B, L, D, E, k;
@@ -62,28 +63,47 @@ struct MixParams {
   int32_t* flags;     // [B][C][ntiles] 1 = contraction not guaranteed
 };
 
-// LDS: table of the workgroup's 64 channels plus per-wave decay accumulators.
+// Per-wave LDS ring holding the wave-uniform data of two blocks of kTB tokens:
+// B_t and C_t as fp32 (32 floats per token), the selected experts and gates.
+struct Ring {
+  float* bc;    // [2][kTB][32]
+  int32_t* e;   // [2][kTB][k]
+  float* g;     // [2][kTB][k]
+};
+
+__host__ __device__ constexpr size_t ring_bytes(int k) {
+  return (size_t)2 * kTB * 32 * 4 + (size_t)2 * 2 * kTB * k * 4;
+}
+
+// LDS: the workgroup's expert table (64 channels), per-wave decay sums, and
+// per-wave staging rings.
 struct Smem {
   float4* A;   // [E][4][64]  A[e, d0+lane, 4q..4q+3]
   float2* BD;  // [E][64]     (dt_bias, Dskip)
-  float* U;    // [waves][E][64]
+  float* U;    // [waves][E][64] (chunk pass only)
+  Ring ring;   // this wave's ring
 };
 
-__device__ __forceinline__ Smem smem_layout(int E, bool with_table) {
+__device__ __forceinline__ Smem smem_layout(int E, int k, bool with_u, int waves, int wave) {
   extern __shared__ float4 smem_raw[];
   Smem s;
-  float4* p = smem_raw;
-  if (with_table) {
-    s.A = p;
-    p += E * 4 * 64;
-    s.BD = reinterpret_cast<float2*>(p);
-    p += E * 64 / 2;
-  } else {
-    s.A = nullptr;
-    s.BD = nullptr;
-  }
+  char* p = reinterpret_cast<char*>(smem_raw);
+  s.A = reinterpret_cast<float4*>(p);
+  p += (size_t)E * 4 * 64 * 16;
+  s.BD = reinterpret_cast<float2*>(p);
+  p += (size_t)E * 64 * 8;
   s.U = reinterpret_cast<float*>(p);
+  if (with_u) p += (size_t)waves * E * 64 * 4;
+  p += ring_bytes(k) * wave;
+  s.ring.bc = reinterpret_cast<float*>(p);
+  s.ring.e = reinterpret_cast<int32_t*>(p + 2 * kTB * 32 * 4);
+  s.ring.g = reinterpret_cast<float*>(p + 2 * kTB * 32 * 4 + 2 * kTB * k * 4);
   return s;
+}
+
+__host__ inline size_t smem_bytes(int E, int k, bool with_u, int waves) {
+  return (size_t)E * (4 * 64 * 16 + 64 * 8) + (with_u ? (size_t)waves * E * 64 * 4 : 0) +
+         ring_bytes(k) * waves;
 }
 
 // Stage the tile's expert parameters; returns 1 if any A in the tile is not
@@ -111,31 +131,108 @@ __device__ __forceinline__ int load_table(const MixParams& p, const Smem& s, int
   return bad;
 }
 
-// Routing slot j of token bt (wave-uniform), clamped into range.
-__device__ __forceinline__ int slot_expert(const MixParams& p, size_t bt, int j) {
-  int e = p.idx[bt * p.k + j];
-  e = e < 0 ? 0 : e;
-  return e >= p.E ? p.E - 1 : e;
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One token of the mixed recurrence for one lane.
+// Registers of one block's staging loads: a 16-byte piece of B_t or C_t per
+// lane, and up to KW routing words (idx, then gates).
+template <int KW>
+struct StageRegs {
+  uint4 piece;
+  int32_t word[KW];
+};
+
+// Issue the loads of tokens [tb, tb + n) of sequence row `row` (n >= 1).  The
+// loads are unconditional -- positions past the block's last token re-read
+// that token -- so no branch waits on them before the commit.
+template <typename TIn, int KW>
+__device__ __forceinline__ void stage_issue(const MixParams& p, size_t row, int tb, int n,
+                                            int k, int lane, StageRegs<KW>& r) {
+  constexpr int PPT = 16 * (int)sizeof(TIn) / 16;  // 16-byte pieces per token per vector
+  constexpr int NP = 2 * kTB * PPT;
+  const int q = lane < NP ? lane : NP - 1;
+  const int arr = q / (kTB * PPT), rr = q % (kTB * PPT), part = rr % PPT;
+  const int tok = min(rr / PPT, n - 1);
+  const TIn* base = reinterpret_cast<const TIn*>(arr ? p.Cm : p.Bm) + (row + tb) * kN;
+  const uint32_t o = (uint32_t)(tok * kN + part * (16 / (int)sizeof(TIn)));
+  r.piece = at32(reinterpret_cast<const uint4*>(base), o / (16 / (uint32_t)sizeof(TIn)));
+  const int nw = kTB * k;
+  const int32_t* ib = p.idx + (row + tb) * k;
+  const int32_t* gb = reinterpret_cast<const int32_t*>(p.gate) + (row + tb) * k;
+#pragma unroll
+  for (int i = 0; i < KW; ++i) {
+    int w = lane + 64 * i;
+    w = w < 2 * nw ? w : 2 * nw - 1;
+    const int arr2 = w / nw, r2 = w % nw;
+    const uint32_t at = (uint32_t)(min(r2 / k, n - 1) * k + r2 % k);
+    r.word[i] = arr2 ? at32(gb, at) : at32(ib, at);
+  }
+}
+
+// Convert the issued loads and write them to ring slot `slot`.
+template <typename TIn, int KW>
+__device__ __forceinline__ void stage_commit(const MixParams& p, const Ring& ring, int slot,
+                                             int n, int k, int lane, const StageRegs<KW>& r,
+                                             int& gate_bad) {
+  constexpr int PPT = 16 * (int)sizeof(TIn) / 16;
+  const int q = lane;
+  if (q < 2 * kTB * PPT) {
+    const int arr = q / (kTB * PPT), rr = q % (kTB * PPT), tok = rr / PPT, part = rr % PPT;
+    float* dst = ring.bc + (slot * kTB + tok) * 32 + arr * 16 + part * (16 / sizeof(TIn));
+    if (sizeof(TIn) == 2) {
+      const uint32_t w4[4] = {r.piece.x, r.piece.y, r.piece.z, r.piece.w};
+      float4 lo = make_float4(__uint_as_float(w4[0] << 16), __uint_as_float(w4[0] & 0xffff0000u),
+                              __uint_as_float(w4[1] << 16), __uint_as_float(w4[1] & 0xffff0000u));
+      float4 hi = make_float4(__uint_as_float(w4[2] << 16), __uint_as_float(w4[2] & 0xffff0000u),
+                              __uint_as_float(w4[3] << 16), __uint_as_float(w4[3] & 0xffff0000u));
+      reinterpret_cast<float4*>(dst)[0] = lo;
+      reinterpret_cast<float4*>(dst)[1] = hi;
+    } else {
+      *reinterpret_cast<float4*>(dst) =
+          make_float4(__uint_as_float(r.piece.x), __uint_as_float(r.piece.y),
+                      __uint_as_float(r.piece.z), __uint_as_float(r.piece.w));
+    }
+  }
+  const int nw = kTB * k;
+#pragma unroll
+  for (int i = 0; i < KW; ++i) {
+    const int w = lane + 64 * i;
+    if (w < 2 * nw) {
+      const int arr = w / nw, rr = w % nw, tok = rr / k;
+      if (arr == 0) {
+        int e = r.word[i];
+        e = e < 0 ? 0 : (e >= p.E ? p.E - 1 : e);
+        ring.e[slot * nw + rr] = e;
+      } else {
+        const float gv = __int_as_float(r.word[i]);
+        if (tok < n) gate_bad |= !(gv >= 0.f);
+        ring.g[slot * nw + rr] = gv;
+      }
+    }
+  }
+}
+
+// One token of the mixed recurrence for one lane.  Routing (experts e[j],
+// gates g[j], j < k) is wave-uniform; B_t/C_t come from ring slot `slot`,
+// position `i`.  Every LDS address below depends only on (e, lane), so all of
+// a token's reads can be in flight together.
 //   K > 0: k == K known at compile time; K == 0: runtime k.
 //   TRACK: also decay the carried part g (fix-up pass).
-//   ACC_U: accumulate gate-weighted Delta per expert (chunk pass).
-template <int K, typename TIn, bool TRACK, bool ACC_U>
+//   ACC_U: accumulate the gate-weighted Delta per expert (chunk pass).
+template <int K, bool TRACK, bool ACC_U>
 __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, float* U,
-                                           size_t bt, int lane, float xv, float rv, float* h,
-                                           float* g, int& gate_bad) {
+                                           const int* e, const float* gw, int slot, int i,
+                                           int lane, float xv, float rv, float* h, float* g) {
   const int k = K > 0 ? K : p.k;
   // mixed dt_bias and Dskip
   float beta = 0.f, delta = 0.f;
   auto bias_slot = [&](int j) {
-    const int e = slot_expert(p, bt, j);
-    const float gj = p.gate[bt * k + j];
-    gate_bad |= !(gj >= 0.f);
-    const float2 bd = s.BD[e * 64 + lane];
-    beta = fmaf(gj, bd.x, beta);
-    delta = fmaf(gj, bd.y, delta);
+    const float2 bd = s.BD[e[j] * 64 + lane];
+    beta = fmaf(gw[j], bd.x, beta);
+    delta = fmaf(gw[j], bd.y, delta);
   };
   if constexpr (K > 0) {
 #pragma unroll
@@ -150,12 +247,14 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
   for (int n = 0; n < kN; ++n) m[n] = 0.f;
   const float dl2 = dlt * kLog2e;
   auto a_slot = [&](int j) {
-    const int e = slot_expert(p, bt, j);
-    const float u = dl2 * p.gate[bt * k + j];
-    if (ACC_U) atomicAdd(&U[e * 64 + lane], u);
+    const float u = dl2 * gw[j];
+    // each lane owns its column of U, so a plain read-modify-write suffices
+    // (LDS atomics cost far more on this path); LDS operations of one wave
+    // complete in order, so repeated experts within a token still add up
+    if (ACC_U) U[e[j] * 64 + lane] += u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 a = s.A[(e * 4 + q) * 64 + lane];
+      const float4 a = s.A[(e[j] * 4 + q) * 64 + lane];
       if (K > 0 && j == 0) {
         m[4 * q + 0] = u * a.x;
         m[4 * q + 1] = u * a.y;
@@ -175,31 +274,158 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
   } else {
     for (int j = 0; j < k; ++j) a_slot(j);
   }
-  const TIn* Bp = reinterpret_cast<const TIn*>(p.Bm) + bt * kN;
-  const TIn* Cp = reinterpret_cast<const TIn*>(p.Cm) + bt * kN;
+  const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
   const float dx = dlt * xv;
   float yv = 0.f;
 #pragma unroll
-  for (int n = 0; n < kN; ++n) {
-    float a = hw_exp2(m[n]);
-    h[n] = fmaf(a, h[n], dx * to_f32(Bp[n]));
-    yv = fmaf(to_f32(Cp[n]), h[n], yv);
-    if (TRACK) g[n] *= a;
+  for (int q = 0; q < 4; ++q) {
+    const float4 b4 = bc[q], c4 = bc[4 + q];
+    const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = 4 * q + r;
+      const float a = hw_exp2(m[n]);
+      h[n] = fmaf(a, h[n], dx * bv[r]);
+      yv = fmaf(cv[r], h[n], yv);
+      if (TRACK) g[n] *= a;
+    }
   }
   return fmaf(delta, xv, yv);
+}
+
+// Walk tokens [t0, t1) of sequence b for one lane, staging each block of kTB
+// tokens' uniform data and x/dt_raw one block ahead.  With TRACK and
+// `truncate`, stops once the carried part g has decayed on every lane.
+// Addresses are a wave-uniform block base plus a 32-bit per-lane offset, and
+// the prefetch loads are unconditional (clamped to the chunk) so that nothing
+// waits on them until the block that uses them.
+template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U>
+__device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U, int b, int t0,
+                                     int t1, int d, bool active, bool full_tile, int lane,
+                                     bool truncate, float* h, float* g, int& gate_bad) {
+  constexpr int KW = (2 * kTB * (K > 0 ? K : 16) + 63) / 64;
+  const int k = K > 0 ? K : p.k;
+  const TIn* X = reinterpret_cast<const TIn*>(p.x);
+  const TIn* R = reinterpret_cast<const TIn*>(p.dt);
+  TOut* Y = reinterpret_cast<TOut*>(p.y);
+  const size_t row = (size_t)b * p.L;
+  const int D = p.D;
+  const int dd = active ? d : 0;
+  TIn xc[kTB], rc[kTB], xn[kTB], rn[kTB];
+  StageRegs<KW> sr;
+
+  const int n0 = min(kTB, t1 - t0);
+  stage_issue<TIn, KW>(p, row, t0, n0, k, lane, sr);
+  {
+    const TIn* xb = X + (row + t0) * D;
+    const TIn* rb = R + (row + t0) * D;
+#pragma unroll
+    for (int i = 0; i < kTB; ++i) {
+      const uint32_t o = (uint32_t)(min(i, n0 - 1) * D + dd);
+      xc[i] = at32(xb, o);
+      rc[i] = at32(rb, o);
+    }
+  }
+  stage_commit<TIn, KW>(p, s.ring, 0, n0, k, lane, sr, gate_bad);
+
+  int slot = 0;
+  for (int tb = t0; tb < t1; tb += kTB, slot ^= 1) {
+    const int n = min(kTB, t1 - tb);
+    const int tn = tb + kTB;
+    const int nn = tn < t1 ? min(kTB, t1 - tn) : 0;
+    if (nn > 0) {
+      stage_issue<TIn, KW>(p, row, tn, nn, k, lane, sr);
+      const TIn* xb = X + (row + tn) * D;
+      const TIn* rb = R + (row + tn) * D;
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        const uint32_t o = (uint32_t)(min(i, nn - 1) * D + dd);
+        xn[i] = at32(xb, o);
+        rn[i] = at32(rb, o);
+      }
+    }
+    wave_sync();
+    TOut* yb = Y + (row + tb) * D;
+    // full blocks on full tiles run as one branch-free basic block of kTB
+    // tokens, so the scheduler can overlap a token's LDS reads with the
+    // previous token's arithmetic; the ragged tail keeps its guards
+    const bool fast = n == kTB && full_tile;
+    if constexpr (K > 0) {
+      // the block's routing, once, into SGPRs
+      int eb[kTB * K];
+      float gb[kTB * K];
+#pragma unroll
+      for (int w = 0; w < kTB * K; ++w) {
+        eb[w] = uniform(s.ring.e[slot * kTB * K + w]);
+        gb[w] = uniform(s.ring.g[slot * kTB * K + w]);
+      }
+      if (fast) {
+#pragma unroll
+        for (int i = 0; i < kTB; ++i) {
+          const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, eb + i * K, gb + i * K, slot, i,
+                                                      lane, to_f32(xc[i]), to_f32(rc[i]), h, g);
+          at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kTB; ++i) {
+          if (i < n) {
+            const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
+            const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, eb + i * K, gb + i * K, slot,
+                                                        i, lane, xv, rv, h, g);
+            if (active) at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        if (i < n) {
+          int eb[16];
+          float gb[16];
+          for (int j = 0; j < k; ++j) {
+            eb[j] = s.ring.e[(slot * kTB + i) * k + j];
+            gb[j] = s.ring.g[(slot * kTB + i) * k + j];
+          }
+          const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
+          const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, eb, gb, slot, i, lane, xv, rv, h,
+                                                      g);
+          if (active) at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+        }
+      }
+    }
+    if (TRACK && truncate) {
+      float mh = 0.f;
+#pragma unroll
+      for (int q = 0; q < kN; ++q) mh = fmaxf(mh, fabsf(h[q]));
+      const float thr = fmaxf(kFixupTol * mh, kTiny);
+      bool conv = true;
+#pragma unroll
+      for (int q = 0; q < kN; ++q) conv &= fabsf(g[q]) <= thr;  // NaN: not converged
+      if (__all(conv)) break;
+    }
+    if (nn > 0) {
+      stage_commit<TIn, KW>(p, s.ring, slot ^ 1, nn, k, lane, sr, gate_bad);
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        xc[i] = xn[i];
+        rc[i] = rn[i];
+      }
+    }
+  }
 }
 
 // Pass 1 (or the only pass when CHUNKED is false).
 template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED>
 __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
-  const Smem s = smem_layout(p.E, true);
+  const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, CHUNKED, WAVES, wave);
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
   const int tile = bid % p.ntiles;
   bid /= p.ntiles;
   const int cg = bid % ncg;
   const int b = bid / ncg;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
 
@@ -219,25 +445,11 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   for (int n = 0; n < kN; ++n)
     h[n] = (c == 0 && p.h0 != nullptr && active) ? p.h0[((size_t)b * p.D + d) * kN + n] : 0.f;
 
-  const bool write_y = !CHUNKED || c == 0 || p.carry != SWIMBA_CARRY_REWALK;
-  const TIn* X = reinterpret_cast<const TIn*>(p.x);
-  const TIn* R = reinterpret_cast<const TIn*>(p.dt);
-  TOut* Y = reinterpret_cast<TOut*>(p.y);
+  // every chunk writes y (provisional for chunks >= 1, recomputed by the
+  // fix-up pass where the carried-in state still matters)
   int gate_bad = 0;
-  const int dd = active ? d : 0;
-  size_t bt = (size_t)b * p.L + t0;
-  size_t off = bt * p.D + dd;
-  // software pipeline: the next token's x and dt_raw are in flight during the current one
-  float xn = to_f32(X[off]), rn = to_f32(R[off]);
-  for (int t = t0; t < t1; ++t, ++bt, off += p.D) {
-    const float xv = active ? xn : 0.f, rv = active ? rn : 0.f;
-    if (t + 1 < t1) {
-      xn = to_f32(X[off + p.D]);
-      rn = to_f32(R[off + p.D]);
-    }
-    float yv = mix_token<K, TIn, false, CHUNKED>(p, s, U, bt, lane, xv, rv, h, nullptr, gate_bad);
-    if (write_y && active) Y[off] = from_f32<TOut>(yv);
-  }
+  walk<TIn, TOut, K, false, CHUNKED>(p, s, U, b, t0, t1, d, active, d0 + 64 <= p.D, lane, false,
+                                     h, nullptr, gate_bad);
 
   if (CHUNKED) {
     // total decay of the chunk: P[n] = exp2(sum_e U_e A[e, d, n])
@@ -263,6 +475,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
         p.H[base + (size_t)n * p.D] = h[n];
       }
     }
+    gate_bad = __any(gate_bad);
     if (lane == 0) p.flags[((size_t)b * p.nchunks + c) * p.ntiles + tile] = (bad | gate_bad) ? 1 : 0;
   } else if (p.h_final != nullptr && active) {
 #pragma unroll
@@ -274,7 +487,8 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
 // has decayed away (or to the chunk's end).
 template <typename TIn, typename TOut, int WAVES, int K>
 __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
-  const Smem s = smem_layout(p.E, true);
+  const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, false, WAVES, wave);
   const int nfix = p.nchunks - 1;
   const int ncg = (nfix + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
@@ -282,7 +496,6 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   bid /= p.ntiles;
   const int cg = bid % ncg;
   const int b = bid / ncg;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
   load_table(p, s, d0);
@@ -301,33 +514,9 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   }
   const bool truncate = p.carry == SWIMBA_CARRY_FIXUP &&
                         p.flags[((size_t)b * p.nchunks + c) * p.ntiles + tile] == 0;
-  const TIn* X = reinterpret_cast<const TIn*>(p.x);
-  const TIn* R = reinterpret_cast<const TIn*>(p.dt);
-  TOut* Y = reinterpret_cast<TOut*>(p.y);
   int gate_bad = 0;
-  const int dd = active ? d : 0;
-  size_t bt = (size_t)b * p.L + t0;
-  size_t off = bt * p.D + dd;
-  float xn = to_f32(X[off]), rn = to_f32(R[off]);
-  for (int t = t0; t < t1; ++t, ++bt, off += p.D) {
-    const float xv = active ? xn : 0.f, rv = active ? rn : 0.f;
-    if (t + 1 < t1) {
-      xn = to_f32(X[off + p.D]);
-      rn = to_f32(R[off + p.D]);
-    }
-    float yv = mix_token<K, TIn, true, false>(p, s, nullptr, bt, lane, xv, rv, h, g, gate_bad);
-    if (active) Y[off] = from_f32<TOut>(yv);
-    if (truncate && ((t - t0) & 1)) {
-      float mh = 0.f;
-#pragma unroll
-      for (int n = 0; n < kN; ++n) mh = fmaxf(mh, fabsf(h[n]));
-      const float thr = fmaxf(kFixupTol * mh, kTiny);
-      bool conv = true;
-#pragma unroll
-      for (int n = 0; n < kN; ++n) conv &= fabsf(g[n]) <= thr;  // NaN: not converged
-      if (__all(conv)) break;
-    }
-  }
+  walk<TIn, TOut, K, true, false>(p, s, nullptr, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
+                                  truncate, h, g, gate_bad);
 }
 
 template <typename TIn, typename TOut, int WAVES, int K>
@@ -359,16 +548,16 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
   p.flags = pl.nchunks > 1 ? reinterpret_cast<int32_t*>(w + pl.off_flags) : nullptr;
 
-  const size_t table = (size_t)p.E * (4 * 64 * 16 + 64 * 8);
-  const size_t ubytes = (size_t)WAVES * p.E * 64 * 4;
+  const size_t smem1 = smem_bytes(p.E, p.k, true, WAVES);
+  const size_t smem3 = smem_bytes(p.E, p.k, false, WAVES);
   hipEvent_t* ev = a->phase_events;
   if (ev) (void)hipEventRecord(ev[0], st);
   if (pl.nchunks <= 1) {
     p.nchunks = 1;
     dim3 grid((unsigned)((size_t)p.B * p.ntiles));
-    allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, false>, table);
+    allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, false>, smem3);
     hipLaunchKernelGGL((mix_chunk_kernel<TIn, TOut, WAVES, K, false>), grid, dim3(WAVES * 64),
-                       table, st, p);
+                       smem3, st, p);
     if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
     if (ev) {
       (void)hipEventRecord(ev[1], st);
@@ -379,9 +568,9 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   }
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   dim3 grid1((unsigned)((size_t)p.B * ncg * p.ntiles));
-  allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, true>, table + ubytes);
+  allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, true>, smem1);
   hipLaunchKernelGGL((mix_chunk_kernel<TIn, TOut, WAVES, K, true>), grid1, dim3(WAVES * 64),
-                     table + ubytes, st, p);
+                     smem1, st, p);
   if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
   if (ev) (void)hipEventRecord(ev[1], st);
   const int rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 0, st);
@@ -389,8 +578,8 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   if (ev) (void)hipEventRecord(ev[2], st);
   const int ncg3 = (p.nchunks - 1 + WAVES - 1) / WAVES;
   dim3 grid3((unsigned)((size_t)p.B * ncg3 * p.ntiles));
-  allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K>, table);
-  hipLaunchKernelGGL((mix_fixup_kernel<TIn, TOut, WAVES, K>), grid3, dim3(WAVES * 64), table, st,
+  allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K>, smem3);
+  hipLaunchKernelGGL((mix_fixup_kernel<TIn, TOut, WAVES, K>), grid3, dim3(WAVES * 64), smem3, st,
                      p);
   if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
   if (ev) (void)hipEventRecord(ev[3], st);

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(WAVES * 64) void sep_kernel(SepParams p) {
   bid /= p.ntiles;
   const int cg = bid % ncg;
   const int b = bid / ncg;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
 

@@ -44,6 +44,9 @@ int validate_scan_pointers(const swimba_scan_args* a) {
     if (a->x == nullptr || a->dt_raw == nullptr || a->Bm == nullptr || a->Cm == nullptr ||
         a->idx == nullptr || a->gate == nullptr || a->y == nullptr)
       return SWIMBA_EINVAL;
+    // B_t and C_t rows are staged as 16-byte vectors
+    if ((reinterpret_cast<uintptr_t>(a->Bm) & 15) || (reinterpret_cast<uintptr_t>(a->Cm) & 15))
+      return SWIMBA_EINVAL;
   }
   return SWIMBA_OK;
 }
@@ -92,6 +95,9 @@ int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p) {
   if (chunk > a->L) chunk = a->L;
   p->chunk = chunk;
   p->nchunks = (int)(((long long)a->L + chunk - 1) / chunk);
+  // chunks of one tile share the workgroup's expert table: 8 waves when there
+  // are enough chunks to fill them
+  if (!separate && p->nchunks >= 8) p->waves = 8;
   if (p->nchunks > 1) {
     const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N : SWIMBA_STATE_N;
     const size_t arr = (size_t)a->B * p->nchunks * rows * a->D * sizeof(float);
@@ -156,6 +162,15 @@ size_t swimba_scan_workspace_size(const swimba_scan_args* a, int separate) {
   ScanPlan p;
   if (plan_scan(a, separate ? 1 : 0, &p) != SWIMBA_OK) return 0;
   return p.bytes;
+}
+
+int swimba_scan_plan(const swimba_scan_args* a, int separate, int* chunk, int* nchunks) {
+  ScanPlan p;
+  const int rc = plan_scan(a, separate ? 1 : 0, &p);
+  if (rc != SWIMBA_OK) return rc;
+  if (chunk) *chunk = p.chunk;
+  if (nchunks) *nchunks = p.nchunks;
+  return SWIMBA_OK;
 }
 
 int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -39,6 +39,17 @@ __device__ __forceinline__ float softplus_f32(float z) {
   return fmaxf(z, 0.0f) + hw_log2(1.0f + e) * kLn2;
 }
 
+// Element `i` of a wave-uniform base with a 32-bit byte offset: lets the
+// backend address it as SGPR base + unsigned VGPR offset (no 64-bit math).
+template <typename T>
+__device__ __forceinline__ const T& at32(const T* base, uint32_t i) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + i * (uint32_t)sizeof(T));
+}
+template <typename T>
+__device__ __forceinline__ T& at32(T* base, uint32_t i) {
+  return *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + i * (uint32_t)sizeof(T));
+}
+
 // Wave-uniform value into an SGPR (the argument must already be uniform).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ float uniform(float v) {

@@ -66,6 +66,9 @@ def load(path: str | None = None):
     for fn in (lib.swimba_scan, lib.swimba_scan_separate):
         fn.argtypes = [ctypes.POINTER(ScanArgs), _vp, ctypes.c_size_t, _vp]
         fn.restype = _ci
+    lib.swimba_scan_plan.argtypes = [ctypes.POINTER(ScanArgs), _ci, ctypes.POINTER(_ci),
+                                     ctypes.POINTER(_ci)]
+    lib.swimba_scan_plan.restype = _ci
     lib.swimba_step.argtypes = [ctypes.POINTER(StepArgs), _vp]
     lib.swimba_step.restype = _ci
     lib.swimba_status_string.argtypes = [_ci]
@@ -212,15 +215,76 @@ def scan_separate(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw
     return _scan(True, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
 
 
-def scan_workspace_bytes(x, A, idx, separate=False, chunk=0, y_dtype=None):
-    """Workspace bytes swimba_scan(_separate) needs for these shapes."""
+def _shape_args(x, A, idx, chunk, y_dtype):
     B, L, D = x.shape
     a = ScanArgs()
     a.B, a.L, a.D, a.N, a.E, a.k = B, L, D, A.shape[2], A.shape[0], idx.shape[2]
     a.in_dtype = _dt(x)
     a.y_dtype = a.in_dtype if y_dtype is None else (BF16 if y_dtype == torch.bfloat16 else F32)
     a.chunk = chunk
-    return workspace_size(a, separate)
+    return a
+
+
+def scan_workspace_bytes(x, A, idx, separate=False, chunk=0, y_dtype=None):
+    """Workspace bytes swimba_scan(_separate) needs for these shapes."""
+    return workspace_size(_shape_args(x, A, idx, chunk, y_dtype), separate)
+
+
+def scan_plan(x, A, idx, separate=False, chunk=0):
+    """(tokens per chunk, number of chunks) the scan will use (swimba_scan_plan)."""
+    c, n = _ci(), _ci()
+    rc = load().swimba_scan_plan(ctypes.byref(_shape_args(x, A, idx, chunk, None)),
+                                 1 if separate else 0, ctypes.byref(c), ctypes.byref(n))
+    _check("swimba_scan_plan", rc)
+    return c.value, n.value
+
+
+class PreparedScan:
+    """A scan call marshalled once (argument struct, workspace) for callers
+    that issue the same call repeatedly; __call__ goes straight to the C ABI."""
+
+    def __init__(self, separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None,
+                 y=None, h_final=None, chunk=0, carry="auto", workspace=None, stream=None):
+        self.args = _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final,
+                               chunk, carry, separate, None)
+        need = workspace_size(self.args, separate)
+        self.workspace = workspace if workspace is not None else torch.empty(
+            max(need, 1), dtype=torch.uint8, device=x.device)
+        self._keep = (x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final)
+        lib = load()
+        self._fn = lib.swimba_scan_separate if separate else lib.swimba_scan
+        self._ref = ctypes.byref(self.args)
+        self._ws = self.workspace.data_ptr()
+        self._wsn = self.workspace.numel()
+        self.stream = _stream(stream)
+
+    def __call__(self, phase_events=None):
+        self.args.phase_events = phase_events
+        rc = self._fn(self._ref, self._ws, self._wsn, self.stream)
+        if rc != OK:
+            raise SwimbaError("swimba_scan", rc)
+
+
+class PreparedRoute:
+    """swimba_route marshalled once (see PreparedScan)."""
+
+    def __init__(self, x, Wr, k, idx, gate, stream=None):
+        _need(x, "x")
+        D = x.shape[-1]
+        E = Wr.shape[1]
+        _need(Wr, "Wr", (D, E), torch.float32, x.device)
+        lead = tuple(x.shape[:-1])
+        _need(idx, "idx", lead + (k,), torch.int32, x.device)
+        _need(gate, "gate", lead + (k,), torch.float32, x.device)
+        self._keep = (x, Wr, idx, gate)
+        self._a = (x.data_ptr(), _dt(x), Wr.data_ptr(), x.numel() // D, D, E, k, idx.data_ptr(),
+                   gate.data_ptr(), _stream(stream))
+        self._fn = load().swimba_route
+
+    def __call__(self):
+        rc = self._fn(*self._a)
+        if rc != OK:
+            raise SwimbaError("swimba_route", rc)
 
 
 def step(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None, gate=None,
