@@ -3,19 +3,19 @@
 // "Kernmechanisme van Swimba": a router gives each token weights over the
 // active experts, top-1 or top-k).
 //
-// Mapping.  A workgroup of four waves owns 64 tokens; lane t of every wave is
-// token t.  The waves split the channels into 128-byte pieces, interleaved, so
-// the four partial sums per token cover disjoint channel sets.  Each wave
-// stages its 64 x-rows of a piece through LDS (coalesced 16-byte loads in, one
-// conflict-free row per lane out) and multiplies them by Wr rows that are the
-// same for every lane, hence read by the scalar unit into SGPR operands: one
-// v_fma per (token, channel, expert).
+// Mapping.  A wave owns R = 64 / EC tokens (EC = E rounded up to a power of
+// two).  Per step, lane l reads channels [s*256 + 4l, s*256 + 4l + 4) of each
+// of its R token rows -- contiguous across the wave, straight from HBM into
+// VGPRs -- and the matching 4 rows of Wr (L2-resident), and accumulates R x EC
+// partial logits.  A transpose-reduce across the 64 lanes (6 lane-exchange
+// levels, halving the values per lane each time) then leaves lane l holding
+// the full logit of (token l / EC, expert l % EC).  The top k of a token are
+// picked by a tournament among its EC lanes.
 //
-// Rounding.  Every 128-byte piece is summed from zero and then added to the
-// wave's total; the four wave totals are added in a fixed order.  The fp32
-// logit therefore differs from the exact sum by at most
-// gamma_{m} * sum_d |x_d Wr[d,e]| with m = (channels per piece) +
-// (pieces per wave) + 2, gamma_m = m u / (1 - m u), u = 2^-24.
+// Rounding.  Each lane sums its D/64 channels in order, then the 6 levels add
+// pairs, so the fp32 logit differs from the exact sum by at most
+// gamma_m * sum_d |x_d Wr[d,e]| with m = ceil(D / 64) + 6,
+// gamma_m = m u / (1 - m u), u = 2^-24.
 #pragma once
 #include "swimba_device.hpp"
 #include "swimba_internal.hpp"
@@ -23,159 +23,153 @@
 namespace swimba {
 namespace router {
 
-constexpr int kRouteWaves = 4;
-constexpr int kRowBytes = 144;  // 128 data bytes + 16 pad: conflict-free row reads
+constexpr int kRouteThreads = 256;
+constexpr int kCPL = 4;  // channels per lane per step
 
-template <typename TIn, int EC, bool EXACT, bool VEC>
-__global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const TIn* __restrict__ x,
-                                                                const float* __restrict__ Wr,
-                                                                int64_t T, int D, int E, int k,
-                                                                int32_t* __restrict__ idx,
-                                                                float* __restrict__ gate) {
-  constexpr int CH = 128 / sizeof(TIn);  // channels per piece
-  constexpr int PER16 = 16 / sizeof(TIn);
-  constexpr int kTileBytes = kRouteWaves * 64 * kRowBytes;
-  constexpr int kRedBytes = (kRouteWaves - 1) * EC * 64 * 4;
-  constexpr int kSmem = kTileBytes > kRedBytes ? kTileBytes : kRedBytes;
-  // full unrolling of the piece for the common expert counts only (code size)
-  constexpr int kUnroll = EC <= 16 ? 8 : 1;
-  __shared__ __align__(16) unsigned char smem[kSmem];
-
-  const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
-  unsigned char* tile = smem + wave * 64 * kRowBytes;
-  const int npieces = (D + CH - 1) / CH;
-
-  float acc[EC];
-#pragma unroll
-  for (int e = 0; e < EC; ++e) acc[e] = 0.f;
-
-  for (int pc = wave; pc < npieces; pc += kRouteWaves) {
-    const int dc = pc * CH;
-    // stage 64 rows x 128 bytes: lane covers (row, 16-byte column) pairs
-    if (VEC) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = lane + 64 * i, r = q >> 3, col = q & 7;
-        const int64_t t = t0 + r;
-        const int dd = dc + col * PER16;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < T && dd < D) v = *reinterpret_cast<const uint4*>(x + t * D + dd);
-        *reinterpret_cast<uint4*>(tile + r * kRowBytes + col * 16) = v;
-      }
+// Load 4 consecutive channels of x as fp32.  VEC: one 8- or 16-byte load.
+template <typename TIn, bool VEC>
+__device__ __forceinline__ void load4(const TIn* row, int d, int D, bool ok, float* v) {
+  if (VEC) {
+    if (sizeof(TIn) == 2) {
+      uint2 u = make_uint2(0, 0);
+      if (ok) u = *reinterpret_cast<const uint2*>(row + d);
+      v[0] = __uint_as_float(u.x << 16);
+      v[1] = __uint_as_float(u.x & 0xffff0000u);
+      v[2] = __uint_as_float(u.y << 16);
+      v[3] = __uint_as_float(u.y & 0xffff0000u);
     } else {
-      for (int i = 0; i < CH; ++i) {
-        const int q = lane + 64 * i, r = q / CH, c = q % CH;
-        const int64_t t = t0 + r;
-        const int dd = dc + c;
-        TIn v = 0;
-        if (t < T && dd < D) v = x[t * D + dd];
-        *reinterpret_cast<TIn*>(tile + r * kRowBytes + c * sizeof(TIn)) = v;
-      }
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok) f = *reinterpret_cast<const float4*>(row + d);
+      v[0] = f.x;
+      v[1] = f.y;
+      v[2] = f.z;
+      v[3] = f.w;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    float part[EC];
+  } else {
 #pragma unroll
-    for (int e = 0; e < EC; ++e) part[e] = 0.f;
-    const int cmax = min(CH, D - dc);  // wave-uniform
-    const unsigned char* row = tile + lane * kRowBytes;
-    if (cmax == CH) {
-#pragma unroll kUnroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + i * 16);
-        float xv[PER16];
-        if (sizeof(TIn) == 2) {
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            xv[2 * j] = __uint_as_float(w4[j] << 16);
-            xv[2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
-          }
-        } else {
-          xv[0] = __uint_as_float(v.x);
-          xv[1] = __uint_as_float(v.y);
-          xv[2] = __uint_as_float(v.z);
-          xv[3] = __uint_as_float(v.w);
-        }
-#pragma unroll
-        for (int j = 0; j < PER16; ++j) {
-          const float* w = Wr + (size_t)(dc + i * PER16 + j) * E;
-#pragma unroll
-          for (int e = 0; e < EC; ++e)
-            if (EXACT || e < E) part[e] = fmaf(xv[j], w[e], part[e]);
-        }
-      }
-    } else {
-      for (int c = 0; c < cmax; ++c) {
-        const float xv = to_f32(*reinterpret_cast<const TIn*>(row + c * sizeof(TIn)));
-        const float* w = Wr + (size_t)(dc + c) * E;
-#pragma unroll
-        for (int e = 0; e < EC; ++e)
-          if (EXACT || e < E) part[e] = fmaf(xv, w[e], part[e]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < EC; ++e) acc[e] += part[e];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int c = 0; c < kCPL; ++c) v[c] = (ok && d + c < D) ? to_f32(row[d + c]) : 0.f;
   }
-
-  // reduce the four wave totals in a fixed order (wave 0 + 1 + 2 + 3)
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
-  if (wave > 0) {
-#pragma unroll
-    for (int e = 0; e < EC; ++e)
-      if (e < E) red[((wave - 1) * EC + e) * 64 + lane] = acc[e];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  const int64_t t = t0 + lane;
-#pragma unroll
-  for (int w = 0; w < kRouteWaves - 1; ++w)
-#pragma unroll
-    for (int e = 0; e < EC; ++e)
-      if (e < E) acc[e] += red[(w * EC + e) * 64 + lane];
-  if (t >= T) return;
-
-  // top-k by (logit descending, expert ascending).  The selected logits go to
-  // LDS column `lane` (each lane has consumed its own column of `red` above,
-  // and k <= E rows fit in the buffer).
-  float* sel = red;
-  uint64_t taken = 0;
-  float m = 0.f;
-  for (int j = 0; j < k; ++j) {
-    int best = -1;
-    float bv = 0.f;
-#pragma unroll
-    for (int e = 0; e < EC; ++e) {
-      if (e < E && !((taken >> e) & 1ull)) {
-        if (best < 0 || acc[e] > bv) {
-          best = e;
-          bv = acc[e];
-        }
-      }
-    }
-    taken |= 1ull << best;
-    if (j == 0) m = bv;
-    idx[t * k + j] = best;
-    sel[j * 64 + lane] = bv;
-  }
-  float z = 0.f;
-  for (int j = 0; j < k; ++j) z += hw_exp2((sel[j * 64 + lane] - m) * kLog2e);
-  for (int j = 0; j < k; ++j) gate[t * k + j] = hw_exp2((sel[j * 64 + lane] - m) * kLog2e) / z;
 }
 
-// EXACT: E == EC, no per-expert guard in the inner loop.
+// EXACT: E == EC (no padded experts).  VEC: D is a multiple of 4 and x is
+// aligned for 4-channel vector loads.
+template <typename TIn, int EC, bool EXACT, bool VEC>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restrict__ x,
+                                                             const float* __restrict__ Wr,
+                                                             int64_t T, int D, int E, int k,
+                                                             int32_t* __restrict__ idx,
+                                                             float* __restrict__ gate) {
+  constexpr int R = 64 / EC;  // tokens per wave
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (kRouteThreads / 64) +
+                       uniform((int)(threadIdx.x >> 6));
+  const int64_t t0 = wave * R;
+  if (t0 >= T) return;
+
+  // partial logits acc[r * EC + e]
+  float acc[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) acc[i] = 0.f;
+
+  const TIn* rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = x + (t0 + r < T ? t0 + r : T - 1) * D;
+
+  for (int dc = 0; dc < D; dc += 64 * kCPL) {
+    const int d = dc + lane * kCPL;
+    const bool ok = d < D;
+    float xv[R][kCPL];
+#pragma unroll
+    for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], d, D, ok, xv[r]);
+    // Wr rows of this lane's channels.  Lanes past D (x = 0 there) and padded
+    // experts (lanes e >= E, never reported) read clamped, valid rows/columns.
+    float w[kCPL][EC];
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c) {
+      const int row = ok ? (VEC ? d + c : min(d + c, D - 1)) : 0;
+      const float* wr = Wr + (size_t)row * E;
+#pragma unroll
+      for (int e = 0; e < EC; ++e) w[c][e] = wr[EXACT ? e : min(e, E - 1)];
+    }
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < EC; ++e) acc[r * EC + e] = fmaf(xv[r][c], w[c][e], acc[r * EC + e]);
+  }
+
+  // transpose-reduce: at level m (32, 16, ..., 1) a lane keeps the half of its
+  // values selected by its bit m and adds its partner's copy of that half; at
+  // the end lane l holds the full sum of value l.
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const bool hi = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+      const float send = hi ? acc[i] : acc[i + m];
+      const float keep = hi ? acc[i + m] : acc[i];
+      acc[i] = keep + __shfl_xor(send, m, 64);
+    }
+  }
+  const int r = lane / EC, e = lane % EC;
+  const int64_t t = t0 + r;
+  float v = acc[0];
+  const bool real = e < E;
+
+  // top-k among the EC lanes of token r: (logit desc, expert asc)
+  bool taken = false;
+  float m0 = 0.f, z = 0.f;
+  float my_sel = 0.f;  // logit of the slot this lane reports (lane e reports slot e)
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    bool cand = real && !taken;
+    float bv = v;
+    int be = e;
+#pragma unroll
+    for (int o = 1; o < EC; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      const bool oc = __shfl_xor((int)cand, o, 64) != 0;
+      // the lower expert index wins unless the higher one is strictly larger
+      bool take_other;
+      if (!cand)
+        take_other = oc;
+      else if (!oc)
+        take_other = false;
+      else if (oe < be)
+        take_other = !(bv > ov);
+      else
+        take_other = ov > bv;
+      if (take_other) {
+        bv = ov;
+        be = oe;
+        cand = true;
+      }
+    }
+    if (e == be) taken = true;
+    if (j == 0) m0 = bv;
+    if (e == j) {
+      my_sel = bv;
+      my_idx = be;
+    }
+    z += hw_exp2((bv - m0) * kLog2e);
+  }
+  if (t < T && e < k) {
+    idx[t * k + e] = my_idx;
+    gate[t * k + e] = hw_exp2((my_sel - m0) * kLog2e) / z;
+  }
+}
+
 template <typename TIn, int EC>
 int launch_route_t(const void* x, const float* Wr, int64_t T, int D, int E, int k, int32_t* idx,
                    float* gate, hipStream_t s) {
-  const dim3 grid((unsigned)((T + 63) / 64)), block(kRouteWaves * 64);
-  const bool vec = ((D * sizeof(TIn)) % 16 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+  constexpr int R = 64 / EC;
+  const int64_t waves = (T + R - 1) / R;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(kRouteThreads);
+  const size_t vec_bytes = sizeof(TIn) * kCPL;
+  const bool vec = ((size_t)D * sizeof(TIn)) % vec_bytes == 0 &&
+                   reinterpret_cast<uintptr_t>(x) % vec_bytes == 0;
   const TIn* xp = static_cast<const TIn*>(x);
   const bool exact = E == EC;
   if (vec && exact)

@@ -80,12 +80,12 @@ def assert_faithful_bf16(got_bf16: torch.Tensor, ref: np.ndarray, what="", tol=T
             what, int(bad.sum()), list(zip(got.ravel()[i].tolist(), ref.ravel()[i].tolist()))))
 
 
-def route_tolerance(absdot: np.ndarray, D: int, per_piece: int, waves: int = 4) -> np.ndarray:
-    """Bound on |fp32 logit - exact logit| for the router's summation: every
-    piece of `per_piece` channels is summed from zero, pieces are added per
-    wave, then `waves` partials are added (gamma_m * sum |x_d Wr[d,e]|)."""
-    pieces = -(-D // per_piece)
-    m = per_piece + -(-pieces // waves) + waves + 2
+def route_tolerance(absdot: np.ndarray, D: int) -> np.ndarray:
+    """Bound on |fp32 logit - exact logit| for the routers' summations: each
+    lane sums at most ceil(D/64) products in order and the partial sums are
+    combined in at most 8 more levels (gamma_m * sum_d |x_d Wr[d,e]|,
+    m = ceil(D/64) + 8)."""
+    m = -(-D // 64) + 8
     gamma = m * U32 / (1 - m * U32)
     return gamma * absdot
 
