@@ -8,18 +8,27 @@
 // A lane owns one channel and holds the E x 16 expert states in VGPRs.  The
 // selected expert is wave-uniform, so the update of H[e] is reached through a
 // uniform branch to code with constant register indices (no dynamic VGPR
-// indexing, no scratch).  Chunks are joined exactly: pass 1 runs every chunk
+// indexing, no scratch).  Per-token routing and B_t/C_t are staged through the
+// same per-wave LDS ring as the mixed scan, one block of tokens ahead.  Chunks are joined exactly: pass 1 runs every chunk
 // from zero (chunk 0 from h0) and records each expert's end state and decay
 // P_e[n] = exp2(S_e A[e,n] log2 e) with S_e the Delta summed over the tokens
 // that selected e; pass 2 carries the states across chunks (shared with the
 // mixed scan); pass 3 re-runs chunks 1.. from their carried-in states.
 #pragma once
+#include "scan_common.hpp"
 #include "swimba_device.hpp"
 #include "swimba_internal.hpp"
 
 namespace swimba {
-
 namespace sep {
+
+using stage::kTB;
+using stage::Ring;
+using stage::StageRegs;
+using stage::ring_bytes;
+using stage::stage_commit;
+using stage::stage_issue;
+using stage::wave_sync;
 
 struct SepParams {
   int B, L, D, E, k;
@@ -42,50 +51,202 @@ struct SepParams {
 
 enum { kPassFirst = 0, kPassFixup = 1, kPassSingle = 2 };
 
-template <typename TIn, bool READOUT>
-__device__ __forceinline__ float expert_update(float* h, float& S, const float4* sA,
-                                               float2 bd, int lane, float xv, float rv,
-                                               const TIn* Bp, const TIn* Cp) {
+__host__ inline size_t sep_smem_bytes(int E, int k, int waves) {
+  return (size_t)E * (4 * 64 * 16 + 64 * 8) + ring_bytes(k) * waves;
+}
+
+// Advance expert state h (16 entries) by one token with the expert's own
+// parameters (its A row a4, bias/Dskip bd, already read); returns that
+// expert's output (READOUT) or 0.
+template <bool READOUT>
+__device__ __forceinline__ float expert_update(float* h, float& S, const float4* a4, float2 bd,
+                                               float xv, float rv, const float4* b4,
+                                               const float4* c4) {
   const float dlt = softplus_f32(rv + bd.x);
   S += dlt;
   const float dl2 = dlt * kLog2e, dx = dlt * xv;
   float ye = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float4 a4 = sA[q * 64 + lane];
-    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+    const float av[4] = {a4[q].x, a4[q].y, a4[q].z, a4[q].w};
+    const float bv[4] = {b4[q].x, b4[q].y, b4[q].z, b4[q].w};
+    const float cv[4] = {c4[q].x, c4[q].y, c4[q].z, c4[q].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int n = 4 * q + i;
       const float a = hw_exp2(dl2 * av[i]);
-      h[n] = fmaf(a, h[n], dx * to_f32(Bp[n]));
-      if (READOUT) ye = fmaf(to_f32(Cp[n]), h[n], ye);
+      h[n] = fmaf(a, h[n], dx * bv[i]);
+      if (READOUT) ye = fmaf(cv[i], h[n], ye);
     }
   }
   return READOUT ? fmaf(bd.y, xv, ye) : 0.f;
 }
 
-// Uniform dispatch to the expert `e` (compile-time register indices).
-template <typename TIn, bool READOUT, int EMAX, int EE = 0>
+// Uniform dispatch to expert `e` (compile-time register indices).
+template <bool READOUT, int EMAX, int EE = 0>
 __device__ __forceinline__ float dispatch_update(float (&H)[EMAX][kN], float (&S)[EMAX], int e,
-                                                 const float4* sA, float2 bd, int lane,
-                                                 float xv, float rv, const TIn* Bp,
-                                                 const TIn* Cp) {
+                                                 const float4* a4, float2 bd, float xv, float rv,
+                                                 const float4* b4, const float4* c4) {
   if constexpr (EE < EMAX) {
-    if (e == EE)
-      return expert_update<TIn, READOUT>(H[EE], S[EE], sA + EE * 4 * 64, bd, lane, xv, rv, Bp,
-                                         Cp);
-    return dispatch_update<TIn, READOUT, EMAX, EE + 1>(H, S, e, sA, bd, lane, xv, rv, Bp, Cp);
+    if (e == EE) return expert_update<READOUT>(H[EE], S[EE], a4, bd, xv, rv, b4, c4);
+    return dispatch_update<READOUT, EMAX, EE + 1>(H, S, e, a4, bd, xv, rv, b4, c4);
   } else {
     return 0.f;
   }
 }
 
-template <typename TIn, typename TOut, int EMAX, int WAVES, int PASS>
+// One token for one lane: all LDS reads of the token (B_t, C_t, the selected
+// experts' A rows and bias/Dskip) are issued before the uniform dispatches.
+template <bool READOUT, int EMAX, int K>
+__device__ __forceinline__ float sep_token(float (&H)[EMAX][kN], float (&S)[EMAX], const int* e,
+                                           const float* gw, int k, const float4* sA,
+                                           const float2* sBD, const float4* bc, int lane, float xv,
+                                           float rv) {
+  float4 b4[4], c4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    b4[q] = bc[q];
+    c4[q] = bc[4 + q];
+  }
+  float yv = 0.f;
+  auto slot = [&](int j, const float4* a4, float2 bd) {
+    const float ye = dispatch_update<READOUT, EMAX>(H, S, e[j], a4, bd, xv, rv, b4, c4);
+    yv = fmaf(gw[j], ye, yv);
+  };
+  if constexpr (K > 0) {
+    float4 a4[K][4];
+    float2 bd[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      bd[j] = sBD[e[j] * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a4[j][q] = sA[(e[j] * 4 + q) * 64 + lane];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) slot(j, a4[j], bd[j]);
+  } else {
+    for (int j = 0; j < k; ++j) {
+      float4 a4[4];
+      const float2 bd = sBD[e[j] * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a4[q] = sA[(e[j] * 4 + q) * 64 + lane];
+      slot(j, a4, bd);
+    }
+  }
+  return yv;
+}
+
+// Walk tokens [t0, t1) for one lane with the staged pipeline of the mixed
+// scan.  READOUT: produce and store y.
+template <typename TIn, typename TOut, int EMAX, int K, bool READOUT>
+__device__ __forceinline__ void walk_sep(const SepParams& p, const float4* sA, const float2* sBD,
+                                         const Ring& ring, int b, int t0, int t1, int d,
+                                         bool active, int lane, float (&H)[EMAX][kN],
+                                         float (&S)[EMAX]) {
+  constexpr int KW = (2 * kTB * (K > 0 ? K : 16) + 63) / 64;
+  const int k = K > 0 ? K : p.k;
+  const TIn* X = reinterpret_cast<const TIn*>(p.x);
+  const TIn* R = reinterpret_cast<const TIn*>(p.dt);
+  TOut* Y = reinterpret_cast<TOut*>(p.y);
+  const size_t row = (size_t)b * p.L;
+  const int D = p.D;
+  const int dd = active ? d : 0;
+  TIn xc[kTB], rc[kTB], xn[kTB], rn[kTB];
+  StageRegs<KW> sr;
+  int gate_bad = 0;
+
+  const int n0 = min(kTB, t1 - t0);
+  stage_issue<TIn, KW>(p, row, t0, n0, k, lane, sr);
+  {
+    const TIn* xb = X + (row + t0) * D;
+    const TIn* rb = R + (row + t0) * D;
+#pragma unroll
+    for (int i = 0; i < kTB; ++i) {
+      const uint32_t o = (uint32_t)(min(i, n0 - 1) * D + dd);
+      xc[i] = at32(xb, o);
+      rc[i] = at32(rb, o);
+    }
+  }
+  stage_commit<TIn, KW>(p, ring, 0, n0, k, lane, sr, gate_bad);
+
+  int slot = 0;
+  for (int tb = t0; tb < t1; tb += kTB, slot ^= 1) {
+    const int n = min(kTB, t1 - tb);
+    const int tn = tb + kTB;
+    const int nn = tn < t1 ? min(kTB, t1 - tn) : 0;
+    if (nn > 0) {
+      stage_issue<TIn, KW>(p, row, tn, nn, k, lane, sr);
+      const TIn* xb = X + (row + tn) * D;
+      const TIn* rb = R + (row + tn) * D;
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        const uint32_t o = (uint32_t)(min(i, nn - 1) * D + dd);
+        xn[i] = at32(xb, o);
+        rn[i] = at32(rb, o);
+      }
+    }
+    wave_sync();
+    TOut* yb = Y + (row + tb) * D;
+    if constexpr (K > 0) {
+      // the block's routing, once, into SGPRs
+      int eb[kTB * K];
+      float gb[kTB * K];
+#pragma unroll
+      for (int w = 0; w < kTB * K; ++w) {
+        eb[w] = uniform(ring.e[slot * kTB * K + w]);
+        gb[w] = uniform(ring.g[slot * kTB * K + w]);
+      }
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        if (i < n) {
+          const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
+          const float4* bc = reinterpret_cast<const float4*>(ring.bc + (slot * kTB + i) * 32);
+          const float yv = sep_token<READOUT, EMAX, K>(H, S, eb + i * K, gb + i * K, K, sA, sBD,
+                                                       bc, lane, xv, rv);
+          if (READOUT && active) at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        if (i < n) {
+          int eb[16];
+          float gb[16];
+          for (int j = 0; j < k; ++j) {
+            eb[j] = uniform(ring.e[(slot * kTB + i) * k + j]);
+            gb[j] = uniform(ring.g[(slot * kTB + i) * k + j]);
+          }
+          const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
+          const float4* bc = reinterpret_cast<const float4*>(ring.bc + (slot * kTB + i) * 32);
+          const float yv = sep_token<READOUT, EMAX, K>(H, S, eb, gb, k, sA, sBD, bc, lane, xv, rv);
+          if (READOUT && active) at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+        }
+      }
+    }
+    if (nn > 0) {
+      stage_commit<TIn, KW>(p, ring, slot ^ 1, nn, k, lane, sr, gate_bad);
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        xc[i] = xn[i];
+        rc[i] = rn[i];
+      }
+    }
+  }
+}
+
+template <typename TIn, typename TOut, int EMAX, int WAVES, int PASS, int K>
 __global__ __launch_bounds__(WAVES * 64) void sep_kernel(SepParams p) {
   extern __shared__ float4 smem_raw[];
+  const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int k = K > 0 ? K : p.k;
   float4* sA = smem_raw;                                       // [E][4][64]
   float2* sBD = reinterpret_cast<float2*>(sA + p.E * 4 * 64);  // [E][64]
+  char* rp = reinterpret_cast<char*>(sBD + p.E * 64) + ring_bytes(k) * wave;
+  Ring ring;
+  ring.bc = reinterpret_cast<float*>(rp);
+  ring.e = reinterpret_cast<int32_t*>(rp + 2 * kTB * 32 * 4);
+  ring.g = reinterpret_cast<float*>(rp + 2 * kTB * 32 * 4 + 2 * kTB * k * 4);
+
   const int first_chunk = PASS == kPassFixup ? 1 : 0;
   const int nwork = PASS == kPassSingle ? 1 : p.nchunks - first_chunk;
   const int ncg = (nwork + WAVES - 1) / WAVES;
@@ -94,24 +255,10 @@ __global__ __launch_bounds__(WAVES * 64) void sep_kernel(SepParams p) {
   bid /= p.ntiles;
   const int cg = bid % ncg;
   const int b = bid / ncg;
-  const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
 
-  for (int i = threadIdx.x; i < p.E * 256; i += blockDim.x) {
-    int e = i >> 8, r = i & 255, dl = r >> 2, q = r & 3, dd = d0 + dl;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (dd < p.D) {
-      const float* a = p.A + ((size_t)e * p.D + dd) * kN + q * 4;
-      v = make_float4(a[0], a[1], a[2], a[3]);
-    }
-    sA[(e * 4 + q) * 64 + dl] = v;
-  }
-  for (int i = threadIdx.x; i < p.E * 64; i += blockDim.x) {
-    int e = i >> 6, dl = i & 63, dd = d0 + dl;
-    sBD[i] = dd < p.D ? make_float2(p.bias[(size_t)e * p.D + dd], p.Dsk[(size_t)e * p.D + dd])
-                      : make_float2(0.f, 0.f);
-  }
+  stage::load_table(p, sA, sBD, d0);
   __syncthreads();
 
   const int c = first_chunk + cg * WAVES + wave;
@@ -138,38 +285,12 @@ __global__ __launch_bounds__(WAVES * 64) void sep_kernel(SepParams p) {
     }
   }
 
-  constexpr bool kReadout = true;
-  const bool write_y = PASS != kPassFirst || c == 0;
-  const TIn* X = reinterpret_cast<const TIn*>(p.x);
-  const TIn* R = reinterpret_cast<const TIn*>(p.dt);
-  TOut* Y = reinterpret_cast<TOut*>(p.y);
-  const int dd = active ? d : 0;
-  size_t bt = (size_t)b * p.L + t0;
-  size_t off = bt * p.D + dd;
-  float xn = to_f32(X[off]), rn = to_f32(R[off]);
-  for (int t = t0; t < t1; ++t, ++bt, off += p.D) {
-    const float xv = active ? xn : 0.f, rv = active ? rn : 0.f;
-    if (t + 1 < t1) {
-      xn = to_f32(X[off + p.D]);
-      rn = to_f32(R[off + p.D]);
-    }
-    const TIn* Bp = reinterpret_cast<const TIn*>(p.Bm) + bt * kN;
-    const TIn* Cp = reinterpret_cast<const TIn*>(p.Cm) + bt * kN;
-    float yv = 0.f;
-    for (int j = 0; j < p.k; ++j) {
-      int e = p.idx[bt * p.k + j];
-      e = e < 0 ? 0 : (e >= p.E ? p.E - 1 : e);
-      const float gj = p.gate[bt * p.k + j];
-      const float2 bd = sBD[e * 64 + lane];
-      float ye;
-      if (write_y)
-        ye = dispatch_update<TIn, kReadout, EMAX>(H, S, e, sA, bd, lane, xv, rv, Bp, Cp);
-      else
-        ye = dispatch_update<TIn, false, EMAX>(H, S, e, sA, bd, lane, xv, rv, Bp, Cp);
-      yv = fmaf(gj, ye, yv);
-    }
-    if (write_y && active) Y[off] = from_f32<TOut>(yv);
-  }
+  // pass 1 needs no output for chunks >= 1 (pass 3 recomputes them)
+  const bool readout = PASS != kPassFirst || c == 0;
+  if (readout)
+    walk_sep<TIn, TOut, EMAX, K, true>(p, sA, sBD, ring, b, t0, t1, d, active, lane, H, S);
+  else
+    walk_sep<TIn, TOut, EMAX, K, false>(p, sA, sBD, ring, b, t0, t1, d, active, lane, H, S);
 
   if (PASS == kPassFirst) {
     if (active) {
@@ -201,7 +322,7 @@ __global__ __launch_bounds__(WAVES * 64) void sep_kernel(SepParams p) {
   }
 }
 
-template <typename TIn, typename TOut, int EMAX>
+template <typename TIn, typename TOut, int EMAX, int K>
 int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   constexpr int W = 4;
   SepParams p;
@@ -228,14 +349,14 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
   char* w = static_cast<char*>(ws);
   p.P = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_P) : nullptr;
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
-  const size_t smem = (size_t)p.E * (4 * 64 * 16 + 64 * 8);
+  const size_t smem = sep_smem_bytes(p.E, p.k, W);
   hipEvent_t* ev = a->phase_events;
   if (ev) (void)hipEventRecord(ev[0], st);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, EMAX, W, kPassSingle>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, EMAX, W, kPassFirst>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, EMAX, W, kPassFixup>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, EMAX, W, kPassSingle, K>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, EMAX, W, kPassFirst, K>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, EMAX, W, kPassFixup, K>, smem);
   if (pl.nchunks <= 1) {
-    hipLaunchKernelGGL((sep_kernel<TIn, TOut, EMAX, W, kPassSingle>),
+    hipLaunchKernelGGL((sep_kernel<TIn, TOut, EMAX, W, kPassSingle, K>),
                        dim3((unsigned)((size_t)p.B * p.ntiles)), dim3(W * 64), smem, st, p);
     if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
     if (ev)
@@ -243,7 +364,7 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
     return SWIMBA_OK;
   }
   const int ncg1 = (p.nchunks + W - 1) / W;
-  hipLaunchKernelGGL((sep_kernel<TIn, TOut, EMAX, W, kPassFirst>),
+  hipLaunchKernelGGL((sep_kernel<TIn, TOut, EMAX, W, kPassFirst, K>),
                      dim3((unsigned)((size_t)p.B * ncg1 * p.ntiles)), dim3(W * 64), smem, st, p);
   if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
   if (ev) (void)hipEventRecord(ev[1], st);
@@ -251,18 +372,30 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
   if (rc != SWIMBA_OK) return rc;
   if (ev) (void)hipEventRecord(ev[2], st);
   const int ncg3 = (p.nchunks - 1 + W - 1) / W;
-  hipLaunchKernelGGL((sep_kernel<TIn, TOut, EMAX, W, kPassFixup>),
+  hipLaunchKernelGGL((sep_kernel<TIn, TOut, EMAX, W, kPassFixup, K>),
                      dim3((unsigned)((size_t)p.B * ncg3 * p.ntiles)), dim3(W * 64), smem, st, p);
   if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
   if (ev) (void)hipEventRecord(ev[3], st);
   return SWIMBA_OK;
 }
 
+template <typename TIn, typename TOut, int EMAX>
+int launch_sep_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
+  switch (a->k) {
+    case 1:
+      return launch_sep_t<TIn, TOut, EMAX, 1>(a, pl, ws, st);
+    case 2:
+      return launch_sep_t<TIn, TOut, EMAX, 2>(a, pl, ws, st);
+    default:
+      return launch_sep_t<TIn, TOut, EMAX, 0>(a, pl, ws, st);
+  }
+}
+
 template <typename TIn, typename TOut>
 int launch_sep_e(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
-  if (a->E <= 4) return launch_sep_t<TIn, TOut, 4>(a, pl, ws, st);
-  if (a->E <= 8) return launch_sep_t<TIn, TOut, 8>(a, pl, ws, st);
-  return launch_sep_t<TIn, TOut, 16>(a, pl, ws, st);
+  if (a->E <= 4) return launch_sep_k<TIn, TOut, 4>(a, pl, ws, st);
+  if (a->E <= 8) return launch_sep_k<TIn, TOut, 8>(a, pl, ws, st);
+  return launch_sep_k<TIn, TOut, 16>(a, pl, ws, st);
 }
 
 }  // namespace sep
