@@ -17,6 +17,8 @@
 // gamma_m * sum_d |x_d Wr[d,e]| with m = ceil(D / 64) + 6,
 // gamma_m = m u / (1 - m u), u = 2^-24.
 #pragma once
+#include <type_traits>
+
 #include "swimba_device.hpp"
 #include "swimba_internal.hpp"
 
@@ -26,34 +28,99 @@ namespace router {
 constexpr int kRouteThreads = 256;
 constexpr int kCPL = 4;  // channels per lane per step
 
-// Load 4 consecutive channels of x as fp32.  VEC: one 8- or 16-byte load.
+// Raw 4 consecutive channels of x.  VEC: one 8- or 16-byte load.  Loads are
+// unconditional from a clamped (valid) address -- a load under a branch would
+// be waited on inside that branch -- and masked when converted.
 template <typename TIn, bool VEC>
-__device__ __forceinline__ void load4(const TIn* row, int d, int D, bool ok, float* v) {
+struct Raw4 {
+  using V = typename std::conditional<sizeof(TIn) == 2, uint2, float4>::type;
+  V v;
+  TIn s[kCPL];
+};
+
+template <typename TIn, bool VEC>
+__device__ __forceinline__ void load4(const TIn* row, int d, int D, bool ok, Raw4<TIn, VEC>& r) {
   if (VEC) {
-    if (sizeof(TIn) == 2) {
-      uint2 u = make_uint2(0, 0);
-      if (ok) u = *reinterpret_cast<const uint2*>(row + d);
-      v[0] = __uint_as_float(u.x << 16);
-      v[1] = __uint_as_float(u.x & 0xffff0000u);
-      v[2] = __uint_as_float(u.y << 16);
-      v[3] = __uint_as_float(u.y & 0xffff0000u);
-    } else {
-      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ok) f = *reinterpret_cast<const float4*>(row + d);
-      v[0] = f.x;
-      v[1] = f.y;
-      v[2] = f.z;
-      v[3] = f.w;
-    }
+    r.v = *reinterpret_cast<const typename Raw4<TIn, VEC>::V*>(row + (ok ? d : 0));
   } else {
 #pragma unroll
-    for (int c = 0; c < kCPL; ++c) v[c] = (ok && d + c < D) ? to_f32(row[d + c]) : 0.f;
+    for (int c = 0; c < kCPL; ++c) r.s[c] = row[min(ok ? d + c : 0, D - 1)];
+  }
+}
+
+template <typename TIn, bool VEC>
+__device__ __forceinline__ void cvt4(const Raw4<TIn, VEC>& r, int d, int D, bool ok, float* v) {
+  if (VEC) {
+    if constexpr (sizeof(TIn) == 2) {
+      v[0] = __uint_as_float(r.v.x << 16);
+      v[1] = __uint_as_float(r.v.x & 0xffff0000u);
+      v[2] = __uint_as_float(r.v.y << 16);
+      v[3] = __uint_as_float(r.v.y & 0xffff0000u);
+    } else {
+      v[0] = r.v.x;
+      v[1] = r.v.y;
+      v[2] = r.v.z;
+      v[3] = r.v.w;
+    }
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c) v[c] = ok ? v[c] : 0.f;
+  } else {
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c) v[c] = (ok && d + c < D) ? to_f32(r.s[c]) : 0.f;
+  }
+}
+
+// Wr rows of one 256-channel step in LDS, shared by the workgroup's four
+// waves (each owns different tokens): element (channel 4l + c, expert 4qe..)
+// sits at float4 index (c * EC/4 + qe) * 64 + l, so lane l's reads of its four
+// rows are contiguous across the wave (no bank conflicts).
+template <int EC>
+struct WStage {
+  static_assert(EC >= 4 && EC % 4 == 0, "experts are staged as float4s");
+  static constexpr int kVecs = 64 * kCPL * EC / 4;                  // float4s per step
+  static constexpr int kPerThread = (kVecs + kRouteThreads - 1) / kRouteThreads;
+  float4 v[kPerThread];
+};
+
+template <int EC, bool EXACT>
+__device__ __forceinline__ void wstage_load(const float* Wr, int D, int E, int dc, int tid,
+                                            WStage<EC>& st) {
+#pragma unroll
+  for (int j = 0; j < WStage<EC>::kPerThread; ++j) {
+    const int i = tid + kRouteThreads * j;
+    const int ch = i / (EC / 4), qe = i % (EC / 4);
+    const int d = dc + ch;
+    const int row = d < D ? d : D - 1;
+    const float* w = Wr + (size_t)row * E;
+    float4 v;
+    if (EXACT) {
+      v = *reinterpret_cast<const float4*>(w + qe * 4);
+    } else {
+      v = make_float4(w[min(qe * 4 + 0, E - 1)], w[min(qe * 4 + 1, E - 1)],
+                      w[min(qe * 4 + 2, E - 1)], w[min(qe * 4 + 3, E - 1)]);
+    }
+    const bool ok = i < WStage<EC>::kVecs && d < D;
+    st.v[j] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+template <int EC>
+__device__ __forceinline__ void wstage_store(float4* buf, int tid, const WStage<EC>& st) {
+#pragma unroll
+  for (int j = 0; j < WStage<EC>::kPerThread; ++j) {
+    const int i = tid + kRouteThreads * j;
+    if (i < WStage<EC>::kVecs) {
+      const int ch = i / (EC / 4), qe = i % (EC / 4);
+      const int l = ch / kCPL, c = ch % kCPL;
+      buf[(c * (EC / 4) + qe) * 64 + l] = st.v[j];
+    }
   }
 }
 
 // EXACT: E == EC (no padded experts).  VEC: D is a multiple of 4 and x is
-// aligned for 4-channel vector loads.
-template <typename TIn, int EC, bool EXACT, bool VEC>
+// aligned for 4-channel vector loads.  WLDS: Wr steps are staged in LDS and
+// shared by the workgroup's waves (4 <= EC <= 16).
+template <typename TIn, int EC, bool EXACT, bool VEC, bool WLDS>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restrict__ x,
                                                              const float* __restrict__ Wr,
                                                              int64_t T, int D, int E, int k,
@@ -64,7 +131,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
   const int64_t wave = (int64_t)blockIdx.x * (kRouteThreads / 64) +
                        uniform((int)(threadIdx.x >> 6));
   const int64_t t0 = wave * R;
-  if (t0 >= T) return;
+  // waves past the last token still take part in the staging barriers
+  if (!WLDS && t0 >= T) return;
+  const bool live = t0 < T;
 
   // partial logits acc[r * EC + e]
   float acc[64];
@@ -74,29 +143,82 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
   const TIn* rows[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rows[r] = x + (t0 + r < T ? t0 + r : T - 1) * D;
+  (void)live;
 
-  for (int dc = 0; dc < D; dc += 64 * kCPL) {
-    const int d = dc + lane * kCPL;
-    const bool ok = d < D;
-    float xv[R][kCPL];
+  // x rows of the next step are in flight while the current step computes
+  Raw4<TIn, VEC> xn[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], d, D, ok, xv[r]);
-    // Wr rows of this lane's channels.  Lanes past D (x = 0 there) and padded
-    // experts (lanes e >= E, never reported) read clamped, valid rows/columns.
-    float w[kCPL][EC];
+  for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], lane * kCPL, D, lane * kCPL < D, xn[r]);
+  if constexpr (WLDS) {
+    __shared__ float4 wbuf[2][WStage<EC>::kVecs];
+    const int tid = threadIdx.x;
+    WStage<EC> st;
+    wstage_load<EC, EXACT>(Wr, D, E, 0, tid, st);
+    wstage_store<EC>(wbuf[0], tid, st);
+    __syncthreads();
+    int buf = 0;
+    for (int dc = 0; dc < D; dc += 64 * kCPL, buf ^= 1) {
+      const int d = dc + lane * kCPL;
+      const bool ok = d < D;
+      const bool more = dc + 64 * kCPL < D;
+      float xv[R][kCPL];
 #pragma unroll
-    for (int c = 0; c < kCPL; ++c) {
-      const int row = ok ? (VEC ? d + c : min(d + c, D - 1)) : 0;
-      const float* wr = Wr + (size_t)row * E;
+      for (int r = 0; r < R; ++r) cvt4<TIn, VEC>(xn[r], d, D, ok, xv[r]);
+      if (more) {
+        const int dn = d + 64 * kCPL;
 #pragma unroll
-      for (int e = 0; e < EC; ++e) w[c][e] = wr[EXACT ? e : min(e, E - 1)];
+        for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], dn, D, dn < D, xn[r]);
+        wstage_load<EC, EXACT>(Wr, D, E, dc + 64 * kCPL, tid, st);
+      }
+#pragma unroll
+      for (int c = 0; c < kCPL; ++c) {
+        float w[EC];
+#pragma unroll
+        for (int qe = 0; qe < EC / 4; ++qe) {
+          const float4 v = wbuf[buf][(c * (EC / 4) + qe) * 64 + lane];
+          w[4 * qe + 0] = v.x;
+          w[4 * qe + 1] = v.y;
+          w[4 * qe + 2] = v.z;
+          w[4 * qe + 3] = v.w;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < EC; ++e) acc[r * EC + e] = fmaf(xv[r][c], w[e], acc[r * EC + e]);
+      }
+      if (more) wstage_store<EC>(wbuf[buf ^ 1], tid, st);
+      __syncthreads();
     }
+  } else {
+    for (int dc = 0; dc < D; dc += 64 * kCPL) {
+      const int d = dc + lane * kCPL;
+      const bool ok = d < D;
+      float xv[R][kCPL];
 #pragma unroll
-    for (int c = 0; c < kCPL; ++c)
+      for (int r = 0; r < R; ++r) cvt4<TIn, VEC>(xn[r], d, D, ok, xv[r]);
+      const int dn = d + 64 * kCPL;
+      if (dc + 64 * kCPL < D) {
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+        for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], dn, D, dn < D, xn[r]);
+      }
+      // Wr rows of this lane's channels.  Lanes past D (x = 0 there) and padded
+      // experts (lanes e >= E, never reported) read clamped, valid rows/columns.
+      float w[kCPL][EC];
 #pragma unroll
-        for (int e = 0; e < EC; ++e) acc[r * EC + e] = fmaf(xv[r][c], w[c][e], acc[r * EC + e]);
+      for (int c = 0; c < kCPL; ++c) {
+        const int row = ok ? (VEC ? d + c : min(d + c, D - 1)) : 0;
+        const float* wr = Wr + (size_t)row * E;
+#pragma unroll
+        for (int e = 0; e < EC; ++e) w[c][e] = wr[EXACT ? e : min(e, E - 1)];
+      }
+#pragma unroll
+      for (int c = 0; c < kCPL; ++c)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < EC; ++e)
+            acc[r * EC + e] = fmaf(xv[r][c], w[c][e], acc[r * EC + e]);
+    }
   }
 
   // transpose-reduce: at level m (32, 16, ..., 1) a lane keeps the half of its
@@ -155,7 +277,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
     }
     z += hw_exp2((bv - m0) * kLog2e);
   }
-  if (t < T && e < k) {
+  if (live && t < T && e < k) {
     idx[t * k + e] = my_idx;
     gate[t * k + e] = hw_exp2((my_sel - m0) * kLog2e) / z;
   }
@@ -172,18 +294,19 @@ int launch_route_t(const void* x, const float* Wr, int64_t T, int D, int E, int 
                    reinterpret_cast<uintptr_t>(x) % vec_bytes == 0;
   const TIn* xp = static_cast<const TIn*>(x);
   const bool exact = E == EC;
+  constexpr bool W = EC >= 4 && EC <= 16;  // whole float4s of experts, LDS-sized
   if (vec && exact)
-    hipLaunchKernelGGL((route_kernel<TIn, EC, true, true>), grid, block, 0, s, xp, Wr, T, D, E, k,
-                       idx, gate);
+    hipLaunchKernelGGL((route_kernel<TIn, EC, true, true, W>), grid, block, 0, s, xp, Wr, T, D, E,
+                       k, idx, gate);
   else if (vec)
-    hipLaunchKernelGGL((route_kernel<TIn, EC, false, true>), grid, block, 0, s, xp, Wr, T, D, E,
-                       k, idx, gate);
+    hipLaunchKernelGGL((route_kernel<TIn, EC, false, true, W>), grid, block, 0, s, xp, Wr, T, D,
+                       E, k, idx, gate);
   else if (exact)
-    hipLaunchKernelGGL((route_kernel<TIn, EC, true, false>), grid, block, 0, s, xp, Wr, T, D, E,
-                       k, idx, gate);
+    hipLaunchKernelGGL((route_kernel<TIn, EC, true, false, W>), grid, block, 0, s, xp, Wr, T, D,
+                       E, k, idx, gate);
   else
-    hipLaunchKernelGGL((route_kernel<TIn, EC, false, false>), grid, block, 0, s, xp, Wr, T, D, E,
-                       k, idx, gate);
+    hipLaunchKernelGGL((route_kernel<TIn, EC, false, false, W>), grid, block, 0, s, xp, Wr, T, D,
+                       E, k, idx, gate);
   return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
 }
 

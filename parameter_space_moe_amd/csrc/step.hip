@@ -9,17 +9,22 @@
 // so it is laid out for HBM streaming: four lanes share a channel and each owns
 // four consecutive states (one float4), so a wave reads and writes 1 KiB of
 // contiguous state per instruction.  The quad adds its partial readouts with
-// two lane exchanges.  A workgroup handles one slice of one batch row; when the
-// routing is not given, every workgroup first computes the router for its row
-// (the row is 2*D bytes, read from L2), which costs far less than a second
-// launch.
+// two lane exchanges.  A workgroup of 16 waves handles one batch row (or one
+// slice of a row when there are fewer rows than compute units).  When the
+// routing is not given, the workgroup first computes the router for its row:
+// 2*D bytes of x and the D x E router table, read once per row from L2, which
+// costs less than a second launch and an HBM round trip of the routing.
 #include "swimba_device.hpp"
 #include "swimba_internal.hpp"
 
 namespace swimba {
 namespace {
 
-constexpr int kStepThreads = 256;
+// One workgroup of 16 waves per batch row (or per slice of a row when the
+// batch is small): the row's router is computed once per workgroup, so Wr is
+// read once per row per step.
+constexpr int kStepThreads = 1024;
+constexpr int kStepWaves = kStepThreads / 64;
 constexpr int kStepChan = kStepThreads / 4;  // channels per workgroup iteration
 
 struct StepParams {
@@ -40,16 +45,46 @@ struct StepParams {
   void* y;
 };
 
+// Channels a thread handles per batch: all their loads are issued before any
+// of them is used, so each thread keeps 4 x 16 bytes of state in flight.
+constexpr int kBatch = 4;
+
+template <typename TIn>
+struct ChanLoads {
+  float4 h;
+  TIn x, r;
+};
+
 template <typename TIn, typename TOut>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
-  __shared__ float s_part[kStepThreads / 64][64];
+  __shared__ float s_part[kStepWaves][64];
   __shared__ int s_idx[64];
   __shared__ float s_gate[64];
   const int b = blockIdx.x / p.slices;
   const int slice = blockIdx.x % p.slices;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = uniform((int)(threadIdx.x >> 6)), lane = tid & 63;
   const TIn* X = reinterpret_cast<const TIn*>(p.x) + (size_t)b * p.D;
   const TIn* R = reinterpret_cast<const TIn*>(p.dt) + (size_t)b * p.D;
+  const int per = (p.D + p.slices - 1) / p.slices;
+  const int dbeg = slice * per, dend = min(p.D, dbeg + per);
+  float4* St = reinterpret_cast<float4*>(p.state) + (size_t)b * p.D * 4;
+  const int q = tid & 3;
+  const int cl = tid >> 2;
+
+  // state, x and dt_raw of this thread's first batch do not depend on the
+  // routing: start them before the router
+  auto issue = [&](int dc, ChanLoads<TIn>* L) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int d = dc + u * kStepChan + cl;
+      const int dd = d < dend ? d : dbeg;
+      L[u].h = St[(size_t)dd * 4 + q];
+      L[u].x = X[dd];
+      L[u].r = R[dd];
+    }
+  };
+  ChanLoads<TIn> cur[kBatch];
+  if (dbeg < dend) issue(dbeg, cur);
 
   if (p.idx != nullptr) {
     if (tid < p.k) {
@@ -59,18 +94,31 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     }
   } else {
     // router for row b (E <= 64): each thread sums a strided subset of the
-    // channels, then the wave adds with lane exchanges and the four waves add
-    // through LDS in a fixed order.
+    // channels (four at a time, loads first), then the wave adds with lane
+    // exchanges and the four waves add through LDS in a fixed order.
     for (int eb = 0; eb < p.E; eb += 8) {
       float part[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) part[i] = 0.f;
-      for (int d = tid; d < p.D; d += kStepThreads) {
-        const float xv = to_f32(X[d]);
-        const float* w = p.Wr + (size_t)d * p.E + eb;
+      for (int d0 = tid; d0 < p.D; d0 += 4 * kStepThreads) {
+        float xv[4], wv[4][8];
+        // unconditional loads from clamped (valid) addresses, masked after:
+        // a load under a branch would be waited on inside that branch
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (eb + i < p.E) part[i] = fmaf(xv, w[i], part[i]);
+        for (int u = 0; u < 4; ++u) {
+          const int d = d0 + u * kStepThreads;
+          const bool ok = d < p.D;
+          const int dd = ok ? d : 0;
+          const float xr = to_f32(X[dd]);
+          xv[u] = ok ? xr : 0.f;
+          const float* w = p.Wr + (size_t)dd * p.E;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wv[u][i] = w[min(eb + i, p.E - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) part[i] = fmaf(xv[u], wv[u][i], part[i]);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -84,7 +132,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     if (tid < p.E) {
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < kStepThreads / 64; ++w) v += s_part[w][tid];
+      for (int w = 0; w < kStepWaves; ++w) v += s_part[w][tid];
       s_part[0][tid] = v;  // column tid is read and written by thread tid only
     }
     __syncthreads();
@@ -119,8 +167,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
   }
 
   // state update: thread = (channel within the iteration, quad of states)
-  const int q = tid & 3;
-  const int cl = tid >> 2;
   const TIn* Bp = reinterpret_cast<const TIn*>(p.Bm) + (size_t)b * kN + 4 * q;
   const TIn* Cp = reinterpret_cast<const TIn*>(p.Cm) + (size_t)b * kN + 4 * q;
   float Bv[4], Cv[4];
@@ -129,46 +175,51 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     Bv[i] = to_f32(Bp[i]);
     Cv[i] = to_f32(Cp[i]);
   }
-  const int per = (p.D + p.slices - 1) / p.slices;
-  const int dbeg = slice * per, dend = min(p.D, dbeg + per);
   TOut* Y = reinterpret_cast<TOut*>(p.y) + (size_t)b * p.D;
-  float4* St = reinterpret_cast<float4*>(p.state) + (size_t)b * p.D * 4;
-  for (int dc = dbeg; dc < dend; dc += kStepChan) {
-    const int d = dc + cl;
-    const bool active = d < dend;
-    const int dd = active ? d : dbeg;
-    float4 h = St[(size_t)dd * 4 + q];
-    const float xv = to_f32(X[dd]), rv = to_f32(R[dd]);
-    float beta = 0.f, delta = 0.f;
-    float m[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < p.k; ++j) {
-      const int e = s_idx[j];
-      const float gj = s_gate[j];
-      beta = fmaf(gj, p.bias[(size_t)e * p.D + dd], beta);
-      delta = fmaf(gj, p.Dsk[(size_t)e * p.D + dd], delta);
-      const float4 a = *reinterpret_cast<const float4*>(p.A + ((size_t)e * p.D + dd) * kN + 4 * q);
-      m[0] = fmaf(gj, a.x, m[0]);
-      m[1] = fmaf(gj, a.y, m[1]);
-      m[2] = fmaf(gj, a.z, m[2]);
-      m[3] = fmaf(gj, a.w, m[3]);
-    }
-    const float dlt = softplus_f32(rv + beta);
-    const float dl2 = dlt * kLog2e, dx = dlt * xv;
-    float hv[4] = {h.x, h.y, h.z, h.w};
-    float yv = 0.f;
+  for (int dc = dbeg; dc < dend; dc += kBatch * kStepChan) {
+    ChanLoads<TIn> nxt[kBatch];
+    const int dn = dc + kBatch * kStepChan;
+    if (dn < dend) issue(dn, nxt);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = hw_exp2(dl2 * m[i]);
-      hv[i] = fmaf(a, hv[i], dx * Bv[i]);
-      yv = fmaf(Cv[i], hv[i], yv);
+    for (int u = 0; u < kBatch; ++u) {
+      const int d = dc + u * kStepChan + cl;
+      const bool active = d < dend;
+      const int dd = active ? d : dbeg;
+      const float xv = to_f32(cur[u].x), rv = to_f32(cur[u].r);
+      float beta = 0.f, delta = 0.f;
+      float m[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < p.k; ++j) {
+        const int e = s_idx[j];
+        const float gj = s_gate[j];
+        beta = fmaf(gj, p.bias[(size_t)e * p.D + dd], beta);
+        delta = fmaf(gj, p.Dsk[(size_t)e * p.D + dd], delta);
+        const float4 a =
+            *reinterpret_cast<const float4*>(p.A + ((size_t)e * p.D + dd) * kN + 4 * q);
+        m[0] = fmaf(gj, a.x, m[0]);
+        m[1] = fmaf(gj, a.y, m[1]);
+        m[2] = fmaf(gj, a.z, m[2]);
+        m[3] = fmaf(gj, a.w, m[3]);
+      }
+      const float dlt = softplus_f32(rv + beta);
+      const float dl2 = dlt * kLog2e, dx = dlt * xv;
+      float hv[4] = {cur[u].h.x, cur[u].h.y, cur[u].h.z, cur[u].h.w};
+      float yv = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = hw_exp2(dl2 * m[i]);
+        hv[i] = fmaf(a, hv[i], dx * Bv[i]);
+        yv = fmaf(Cv[i], hv[i], yv);
+      }
+      // quad sum of the readout (lanes 4c..4c+3 hold one channel)
+      yv += __shfl_xor(yv, 1, 64);
+      yv += __shfl_xor(yv, 2, 64);
+      if (active) {
+        St[(size_t)d * 4 + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        if (q == 0) Y[d] = from_f32<TOut>(fmaf(delta, xv, yv));
+      }
     }
-    // quad sum of the readout (lanes 4c..4c+3 hold one channel)
-    yv += __shfl_xor(yv, 1, 64);
-    yv += __shfl_xor(yv, 2, 64);
-    if (active) {
-      St[(size_t)d * 4 + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
-      if (q == 0) Y[d] = from_f32<TOut>(fmaf(delta, xv, yv));
-    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) cur[u] = nxt[u];
   }
 }
 
@@ -179,9 +230,9 @@ int launch_step_t(const swimba_step_args* a, hipStream_t s) {
   p.D = a->D;
   p.E = a->E;
   p.k = a->k;
-  // enough workgroups to fill the chip: ~4 per CU
+  // one workgroup per row; small batches split rows so every CU has work
   const int cus = device_cus();
-  int slices = (4 * cus + a->B - 1) / (a->B > 0 ? a->B : 1);
+  int slices = (cus + a->B - 1) / (a->B > 0 ? a->B : 1);
   const int maxs = (a->D + kStepChan - 1) / kStepChan;
   slices = slices < 1 ? 1 : (slices > maxs ? maxs : slices);
   p.slices = slices;
