@@ -110,9 +110,11 @@ typedef struct {
   float* h_final;               /* NULL = not written; [B, D, N] (separate: [B, E, D, N]) */
   int chunk;                    /* tokens per chunk; 0 = library's choice                 */
   swimba_carry carry;           /* chunk join method                                      */
-  hipEvent_t* phase_events;     /* NULL, or 4 events recorded on `stream`: before the
-                                   chunk pass, before the carry pass, before the fix-up
-                                   pass, after the fix-up pass (timing only)              */
+  hipEvent_t* phase_events;     /* NULL, or 6 timing events: start and end of the chunk
+                                   pass, of the carry pass and of the fix-up pass, in
+                                   that order, stamped by each pass's kernel dispatch
+                                   (no extra packets on `stream`); a pass that does not
+                                   run has both events recorded where it would run      */
 } swimba_scan_args;
 
 /*

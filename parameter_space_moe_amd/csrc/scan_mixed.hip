@@ -72,12 +72,11 @@ int launch_scan(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStre
 
 // Shared with the separate design (same chunk-carry arithmetic per state row).
 int launch_carry(int B, int C, int D, int E, const float* P, float* H, float* h_final,
-                 int separate, hipStream_t st) {
+                 int separate, hipStream_t st, const hipEvent_t* ev) {
   const size_t rows = separate ? (size_t)E * kN : kN;
   const size_t total = (size_t)B * rows * D;
-  hipLaunchKernelGGL(mixed::mix_carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, B,
-                     C, D, E, P, H, h_final, separate);
-  return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
+  return launch_timed(mixed::mix_carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                      0, st, ev, B, C, D, E, P, H, h_final, separate);
 }
 
 }  // namespace swimba

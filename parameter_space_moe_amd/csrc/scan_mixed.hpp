@@ -437,40 +437,31 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
 
   const size_t smem1 = smem_bytes(p.E, p.k, true, WAVES);
   const size_t smem3 = smem_bytes(p.E, p.k, false, WAVES);
-  hipEvent_t* ev = a->phase_events;
-  if (ev) (void)hipEventRecord(ev[0], st);
+  const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
   if (pl.nchunks <= 1) {
     p.nchunks = 1;
     dim3 grid((unsigned)((size_t)p.B * p.ntiles));
     allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, false>, smem3);
-    hipLaunchKernelGGL((mix_chunk_kernel<TIn, TOut, WAVES, K, false>), grid, dim3(WAVES * 64),
-                       smem3, st, p);
-    if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
-    if (ev) {
-      (void)hipEventRecord(ev[1], st);
-      (void)hipEventRecord(ev[2], st);
-      (void)hipEventRecord(ev[3], st);
-    }
+    const int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, false>, grid,
+                                dim3(WAVES * 64), smem3, st, ev, p);
+    if (rc != SWIMBA_OK) return rc;
+    record_skipped(ev ? ev + 2 : nullptr, st);
+    record_skipped(ev ? ev + 4 : nullptr, st);
     return SWIMBA_OK;
   }
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   dim3 grid1((unsigned)((size_t)p.B * ncg * p.ntiles));
   allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, true>, smem1);
-  hipLaunchKernelGGL((mix_chunk_kernel<TIn, TOut, WAVES, K, true>), grid1, dim3(WAVES * 64),
-                     smem1, st, p);
-  if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
-  if (ev) (void)hipEventRecord(ev[1], st);
-  const int rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 0, st);
+  int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, true>, grid1, dim3(WAVES * 64),
+                        smem1, st, ev, p);
   if (rc != SWIMBA_OK) return rc;
-  if (ev) (void)hipEventRecord(ev[2], st);
+  rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 0, st, ev ? ev + 2 : nullptr);
+  if (rc != SWIMBA_OK) return rc;
   const int ncg3 = (p.nchunks - 1 + WAVES - 1) / WAVES;
   dim3 grid3((unsigned)((size_t)p.B * ncg3 * p.ntiles));
   allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K>, smem3);
-  hipLaunchKernelGGL((mix_fixup_kernel<TIn, TOut, WAVES, K>), grid3, dim3(WAVES * 64), smem3, st,
-                     p);
-  if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
-  if (ev) (void)hipEventRecord(ev[3], st);
-  return SWIMBA_OK;
+  return launch_timed(mix_fixup_kernel<TIn, TOut, WAVES, K>, grid3, dim3(WAVES * 64), smem3, st,
+                      ev ? ev + 4 : nullptr, p);
 }
 
 template <typename TIn, typename TOut, int WAVES>

@@ -350,33 +350,30 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
   p.P = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_P) : nullptr;
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
   const size_t smem = sep_smem_bytes(p.E, p.k, W);
-  hipEvent_t* ev = a->phase_events;
-  if (ev) (void)hipEventRecord(ev[0], st);
+  const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
   allow_dynamic_lds(sep_kernel<TIn, TOut, EMAX, W, kPassSingle, K>, smem);
   allow_dynamic_lds(sep_kernel<TIn, TOut, EMAX, W, kPassFirst, K>, smem);
   allow_dynamic_lds(sep_kernel<TIn, TOut, EMAX, W, kPassFixup, K>, smem);
   if (pl.nchunks <= 1) {
-    hipLaunchKernelGGL((sep_kernel<TIn, TOut, EMAX, W, kPassSingle, K>),
-                       dim3((unsigned)((size_t)p.B * p.ntiles)), dim3(W * 64), smem, st, p);
-    if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
-    if (ev)
-      for (int i = 1; i < 4; ++i) (void)hipEventRecord(ev[i], st);
+    const int rc = launch_timed(sep_kernel<TIn, TOut, EMAX, W, kPassSingle, K>,
+                                dim3((unsigned)((size_t)p.B * p.ntiles)), dim3(W * 64), smem, st,
+                                ev, p);
+    if (rc != SWIMBA_OK) return rc;
+    record_skipped(ev ? ev + 2 : nullptr, st);
+    record_skipped(ev ? ev + 4 : nullptr, st);
     return SWIMBA_OK;
   }
   const int ncg1 = (p.nchunks + W - 1) / W;
-  hipLaunchKernelGGL((sep_kernel<TIn, TOut, EMAX, W, kPassFirst, K>),
-                     dim3((unsigned)((size_t)p.B * ncg1 * p.ntiles)), dim3(W * 64), smem, st, p);
-  if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
-  if (ev) (void)hipEventRecord(ev[1], st);
-  int rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 1, st);
+  int rc = launch_timed(sep_kernel<TIn, TOut, EMAX, W, kPassFirst, K>,
+                        dim3((unsigned)((size_t)p.B * ncg1 * p.ntiles)), dim3(W * 64), smem, st,
+                        ev, p);
   if (rc != SWIMBA_OK) return rc;
-  if (ev) (void)hipEventRecord(ev[2], st);
+  rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 1, st, ev ? ev + 2 : nullptr);
+  if (rc != SWIMBA_OK) return rc;
   const int ncg3 = (p.nchunks - 1 + W - 1) / W;
-  hipLaunchKernelGGL((sep_kernel<TIn, TOut, EMAX, W, kPassFixup, K>),
-                     dim3((unsigned)((size_t)p.B * ncg3 * p.ntiles)), dim3(W * 64), smem, st, p);
-  if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
-  if (ev) (void)hipEventRecord(ev[3], st);
-  return SWIMBA_OK;
+  return launch_timed(sep_kernel<TIn, TOut, EMAX, W, kPassFixup, K>,
+                      dim3((unsigned)((size_t)p.B * ncg3 * p.ntiles)), dim3(W * 64), smem, st,
+                      ev ? ev + 4 : nullptr, p);
 }
 
 template <typename TIn, typename TOut, int EMAX>

@@ -136,7 +136,7 @@ int run_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t s
   }
   if (a->B == 0 || a->L == 0) {
     if (a->phase_events)
-      for (int i = 0; i < 4; ++i) (void)hipEventRecord(a->phase_events[i], s);
+      for (int i = 0; i < 6; ++i) (void)hipEventRecord(a->phase_events[i], s);
     return empty_sequence(a, separate, s);
   }
   return separate ? launch_scan_separate(a, p, ws, s) : launch_scan(a, p, ws, s);

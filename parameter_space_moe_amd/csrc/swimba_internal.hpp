@@ -5,7 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
 
 #include "swimba.h"
 
@@ -31,7 +32,7 @@ int launch_scan_separate(const swimba_scan_args* a, const ScanPlan& p, void* ws,
 int launch_step(const swimba_step_args* a, hipStream_t s);
 // Pass 2 of the chunked scans: carried-in state per chunk (rows = 16 or E*16).
 int launch_carry(int B, int C, int D, int E, const float* P, float* H, float* h_final,
-                 int separate, hipStream_t st);
+                 int separate, hipStream_t st, const hipEvent_t* ev);
 
 // Compute units of the current device (cached per device).
 int device_cus();
@@ -43,6 +44,26 @@ inline void allow_dynamic_lds(Kernel kernel, size_t bytes) {
   if (bytes > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// Launch on `st`; when `ev` is given, ev[0] and ev[1] are stamped by the
+// dispatch itself at the kernel's start and end (no extra stream packets).
+template <typename... KArgs, typename... Args>
+inline int launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t smem,
+                        hipStream_t st, const hipEvent_t* ev, Args... args) {
+  if (ev)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)smem, st, ev[0], ev[1], 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, smem, st, args...);
+  return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
+}
+
+// Both events of a pass that does not run, recorded at this point of the stream.
+inline void record_skipped(const hipEvent_t* ev, hipStream_t st) {
+  if (ev) {
+    (void)hipEventRecord(ev[0], st);
+    (void)hipEventRecord(ev[1], st);
+  }
 }
 
 }  // namespace swimba

@@ -124,3 +124,37 @@ def gate_bound(idx, tol):
     2 g_j (1 - g_j) <= 1/2), plus a few fp32 roundings of exp and divide."""
     sel_tol = np.take_along_axis(tol, idx.astype(np.int64), axis=1)
     return 3e-7 + 0.5 * sel_tol.max(axis=1, keepdims=True)
+
+
+class HipEvents:
+    """Timing events through the HIP runtime's C API (for the scans'
+    phase_events argument, which takes raw hipEvent_t handles)."""
+
+    def __init__(self, n):
+        import ctypes
+        self._ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e)
+        self.array = (ctypes.c_void_p * n)(*[e.value for e in self.ev])
+
+    @property
+    def address(self):
+        return self._ct.addressof(self.array)
+
+    def ms(self, i, j):
+        v = self._ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self._ct.byref(v), self.ev[i], self.ev[j])
+        assert rc == 0, rc
+        return float(v.value)
+
+    def close(self):
+        for e in self.ev:
+            self.lib.hipEventDestroy(e)

@@ -17,8 +17,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (TOL_BF16, TOL_F32, assert_faithful_bf16, check_route, dev_tensors,
-                         gate_bound, host, rel_err, route_tolerance)
+from gpu_helpers import (TOL_BF16, TOL_F32, HipEvents, assert_faithful_bf16, check_route,
+                         dev_tensors, gate_bound, host, rel_err, route_tolerance)
 from parameter_space_moe_amd import swimba, workloads
 
 pytestmark = pytest.mark.gpu
@@ -244,6 +244,29 @@ def test_scan_deterministic():
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
     i2, g2 = route_on_gpu(t, w)
     assert torch.equal(idx, i2) and torch.equal(gate, g2)
+
+
+@pytest.mark.parametrize("separate", [False, True])
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_scan_phase_events(separate, chunk):
+    """The six phase events are stamped in pass order, the chunk and fix-up
+    passes take time when the sequence is chunked, and timing changes no output."""
+    w, inp, t = small_case(B=2, L=300, D=128, E=4, k=2, dtype="bf16", seed=33)
+    idx, gate = route_on_gpu(t, w)
+    fn = swimba.scan_separate if separate else swimba.scan
+    y0, h0_ = fn(*scan_args(t, idx, gate), chunk=chunk)
+    ev = HipEvents(6)
+    try:
+        y1, h1 = fn(*scan_args(t, idx, gate), chunk=chunk, phase_events=ev.address)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1) and torch.equal(h0_, h1)
+        for i in range(5):
+            assert ev.ms(i, i + 1) >= 0.0, (i, ev.ms(i, i + 1))
+        assert ev.ms(0, 1) > 0.0
+        if chunk:
+            assert ev.ms(4, 5) > 0.0
+    finally:
+        ev.close()
 
 
 def test_scan_split_composition():
