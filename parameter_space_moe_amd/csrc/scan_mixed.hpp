@@ -11,8 +11,8 @@
 // Layout of the work.  A lane owns one channel d of one sequence b and keeps its
 // 16 fp32 states in VGPRs for a whole chunk of tokens.  The 64 lanes of a wave
 // are 64 consecutive channels of the same token, so everything per token
-// (routing, gates, B_t, C_t) is wave-uniform and read through the scalar unit,
-// while x, dt_raw and y stream as coalesced 64-lane rows.  The expert tables
+// (routing, gates, B_t, C_t) is wave-uniform: a per-wave LDS ring stages it one
+// block of 8 tokens ahead, while x, dt_raw and y stream as coalesced 64-lane rows.  The expert tables
 // A[e, tile, :], dt_bias and Dskip of the wave's 64 channels are staged once in
 // LDS and read back as conflict-free 16-byte rows for the selected experts.
 // The waves of a workgroup are consecutive chunks of the same channel tile and
