@@ -57,83 +57,124 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Registers of one block's staging loads: a 16-byte piece of B_t or C_t per
-// lane, and up to KW routing words (idx, then gates).
-template <int KW>
-struct StageRegs {
-  uint4 piece;
-  int32_t word[KW];
-};
+// ---------------------------------------------------------------------------
+// Buffer-resource addressing.  Every streamed tensor is read and written as a
+// raw buffer whose base is the current block's first token: the per-lane part
+// of each address is a loop-invariant VGPR offset, the per-token part a scalar
+// offset, so the walk spends no vector instructions on addresses.  A buffer's
+// size is the valid part of the block: loads whose per-lane offset falls past
+// it return 0 and such stores are dropped.  The scalar offset is not part of
+// that check, so callers keep scalar offsets inside the valid rows.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-// Issue the loads of tokens [tb, tb + n) of sequence row `row` (n >= 1).  The
-// loads are unconditional -- positions past the block's last token re-read
-// that token -- so no branch waits on them before the commit.
-template <typename TIn, int KW, typename P>
-__device__ __forceinline__ void stage_issue(const P& p, size_t row, int tb, int n,
-                                            int k, int lane, StageRegs<KW>& r) {
-  constexpr int PPT = 16 * (int)sizeof(TIn) / 16;  // 16-byte pieces per token per vector
-  constexpr int NP = 2 * kTB * PPT;
-  const int q = lane < NP ? lane : NP - 1;
-  const int arr = q / (kTB * PPT), rr = q % (kTB * PPT), part = rr % PPT;
-  const int tok = min(rr / PPT, n - 1);
-  const TIn* base = reinterpret_cast<const TIn*>(arr ? p.Cm : p.Bm) + (row + tb) * kN;
-  const uint32_t o = (uint32_t)(tok * kN + part * (16 / (int)sizeof(TIn)));
-  r.piece = at32(reinterpret_cast<const uint4*>(base), o / (16 / (uint32_t)sizeof(TIn)));
-  const int nw = kTB * k;
-  const int32_t* ib = p.idx + (row + tb) * k;
-  const int32_t* gb = reinterpret_cast<const int32_t*>(p.gate) + (row + tb) * k;
-#pragma unroll
-  for (int i = 0; i < KW; ++i) {
-    int w = lane + 64 * i;
-    w = w < 2 * nw ? w : 2 * nw - 1;
-    const int arr2 = w / nw, r2 = w % nw;
-    const uint32_t at = (uint32_t)(min(r2 / k, n - 1) * k + r2 % k);
-    r.word[i] = arr2 ? at32(gb, at) : at32(ib, at);
-  }
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // third dword of a raw (untyped, unswizzled) buffer on gfx9-family parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
-// Convert the issued loads and write them to ring slot `slot`.
-template <typename TIn, int KW, typename P>
-__device__ __forceinline__ void stage_commit(const P& p, const Ring& ring, int slot,
-                                             int n, int k, int lane, const StageRegs<KW>& r,
-                                             int& gate_bad) {
-  constexpr int PPT = 16 * (int)sizeof(TIn) / 16;
-  const int q = lane;
-  if (q < 2 * kTB * PPT) {
-    const int arr = q / (kTB * PPT), rr = q % (kTB * PPT), tok = rr / PPT, part = rr % PPT;
-    float* dst = ring.bc + (slot * kTB + tok) * 32 + arr * 16 + part * (16 / sizeof(TIn));
-    if (sizeof(TIn) == 2) {
-      const uint32_t w4[4] = {r.piece.x, r.piece.y, r.piece.z, r.piece.w};
-      float4 lo = make_float4(__uint_as_float(w4[0] << 16), __uint_as_float(w4[0] & 0xffff0000u),
-                              __uint_as_float(w4[1] << 16), __uint_as_float(w4[1] & 0xffff0000u));
-      float4 hi = make_float4(__uint_as_float(w4[2] << 16), __uint_as_float(w4[2] & 0xffff0000u),
-                              __uint_as_float(w4[3] << 16), __uint_as_float(w4[3] & 0xffff0000u));
-      reinterpret_cast<float4*>(dst)[0] = lo;
-      reinterpret_cast<float4*>(dst)[1] = hi;
-    } else {
-      *reinterpret_cast<float4*>(dst) =
-          make_float4(__uint_as_float(r.piece.x), __uint_as_float(r.piece.y),
-                      __uint_as_float(r.piece.z), __uint_as_float(r.piece.w));
+template <typename T>
+__device__ __forceinline__ T buf_load(rsrc_t r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ bf16_t buf_load<bf16_t>(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+template <>
+__device__ __forceinline__ float buf_load<float>(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t voff, uint32_t soff, bf16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, (int)soff, 0);
+}
+
+// Buffer over tokens [tok, tok + n) of a [tokens, width] tensor of T.
+template <typename T>
+__device__ __forceinline__ rsrc_t rows_rsrc(const void* base, size_t tok, int n, int width) {
+  return make_rsrc(reinterpret_cast<const T*>(base) + tok * (size_t)width,
+                   (uint32_t)n * (uint32_t)width * (uint32_t)sizeof(T));
+}
+
+// Per-lane state of the staging loads of one block: the lane's 16-byte piece
+// of B_t and of C_t, and up to KW routing words of idx and of gate.  The lane
+// offsets are fixed for the whole walk.
+template <typename TIn, int KW>
+struct Stager {
+  static constexpr int kPieces = kTB * kN * (int)sizeof(TIn) / 16;  // per vector per block
+  uint32_t piece_off;
+  uint32_t word_off[KW];
+  v4u pb, pc;
+  int32_t wi[KW], wg[KW];
+
+  __device__ __forceinline__ void init(int lane) {
+    piece_off = (uint32_t)(lane % kPieces) * 16u;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) word_off[i] = (uint32_t)(lane + 64 * i) * 4u;
+  }
+
+  // Loads of tokens [tok, tok + kTB) (global token index); `valid` is how
+  // many of them exist in the tensors (later ones read as 0).
+  template <typename P>
+  __device__ __forceinline__ void issue(const P& p, size_t tok, int valid, int k) {
+    const rsrc_t rb = rows_rsrc<TIn>(p.Bm, tok, valid, kN);
+    const rsrc_t rc = rows_rsrc<TIn>(p.Cm, tok, valid, kN);
+    pb = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)piece_off, 0, 0);
+    pc = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)piece_off, 0, 0);
+    const rsrc_t ri = rows_rsrc<int32_t>(p.idx, tok, valid, k);
+    const rsrc_t rg = rows_rsrc<int32_t>(p.gate, tok, valid, k);
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+      wi[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (int)word_off[i], 0, 0);
+      wg[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rg, (int)word_off[i], 0, 0);
     }
   }
-  const int nw = kTB * k;
-#pragma unroll
-  for (int i = 0; i < KW; ++i) {
-    const int w = lane + 64 * i;
-    if (w < 2 * nw) {
-      const int arr = w / nw, rr = w % nw, tok = rr / k;
-      if (arr == 0) {
-        int e = r.word[i];
-        e = e < 0 ? 0 : (e >= p.E ? p.E - 1 : e);
-        ring.e[slot * nw + rr] = e;
+
+  // Convert and write to ring slot `slot`; n = tokens of the block that are
+  // used (their gates are checked for the contraction condition, g >= 0).
+  __device__ __forceinline__ void commit(const Ring& ring, int slot, int n, int k, int E,
+                                         int lane, int& gate_bad) const {
+    if (lane < kPieces) {
+      constexpr int kVals = 16 / (int)sizeof(TIn);  // values per piece
+      const int tok = lane * kVals / kN, col = lane * kVals % kN;
+      float* dst = ring.bc + (slot * kTB + tok) * 32 + col;
+      if (sizeof(TIn) == 2) {
+        const uint32_t b4[4] = {pb.x, pb.y, pb.z, pb.w}, c4[4] = {pc.x, pc.y, pc.z, pc.w};
+        float4* db = reinterpret_cast<float4*>(dst);
+        float4* dc = reinterpret_cast<float4*>(dst + kN);
+        db[0] = make_float4(__uint_as_float(b4[0] << 16), __uint_as_float(b4[0] & 0xffff0000u),
+                            __uint_as_float(b4[1] << 16), __uint_as_float(b4[1] & 0xffff0000u));
+        db[1] = make_float4(__uint_as_float(b4[2] << 16), __uint_as_float(b4[2] & 0xffff0000u),
+                            __uint_as_float(b4[3] << 16), __uint_as_float(b4[3] & 0xffff0000u));
+        dc[0] = make_float4(__uint_as_float(c4[0] << 16), __uint_as_float(c4[0] & 0xffff0000u),
+                            __uint_as_float(c4[1] << 16), __uint_as_float(c4[1] & 0xffff0000u));
+        dc[1] = make_float4(__uint_as_float(c4[2] << 16), __uint_as_float(c4[2] & 0xffff0000u),
+                            __uint_as_float(c4[3] << 16), __uint_as_float(c4[3] & 0xffff0000u));
       } else {
-        const float gv = __int_as_float(r.word[i]);
-        if (tok < n) gate_bad |= !(gv >= 0.f);
-        ring.g[slot * nw + rr] = gv;
+        *reinterpret_cast<float4*>(dst) = make_float4(
+            __uint_as_float(pb.x), __uint_as_float(pb.y), __uint_as_float(pb.z), __uint_as_float(pb.w));
+        *reinterpret_cast<float4*>(dst + kN) = make_float4(
+            __uint_as_float(pc.x), __uint_as_float(pc.y), __uint_as_float(pc.z), __uint_as_float(pc.w));
+      }
+    }
+    const int nw = kTB * k;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+      const int w = lane + 64 * i;
+      if (w < nw) {
+        int e = wi[i];
+        e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+        ring.e[slot * nw + w] = e;
+        const float gv = __int_as_float(wg[i]);
+        if (w / k < n) gate_bad |= !(gv >= 0.f);
+        ring.g[slot * nw + w] = gv;
       }
     }
   }
-}
+};
 
 }  // namespace stage
 }  // namespace swimba

@@ -41,10 +41,7 @@ namespace mixed {
 
 using stage::kTB;
 using stage::Ring;
-using stage::StageRegs;
 using stage::ring_bytes;
-using stage::stage_commit;
-using stage::stage_issue;
 using stage::wave_sync;
 
 constexpr float kFixupTol = 5.9604645e-08f;  // 2^-24
@@ -183,84 +180,91 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
 // Walk tokens [t0, t1) of sequence b for one lane, staging each block of kTB
 // tokens' uniform data and x/dt_raw one block ahead.  With TRACK and
 // `truncate`, stops once the carried part g has decayed on every lane.
-// Addresses are a wave-uniform block base plus a 32-bit per-lane offset, and
-// the prefetch loads are unconditional (clamped to the chunk) so that nothing
-// waits on them until the block that uses them.
+// x, dt_raw and y go through per-block buffer resources (scalar token offsets,
+// a fixed per-lane channel offset); the prefetch of the next block is issued
+// before the current one computes and is waited on only when it is used.
 template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U>
 __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U, int b, int t0,
                                      int t1, int d, bool active, bool full_tile, int lane,
                                      bool truncate, float* h, float* g, int& gate_bad) {
-  constexpr int KW = (2 * kTB * (K > 0 ? K : 16) + 63) / 64;
+  constexpr int KW = (kTB * (K > 0 ? K : 16) + 63) / 64;
   const int k = K > 0 ? K : p.k;
-  const TIn* X = reinterpret_cast<const TIn*>(p.x);
-  const TIn* R = reinterpret_cast<const TIn*>(p.dt);
-  TOut* Y = reinterpret_cast<TOut*>(p.y);
-  const size_t row = (size_t)b * p.L;
   const int D = p.D;
-  const int dd = active ? d : 0;
+  const size_t row = (size_t)b * p.L;
+  const size_t total = (size_t)p.B * p.L;
+  // lanes past D (ragged tile) read the next row's channels or 0, never stored
+  const uint32_t xoff = (uint32_t)d * (uint32_t)sizeof(TIn);
+  const uint32_t yoff = (uint32_t)d * (uint32_t)sizeof(TOut);
+  const uint32_t xrow = (uint32_t)D * (uint32_t)sizeof(TIn);
+  const uint32_t yrow = (uint32_t)D * (uint32_t)sizeof(TOut);
   TIn xc[kTB], rc[kTB], xn[kTB], rn[kTB];
-  StageRegs<KW> sr;
-
-  const int n0 = min(kTB, t1 - t0);
-  stage_issue<TIn, KW>(p, row, t0, n0, k, lane, sr);
-  {
-    const TIn* xb = X + (row + t0) * D;
-    const TIn* rb = R + (row + t0) * D;
+  stage::Stager<TIn, KW> st;
+  st.init(lane);
+  auto valid_at = [&](int t) { return (int)min((size_t)kTB, total - (row + t)); };
+  auto load_xr = [&](int t, TIn* xs, TIn* rs) {
+    const int v = valid_at(t);
+    const stage::rsrc_t rx = stage::rows_rsrc<TIn>(p.x, row + t, v, D);
+    const stage::rsrc_t rr = stage::rows_rsrc<TIn>(p.dt, row + t, v, D);
+    // the scalar offset is not range-checked by the hardware: rows past the
+    // tensor's end re-read its last row
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
-      const uint32_t o = (uint32_t)(min(i, n0 - 1) * D + dd);
-      xc[i] = at32(xb, o);
-      rc[i] = at32(rb, o);
+      const uint32_t so = (uint32_t)min(i, v - 1) * xrow;
+      xs[i] = stage::buf_load<TIn>(rx, xoff, so);
+      rs[i] = stage::buf_load<TIn>(rr, xoff, so);
     }
-  }
-  stage_commit<TIn, KW>(p, s.ring, 0, n0, k, lane, sr, gate_bad);
+  };
+
+  st.issue(p, row + t0, valid_at(t0), k);
+  load_xr(t0, xc, rc);
+  st.commit(s.ring, 0, min(kTB, t1 - t0), k, p.E, lane, gate_bad);
 
   int slot = 0;
   for (int tb = t0; tb < t1; tb += kTB, slot ^= 1) {
     const int n = min(kTB, t1 - tb);
     const int tn = tb + kTB;
-    const int nn = tn < t1 ? min(kTB, t1 - tn) : 0;
-    if (nn > 0) {
-      stage_issue<TIn, KW>(p, row, tn, nn, k, lane, sr);
-      const TIn* xb = X + (row + tn) * D;
-      const TIn* rb = R + (row + tn) * D;
-#pragma unroll
-      for (int i = 0; i < kTB; ++i) {
-        const uint32_t o = (uint32_t)(min(i, nn - 1) * D + dd);
-        xn[i] = at32(xb, o);
-        rn[i] = at32(rb, o);
-      }
+    const bool more = tn < t1;
+    if (more) {
+      st.issue(p, row + tn, valid_at(tn), k);
+      load_xr(tn, xn, rn);
     }
     wave_sync();
-    TOut* yb = Y + (row + tb) * D;
+    // stores past the block's n tokens fall outside this buffer and are dropped
+    const stage::rsrc_t ry = stage::rows_rsrc<TOut>(p.y, row + tb, n, D);
     // full blocks on full tiles run as one branch-free basic block of kTB
     // tokens, so the scheduler can overlap a token's LDS reads with the
     // previous token's arithmetic; the ragged tail keeps its guards
     const bool fast = n == kTB && full_tile;
     if constexpr (K > 0) {
-      // the block's routing, once, into SGPRs
-      int eb[kTB * K];
-      float gb[kTB * K];
-#pragma unroll
-      for (int w = 0; w < kTB * K; ++w) {
-        eb[w] = uniform(s.ring.e[slot * kTB * K + w]);
-        gb[w] = uniform(s.ring.g[slot * kTB * K + w]);
-      }
       if (fast) {
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
-          const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, eb + i * K, gb + i * K, slot, i,
-                                                      lane, to_f32(xc[i]), to_f32(rc[i]), h, g);
-          at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+          int ev[K];
+          float gv[K];
+#pragma unroll
+          for (int j = 0; j < K; ++j) {
+            ev[j] = s.ring.e[(slot * kTB + i) * K + j];
+            gv[j] = s.ring.g[(slot * kTB + i) * K + j];
+          }
+          const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, ev, gv, slot, i, lane,
+                                                      to_f32(xc[i]), to_f32(rc[i]), h, g);
+          stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
       } else {
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
           if (i < n) {
+            int ev[K];
+            float gv[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+              ev[j] = s.ring.e[(slot * kTB + i) * K + j];
+              gv[j] = s.ring.g[(slot * kTB + i) * K + j];
+            }
             const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
-            const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, eb + i * K, gb + i * K, slot,
-                                                        i, lane, xv, rv, h, g);
-            if (active) at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+            const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, ev, gv, slot, i, lane, xv, rv,
+                                                        h, g);
+            if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
           }
         }
       }
@@ -277,7 +281,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
           const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
           const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, eb, gb, slot, i, lane, xv, rv, h,
                                                       g);
-          if (active) at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+          if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
       }
     }
@@ -291,8 +295,8 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
       for (int q = 0; q < kN; ++q) conv &= fabsf(g[q]) <= thr;  // NaN: not converged
       if (__all(conv)) break;
     }
-    if (nn > 0) {
-      stage_commit<TIn, KW>(p, s.ring, slot ^ 1, nn, k, lane, sr, gate_bad);
+    if (more) {
+      st.commit(s.ring, slot ^ 1, min(kTB, t1 - tn), k, p.E, lane, gate_bad);
 #pragma unroll
       for (int i = 0; i < kTB; ++i) {
         xc[i] = xn[i];

@@ -24,10 +24,7 @@ namespace sep {
 
 using stage::kTB;
 using stage::Ring;
-using stage::StageRegs;
 using stage::ring_bytes;
-using stage::stage_commit;
-using stage::stage_issue;
 using stage::wave_sync;
 
 struct SepParams {
@@ -143,50 +140,49 @@ __device__ __forceinline__ void walk_sep(const SepParams& p, const float4* sA, c
                                          const Ring& ring, int b, int t0, int t1, int d,
                                          bool active, int lane, float (&H)[EMAX][kN],
                                          float (&S)[EMAX]) {
-  constexpr int KW = (2 * kTB * (K > 0 ? K : 16) + 63) / 64;
+  constexpr int KW = (kTB * (K > 0 ? K : 16) + 63) / 64;
   const int k = K > 0 ? K : p.k;
-  const TIn* X = reinterpret_cast<const TIn*>(p.x);
-  const TIn* R = reinterpret_cast<const TIn*>(p.dt);
-  TOut* Y = reinterpret_cast<TOut*>(p.y);
-  const size_t row = (size_t)b * p.L;
   const int D = p.D;
-  const int dd = active ? d : 0;
+  const size_t row = (size_t)b * p.L;
+  const size_t total = (size_t)p.B * p.L;
+  const uint32_t xoff = (uint32_t)d * (uint32_t)sizeof(TIn);
+  const uint32_t yoff = (uint32_t)d * (uint32_t)sizeof(TOut);
+  const uint32_t xrow = (uint32_t)D * (uint32_t)sizeof(TIn);
+  const uint32_t yrow = (uint32_t)D * (uint32_t)sizeof(TOut);
   TIn xc[kTB], rc[kTB], xn[kTB], rn[kTB];
-  StageRegs<KW> sr;
+  stage::Stager<TIn, KW> st;
+  st.init(lane);
   int gate_bad = 0;
-
-  const int n0 = min(kTB, t1 - t0);
-  stage_issue<TIn, KW>(p, row, t0, n0, k, lane, sr);
-  {
-    const TIn* xb = X + (row + t0) * D;
-    const TIn* rb = R + (row + t0) * D;
+  auto valid_at = [&](int t) { return (int)min((size_t)kTB, total - (row + t)); };
+  auto load_xr = [&](int t, TIn* xs, TIn* rs) {
+    const int v = valid_at(t);
+    const stage::rsrc_t rx = stage::rows_rsrc<TIn>(p.x, row + t, v, D);
+    const stage::rsrc_t rr = stage::rows_rsrc<TIn>(p.dt, row + t, v, D);
+    // the scalar offset is not range-checked by the hardware: rows past the
+    // tensor's end re-read its last row
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
-      const uint32_t o = (uint32_t)(min(i, n0 - 1) * D + dd);
-      xc[i] = at32(xb, o);
-      rc[i] = at32(rb, o);
+      const uint32_t so = (uint32_t)min(i, v - 1) * xrow;
+      xs[i] = stage::buf_load<TIn>(rx, xoff, so);
+      rs[i] = stage::buf_load<TIn>(rr, xoff, so);
     }
-  }
-  stage_commit<TIn, KW>(p, ring, 0, n0, k, lane, sr, gate_bad);
+  };
+
+  st.issue(p, row + t0, valid_at(t0), k);
+  load_xr(t0, xc, rc);
+  st.commit(ring, 0, min(kTB, t1 - t0), k, p.E, lane, gate_bad);
 
   int slot = 0;
   for (int tb = t0; tb < t1; tb += kTB, slot ^= 1) {
     const int n = min(kTB, t1 - tb);
     const int tn = tb + kTB;
-    const int nn = tn < t1 ? min(kTB, t1 - tn) : 0;
-    if (nn > 0) {
-      stage_issue<TIn, KW>(p, row, tn, nn, k, lane, sr);
-      const TIn* xb = X + (row + tn) * D;
-      const TIn* rb = R + (row + tn) * D;
-#pragma unroll
-      for (int i = 0; i < kTB; ++i) {
-        const uint32_t o = (uint32_t)(min(i, nn - 1) * D + dd);
-        xn[i] = at32(xb, o);
-        rn[i] = at32(rb, o);
-      }
+    const bool more = tn < t1;
+    if (more) {
+      st.issue(p, row + tn, valid_at(tn), k);
+      load_xr(tn, xn, rn);
     }
     wave_sync();
-    TOut* yb = Y + (row + tb) * D;
+    const stage::rsrc_t ry = stage::rows_rsrc<TOut>(p.y, row + tb, n, D);
     if constexpr (K > 0) {
       // the block's routing, once, into SGPRs
       int eb[kTB * K];
@@ -203,7 +199,8 @@ __device__ __forceinline__ void walk_sep(const SepParams& p, const float4* sA, c
           const float4* bc = reinterpret_cast<const float4*>(ring.bc + (slot * kTB + i) * 32);
           const float yv = sep_token<READOUT, EMAX, K>(H, S, eb + i * K, gb + i * K, K, sA, sBD,
                                                        bc, lane, xv, rv);
-          if (READOUT && active) at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+          if (READOUT && active)
+            stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
       }
     } else {
@@ -219,12 +216,13 @@ __device__ __forceinline__ void walk_sep(const SepParams& p, const float4* sA, c
           const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
           const float4* bc = reinterpret_cast<const float4*>(ring.bc + (slot * kTB + i) * 32);
           const float yv = sep_token<READOUT, EMAX, K>(H, S, eb, gb, k, sA, sBD, bc, lane, xv, rv);
-          if (READOUT && active) at32(yb, (uint32_t)(i * D + d)) = from_f32<TOut>(yv);
+          if (READOUT && active)
+            stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
       }
     }
-    if (nn > 0) {
-      stage_commit<TIn, KW>(p, ring, slot ^ 1, nn, k, lane, sr, gate_bad);
+    if (more) {
+      st.commit(ring, slot ^ 1, min(kTB, t1 - tn), k, p.E, lane, gate_bad);
 #pragma unroll
       for (int i = 0; i < kTB; ++i) {
         xc[i] = xn[i];
