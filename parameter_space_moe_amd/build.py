@@ -22,11 +22,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-# Per-source flags.  scan_separate: keep SimplifyCFG from merging the
-# per-expert branches into one dynamically indexed update (that would move the
-# expert states from VGPRs to scratch memory).
-PER_SOURCE = {"scan_separate_%s.hip" % t: ["-mllvm", "-simplifycfg-sink-common=false"]
-              for t in ("ff", "fb", "bf", "bb")}
+# Per-source flags (none at present).
+PER_SOURCE: dict[str, list[str]] = {}
 # the host pass does not know the device-only feature name: drop that warning
 _NOISE = "is not a recognized feature for this target"
 

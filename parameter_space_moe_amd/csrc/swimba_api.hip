@@ -79,18 +79,25 @@ int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p) {
   }
   int chunk = a->chunk;
   if (chunk == 0) {
-    // Aim for about four resident waves per SIMD (16 per CU) from the
-    // independent (b, tile) recurrences, then cut sequences into chunks no
-    // shorter than a few fix-up horizons.
     const long long cus = device_cus();
-    const long long target = 16 * cus / (separate ? 2 : 1);
     const long long base = (long long)a->B * p->ntiles;
-    long long want = (target + base - 1) / base;
-    const int min_chunk = separate ? 256 : 128;
-    long long maxc = (a->L + min_chunk - 1) / min_chunk;
+    long long want, min_chunk;
+    if (separate) {
+      // a workgroup per (sequence, tile, chunk) with one wave per expert: aim
+      // for four workgroups per CU (two resident, two rounds)
+      want = (4 * cus + base - 1) / base;
+      min_chunk = 64;
+    } else {
+      // about four resident waves per SIMD (16 per CU) from the independent
+      // (b, tile) recurrences, in chunks no shorter than a few fix-up horizons
+      want = (16 * cus + base - 1) / base;
+      min_chunk = 128;
+    }
+    const long long maxc = (a->L + min_chunk - 1) / min_chunk;
     if (want > maxc) want = maxc;
     if (want < 1) want = 1;
     chunk = (int)((a->L + want - 1) / want);
+    if (separate) chunk = (int)(((long long)chunk + 63) / 64 * 64);  // whole staging rounds
   }
   if (chunk > a->L) chunk = a->L;
   p->chunk = chunk;

@@ -98,10 +98,11 @@ def test_route_workload(name):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D,E,k", [(100, 1, 1), (100, 3, 2), (96, 5, 5), (64, 17, 3),
-                                   (72, 64, 4), (1, 8, 2), (513, 16, 16)])
+                                   (72, 64, 4), (1, 8, 2), (513, 16, 16), (1030, 5, 2),
+                                   (2048, 8, 2), (1100, 33, 4), (4099, 16, 3)])
 def test_route_shapes(dtype, D, E, k):
     """Ragged D (scalar staging path), E not a kernel width, the wide-E path,
-    k = E, D = 1, and a token count that is not a multiple of 64."""
+    k = E, D = 1, a token count that is not a multiple of 64, and wide rows."""
     w, inp, t = small_case(B=3, L=45, D=D, E=E, k=k, dtype=dtype, seed=D + E)
     idx, gate = route_on_gpu(t, w)
     gi = idx.cpu().numpy().reshape(-1, k)
