@@ -12,8 +12,9 @@
 // the full logit of (token l / EC, expert l % EC).  The top k of a token are
 // picked by a tournament among its EC lanes.
 //
-// Rounding.  Each lane sums its D/64 channels in order, then the 6 levels add
-// pairs, so the fp32 logit differs from the exact sum by at most
+// Rounding.  Each lane sums its D/64 channels in the workgroup's step order,
+// then the 6 levels add pairs, so the fp32 logit differs from the exact sum by
+// at most
 // gamma_m * sum_d |x_d Wr[d,e]| with m = ceil(D / 64) + 6,
 // gamma_m = m u / (1 - m u), u = 2^-24.
 #pragma once
@@ -145,30 +146,44 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
   for (int r = 0; r < R; ++r) rows[r] = x + (t0 + r < T ? t0 + r : T - 1) * D;
   (void)live;
 
+  // Steps of 256 channels, visited from a per-workgroup starting step: every
+  // workgroup reads all of Wr, and staggered starts spread those reads over
+  // the L2 channels instead of sending all compute units to the same lines.
+  constexpr int kStep = 64 * kCPL;
+  const int nsteps = (D + kStep - 1) / kStep;
+  const int s0 = (int)(blockIdx.x % (unsigned)nsteps);
+  auto step_base = [&](int i) {
+    const int st = s0 + i;
+    return (st >= nsteps ? st - nsteps : st) * kStep;
+  };
+
   // x rows of the next step are in flight while the current step computes
   Raw4<TIn, VEC> xn[R];
+  {
+    const int d = step_base(0) + lane * kCPL;
 #pragma unroll
-  for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], lane * kCPL, D, lane * kCPL < D, xn[r]);
+    for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], d, D, d < D, xn[r]);
+  }
   if constexpr (WLDS) {
     __shared__ float4 wbuf[2][WStage<EC>::kVecs];
     const int tid = threadIdx.x;
     WStage<EC> st;
-    wstage_load<EC, EXACT>(Wr, D, E, 0, tid, st);
+    wstage_load<EC, EXACT>(Wr, D, E, step_base(0), tid, st);
     wstage_store<EC>(wbuf[0], tid, st);
     __syncthreads();
     int buf = 0;
-    for (int dc = 0; dc < D; dc += 64 * kCPL, buf ^= 1) {
-      const int d = dc + lane * kCPL;
+    for (int i = 0; i < nsteps; ++i, buf ^= 1) {
+      const int d = step_base(i) + lane * kCPL;
       const bool ok = d < D;
-      const bool more = dc + 64 * kCPL < D;
+      const bool more = i + 1 < nsteps;
       float xv[R][kCPL];
 #pragma unroll
       for (int r = 0; r < R; ++r) cvt4<TIn, VEC>(xn[r], d, D, ok, xv[r]);
       if (more) {
-        const int dn = d + 64 * kCPL;
+        const int dcn = step_base(i + 1), dn = dcn + lane * kCPL;
 #pragma unroll
         for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], dn, D, dn < D, xn[r]);
-        wstage_load<EC, EXACT>(Wr, D, E, dc + 64 * kCPL, tid, st);
+        wstage_load<EC, EXACT>(Wr, D, E, dcn, tid, st);
       }
 #pragma unroll
       for (int c = 0; c < kCPL; ++c) {
@@ -190,14 +205,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
       __syncthreads();
     }
   } else {
-    for (int dc = 0; dc < D; dc += 64 * kCPL) {
-      const int d = dc + lane * kCPL;
+    for (int i = 0; i < nsteps; ++i) {
+      const int d = step_base(i) + lane * kCPL;
       const bool ok = d < D;
       float xv[R][kCPL];
 #pragma unroll
       for (int r = 0; r < R; ++r) cvt4<TIn, VEC>(xn[r], d, D, ok, xv[r]);
-      const int dn = d + 64 * kCPL;
-      if (dc + 64 * kCPL < D) {
+      const int dn = step_base(i + 1 < nsteps ? i + 1 : i) + lane * kCPL;
+      if (i + 1 < nsteps) {
 #pragma unroll
         for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], dn, D, dn < D, xn[r]);
       }

@@ -95,8 +95,16 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
   } else {
     // router for row b (E <= 64): each thread sums a strided subset of the
     // channels (four at a time, loads first), then the wave adds with lane
-    // exchanges and the four waves add through LDS in a fixed order.
+    // exchanges and the waves add through LDS in a fixed order.  Rows of Wr
+    // are read as 16-byte vectors when E is a multiple of 4 (one cache-line
+    // visit per row instead of one per expert).
+    const bool vec = (p.E & 3) == 0 && (reinterpret_cast<uintptr_t>(p.Wr) & 15) == 0;
+    // Every workgroup reads all of Wr at the same time; starting each at a
+    // different channel spreads the reads over the L2 channels instead of
+    // sending all compute units to the same lines at once.
+    const int rot = (int)(((long long)blockIdx.x * 1031) % p.D);
     for (int eb = 0; eb < p.E; eb += 8) {
+      const bool two = eb + 4 < p.E;  // the block's second group of 4 exists
       float part[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) part[i] = 0.f;
@@ -104,16 +112,39 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
         float xv[4], wv[4][8];
         // unconditional loads from clamped (valid) addresses, masked after:
         // a load under a branch would be waited on inside that branch
+        if (vec) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int d = d0 + u * kStepThreads;
-          const bool ok = d < p.D;
-          const int dd = ok ? d : 0;
-          const float xr = to_f32(X[dd]);
-          xv[u] = ok ? xr : 0.f;
-          const float* w = p.Wr + (size_t)dd * p.E;
+          for (int u = 0; u < 4; ++u) {
+            const int d = d0 + u * kStepThreads;
+            const bool ok = d < p.D;
+            const int dr = d + rot;
+            const int dd = ok ? (dr >= p.D ? dr - p.D : dr) : 0;
+            const float xr = to_f32(X[dd]);
+            xv[u] = ok ? xr : 0.f;
+            const float4* w4 = reinterpret_cast<const float4*>(p.Wr + (size_t)dd * p.E + eb);
+            const float4 lo = w4[0], hi = w4[two ? 1 : 0];
+            wv[u][0] = lo.x;
+            wv[u][1] = lo.y;
+            wv[u][2] = lo.z;
+            wv[u][3] = lo.w;
+            wv[u][4] = hi.x;
+            wv[u][5] = hi.y;
+            wv[u][6] = hi.z;
+            wv[u][7] = hi.w;
+          }
+        } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) wv[u][i] = w[min(eb + i, p.E - 1)];
+          for (int u = 0; u < 4; ++u) {
+            const int d = d0 + u * kStepThreads;
+            const bool ok = d < p.D;
+            const int dr = d + rot;
+            const int dd = ok ? (dr >= p.D ? dr - p.D : dr) : 0;
+            const float xr = to_f32(X[dd]);
+            xv[u] = ok ? xr : 0.f;
+            const float* w = p.Wr + (size_t)dd * p.E;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wv[u][i] = w[min(eb + i, p.E - 1)];
+          }
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -129,35 +160,49 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
       }
     }
     __syncthreads();
-    if (tid < p.E) {
+    if (wave == 0) {
+      // lane e holds logit e (waves added in order); top-k by a tournament
+      // over the lanes: (logit desc, expert asc); softmax over the selected
       float v = 0.f;
+      if (lane < p.E) {
 #pragma unroll
-      for (int w = 0; w < kStepWaves; ++w) v += s_part[w][tid];
-      s_part[0][tid] = v;  // column tid is read and written by thread tid only
-    }
-    __syncthreads();
-    if (tid == 0) {
-      // top-k by (logit desc, expert asc); softmax over the selected logits
-      uint64_t taken = 0;
-      float m = 0.f, z = 0.f;
+        for (int w = 0; w < kStepWaves; ++w) v += s_part[w][lane];
+      }
+      bool free_e = lane < p.E;
+      float m = 0.f, z = 0.f, my_l = 0.f;
       for (int j = 0; j < p.k; ++j) {
-        int best = -1;
-        float bv = 0.f;
-        for (int e = 0; e < p.E; ++e) {
-          if ((taken >> e) & 1ull) continue;
-          const float v = s_part[0][e];
-          if (best < 0 || v > bv) {
-            best = e;
-            bv = v;
+        float bv = v;
+        int be = lane;
+        bool bc = free_e;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float ov = __shfl_xor(bv, off, 64);
+          const int oe = __shfl_xor(be, off, 64);
+          const bool oc = __shfl_xor((int)bc, off, 64) != 0;
+          bool take;
+          if (!bc)
+            take = oc;
+          else if (!oc)
+            take = false;
+          else if (oe < be)
+            take = !(bv > ov);
+          else
+            take = ov > bv;
+          if (take) {
+            bv = ov;
+            be = oe;
+            bc = true;
           }
         }
-        taken |= 1ull << best;
+        if (lane == be) free_e = false;
         if (j == 0) m = bv;
-        s_idx[j] = best;
-        s_gate[j] = bv;
+        if (lane == j) {
+          my_l = bv;
+          s_idx[j] = be;
+        }
+        z += hw_exp2((bv - m) * kLog2e);
       }
-      for (int j = 0; j < p.k; ++j) z += hw_exp2((s_gate[j] - m) * kLog2e);
-      for (int j = 0; j < p.k; ++j) s_gate[j] = hw_exp2((s_gate[j] - m) * kLog2e) / z;
+      if (lane < p.k) s_gate[lane] = hw_exp2((my_l - m) * kLog2e) / z;
     }
   }
   __syncthreads();
