@@ -78,20 +78,28 @@ int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p) {
     return SWIMBA_OK;
   }
   int chunk = a->chunk;
+  bool small = false;  // mixed scan with too little work for four waves per SIMD
   if (chunk == 0) {
     const long long cus = device_cus();
     const long long base = (long long)a->B * p->ntiles;
-    long long want, min_chunk;
+    long long want, min_chunk = 128;
     if (separate) {
       // a workgroup per (sequence, tile, chunk) with one wave per expert: aim
       // for four workgroups per CU (two resident, two rounds)
       want = (4 * cus + base - 1) / base;
       min_chunk = 64;
-    } else {
+    } else if (base * (a->L / 256) >= 16 * cus) {
       // about four resident waves per SIMD (16 per CU) from the independent
       // (b, tile) recurrences, in chunks no shorter than a few fix-up horizons
       want = (16 * cus + base - 1) / base;
-      min_chunk = 128;
+    } else {
+      // Too few recurrences for that: two 4-wave workgroups per CU (two
+      // waves per SIMD, every SIMD busy), i.e. the largest multiple of 4
+      // chunks per tile whose workgroups all fit at once.
+      small = a->E <= 8;
+      want = 2 * 4 * cus / base;
+      if (small && want >= 4) want = want / 4 * 4;
+      min_chunk = 64;
     }
     const long long maxc = (a->L + min_chunk - 1) / min_chunk;
     if (want > maxc) want = maxc;
@@ -103,8 +111,8 @@ int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p) {
   p->chunk = chunk;
   p->nchunks = (int)(((long long)a->L + chunk - 1) / chunk);
   // chunks of one tile share the workgroup's expert table: 8 waves when there
-  // are enough chunks to fill them
-  if (!separate && p->nchunks >= 8) p->waves = 8;
+  // are enough chunks to fill them (and the problem is not the small case)
+  if (!separate && p->nchunks >= 8 && !small) p->waves = 8;
   if (p->nchunks > 1) {
     const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N : SWIMBA_STATE_N;
     const size_t arr = (size_t)a->B * p->nchunks * rows * a->D * sizeof(float);
