@@ -19,6 +19,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -269,6 +270,46 @@ def _time(fn, reps, warm=2):
     return (time.perf_counter() - t0) * 1e3 / reps
 
 
+def expert_sweep(swimba, dev, reps):
+    """Router + mixed scan at the Mamba-1.4B-like layer shape (B=8, L=4096,
+    D=4096, top-2) for E = 2, 4, 8, 16 experts: the active experts, not the
+    total, set the cost ("Fondements Théoriques", Theorem 2).  Inputs are
+    seeded normal draws made on the GPU; E = 32 is beyond the scans' 16."""
+    import torch
+    B, L, D, k = 8, 4096, 4096, 2
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    bf = torch.bfloat16
+    x = torch.randn((B, L, D), generator=g, device=dev).to(bf)
+    dtr = torch.randn((B, L, D), generator=g, device=dev).to(bf)
+    Bm = torch.randn((B, L, N_STATE), generator=g, device=dev).to(bf)
+    Cm = torch.randn((B, L, N_STATE), generator=g, device=dev).to(bf)
+    y = torch.empty((B, L, D), dtype=bf, device=dev)
+    hf = torch.empty((B, D, N_STATE), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, L, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((B, L, k), dtype=torch.float32, device=dev)
+    out = {"shape": "B=%d L=%d D=%d k=%d bf16" % (B, L, D, k)}
+    base = None
+    for E in (2, 4, 8, 16):
+        Wr = torch.randn((D, E), generator=g, device=dev) / D ** 0.5
+        A = -torch.exp(torch.rand((E, D, N_STATE), generator=g, device=dev) * math.log(16.0))
+        bias = torch.randn((E, D), generator=g, device=dev) * 0.1 ** 0.5
+        Dsk = torch.randn((E, D), generator=g, device=dev)
+        route = swimba.PreparedRoute(x, Wr, k, idx, gate)
+        scan = swimba.PreparedScan(False, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y=y,
+                                   h_final=hf)
+
+        def step():
+            route()
+            scan()
+
+        ms = _time(step, reps)
+        base = base or ms
+        out["E%d" % E] = {"ms": round(ms, 4), "G_tc_per_s": round(B * L * D / ms / 1e6, 3),
+                          "over_E2": round(ms / base, 3)}
+    return out
+
+
 def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gate, y, hf):
     import numpy as np
     import torch
@@ -298,6 +339,26 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
     ms_dense = _time(dense, reps)
     res["dense_scan"] = {"ms": round(ms_dense, 4), "G_tc_per_s": round(tc / ms_dense / 1e6, 3),
                          "mixed_over_dense": round(ms_mixed / ms_dense, 3)}
+    # the timed step again, one step at a time, each after writing 512 MB so
+    # that the 256 MB Infinity Cache holds none of its inputs (this workload's
+    # inputs fit in it, so back-to-back steps read them from the cache)
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    route = swimba.PreparedRoute(x, Wr, w.k, idx, gate)
+    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    evs = [(hip.event(), hip.event()) for _ in range(reps)]
+    for e0, e1 in evs:
+        flush.fill_(1.0)
+        hip.record(e0, stream)
+        route()
+        mixed()
+        hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms_cold = sum(hip.ms(e0, e1) for e0, e1 in evs) / reps
+    res["step_mall_flushed"] = {"ms": round(ms_cold, 4), "G_tc_per_s": round(tc / ms_cold / 1e6, 3),
+                                "note": "route + mixed scan after a 512 MB write, HIP events"}
+    del flush
+    res["expert_sweep"] = expert_sweep(swimba, dev, reps)
     # decode workload: 128 routed steps on a persistent fp32 state
     wd = workloads.BY_NAME["decode"]
     p, steps = workloads.decode_steps(wd)
