@@ -48,6 +48,8 @@ struct StepParams {
 // Channels a thread handles per batch: all their loads are issued before any
 // of them is used, so each thread keeps 4 x 16 bytes of state in flight.
 constexpr int kBatch = 4;
+// Channels a thread reads per round of the fused router (loads first).
+constexpr int kRU = 4;
 
 template <typename TIn>
 struct ChanLoads {
@@ -108,13 +110,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
       float part[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) part[i] = 0.f;
-      for (int d0 = tid; d0 < p.D; d0 += 4 * kStepThreads) {
-        float xv[4], wv[4][8];
+      for (int d0 = tid; d0 < p.D; d0 += kRU * kStepThreads) {
+        float xv[kRU], wv[kRU][8];
         // unconditional loads from clamped (valid) addresses, masked after:
         // a load under a branch would be waited on inside that branch
         if (vec) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < kRU; ++u) {
             const int d = d0 + u * kStepThreads;
             const bool ok = d < p.D;
             const int dr = d + rot;
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
             const float xr = to_f32(X[dd]);
             xv[u] = ok ? xr : 0.f;
             const float4* w4 = reinterpret_cast<const float4*>(p.Wr + (size_t)dd * p.E + eb);
-            const float4 lo = w4[0], hi = w4[two ? 1 : 0];
+            const float4 lo = load_nt(w4), hi = load_nt(w4 + (two ? 1 : 0));
             wv[u][0] = lo.x;
             wv[u][1] = lo.y;
             wv[u][2] = lo.z;
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
           }
         } else {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < kRU; ++u) {
             const int d = d0 + u * kStepThreads;
             const bool ok = d < p.D;
             const int dr = d + rot;
@@ -143,11 +145,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
             xv[u] = ok ? xr : 0.f;
             const float* w = p.Wr + (size_t)dd * p.E;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) wv[u][i] = w[min(eb + i, p.E - 1)];
+            for (int i = 0; i < 8; ++i) wv[u][i] = load_nt(w + min(eb + i, p.E - 1));
           }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kRU; ++u)
 #pragma unroll
           for (int i = 0; i < 8; ++i) part[i] = fmaf(xv[u], wv[u][i], part[i]);
       }

@@ -50,6 +50,16 @@ __device__ __forceinline__ T& at32(T* base, uint32_t i) {
   return *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + i * (uint32_t)sizeof(T));
 }
 
+// Non-temporal loads: they do not allocate in the per-CU vector cache.  Used
+// where every CU streams the same L2-resident table once (the decode step's
+// router), which the cache's miss handling would otherwise throttle.
+typedef float f4v_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+  const f4v_t v = __builtin_nontemporal_load(reinterpret_cast<const f4v_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float load_nt(const float* p) { return __builtin_nontemporal_load(p); }
+
 // Wave-uniform value into an SGPR (the argument must already be uniform).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ float uniform(float v) {

@@ -287,11 +287,8 @@ class PreparedRoute:
             raise SwimbaError("swimba_route", rc)
 
 
-def step(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None, gate=None,
-         y=None, idx_out=None, gate_out=None, y_dtype=None, stream=None):
-    """One decode step (include/swimba.h: swimba_step).  x, dt_raw [B,D];
-    Bm, Cm [B,16]; state [B,D,16] f32 updated in place.  Routing from Wr [D,E]
-    with top-k, or forced idx/gate [B,k].  Returns y [B,D]."""
+def _step_args(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, k, idx, gate, y, idx_out,
+               gate_out, y_dtype):
     _need(x, "x")
     B, D = x.shape
     E, N = A.shape[0], A.shape[2]
@@ -326,6 +323,37 @@ def step(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None,
     a.idx_out, a.gate_out = _ptr(idx_out), _ptr(gate_out)
     a.A, a.dt_bias, a.Dskip, a.state, a.y = _ptr(A), _ptr(dt_bias), _ptr(Dskip), _ptr(state), \
         _ptr(y)
+    return a, y
+
+
+def step(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None, gate=None,
+         y=None, idx_out=None, gate_out=None, y_dtype=None, stream=None):
+    """One decode step (include/swimba.h: swimba_step).  x, dt_raw [B,D];
+    Bm, Cm [B,16]; state [B,D,16] f32 updated in place.  Routing from Wr [D,E]
+    with top-k, or forced idx/gate [B,k].  Returns y [B,D]."""
+    a, y = _step_args(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, k, idx, gate, y, idx_out,
+                      gate_out, y_dtype)
     rc = load().swimba_step(ctypes.byref(a), _stream(stream))
     _check("swimba_step", rc)
     return y
+
+
+class PreparedStep:
+    """swimba_step marshalled once for fixed tensors (a decode loop that keeps
+    its buffers calls the C ABI directly, without per-call checks)."""
+
+    def __init__(self, x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None,
+                 gate=None, y=None, idx_out=None, gate_out=None, y_dtype=None, stream=None):
+        self.args, self.y = _step_args(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, k, idx,
+                                       gate, y, idx_out, gate_out, y_dtype)
+        self._keep = (x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, idx, gate, idx_out,
+                      gate_out)
+        self._ref = ctypes.byref(self.args)
+        self._fn = load().swimba_step
+        self.stream = _stream(stream)
+
+    def __call__(self):
+        rc = self._fn(self._ref, self.stream)
+        if rc != OK:
+            raise SwimbaError("swimba_step", rc)
+        return self.y

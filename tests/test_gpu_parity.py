@@ -481,3 +481,23 @@ def test_step_shapes(B, D, E, k, dtype):
                            idx=idx_out.cpu().numpy(), gate=host(gate_out))
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
     assert rel_err(host(y), ry) < tol and rel_err(host(state), rstate) < tol
+
+
+def test_prepared_step_matches_step():
+    """PreparedStep (marshalled once) gives bit-identical results to step()."""
+    w = workloads.Workload("case", B=5, L=1, D=200, N=16, E=6, k=2, dtype="bf16", seed=61)
+    p, steps = workloads.decode_steps(w, steps=3)
+    P = {kk: torch.from_numpy(v).to(DEV) for kk, v in p.items()}
+    S = [{kk: torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).to(DEV)
+          for kk, v in s.items()} for s in steps]
+    st1 = torch.zeros((w.B, w.D, 16), dtype=torch.float32, device=DEV)
+    st2 = st1.clone()
+    y1 = torch.empty((w.B, w.D), dtype=torch.float32, device=DEV)
+    y2 = torch.empty_like(y1)
+    for s in S:
+        swimba.step(s["x"], s["dt_raw"], s["Bm"], s["Cm"], P["A"], P["dt_bias"], P["Dskip"], st1,
+                    Wr=P["Wr"], k=w.k, y=y1)
+        swimba.PreparedStep(s["x"], s["dt_raw"], s["Bm"], s["Cm"], P["A"], P["dt_bias"],
+                            P["Dskip"], st2, Wr=P["Wr"], k=w.k, y=y2)()
+        assert torch.equal(y1, y2)
+    assert torch.equal(st1, st2)
