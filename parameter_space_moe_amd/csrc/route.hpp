@@ -180,10 +180,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
 #pragma unroll
       for (int r = 0; r < R; ++r) cvt4<TIn, VEC>(xn[r], d, D, ok, xv[r]);
       if (more) {
+        // the stage first: waiting for it below leaves the x loads in flight
         const int dcn = step_base(i + 1), dn = dcn + lane * kCPL;
+        wstage_load<EC, EXACT>(Wr, D, E, dcn, tid, st);
 #pragma unroll
         for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], dn, D, dn < D, xn[r]);
-        wstage_load<EC, EXACT>(Wr, D, E, dcn, tid, st);
       }
 #pragma unroll
       for (int c = 0; c < kCPL; ++c) {
