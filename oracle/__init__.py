@@ -53,9 +53,11 @@ def load(path: str | None = None):
     lib.ref_scan.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7
     lib.ref_scan_separate.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7
     lib.ref_mamba_scan.argtypes = [ci] * 4 + [_f64p] * 9
+    lib.ref_scan_streams.argtypes = [ci] * 5 + [_f64p] * 10
     lib.ref_step.argtypes = [ci] * 5 + [_f64p] * 5 + [_i32p] + [_f64p] * 6 + [_i32p, _f64p]
     lib.ref_num_threads.restype = ci
-    for f in (lib.ref_route, lib.ref_scan, lib.ref_scan_separate, lib.ref_mamba_scan, lib.ref_step):
+    for f in (lib.ref_route, lib.ref_scan, lib.ref_scan_separate, lib.ref_mamba_scan,
+              lib.ref_scan_streams, lib.ref_step):
         f.restype = None
     if path is None:
         _lib = lib
@@ -150,6 +152,28 @@ def mamba_scan(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, h0=None, lib=None):
     hf = np.zeros((B, D, N))
     lib.ref_mamba_scan(B, L, D, N, _p(x), _p(dt_raw), _p(Bm), _p(Cm), _p(A), _p(dt_bias),
                        _p(Dskip), _p(h0), _p(y), _p(hf))
+    return y, hf
+
+
+def scan_streams(X, dt_raw, Bs, Cs, gate, A, dt_bias, h0=None, lib=None):
+    """Stream-mixed scan (shared A; mixed B X injection and C readout).
+    Shapes: X [B,L,k,D]; dt_raw [B,L,D]; Bs, Cs [B,L,k,N]; gate [B,L,k];
+    A [D,N]; dt_bias [D]; h0 [B,D,N] or None.  Returns y [B,L,D], h_final
+    [B,D,N] (fp64)."""
+    lib = lib or load()
+    X, dt_raw, Bs, Cs, gate = _d(X), _d(dt_raw), _d(Bs), _d(Cs), _d(gate)
+    A, dt_bias = _d(A), _d(dt_bias)
+    B, L, k, D = X.shape
+    N = Bs.shape[3]
+    assert dt_raw.shape == (B, L, D) and Bs.shape == (B, L, k, N) and Cs.shape == (B, L, k, N)
+    assert gate.shape == (B, L, k) and A.shape == (D, N) and dt_bias.shape == (D,)
+    h0 = None if h0 is None else _d(h0)
+    if h0 is not None:
+        assert h0.shape == (B, D, N)
+    y = np.zeros((B, L, D))
+    hf = np.zeros((B, D, N))
+    lib.ref_scan_streams(B, L, D, N, k, _p(X), _p(dt_raw), _p(Bs), _p(Cs), _p(gate), _p(A),
+                         _p(dt_bias), _p(h0), _p(y), _p(hf))
     return y, hf
 
 

@@ -30,7 +30,9 @@
  *   recurrence h[n] <- a[n] h[n] + Delta B[t,n] x      ([MB], [SW])
  *   readout    y = sum_n C[t,n] h[n] + delta x          (after the update)
  * The separate design keeps one state per expert and advances only the
- * selected ones ([SW] the two MoE-SSM designs; Theorem 4).
+ * selected ones ([SW] the two MoE-SSM designs; Theorem 4).  The stream-mixed
+ * form (ref_scan_streams) shares A and mixes the experts' B X injections and
+ * C readouts instead ([SW] "Kernmechanisme van Swimba").
  *
  * Readings where the pages are silent are listed in the design document:
  * Euler injection, bias mixed before softplus, gates = softmax over the top
@@ -205,6 +207,64 @@ void ref_scan_separate(int B, int L, int D, int N, int E, int k,
           for (int n = 0; n < N; ++n)
             h_final[(((int64_t)b * E + e) * D + d) * N + n] = H[e * N + n];
       free(H);
+    }
+  }
+}
+
+/* ------------------------------------------------- stream-mixed scan */
+/*
+ * ref_scan_streams: the pages' own form of the mixed layer ([SW] Dutch
+ * summary "Kernmechanisme van Swimba", French "Architecture de Swimba"):
+ * every expert emits candidate streams B_t, C_t and an input X_t; the
+ * transition A is shared by all experts; the state update mixes the
+ * injections, h_t = A h_{t-1} + sum_e pi_{t,e} B^(e)_t X^(e)_t, and the
+ * readout mixes the output vectors, y_t = (sum_e pi_{t,e} C^(e)_t)^T h_t.
+ * The streams arrive per routing slot: slot j of token t holds the streams
+ * of the j-th selected expert and pi_{t,e_j} = gate[t,j].
+ * The shared transition is discretised as in the selective scan ([MB]
+ * "Mamba"; [SW] Theorem 1, one selective SSM): the step size is not an
+ * expert stream, so Delta = softplus(dt_raw + dt_bias) is shared, the
+ * transition is exp(Delta A[d,n]) and the mixed injection enters as
+ * Delta * sum_j g_j B_j[n] X_j[d].  The printed readout has no
+ * feed-through term, so none is added.
+ *   X        [B, L, k, D]   per-slot input streams
+ *   dt_raw   [B, L, D]
+ *   Bs, Cs   [B, L, k, N]   per-slot B and C streams
+ *   gate     [B, L, k]
+ *   A        [D, N]         shared diagonal transition (negative)
+ *   dt_bias  [D]
+ *   h0, h_final [B, D, N] (NULL allowed); y [B, L, D] out
+ */
+void ref_scan_streams(int B, int L, int D, int N, int k, const double* X,
+                      const double* dt_raw, const double* Bs,
+                      const double* Cs, const double* gate, const double* A,
+                      const double* dt_bias, const double* h0, double* y,
+                      double* h_final) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int d = 0; d < D; ++d) {
+      double* h = (double*)malloc(sizeof(double) * (size_t)N);
+      for (int n = 0; n < N; ++n)
+        h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.0;
+      for (int t = 0; t < L; ++t) {
+        int64_t bt = (int64_t)b * L + t;
+        const double* g = gate + bt * k;
+        double Dt = softplus(dt_raw[bt * D + d] + dt_bias[d]);
+        double yv = 0.0;
+        for (int n = 0; n < N; ++n) {
+          double inj = 0.0, c = 0.0;
+          for (int j = 0; j < k; ++j) {
+            inj += g[j] * Bs[(bt * k + j) * N + n] * X[(bt * k + j) * D + d];
+            c += g[j] * Cs[(bt * k + j) * N + n];
+          }
+          h[n] = exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * inj;
+          yv += c * h[n];
+        }
+        y[bt * D + d] = yv;
+      }
+      if (h_final)
+        for (int n = 0; n < N; ++n) h_final[((int64_t)b * D + d) * N + n] = h[n];
+      free(h);
     }
   }
 }

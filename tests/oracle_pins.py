@@ -14,7 +14,12 @@ and the mathematics fix:
   * invariants (stability bound, Theorem 3; split-sequence composition;
     linearity in x; the two designs differ under time-varying routing,
     Theorem 4);
-  * brute-force sorting for the router.
+  * brute-force sorting for the router;
+  * for the stream-mixed form (shared A, mixed B X injection and C readout):
+    one slot or identical slots reduce to the plain Mamba scan, a zero-weight
+    slot drops out, slots permute freely, the state superposes over slots
+    and the readout is linear in C, plus its own worked examples, closed
+    form, stability bound and split composition.
 The same functions run against mutated copies of the oracle in
 ``test_oracle_mutations.py``: every planted mistake must trip at least one.
 """
@@ -479,6 +484,194 @@ def pin_step_equals_scan(lib):
                                c["A"], c["dt_bias"], c["Dskip"], state, idx=c["idx"][:, t],
                                gate=c["gate"][:, t], lib=lib)
         _close(yt, y[:, t], 1e-13, "forced step y t=%d" % t)
+
+
+# -------------------------------------------------- stream-mixed form
+def _stream_case(rng, B=2, L=7, D=3, N=4, k=2, h0=True):
+    X = rng.standard_normal((B, L, k, D))
+    dt_raw = rng.standard_normal((B, L, D))
+    Bs = rng.standard_normal((B, L, k, N))
+    Cs = rng.standard_normal((B, L, k, N))
+    g = rng.uniform(0.1, 1.0, (B, L, k))
+    gate = g / g.sum(-1, keepdims=True)
+    A = -np.exp(rng.uniform(0, math.log(16), (D, N)))
+    dt_bias = rng.standard_normal(D) * 0.3
+    H = rng.standard_normal((B, D, N)) if h0 else None
+    return dict(X=X, dt_raw=dt_raw, Bs=Bs, Cs=Cs, gate=gate, A=A, dt_bias=dt_bias, h0=H)
+
+
+def pin_worked_streams(lib):
+    """Hand-derived stream-mixed examples: gates that change per token, a
+    zero-weight slot, two channels with different step sizes, h0."""
+    gold = json.load(open(GOLDEN))
+    for c in gold["streams_cases"]:
+        h0 = _arr(c["h0"]) if "h0" in c else None
+        y, hf = oracle.scan_streams(_arr(c["X"]), _arr(c["dt_raw"]), _arr(c["Bs"]),
+                                    _arr(c["Cs"]), _arr(c["gate"]), _arr(c["A"]),
+                                    _arr(c["dt_bias"]), h0, lib=lib)
+        _close(y, _frac(c["expected_y"]), 1e-12, c["name"] + " y")
+        _close(hf, _frac(c["expected_h_final"]), 1e-12, c["name"] + " h_final")
+
+
+def pin_streams_one_slot_is_mamba(lib):
+    """One slot with weight 1: the stream form is the plain selective scan of
+    that slot's streams (no feed-through term)."""
+    rng = np.random.default_rng(30)
+    c = _stream_case(rng, B=2, L=9, D=3, N=4, k=1)
+    c["gate"][:] = 1.0
+    y, hf = oracle.scan_streams(**c, lib=lib)
+    ym, hm = oracle.mamba_scan(c["X"][:, :, 0], c["dt_raw"], c["Bs"][:, :, 0], c["Cs"][:, :, 0],
+                               c["A"], c["dt_bias"], np.zeros(3), c["h0"], lib=lib)
+    _close(y, ym, 1e-13, "one slot y")
+    _close(hf, hm, 1e-13, "one slot h")
+
+
+def pin_streams_identical_slots_is_mamba(lib):
+    """Every slot carrying the same streams, convex gates: the mixture is that
+    one stream, whatever the gates (Theorem 1: one selective SSM)."""
+    rng = np.random.default_rng(31)
+    c = _stream_case(rng, B=2, L=8, D=3, N=4, k=3)
+    for key in ("X", "Bs", "Cs"):
+        c[key][:, :, 1:] = c[key][:, :, :1]
+    y, hf = oracle.scan_streams(**c, lib=lib)
+    ym, hm = oracle.mamba_scan(c["X"][:, :, 0], c["dt_raw"], c["Bs"][:, :, 0], c["Cs"][:, :, 0],
+                               c["A"], c["dt_bias"], np.zeros(3), c["h0"], lib=lib)
+    _close(y, ym, 1e-12, "identical slots y")
+    _close(hf, hm, 1e-12, "identical slots h")
+
+
+def pin_streams_superposition(lib):
+    """A is shared, so the transition does not depend on the slots and the
+    state is linear in the injections: the k-slot state is the sum of the
+    single-slot states (slot j alone with its own gate; h0 carried by one of
+    them).  With one readout vector C in every slot, the k-slot readout is C
+    (convex gates) and single-slot run j reads C / g_j, so y adds up too."""
+    rng = np.random.default_rng(32)
+    c = _stream_case(rng, B=2, L=10, D=3, N=4, k=3)
+    c["Cs"][:, :, 1:] = c["Cs"][:, :, :1]
+    y, hf = oracle.scan_streams(**c, lib=lib)
+    ys, hs = np.zeros_like(y), np.zeros_like(hf)
+    for j in range(3):
+        g = c["gate"][:, :, j:j + 1]
+        yj, hj = oracle.scan_streams(c["X"][:, :, j:j + 1], c["dt_raw"], c["Bs"][:, :, j:j + 1],
+                                     c["Cs"][:, :, :1] / g[..., None], g, c["A"], c["dt_bias"],
+                                     c["h0"] if j == 0 else np.zeros_like(c["h0"]), lib=lib)
+        ys += yj
+        hs += hj
+    _close(hf, hs, 1e-12, "superposition h")
+    _close(y, ys, 1e-12, "superposition y")
+
+
+def pin_streams_readout_linear_in_C(lib):
+    """For fixed injections the state does not depend on C, and y is linear
+    in the C streams: the output equals the sum of the outputs with all but
+    one slot's C zeroed."""
+    rng = np.random.default_rng(33)
+    c = _stream_case(rng, B=1, L=9, D=4, N=3, k=3)
+    y, hf = oracle.scan_streams(**c, lib=lib)
+    ys = np.zeros_like(y)
+    for j in range(3):
+        cj = dict(c)
+        cj["Cs"] = np.zeros_like(c["Cs"])
+        cj["Cs"][:, :, j] = c["Cs"][:, :, j]
+        yj, hj = oracle.scan_streams(**cj, lib=lib)
+        _close(hj, hf, 1e-14, "state independent of C")
+        ys += yj
+    _close(y, ys, 1e-12, "readout linear in C")
+
+
+def pin_streams_zero_gate_slot(lib):
+    """A slot with weight zero contributes nothing, whatever its streams."""
+    rng = np.random.default_rng(34)
+    c = _stream_case(rng, B=2, L=8, D=3, N=4, k=3)
+    c["gate"][:, :, 1] = 0.0
+    y, hf = oracle.scan_streams(**c, lib=lib)
+    keep = [0, 2]
+    y2, h2 = oracle.scan_streams(c["X"][:, :, keep], c["dt_raw"], c["Bs"][:, :, keep],
+                                 c["Cs"][:, :, keep], c["gate"][:, :, keep], c["A"],
+                                 c["dt_bias"], c["h0"], lib=lib)
+    _close(y, y2, 1e-14, "zero-gate slot y")
+    _close(hf, h2, 1e-14, "zero-gate slot h")
+
+
+def pin_streams_slot_permutation(lib):
+    """The mixture is a sum over slots: permuting the slots (streams and
+    gates together) changes nothing."""
+    rng = np.random.default_rng(35)
+    c = _stream_case(rng, B=2, L=8, D=3, N=4, k=3)
+    y, hf = oracle.scan_streams(**c, lib=lib)
+    perm = [2, 0, 1]
+    cp = dict(c)
+    for key in ("X", "Bs", "Cs", "gate"):
+        cp[key] = c[key][:, :, perm]
+    yp, hp = oracle.scan_streams(**cp, lib=lib)
+    _close(yp, y, 1e-13, "slot permutation y")
+    _close(hp, hf, 1e-13, "slot permutation h")
+
+
+def pin_streams_constant_geometric(lib):
+    """Constant streams and gates: h_t = a^t h0 + u (1 - a^t) / (1 - a) with
+    a = exp(Delta A) and u = Delta sum_j g_j B_j X_j; y_t = c . h_t."""
+    B, L, D, N, k = 1, 30, 2, 3, 2
+    Xv = np.array([[0.5, -2.0], [1.5, 0.25]])            # [k, D]
+    Bv = np.array([[1.0, -0.5, 2.0], [0.25, 1.0, -1.0]])  # [k, N]
+    Cv = np.array([[2.0, 0.0, -1.0], [-1.0, 3.0, 0.5]])
+    g = np.array([0.3, 0.7])
+    X = np.broadcast_to(Xv, (B, L, k, D)).copy()
+    Bs = np.broadcast_to(Bv, (B, L, k, N)).copy()
+    Cs = np.broadcast_to(Cv, (B, L, k, N)).copy()
+    gate = np.broadcast_to(g, (B, L, k)).copy()
+    dt_raw = np.broadcast_to(np.array([0.4, -1.1]), (B, L, D)).copy()
+    A = -np.array([[1.0, 3.0, 0.5], [2.0, 0.25, 6.0]])
+    dt_bias = np.array([-0.2, 0.3])
+    h0 = np.array([[[1.0, -1.0, 0.5], [0.0, 2.0, -3.0]]])
+    y, hf = oracle.scan_streams(X, dt_raw, Bs, Cs, gate, A, dt_bias, h0, lib=lib)
+    t = np.arange(1, L + 1)[:, None]
+    cvec = g[0] * Cv[0] + g[1] * Cv[1]
+    for d in range(D):
+        Dt = math.log1p(math.exp(dt_raw[0, 0, d] + dt_bias[d]))
+        a = np.exp(Dt * A[d])
+        u = Dt * (g[0] * Bv[0] * Xv[0, d] + g[1] * Bv[1] * Xv[1, d])
+        h = a ** t * h0[0, d] + u * (1 - a ** t) / (1 - a)
+        _close(y[0, :, d], h @ cvec, 1e-12, "stream geometric y d=%d" % d)
+        _close(hf[0, d], h[-1], 1e-12, "stream geometric h d=%d" % d)
+
+
+def pin_streams_stability_bound(lib):
+    """Theorem 3 for the stream form: with a contractive shared transition and
+    convex gates, |h_t[n]| <= a*^t |h0| + M (1 - a*^t) / (1 - a*), where a* is
+    the largest decay and M bounds Delta |B_j[n] X_j[d]| over tokens and slots."""
+    rng = np.random.default_rng(36)
+    c = _stream_case(rng, B=1, L=40, D=3, N=4, k=3)
+    L = 40
+    Dt = _softplus(c["dt_raw"][0] + c["dt_bias"][None, :])       # [L, D]
+    for t_end in (5, 17, 40):
+        y, hf = oracle.scan_streams(c["X"][:, :t_end], c["dt_raw"][:, :t_end],
+                                    c["Bs"][:, :t_end], c["Cs"][:, :t_end], c["gate"][:, :t_end],
+                                    c["A"], c["dt_bias"], c["h0"], lib=lib)
+        for d in range(3):
+            amax = np.max(np.exp(Dt[:t_end, d][:, None] * c["A"][d][None, :]), axis=0)   # [N]
+            M = np.max(Dt[:t_end, d][:, None, None] * np.abs(c["Bs"][0, :t_end])
+                       * np.abs(c["X"][0, :t_end, :, d])[:, :, None], axis=(0, 1))      # [N]
+            bound = amax ** t_end * np.abs(c["h0"][0, d]) + M * (1 - amax ** t_end) / (1 - amax)
+            assert np.all(np.abs(hf[0, d]) <= bound * (1 + 1e-12)), ("bound", t_end, d)
+            assert np.all(amax < 1.0)
+    assert L == 40
+
+
+def pin_streams_split_composition(lib):
+    """scan(L1 || L2) = scan(L2, h0 = scan(L1).h_final), for y and h."""
+    rng = np.random.default_rng(37)
+    c = _stream_case(rng, B=2, L=11, D=3, N=4, k=2)
+    y, hf = oracle.scan_streams(**c, lib=lib)
+    keys = ("X", "dt_raw", "Bs", "Cs", "gate")
+    c1 = dict(c, **{k_: c[k_][:, :4] for k_ in keys})
+    c2 = dict(c, **{k_: c[k_][:, 4:] for k_ in keys})
+    y1, h1 = oracle.scan_streams(**c1, lib=lib)
+    c2["h0"] = h1
+    y2, h2 = oracle.scan_streams(**c2, lib=lib)
+    _close(np.concatenate([y1, y2], axis=1), y, 1e-13, "stream split y")
+    _close(h2, hf, 1e-13, "stream split h")
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -41,10 +41,33 @@ MUTATIONS = [
     ("separate_decays_all",
      "          ye += Dskip[(int64_t)e * D + d] * xv;",
      "          for (int o = 0; o < E; ++o) if (o != e) for (int n = 0; n < N; ++n) H[o * N + n] *= 0.5;\n          ye += Dskip[(int64_t)e * D + d] * xv;"),
-    ("mamba_wrong_A_index", "exp(Dt * A[(int64_t)d * N + n])", "exp(Dt * A[(int64_t)n])"),
+    ("mamba_wrong_A_index", "exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * Bm",
+     "exp(Dt * A[(int64_t)n]) * h[n] + Dt * Bm"),
     ("mamba_no_D", "double out = Dskip[d] * u;", "double out = 0.0;"),
     ("step_routes_first_token_only", "ref_route(B, D, E, k, x, Wr, idx, gate, NULL, NULL);",
      "ref_route(1, D, E, k, x, Wr, idx, gate, NULL, NULL);\n    for (int64_t i = k; i < (int64_t)B * k; ++i) { idx[i] = idx[i % k]; gate[i] = gate[i % k]; }"),
+    ("streams_injection_ungated", "inj += g[j] * Bs[", "inj += Bs["),
+    ("streams_readout_ungated", "c += g[j] * Cs[", "c += Cs["),
+    ("streams_readout_slot0", "c += g[j] * Cs[(bt * k + j) * N + n];",
+     "c += g[j] * Cs[(bt * k + 0) * N + n];"),
+    ("streams_X_transposed", "X[(bt * k + j) * D + d]", "X[(bt * D + d) * k + j]"),
+    ("streams_X_slot0", "X[(bt * k + j) * D + d]", "X[(bt * k) * D + d]"),
+    ("streams_B_slot0", "inj += g[j] * Bs[(bt * k + j) * N + n]", "inj += g[j] * Bs[(bt * k) * N + n]"),
+    ("streams_injection_no_delta", "h[n] = exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * inj;",
+     "h[n] = exp(Dt * A[(int64_t)d * N + n]) * h[n] + inj;"),
+    ("streams_A_transposed", "h[n] = exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * inj;",
+     "h[n] = exp(Dt * A[(int64_t)n * D + d]) * h[n] + Dt * inj;"),
+    ("streams_exp_sign", "h[n] = exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * inj;",
+     "h[n] = exp(-Dt * A[(int64_t)d * N + n]) * h[n] + Dt * inj;"),
+    ("streams_readout_before_update",
+     "          h[n] = exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * inj;\n          yv += c * h[n];",
+     "          yv += c * h[n];\n          h[n] = exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * inj;"),
+    ("streams_bias_ignored",
+     "const double* g = gate + bt * k;\n        double Dt = softplus(dt_raw[bt * D + d] + dt_bias[d]);",
+     "const double* g = gate + bt * k;\n        double Dt = softplus(dt_raw[bt * D + d]);"),
+    ("streams_h0_ignored",
+     "h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.0;\n      for (int t = 0; t < L; ++t) {\n        int64_t bt = (int64_t)b * L + t;\n        const double* g",
+     "h[n] = 0.0;\n      for (int t = 0; t < L; ++t) {\n        int64_t bt = (int64_t)b * L + t;\n        const double* g"),
 ]
 
 
