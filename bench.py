@@ -8,7 +8,8 @@ inputs resident in HBM.  Printed as one JSON line (rank 0):
              ceiling that bounds it, with its HBM rate against 8 TB/s beside it
   modes    = the separate design, the dense single-expert scan (E = 1), the
              scan alone, and the decode step, for the "mixed vs separate" and
-             "mixed vs dense" ratios
+             "mixed vs dense" ratios; the stream-mixed form (shared A, mixed
+             B X injection and C readout) at the same shape
   cpu_baseline = the fp64 oracle timed on this host on the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -43,6 +44,14 @@ def slots_per_tc(k: int) -> float:
     (2 transcendentals = 4 slots, 5 VALU), beta and delta (2k), Delta*g_j (k),
     Delta*x, the D term, and x/dt_raw/y conversions (3)."""
     return N_STATE * (k + 5) + (4 + 5 + 3 * k + 2 + 3)
+
+
+def stream_slots_per_tc(k: int) -> float:
+    """Minimum VALU issue slots per token x channel of the stream-mixed scan
+    (shared A).  Per state entry: Delta*A (1), exp2 (2), the k-slot injection
+    (k), the update (1), the readout (1).  Per (token, channel): softplus
+    (4 + 5), Delta*X_j (k), and the X, dt_raw and y conversions (k + 2)."""
+    return N_STATE * (k + 5) + (9 + 2 * k + 2)
 
 
 # --------------------------------------------------------------- HIP events
@@ -310,6 +319,63 @@ def expert_sweep(swimba, dev, reps):
     return out
 
 
+def stream_mode(swimba, workloads, w, x, Wr, idx, gate, reps):
+    """The pages' stream-mixed form at the same layer shape: shared A, each of
+    the k slots carries its expert's X, B and C streams, the injection and the
+    readout are mixed by the gates ("Kernmechanisme van Swimba").  Times the
+    router on the layer's x plus the stream scan, and the scan's chunk pass
+    alone (dispatch-stamped events) against the VALU ceiling and 8 TB/s."""
+    import numpy as np
+    import torch
+    dev = x.device
+    inp = workloads.generate_streams(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    T = {}
+    for name, v in inp.items():
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        T[name] = (t.to(dt) if name in ("X", "dt_raw", "Bs", "Cs") else t).to(dev)
+    y = torch.empty((w.B, w.L, w.D), dtype=dt, device=dev)
+    hf = torch.empty((w.B, w.D, N_STATE), dtype=torch.float32, device=dev)
+    scan = swimba.PreparedStreams(T["X"], T["dt_raw"], T["Bs"], T["Cs"], T["gate"], T["A"],
+                                  T["dt_bias"], y=y, h_final=hf)
+    route = swimba.PreparedRoute(x, Wr, w.k, idx, gate)
+    chunk_len, nchunks = swimba.scan_streams_plan(T["X"])
+    ms_scan = _time(scan, reps)
+
+    def step():
+        route()
+        scan()
+
+    ms_step = _time(step, reps)
+    hip = Hip()
+    ev = [[hip.event() for _ in range(6)] for _ in range(reps)]
+    arrs = [(ctypes.c_void_p * 6)(*[e_.value for e_ in e]) for e in ev]
+    for a in arrs:
+        scan(ctypes.addressof(a))
+    torch.cuda.synchronize()
+    chunk_ms = sum(hip.ms(e[0], e[1]) for e in ev) / reps
+    carry_ms = sum(hip.ms(e[2], e[3]) for e in ev) / reps
+    fixup_ms = sum(hip.ms(e[4], e[5]) for e in ev) / reps
+    tc, k = w.tc, w.k
+    esz = 2 if w.dtype == "bf16" else 4
+    # X (k slots) and dt_raw read, y written; per token the k B and C streams
+    # and gates; per chunk and channel the decay and end state
+    chunk_bytes = tc * (k + 2) * esz + w.B * w.L * k * (2 * N_STATE * esz + 4)
+    if nchunks > 1:
+        chunk_bytes += 2 * w.B * nchunks * N_STATE * w.D * 4
+    tf = tc * stream_slots_per_tc(k) * 2 / (chunk_ms * 1e-3) / 1e12
+    gbs = chunk_bytes / (chunk_ms * 1e-3) / 1e9
+    return {"shape": "B=%d L=%d D=%d k=%d %s, chunk %d x %d" % (w.B, w.L, w.D, k, w.dtype,
+                                                              chunk_len, nchunks),
+            "scan_ms": round(ms_scan, 4), "G_tc_per_s": round(tc / ms_scan / 1e6, 3),
+            "route_plus_scan_ms": round(ms_step, 4),
+            "chunk_pass_ms": round(chunk_ms, 4), "carry_ms": round(carry_ms, 4),
+            "fixup_ms": round(fixup_ms, 4),
+            "valu_frac": round(tf / VALU_PEAK_TFLOPS, 4),
+            "valu_note": "%d slots/tc as FMA-equivalent flops" % stream_slots_per_tc(k),
+            "hbm_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gate, y, hf):
     import numpy as np
     import torch
@@ -359,6 +425,7 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
                                 "note": "route + mixed scan after a 512 MB write, HIP events"}
     del flush
     res["expert_sweep"] = expert_sweep(swimba, dev, reps)
+    res["stream_mixed"] = stream_mode(swimba, workloads, w, x, Wr, idx, gate, reps)
     # decode workload: 128 routed steps on a persistent fp32 state
     wd = workloads.BY_NAME["decode"]
     p, steps = workloads.decode_steps(wd)

@@ -24,6 +24,10 @@
  *   separate: each expert keeps its own state; at token t each selected
  *            expert e_j advances with its own A, bias, Dskip and emits y_j;
  *            y = sum_j g_j y_j; unselected experts' states do not change.
+ *   streams: A shared by the experts; each selected expert's B, C and X
+ *            streams arrive per routing slot; the injection
+ *            Delta sum_j g_j B_j X_j and the readout vector sum_j g_j C_j
+ *            are mixed ([SW] "Kernmechanisme van Swimba").
  *
  * Conventions (all entry points):
  *   - Every tensor argument is a DEVICE pointer owned by the caller, dense and
@@ -183,6 +187,56 @@ typedef struct {
  * Constraints: B >= 0, D >= 1, N == 16, 1 <= k <= E <= 64; Wr or idx/gate.
  */
 int swimba_step(const swimba_step_args* a, hipStream_t stream);
+
+typedef struct {
+  int B, L, D, N, k;            /* batch, length, channels, states (16), routing slots    */
+  swimba_dtype in_dtype;        /* dtype of X, dt_raw, Bs, Cs                            */
+  swimba_dtype y_dtype;         /* dtype of y                                            */
+  const void* X;                /* [B, L, k, D]  input stream of each slot's expert      */
+  const void* dt_raw;           /* [B, L, D]     shared step size before bias, softplus  */
+  const void* Bs;               /* [B, L, k, N]  each slot's B stream                    */
+  const void* Cs;               /* [B, L, k, N]  each slot's C stream                    */
+  const float* gate;            /* [B, L, k]     router weight of each slot              */
+  const float* A;               /* [D, N]        shared diagonal transition (< 0),
+                                                 16-byte aligned                         */
+  const float* dt_bias;         /* [D]                                                   */
+  const float* h0;              /* NULL = zeros; [B, D, N]                               */
+  void* y;                      /* [B, L, D]     out                                     */
+  float* h_final;               /* NULL = not written; [B, D, N]                         */
+  int chunk;                    /* tokens per chunk; 0 = library's choice                */
+  swimba_carry carry;           /* chunk join method                                     */
+  hipEvent_t* phase_events;     /* NULL, or 6 timing events, as in swimba_scan_args      */
+} swimba_stream_args;
+
+/*
+ * swimba_scan_streams_workspace_size -- device workspace bytes for
+ * swimba_scan_streams (0 when the sequence is one chunk or the arguments are
+ * invalid).  swimba_scan_streams_plan -- its chunking (tokens per chunk,
+ * number of chunks); returns the status the size validation would return.
+ */
+size_t swimba_scan_streams_workspace_size(const swimba_stream_args* a);
+int swimba_scan_streams_plan(const swimba_stream_args* a, int* chunk, int* nchunks);
+
+/*
+ * swimba_scan_streams -- the stream-mixed form of the layer ([SW] Dutch
+ * summary "Kernmechanisme van Swimba", French "Architecture de Swimba"): every
+ * expert emits B, C and X streams, the transition A is shared, and one
+ * recurrence runs over the mixed injection and readout.  Slot j of token t
+ * holds the streams of the token's j-th selected expert with weight
+ * gate[t, j].  Per (b, d), with Delta = softplus(dt_raw + dt_bias[d]):
+ *   h[n] <- exp(Delta A[d,n]) h[n] + Delta sum_j gate_j Bs_j[n] X_j[d]
+ *   y     = sum_n (sum_j gate_j Cs_j[n]) h[n]          (after the update)
+ * The step size is shared (it is not one of the experts' streams) and the
+ * readout has no feed-through term, as printed on the page.
+ *   ws, ws_bytes: device workspace of at least
+ *   swimba_scan_streams_workspace_size(a) bytes, 256-byte aligned.
+ * Constraints: B, L >= 0; D >= 1; N == 16; 1 <= k <= 4 (EUNSUPPORTED above);
+ * chunk >= 0; Bs and Cs aligned to two elements.  L == 0 writes
+ * h_final = h0 (or zeros).  Chunks are joined exactly when A < 0; otherwise
+ * every chunk is recomputed from its carried state.
+ */
+int swimba_scan_streams(const swimba_stream_args* a, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* Static string for a status code. */
 const char* swimba_status_string(int status);

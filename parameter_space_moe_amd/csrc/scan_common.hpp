@@ -66,7 +66,14 @@ __device__ __forceinline__ void wave_sync() {
 // it return 0 and such stores are dropped.  The scalar offset is not part of
 // that check, so callers keep scalar offsets inside the valid rows.
 using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+// A per-lane offset past every buffer's size: loads with it return 0.  Lanes
+// of a ragged tile (channel >= D) use it, because their channel offset alone
+// can pass the range check while the unchecked scalar offset moves the
+// address past the tensor's last row.
+constexpr uint32_t kOffNone = 0x80000000u;
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // third dword of a raw (untyped, unswizzled) buffer on gfx9-family parts

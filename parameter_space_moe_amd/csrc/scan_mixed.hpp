@@ -192,8 +192,8 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
   const int D = p.D;
   const size_t row = (size_t)b * p.L;
   const size_t total = (size_t)p.B * p.L;
-  // lanes past D (ragged tile) read the next row's channels or 0, never stored
-  const uint32_t xoff = (uint32_t)d * (uint32_t)sizeof(TIn);
+  // lanes past D (ragged tile) read 0 and store nothing
+  const uint32_t xoff = active ? (uint32_t)d * (uint32_t)sizeof(TIn) : stage::kOffNone;
   const uint32_t yoff = (uint32_t)d * (uint32_t)sizeof(TOut);
   const uint32_t xrow = (uint32_t)D * (uint32_t)sizeof(TIn);
   const uint32_t yrow = (uint32_t)D * (uint32_t)sizeof(TOut);

@@ -1,0 +1,8 @@
+// Instantiations of the stream-mixed scan for X/dt_raw/B/C in float and y in bf16_t.
+#include "scan_streams.hpp"
+
+namespace swimba {
+int launch_streams_fb(const swimba_stream_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
+  return streams::launch_streams_k<float, bf16_t>(a, pl, ws, st);
+}
+}  // namespace swimba

@@ -66,61 +66,103 @@ int device_cus() {
   return v;
 }
 
-int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p) {
-  int rc = validate_scan(a, separate);
-  if (rc != SWIMBA_OK) return rc;
-  *p = ScanPlan();
-  p->ntiles = (a->D + 63) / 64;
-  p->waves = (!separate && a->E > 8) ? 8 : 4;
-  if (a->L == 0 || a->B == 0) {
-    p->chunk = 0;
-    p->nchunks = 0;
-    return SWIMBA_OK;
+namespace {
+
+// Tokens per chunk when the caller leaves the choice to the library, for a
+// lane-per-channel scan over B * ntiles independent recurrences of length L.
+// `small_ok`: the kernel may run the small-problem layout (two 4-wave
+// workgroups per CU); *small tells whether it was chosen.
+int auto_chunk(long long B, long long L, int ntiles, bool separate, bool small_ok, bool* small) {
+  const long long cus = device_cus();
+  const long long base = B * ntiles;
+  long long want, min_chunk = 128;
+  *small = false;
+  if (separate) {
+    // a workgroup per (sequence, tile, chunk) with one wave per expert: aim
+    // for four workgroups per CU (two resident, two rounds)
+    want = (4 * cus + base - 1) / base;
+    min_chunk = 64;
+  } else if (base * (L / 256) >= 16 * cus) {
+    // about four resident waves per SIMD (16 per CU) from the independent
+    // (b, tile) recurrences, in chunks no shorter than a few fix-up horizons
+    want = (16 * cus + base - 1) / base;
+  } else {
+    // Too few recurrences for that: two 4-wave workgroups per CU (two
+    // waves per SIMD, every SIMD busy), i.e. the largest multiple of 4
+    // chunks per tile whose workgroups all fit at once.
+    *small = small_ok;
+    want = 2 * 4 * cus / base;
+    if (*small && want >= 4) want = want / 4 * 4;
+    min_chunk = 64;
   }
-  int chunk = a->chunk;
-  bool small = false;  // mixed scan with too little work for four waves per SIMD
-  if (chunk == 0) {
-    const long long cus = device_cus();
-    const long long base = (long long)a->B * p->ntiles;
-    long long want, min_chunk = 128;
-    if (separate) {
-      // a workgroup per (sequence, tile, chunk) with one wave per expert: aim
-      // for four workgroups per CU (two resident, two rounds)
-      want = (4 * cus + base - 1) / base;
-      min_chunk = 64;
-    } else if (base * (a->L / 256) >= 16 * cus) {
-      // about four resident waves per SIMD (16 per CU) from the independent
-      // (b, tile) recurrences, in chunks no shorter than a few fix-up horizons
-      want = (16 * cus + base - 1) / base;
-    } else {
-      // Too few recurrences for that: two 4-wave workgroups per CU (two
-      // waves per SIMD, every SIMD busy), i.e. the largest multiple of 4
-      // chunks per tile whose workgroups all fit at once.
-      small = a->E <= 8;
-      want = 2 * 4 * cus / base;
-      if (small && want >= 4) want = want / 4 * 4;
-      min_chunk = 64;
-    }
-    const long long maxc = (a->L + min_chunk - 1) / min_chunk;
-    if (want > maxc) want = maxc;
-    if (want < 1) want = 1;
-    chunk = (int)((a->L + want - 1) / want);
-    if (separate) chunk = (int)(((long long)chunk + 63) / 64 * 64);  // whole staging rounds
-  }
-  if (chunk > a->L) chunk = a->L;
+  const long long maxc = (L + min_chunk - 1) / min_chunk;
+  if (want > maxc) want = maxc;
+  if (want < 1) want = 1;
+  long long chunk = (L + want - 1) / want;
+  if (separate) chunk = (chunk + 63) / 64 * 64;  // whole staging rounds
+  return (int)chunk;
+}
+
+// Chunk count and the P / H (/ flags) workspace of a chunked scan whose
+// chunk pass writes `rows` state rows per (sequence, chunk, channel).
+void plan_layout(const ScanPlan& in, int B, int L, int D, int chunk, size_t rows, bool flags,
+                 ScanPlan* p) {
+  *p = in;
+  if (chunk > L) chunk = L;
   p->chunk = chunk;
-  p->nchunks = (int)(((long long)a->L + chunk - 1) / chunk);
-  // chunks of one tile share the workgroup's expert table: 8 waves when there
-  // are enough chunks to fill them (and the problem is not the small case)
-  if (!separate && p->nchunks >= 8 && !small) p->waves = 8;
+  p->nchunks = (int)(((long long)L + chunk - 1) / chunk);
   if (p->nchunks > 1) {
-    const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N : SWIMBA_STATE_N;
-    const size_t arr = (size_t)a->B * p->nchunks * rows * a->D * sizeof(float);
+    const size_t arr = (size_t)B * p->nchunks * rows * D * sizeof(float);
     p->off_P = 0;
     p->off_H = align256(arr);
     p->off_flags = p->off_H + align256(arr);
-    p->bytes = p->off_flags + align256((size_t)a->B * p->nchunks * p->ntiles * sizeof(int32_t));
+    p->bytes = p->off_flags +
+               (flags ? align256((size_t)B * p->nchunks * p->ntiles * sizeof(int32_t)) : 0);
   }
+}
+
+}  // namespace
+
+int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p) {
+  int rc = validate_scan(a, separate);
+  if (rc != SWIMBA_OK) return rc;
+  ScanPlan q;
+  q.ntiles = (a->D + 63) / 64;
+  q.waves = (!separate && a->E > 8) ? 8 : 4;
+  if (a->L == 0 || a->B == 0) {
+    *p = q;
+    return SWIMBA_OK;
+  }
+  bool small = false;  // mixed scan with too little work for four waves per SIMD
+  const int chunk = a->chunk > 0 ? a->chunk
+                                 : auto_chunk(a->B, a->L, q.ntiles, separate, a->E <= 8, &small);
+  const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N : SWIMBA_STATE_N;
+  plan_layout(q, a->B, a->L, a->D, chunk, rows, true, p);
+  // chunks of one tile share the workgroup's expert table: 8 waves when there
+  // are enough chunks to fill them (and the problem is not the small case)
+  if (!separate && p->nchunks >= 8 && !small) p->waves = 8;
+  return SWIMBA_OK;
+}
+
+int plan_streams(const swimba_stream_args* a, ScanPlan* p) {
+  if (a == nullptr) return SWIMBA_EINVAL;
+  if (a->B < 0 || a->L < 0 || a->D < 1 || a->N < 1 || a->k < 1 || a->chunk < 0)
+    return SWIMBA_EINVAL;
+  if (!dtype_ok(a->in_dtype) || !dtype_ok(a->y_dtype)) return SWIMBA_EINVAL;
+  if (a->carry != SWIMBA_CARRY_AUTO && a->carry != SWIMBA_CARRY_REWALK &&
+      a->carry != SWIMBA_CARRY_FIXUP)
+    return SWIMBA_EINVAL;
+  if (a->N != SWIMBA_STATE_N || a->k > 4) return SWIMBA_EUNSUPPORTED;
+  ScanPlan q;
+  q.ntiles = (a->D + 63) / 64;
+  if (a->L == 0 || a->B == 0) {
+    *p = q;
+    return SWIMBA_OK;
+  }
+  // no expert table in LDS: every problem may take the small-problem layout
+  bool small = false;
+  const int chunk = a->chunk > 0 ? a->chunk : auto_chunk(a->B, a->L, q.ntiles, false, true, &small);
+  plan_layout(q, a->B, a->L, a->D, chunk, SWIMBA_STATE_N, false, p);
   return SWIMBA_OK;
 }
 
@@ -155,6 +197,42 @@ int run_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t s
     return empty_sequence(a, separate, s);
   }
   return separate ? launch_scan_separate(a, p, ws, s) : launch_scan(a, p, ws, s);
+}
+
+int run_streams(const swimba_stream_args* a, void* ws, size_t ws_bytes, hipStream_t s) {
+  ScanPlan p;
+  int rc = plan_streams(a, &p);
+  if (rc != SWIMBA_OK) return rc;
+  if (a->A == nullptr || a->dt_bias == nullptr) return SWIMBA_EINVAL;
+  // each lane reads its A row as 16-byte vectors
+  if (reinterpret_cast<uintptr_t>(a->A) & 15) return SWIMBA_EINVAL;
+  if (a->B > 0 && a->L > 0) {
+    if (a->X == nullptr || a->dt_raw == nullptr || a->Bs == nullptr || a->Cs == nullptr ||
+        a->gate == nullptr || a->y == nullptr)
+      return SWIMBA_EINVAL;
+    // B and C streams are staged as pairs of elements
+    const uintptr_t pair = a->in_dtype == SWIMBA_BF16 ? 3 : 7;
+    if ((reinterpret_cast<uintptr_t>(a->Bs) & pair) || (reinterpret_cast<uintptr_t>(a->Cs) & pair))
+      return SWIMBA_EINVAL;
+  }
+  if (p.bytes > 0) {
+    if (ws == nullptr || ws_bytes < p.bytes || (reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+      return SWIMBA_EWORKSPACE;
+  }
+  if (a->B == 0 || a->L == 0) {
+    if (a->phase_events)
+      for (int i = 0; i < 6; ++i) (void)hipEventRecord(a->phase_events[i], s);
+    if (a->h_final == nullptr || a->B == 0) return SWIMBA_OK;
+    const size_t n = (size_t)a->B * a->D * SWIMBA_STATE_N;
+    hipLaunchKernelGGL(fill_initial_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       a->h0, a->h_final, n);
+    return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
+  }
+  const bool in_bf = a->in_dtype == SWIMBA_BF16, out_bf = a->y_dtype == SWIMBA_BF16;
+  if (in_bf && out_bf) return launch_streams_bb(a, p, ws, s);
+  if (in_bf) return launch_streams_bf(a, p, ws, s);
+  if (out_bf) return launch_streams_fb(a, p, ws, s);
+  return launch_streams_ff(a, p, ws, s);
 }
 
 }  // namespace
@@ -195,6 +273,26 @@ int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_
 int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
   return run_scan(a, ws, ws_bytes, stream, 1);
+}
+
+size_t swimba_scan_streams_workspace_size(const swimba_stream_args* a) {
+  ScanPlan p;
+  if (plan_streams(a, &p) != SWIMBA_OK) return 0;
+  return p.bytes;
+}
+
+int swimba_scan_streams_plan(const swimba_stream_args* a, int* chunk, int* nchunks) {
+  ScanPlan p;
+  const int rc = plan_streams(a, &p);
+  if (rc != SWIMBA_OK) return rc;
+  if (chunk) *chunk = p.chunk;
+  if (nchunks) *nchunks = p.nchunks;
+  return SWIMBA_OK;
+}
+
+int swimba_scan_streams(const swimba_stream_args* a, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  return run_streams(a, ws, ws_bytes, stream);
 }
 
 int swimba_step(const swimba_step_args* a, hipStream_t stream) {

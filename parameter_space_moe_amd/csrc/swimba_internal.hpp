@@ -23,6 +23,7 @@ struct ScanPlan {
 
 // Fills `p` for these arguments; returns a status.  Pure host arithmetic.
 int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p);
+int plan_streams(const swimba_stream_args* a, ScanPlan* p);
 
 // Kernel launchers (validated arguments only).
 int launch_route(const void* x, swimba_dtype xd, const float* Wr, int64_t T, int D, int E,
@@ -30,6 +31,11 @@ int launch_route(const void* x, swimba_dtype xd, const float* Wr, int64_t T, int
 int launch_scan(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_scan_separate(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_step(const swimba_step_args* a, hipStream_t s);
+// Stream-mixed scan, one launcher per (input, output) dtype pair.
+int launch_streams_ff(const swimba_stream_args* a, const ScanPlan& p, void* ws, hipStream_t s);
+int launch_streams_fb(const swimba_stream_args* a, const ScanPlan& p, void* ws, hipStream_t s);
+int launch_streams_bf(const swimba_stream_args* a, const ScanPlan& p, void* ws, hipStream_t s);
+int launch_streams_bb(const swimba_stream_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 // Pass 2 of the chunked scans: carried-in state per chunk (rows = 16 or E*16).
 int launch_carry(int B, int C, int D, int E, const float* P, float* H, float* h_final,
                  int separate, hipStream_t st, const hipEvent_t* ev);

@@ -40,6 +40,14 @@ class StepArgs(ctypes.Structure):
                 ("A", _vp), ("dt_bias", _vp), ("Dskip", _vp), ("state", _vp), ("y", _vp)]
 
 
+class StreamArgs(ctypes.Structure):
+    _fields_ = [("B", _ci), ("L", _ci), ("D", _ci), ("N", _ci), ("k", _ci),
+                ("in_dtype", _ci), ("y_dtype", _ci),
+                ("X", _vp), ("dt_raw", _vp), ("Bs", _vp), ("Cs", _vp), ("gate", _vp),
+                ("A", _vp), ("dt_bias", _vp), ("h0", _vp), ("y", _vp), ("h_final", _vp),
+                ("chunk", _ci), ("carry", _ci), ("phase_events", _vp)]
+
+
 class SwimbaError(RuntimeError):
     def __init__(self, fn, status):
         super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
@@ -69,6 +77,13 @@ def load(path: str | None = None):
     lib.swimba_scan_plan.argtypes = [ctypes.POINTER(ScanArgs), _ci, ctypes.POINTER(_ci),
                                      ctypes.POINTER(_ci)]
     lib.swimba_scan_plan.restype = _ci
+    lib.swimba_scan_streams_workspace_size.argtypes = [ctypes.POINTER(StreamArgs)]
+    lib.swimba_scan_streams_workspace_size.restype = ctypes.c_size_t
+    lib.swimba_scan_streams_plan.argtypes = [ctypes.POINTER(StreamArgs), ctypes.POINTER(_ci),
+                                             ctypes.POINTER(_ci)]
+    lib.swimba_scan_streams_plan.restype = _ci
+    lib.swimba_scan_streams.argtypes = [ctypes.POINTER(StreamArgs), _vp, ctypes.c_size_t, _vp]
+    lib.swimba_scan_streams.restype = _ci
     lib.swimba_step.argtypes = [ctypes.POINTER(StepArgs), _vp]
     lib.swimba_step.restype = _ci
     lib.swimba_status_string.argtypes = [_ci]
@@ -263,6 +278,98 @@ class PreparedScan:
         rc = self._fn(self._ref, self._ws, self._wsn, self.stream)
         if rc != OK:
             raise SwimbaError("swimba_scan", rc)
+
+
+def _stream_args(X, dt_raw, Bs, Cs, gate, A, dt_bias, h0, y, h_final, chunk, carry,
+                 phase_events):
+    _need(X, "X")
+    if X.dim() != 4:
+        raise ValueError("X must be [B, L, k, D]")
+    B, L, k, D = X.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    dev = X.device
+    _need(dt_raw, "dt_raw", (B, L, D), X.dtype, dev)
+    _need(Bs, "Bs", (B, L, k, N), X.dtype, dev)
+    _need(Cs, "Cs", (B, L, k, N), X.dtype, dev)
+    _need(gate, "gate", (B, L, k), torch.float32, dev)
+    _need(A, "A", (D, N), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (D,), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (B, D, N), torch.float32, dev)
+    _need(y, "y", (B, L, D), None, dev)
+    if h_final is not None:
+        _need(h_final, "h_final", (B, D, N), torch.float32, dev)
+    a = StreamArgs()
+    a.B, a.L, a.D, a.N, a.k = B, L, D, N, k
+    a.in_dtype, a.y_dtype = _dt(X), _dt(y)
+    a.X, a.dt_raw, a.Bs, a.Cs, a.gate = _ptr(X), _ptr(dt_raw), _ptr(Bs), _ptr(Cs), _ptr(gate)
+    a.A, a.dt_bias, a.h0, a.y, a.h_final = _ptr(A), _ptr(dt_bias), _ptr(h0), _ptr(y), \
+        _ptr(h_final)
+    a.chunk = int(chunk)
+    a.carry = CARRY[carry] if isinstance(carry, str) else int(carry)
+    a.phase_events = phase_events
+    return a
+
+
+def scan_streams(X, dt_raw, Bs, Cs, gate, A, dt_bias, h0=None, y=None, h_final=None,
+                 y_dtype=None, want_state=True, chunk=0, carry="auto", workspace=None,
+                 stream=None, phase_events=None):
+    """Stream-mixed scan (include/swimba.h: swimba_scan_streams).  X [B,L,k,D];
+    dt_raw [B,L,D]; Bs, Cs [B,L,k,16]; gate [B,L,k] f32; A [D,16], dt_bias [D]
+    f32.  Returns (y [B,L,D], h_final [B,D,16] or None)."""
+    B, L, k, D = X.shape
+    if y is None:
+        y = torch.empty((B, L, D), dtype=y_dtype or X.dtype, device=X.device)
+    if h_final is None and want_state:
+        h_final = torch.empty((B, D, N_STATE), dtype=torch.float32, device=X.device)
+    a = _stream_args(X, dt_raw, Bs, Cs, gate, A, dt_bias, h0, y, h_final, chunk, carry,
+                     phase_events)
+    lib = load()
+    need = int(lib.swimba_scan_streams_workspace_size(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    rc = lib.swimba_scan_streams(ctypes.byref(a), _ptr(workspace), workspace.numel(),
+                                 _stream(stream))
+    _check("swimba_scan_streams", rc)
+    return y, h_final
+
+
+def scan_streams_plan(X, chunk=0):
+    """(tokens per chunk, number of chunks) of swimba_scan_streams for X [B,L,k,D]."""
+    a = StreamArgs()
+    a.B, a.L, a.k, a.D = X.shape
+    a.N = N_STATE
+    a.in_dtype = a.y_dtype = _dt(X)
+    a.chunk = chunk
+    c, n = _ci(), _ci()
+    rc = load().swimba_scan_streams_plan(ctypes.byref(a), ctypes.byref(c), ctypes.byref(n))
+    _check("swimba_scan_streams_plan", rc)
+    return c.value, n.value
+
+
+class PreparedStreams:
+    """swimba_scan_streams marshalled once (see PreparedScan)."""
+
+    def __init__(self, X, dt_raw, Bs, Cs, gate, A, dt_bias, h0=None, y=None, h_final=None,
+                 chunk=0, carry="auto", workspace=None, stream=None):
+        self.args = _stream_args(X, dt_raw, Bs, Cs, gate, A, dt_bias, h0, y, h_final, chunk,
+                                 carry, None)
+        lib = load()
+        need = int(lib.swimba_scan_streams_workspace_size(ctypes.byref(self.args)))
+        self.workspace = workspace if workspace is not None else torch.empty(
+            max(need, 1), dtype=torch.uint8, device=X.device)
+        self._keep = (X, dt_raw, Bs, Cs, gate, A, dt_bias, h0, y, h_final)
+        self._fn = lib.swimba_scan_streams
+        self._ref = ctypes.byref(self.args)
+        self._ws = self.workspace.data_ptr()
+        self._wsn = self.workspace.numel()
+        self.stream = _stream(stream)
+
+    def __call__(self, phase_events=None):
+        self.args.phase_events = phase_events
+        rc = self._fn(self._ref, self._ws, self._wsn, self.stream)
+        if rc != OK:
+            raise SwimbaError("swimba_scan_streams", rc)
 
 
 class PreparedRoute:

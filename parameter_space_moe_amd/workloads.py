@@ -15,6 +15,13 @@ shapes named below.  Recipe (seed = workload index, numpy PCG64):
   dt_bias_e    ~ N(0, 0.1)   (variance 0.1)
   Dskip_e      ~ N(0, 1)
   Wr           ~ N(0, 1/D)   (variance 1/D: unit-variance logits)
+
+Stream-mixed inputs (``generate_streams``; seed = the workload's seed + 1000):
+  draw order   A, dt_bias, then X, dt_raw, Bs, Cs, gate
+  A            = -exp(U(0, ln 16)) per (d, n); dt_bias ~ N(0, 0.1)
+  X [B,L,k,D], dt_raw [B,L,D], Bs, Cs [B,L,k,N] ~ N(0, 1), bf16-rounded for
+               bf16 workloads
+  gate [B,L,k] ~ Dirichlet(1, ..., 1): convex weights of the k slots
 """
 from __future__ import annotations
 
@@ -133,3 +140,26 @@ def decode_steps(w: Workload, steps: int | None = None):
             yield {k: v[:, 0] for k, v in s.items()}
 
     return p, gen()
+
+
+def generate_streams(w: Workload, k: int | None = None, B: int | None = None,
+                     L: int | None = None, D: int | None = None):
+    """Inputs of the stream-mixed scan at a workload's shape: shared A [D,N],
+    dt_bias [D]; per-slot streams X [B,L,k,D], Bs, Cs [B,L,k,N]; dt_raw
+    [B,L,D]; gate [B,L,k].  float32 arrays (streams bf16-rounded for bf16
+    workloads)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed + 1000))
+    k = k or w.k
+    B = w.B if B is None else B
+    L = w.L if L is None else L
+    D = D or w.D
+    N = w.N
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), size=(D, N))).astype(np.float32)
+    dt_bias = _normal(rng, (D,), math.sqrt(0.1))
+    out = dict(A=A, dt_bias=dt_bias)
+    for name, shape in (("X", (B, L, k, D)), ("dt_raw", (B, L, D)), ("Bs", (B, L, k, N)),
+                        ("Cs", (B, L, k, N))):
+        v = _normal(rng, shape)
+        out[name] = bf16_round(v) if w.dtype == "bf16" else v
+    out["gate"] = rng.dirichlet(np.ones(k), size=(B, L)).astype(np.float32)
+    return out

@@ -41,6 +41,9 @@ def test_exports_nothing_but_the_abi():
     assert ours == set(header_functions())
 
 
+STRUCTS = (("swimba_scan_args", sw.ScanArgs), ("swimba_step_args", sw.StepArgs),
+           ("swimba_stream_args", sw.StreamArgs))
+
 LAYOUT_SRC = r"""
 #include <cstddef>
 #include <cstdio>
@@ -49,6 +52,7 @@ LAYOUT_SRC = r"""
 int main() {
   std::printf("swimba_scan_args sizeof %zu\n", sizeof(swimba_scan_args));
   std::printf("swimba_step_args sizeof %zu\n", sizeof(swimba_step_args));
+  std::printf("swimba_stream_args sizeof %zu\n", sizeof(swimba_stream_args));
   %FIELDS%
   return 0;
 }
@@ -57,7 +61,7 @@ int main() {
 
 def test_ctypes_structs_match_header(tmp_path):
     lines = []
-    for cname, cls in (("swimba_scan_args", sw.ScanArgs), ("swimba_step_args", sw.StepArgs)):
+    for cname, cls in STRUCTS:
         for f, _ in cls._fields_:
             lines.append("F(%s, %s)" % (cname, f))
     src = tmp_path / "layout.cpp"
@@ -70,9 +74,9 @@ def test_ctypes_structs_match_header(tmp_path):
     for l in out.splitlines():
         s, m, v = l.split()
         got[(s, m)] = int(v)
-    assert got[("swimba_scan_args", "sizeof")] == ctypes.sizeof(sw.ScanArgs)
-    assert got[("swimba_step_args", "sizeof")] == ctypes.sizeof(sw.StepArgs)
-    for cname, cls in (("swimba_scan_args", sw.ScanArgs), ("swimba_step_args", sw.StepArgs)):
+    for cname, cls in STRUCTS:
+        assert got[(cname, "sizeof")] == ctypes.sizeof(cls), cname
+    for cname, cls in STRUCTS:
         for f, _ in cls._fields_:
             assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
 
@@ -156,3 +160,43 @@ def test_route_and_step_reject(lib):
 def test_status_strings(lib):
     for st in (sw.OK, sw.EINVAL, sw.EUNSUPPORTED, sw.EWORKSPACE, sw.EHIP, 123):
         assert isinstance(sw.status_string(st), str) and sw.status_string(st)
+
+
+def stream_args(**kw):
+    a = sw.StreamArgs()
+    a.B, a.L, a.D, a.N, a.k = 1, 1024, 128, 16, 2
+    a.in_dtype, a.y_dtype = sw.BF16, sw.BF16
+    fake = 0x100000  # never dereferenced: every call below fails validation first
+    for f in ("X", "dt_raw", "Bs", "Cs", "gate", "A", "dt_bias", "y"):
+        setattr(a, f, fake)
+    a.chunk = 0
+    a.carry = 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k", 0, sw.EINVAL), ("k", 5, sw.EUNSUPPORTED), ("D", 0, sw.EINVAL), ("B", -1, sw.EINVAL),
+    ("L", -1, sw.EINVAL), ("chunk", -1, sw.EINVAL), ("carry", 7, sw.EINVAL),
+    ("in_dtype", 5, sw.EINVAL), ("N", 8, sw.EUNSUPPORTED), ("X", None, sw.EINVAL),
+    ("A", None, sw.EINVAL), ("gate", None, sw.EINVAL), ("A", 0x100004, sw.EINVAL),
+    ("Bs", 0x100002, sw.EINVAL),
+])
+def test_streams_rejects(lib, field, value, status):
+    a = stream_args(**{field: value})
+    assert lib.swimba_scan_streams(ctypes.byref(a), None, 0, None) == status
+
+
+def test_streams_workspace_and_plan(lib):
+    # 65536 tokens in chunks of 256: decays and states, no flag array
+    a = stream_args(B=1, L=65536, D=2560, chunk=256)
+    assert lib.swimba_scan_streams_workspace_size(ctypes.byref(a)) == 2 * 256 * 16 * 2560 * 4
+    assert lib.swimba_scan_streams(ctypes.byref(a), None, 0, None) == sw.EWORKSPACE
+    c, n = ctypes.c_int(), ctypes.c_int()
+    assert lib.swimba_scan_streams_plan(ctypes.byref(a), ctypes.byref(c), ctypes.byref(n)) == 0
+    assert (c.value, n.value) == (256, 256)
+    a = stream_args(L=100, chunk=100)
+    assert lib.swimba_scan_streams_workspace_size(ctypes.byref(a)) == 0
+    a = stream_args(k=9)
+    assert lib.swimba_scan_streams_workspace_size(ctypes.byref(a)) == 0
