@@ -9,7 +9,8 @@ inputs resident in HBM.  Printed as one JSON line (rank 0):
   modes    = the separate design, the dense single-expert scan (E = 1), the
              scan alone, and the decode step, for the "mixed vs separate" and
              "mixed vs dense" ratios; the stream-mixed form (shared A, mixed
-             B X injection and C readout) at the same shape
+             B X injection and C readout) and the scalar-transition (Mamba-2)
+             form of the mixed scan at the same shape
   cpu_baseline = the fp64 oracle timed on this host on the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -44,6 +45,15 @@ def slots_per_tc(k: int) -> float:
     (2 transcendentals = 4 slots, 5 VALU), beta and delta (2k), Delta*g_j (k),
     Delta*x, the D term, and x/dt_raw/y conversions (3)."""
     return N_STATE * (k + 5) + (4 + 5 + 3 * k + 2 + 3)
+
+
+def scalar_a_slots_per_tc(k: int) -> float:
+    """Minimum VALU issue slots per token x channel of the mixed scan with one
+    transition per channel (the Mamba-2 form): per state entry Delta*x*B,
+    the update and the readout (3); per (token, channel) softplus (4 + 5),
+    beta, delta and the mixed exponent (3k), Delta*g_j (k), one exp2 (2),
+    Delta*x, the D term and the x/dt_raw/y conversions (5)."""
+    return N_STATE * 3 + (9 + 4 * k + 2 + 5)
 
 
 def stream_slots_per_tc(k: int) -> float:
@@ -319,6 +329,40 @@ def expert_sweep(swimba, dev, reps):
     return out
 
 
+def scalar_a_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y, hf, reps, ms_mixed):
+    """The mixed scan with one transition per (expert, channel), the Mamba-2
+    form A_t = a_t I, on the same inputs (A[e, d] = the n = 0 entry of the
+    diagonal draw): one exponential per (token, channel) instead of 16.  The
+    scan alone, and its chunk pass against the VALU ceiling and 8 TB/s."""
+    import torch
+    As = A[:, :, 0].contiguous()
+    scan = swimba.PreparedScan(False, x, dtr, Bm, Cm, idx, gate, As, bias, Dsk, y=y,
+                               h_final=hf, chunk=w.chunk)
+    ms = _time(scan, reps)
+    hip = Hip()
+    ev = [[hip.event() for _ in range(6)] for _ in range(reps)]
+    arrs = [(ctypes.c_void_p * 6)(*[e_.value for e_ in e]) for e in ev]
+    for a in arrs:
+        scan(ctypes.addressof(a))
+    torch.cuda.synchronize()
+    chunk_ms = sum(hip.ms(e[0], e[1]) for e in ev) / reps
+    fixup_ms = sum(hip.ms(e[4], e[5]) for e in ev) / reps
+    tc, k = w.tc, w.k
+    esz = 2 if w.dtype == "bf16" else 4
+    _, nchunks = swimba.scan_plan(x, As, idx, chunk=w.chunk)
+    chunk_bytes = tc * 3 * esz + w.B * w.L * (2 * N_STATE * esz + 2 * k * 4)
+    if nchunks > 1:
+        chunk_bytes += 2 * w.B * nchunks * N_STATE * w.D * 4
+    tf = tc * scalar_a_slots_per_tc(k) * 2 / (chunk_ms * 1e-3) / 1e12
+    gbs = chunk_bytes / (chunk_ms * 1e-3) / 1e9
+    return {"scan_ms": round(ms, 4), "G_tc_per_s": round(tc / ms / 1e6, 3),
+            "over_diagonal": round(ms / ms_mixed, 3),
+            "chunk_pass_ms": round(chunk_ms, 4), "fixup_ms": round(fixup_ms, 4),
+            "valu_frac": round(tf / VALU_PEAK_TFLOPS, 4),
+            "valu_note": "%d slots/tc as FMA-equivalent flops" % scalar_a_slots_per_tc(k),
+            "hbm_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def stream_mode(swimba, workloads, w, x, Wr, idx, gate, reps):
     """The pages' stream-mixed form at the same layer shape: shared A, each of
     the k slots carries its expert's X, B and C streams, the injection and the
@@ -426,6 +470,8 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
     del flush
     res["expert_sweep"] = expert_sweep(swimba, dev, reps)
     res["stream_mixed"] = stream_mode(swimba, workloads, w, x, Wr, idx, gate, reps)
+    res["scalar_a"] = scalar_a_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y, hf,
+                                    reps, ms_mixed)
     # decode workload: 128 routed steps on a persistent fp32 state
     wd = workloads.BY_NAME["decode"]
     p, steps = workloads.decode_steps(wd)

@@ -96,6 +96,15 @@ typedef enum {
                               decayed below fp32 resolution (needs A < 0)    */
 } swimba_carry;
 
+/*
+ * Shape of the transition A.  DIAGONAL: one entry per state, A[..., D, N].
+ * SCALAR: one entry per channel shared by its N states, A[..., D] -- the
+ * Mamba-2 form A_t = a_t I that Swimba is built on ([SW] Spanish summary
+ * "Arquitectura de Swimba", French "Architecture de Swimba": Mamba-2 and its
+ * SSD operator); one exponential per (token, channel) instead of N.
+ */
+typedef enum { SWIMBA_A_DIAGONAL = 0, SWIMBA_A_SCALAR = 1 } swimba_a_form;
+
 typedef struct {
   int B, L, D, N, E, k;         /* batch, length, channels, states (16), experts, active */
   swimba_dtype in_dtype;        /* dtype of x, dt_raw, Bm, Cm                            */
@@ -106,7 +115,8 @@ typedef struct {
   const void* Cm;               /* [B, L, N]  selective output vector C_t (16-byte aligned) */
   const int32_t* idx;           /* [B, L, k]  routing, 0 <= idx < E                       */
   const float* gate;            /* [B, L, k]  routing weights                             */
-  const float* A;               /* [E, D, N]  per-expert diagonal transition (< 0)        */
+  const float* A;               /* [E, D, N]  per-expert diagonal transition (< 0);
+                                   [E, D] with a_form SCALAR                            */
   const float* dt_bias;         /* [E, D]                                                 */
   const float* Dskip;           /* [E, D]     per-expert feed-through D                   */
   const float* h0;              /* NULL = zeros; [B, D, N] (separate: [B, E, D, N])       */
@@ -119,6 +129,7 @@ typedef struct {
                                    that order, stamped by each pass's kernel dispatch
                                    (no extra packets on `stream`); a pass that does not
                                    run has both events recorded where it would run      */
+  swimba_a_form a_form;         /* A is [E, D, N] (DIAGONAL, 0) or [E, D] (SCALAR)        */
 } swimba_scan_args;
 
 /*
@@ -172,11 +183,12 @@ typedef struct {
   const float* gate;            /* [B, k] with idx                               */
   int32_t* idx_out;             /* NULL, or [B, k]: routing used                 */
   float* gate_out;              /* NULL, or [B, k]                               */
-  const float* A;               /* [E, D, N]                                     */
+  const float* A;               /* [E, D, N], or [E, D] with a_form SCALAR       */
   const float* dt_bias;         /* [E, D]                                        */
   const float* Dskip;           /* [E, D]                                        */
   float* state;                 /* [B, D, N] fp32, read and updated in place     */
   void* y;                      /* [B, D] out                                    */
+  swimba_a_form a_form;         /* A is [E, D, N] (DIAGONAL, 0) or [E, D] (SCALAR) */
 } swimba_step_args;
 
 /*

@@ -26,12 +26,26 @@ __host__ __device__ constexpr size_t ring_bytes(int k) {
 }
 
 // Stage the tile's expert parameters; returns 1 if any A in the tile is not
-// strictly negative (including NaN).
+// strictly negative (including NaN).  scalar_a: A is [E][D] (one transition
+// per expert and channel) and the table [E][64] floats.
 template <typename P>
-__device__ __forceinline__ int load_table(const P& p, float4* sA, float2* sBD, int d0) {
+__device__ __forceinline__ int load_table(const P& p, float4* sA, float2* sBD, int d0,
+                                          bool scalar_a) {
   int bad = 0;
   const int nthr = blockDim.x;
-  for (int i = threadIdx.x; i < p.E * 256; i += nthr) {
+  if (scalar_a) {
+    float* sAs = reinterpret_cast<float*>(sA);
+    for (int i = threadIdx.x; i < p.E * 64; i += nthr) {
+      const int e = i >> 6, d = d0 + (i & 63);
+      float v = 0.f;
+      if (d < p.D) {
+        v = p.A[(size_t)e * p.D + d];
+        bad |= !(v < 0.f);
+      }
+      sAs[i] = v;
+    }
+  }
+  for (int i = threadIdx.x; i < (scalar_a ? 0 : p.E * 256); i += nthr) {
     int e = i >> 8, r = i & 255, dl = r >> 2, q = r & 3;
     int d = d0 + dl;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);

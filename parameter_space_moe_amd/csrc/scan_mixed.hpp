@@ -69,20 +69,26 @@ struct MixParams {
 };
 
 // LDS: the workgroup's expert table (64 channels), per-wave decay sums, and
-// per-wave staging rings.
+// per-wave staging rings.  With a scalar transition per (expert, channel) the
+// A table is [E][64] floats.
 struct Smem {
-  float4* A;   // [E][4][64]  A[e, d0+lane, 4q..4q+3]
+  float4* A;   // [E][4][64]  A[e, d0+lane, 4q..4q+3]  (scalar A: [E][64] floats)
   float2* BD;  // [E][64]     (dt_bias, Dskip)
   float* U;    // [waves][E][64] (chunk pass only)
   Ring ring;   // this wave's ring
 };
 
-__device__ __forceinline__ Smem smem_layout(int E, int k, bool with_u, int waves, int wave) {
+__host__ __device__ inline size_t a_table_bytes(int E, bool scalar_a) {
+  return scalar_a ? (size_t)E * 64 * 4 : (size_t)E * 4 * 64 * 16;
+}
+
+__device__ __forceinline__ Smem smem_layout(int E, int k, bool with_u, int waves, int wave,
+                                            bool scalar_a) {
   extern __shared__ float4 smem_raw[];
   Smem s;
   char* p = reinterpret_cast<char*>(smem_raw);
   s.A = reinterpret_cast<float4*>(p);
-  p += (size_t)E * 4 * 64 * 16;
+  p += a_table_bytes(E, scalar_a);
   s.BD = reinterpret_cast<float2*>(p);
   p += (size_t)E * 64 * 8;
   s.U = reinterpret_cast<float*>(p);
@@ -94,9 +100,9 @@ __device__ __forceinline__ Smem smem_layout(int E, int k, bool with_u, int waves
   return s;
 }
 
-__host__ inline size_t smem_bytes(int E, int k, bool with_u, int waves) {
-  return (size_t)E * (4 * 64 * 16 + 64 * 8) + (with_u ? (size_t)waves * E * 64 * 4 : 0) +
-         ring_bytes(k) * waves;
+__host__ inline size_t smem_bytes(int E, int k, bool with_u, int waves, bool scalar_a) {
+  return a_table_bytes(E, scalar_a) + (size_t)E * 64 * 8 +
+         (with_u ? (size_t)waves * E * 64 * 4 : 0) + ring_bytes(k) * waves;
 }
 
 // One token of the mixed recurrence for one lane.  Routing (experts e[j],
@@ -104,9 +110,12 @@ __host__ inline size_t smem_bytes(int E, int k, bool with_u, int waves) {
 // position `i`.  Every LDS address below depends only on (e, lane), so all of
 // a token's reads can be in flight together.
 //   K > 0: k == K known at compile time; K == 0: runtime k.
-//   TRACK: also decay the carried part g (fix-up pass).
+//   TRACK: also decay the carried part g (fix-up pass; with SA, g[0] is the
+//          carried part's common decay factor).
 //   ACC_U: accumulate the gate-weighted Delta per expert (chunk pass).
-template <int K, bool TRACK, bool ACC_U>
+//   SA: one transition per (expert, channel), shared by the 16 states (the
+//       Mamba-2 form A = a I): one exponential per token instead of 16.
+template <int K, bool TRACK, bool ACC_U, bool SA>
 __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, float* U,
                                            const int* e, const float* gw, int slot, int i,
                                            int lane, float xv, float rv, float* h, float* g) {
@@ -125,6 +134,40 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
     for (int j = 0; j < k; ++j) bias_slot(j);
   }
   const float dlt = softplus_f32(rv + beta);
+  if constexpr (SA) {
+    // mixed exponent Delta * sum_j g_j A[e_j, d] * log2(e), one per token
+    const float dl2 = dlt * kLog2e;
+    const float* As = reinterpret_cast<const float*>(s.A);
+    float m = 0.f;
+    auto a_slot = [&](int j) {
+      const float u = dl2 * gw[j];
+      if (ACC_U) U[e[j] * 64 + lane] += u;
+      m = fmaf(u, As[e[j] * 64 + lane], m);
+    };
+    if constexpr (K > 0) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) a_slot(j);
+    } else {
+      for (int j = 0; j < k; ++j) a_slot(j);
+    }
+    const float a = hw_exp2(m);
+    const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
+    const float dx = dlt * xv;
+    float yv = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 b4 = bc[q], c4 = bc[4 + q];
+      const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = 4 * q + r;
+        h[n] = fmaf(a, h[n], dx * bv[r]);
+        yv = fmaf(cv[r], h[n], yv);
+      }
+    }
+    if (TRACK) g[0] *= a;
+    return fmaf(delta, xv, yv);
+  }
   // mixed exponent m[n] = Delta * sum_j g_j A[e_j, d, n] * log2(e)
   float m[kN];
 #pragma unroll
@@ -183,7 +226,7 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
 // x, dt_raw and y go through per-block buffer resources (scalar token offsets,
 // a fixed per-lane channel offset); the prefetch of the next block is issued
 // before the current one computes and is waited on only when it is used.
-template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U>
+template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA>
 __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U, int b, int t0,
                                      int t1, int d, bool active, bool full_tile, int lane,
                                      bool truncate, float* h, float* g, int& gate_bad) {
@@ -246,7 +289,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
             ev[j] = s.ring.e[(slot * kTB + i) * K + j];
             gv[j] = s.ring.g[(slot * kTB + i) * K + j];
           }
-          const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, ev, gv, slot, i, lane,
+          const float yv = mix_token<K, TRACK, ACC_U, SA>(p, s, U, ev, gv, slot, i, lane,
                                                       to_f32(xc[i]), to_f32(rc[i]), h, g);
           stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
@@ -262,7 +305,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
               gv[j] = s.ring.g[(slot * kTB + i) * K + j];
             }
             const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
-            const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, ev, gv, slot, i, lane, xv, rv,
+            const float yv = mix_token<K, TRACK, ACC_U, SA>(p, s, U, ev, gv, slot, i, lane, xv, rv,
                                                         h, g);
             if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
           }
@@ -279,7 +322,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
             gb[j] = s.ring.g[(slot * kTB + i) * k + j];
           }
           const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
-          const float yv = mix_token<K, TRACK, ACC_U>(p, s, U, eb, gb, slot, i, lane, xv, rv, h,
+          const float yv = mix_token<K, TRACK, ACC_U, SA>(p, s, U, eb, gb, slot, i, lane, xv, rv, h,
                                                       g);
           if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
@@ -291,8 +334,12 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
       for (int q = 0; q < kN; ++q) mh = fmaxf(mh, fabsf(h[q]));
       const float thr = fmaxf(kFixupTol * mh, kTiny);
       bool conv = true;
+      if constexpr (SA) {
+        conv = fabsf(g[0]) * g[1] <= thr;  // g[1] = max_n |h_in[n]|; NaN: not converged
+      } else {
 #pragma unroll
-      for (int q = 0; q < kN; ++q) conv &= fabsf(g[q]) <= thr;  // NaN: not converged
+        for (int q = 0; q < kN; ++q) conv &= fabsf(g[q]) <= thr;  // NaN: not converged
+      }
       if (__all(conv)) break;
     }
     if (more) {
@@ -307,10 +354,10 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
 }
 
 // Pass 1 (or the only pass when CHUNKED is false).
-template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED>
+template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA>
 __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, CHUNKED, WAVES, wave);
+  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, CHUNKED, WAVES, wave, SA);
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
   const int tile = bid % p.ntiles;
@@ -320,7 +367,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
 
-  int bad = stage::load_table(p, s.A, s.BD, d0);
+  int bad = stage::load_table(p, s.A, s.BD, d0, SA);
   float* U = s.U + wave * p.E * 64;
   if (CHUNKED)
     for (int e = 0; e < p.E; ++e) U[e * 64 + lane] = 0.f;
@@ -339,7 +386,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   // every chunk writes y (provisional for chunks >= 1, recomputed by the
   // fix-up pass where the carried-in state still matters)
   int gate_bad = 0;
-  walk<TIn, TOut, K, false, CHUNKED>(p, s, U, b, t0, t1, d, active, d0 + 64 <= p.D, lane, false,
+  walk<TIn, TOut, K, false, CHUNKED, SA>(p, s, U, b, t0, t1, d, active, d0 + 64 <= p.D, lane, false,
                                      h, nullptr, gate_bad);
 
   if (CHUNKED) {
@@ -347,7 +394,14 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
     float m[kN];
 #pragma unroll
     for (int n = 0; n < kN; ++n) m[n] = 0.f;
-    for (int e = 0; e < p.E; ++e) {
+    if (SA) {
+      // one decay per channel, written to every state row for the carry pass
+      const float* As = reinterpret_cast<const float*>(s.A);
+      for (int e = 0; e < p.E; ++e) m[0] = fmaf(U[e * 64 + lane], As[e * 64 + lane], m[0]);
+#pragma unroll
+      for (int n = 1; n < kN; ++n) m[n] = m[0];
+    }
+    for (int e = 0; e < (SA ? 0 : p.E); ++e) {
       float u = U[e * 64 + lane];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -376,10 +430,10 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
 
 // Pass 3: chunks 1.. re-run from their carried-in state until the carried part
 // has decayed away (or to the chunk's end).
-template <typename TIn, typename TOut, int WAVES, int K>
+template <typename TIn, typename TOut, int WAVES, int K, bool SA>
 __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, false, WAVES, wave);
+  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, false, WAVES, wave, SA);
   const int nfix = p.nchunks - 1;
   const int ncg = (nfix + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
@@ -389,7 +443,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const int b = bid / ncg;
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
-  stage::load_table(p, s.A, s.BD, d0);
+  stage::load_table(p, s.A, s.BD, d0, SA);
   __syncthreads();
 
   const int c = 1 + cg * WAVES + wave;
@@ -403,14 +457,22 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
     h[n] = active ? p.H[base + (size_t)n * p.D] : 0.f;
     g[n] = h[n];
   }
+  if (SA) {
+    // the carried part is G * h_in: track G and max |h_in|
+    float mh = 0.f;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) mh = fmaxf(mh, fabsf(h[n]));
+    g[0] = 1.f;
+    g[1] = mh;
+  }
   const bool truncate = p.carry == SWIMBA_CARRY_FIXUP &&
                         p.flags[((size_t)b * p.nchunks + c) * p.ntiles + tile] == 0;
   int gate_bad = 0;
-  walk<TIn, TOut, K, true, false>(p, s, nullptr, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
+  walk<TIn, TOut, K, true, false, SA>(p, s, nullptr, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
                                   truncate, h, g, gate_bad);
 }
 
-template <typename TIn, typename TOut, int WAVES, int K>
+template <typename TIn, typename TOut, int WAVES, int K, bool SA>
 int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   MixParams p;
   p.B = a->B;
@@ -439,14 +501,14 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
   p.flags = pl.nchunks > 1 ? reinterpret_cast<int32_t*>(w + pl.off_flags) : nullptr;
 
-  const size_t smem1 = smem_bytes(p.E, p.k, true, WAVES);
-  const size_t smem3 = smem_bytes(p.E, p.k, false, WAVES);
+  const size_t smem1 = smem_bytes(p.E, p.k, true, WAVES, SA);
+  const size_t smem3 = smem_bytes(p.E, p.k, false, WAVES, SA);
   const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
   if (pl.nchunks <= 1) {
     p.nchunks = 1;
     dim3 grid((unsigned)((size_t)p.B * p.ntiles));
-    allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, false>, smem3);
-    const int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, false>, grid,
+    allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA>, smem3);
+    const int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA>, grid,
                                 dim3(WAVES * 64), smem3, st, ev, p);
     if (rc != SWIMBA_OK) return rc;
     record_skipped(ev ? ev + 2 : nullptr, st);
@@ -455,35 +517,39 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   }
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   dim3 grid1((unsigned)((size_t)p.B * ncg * p.ntiles));
-  allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, true>, smem1);
-  int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, true>, grid1, dim3(WAVES * 64),
+  allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA>, smem1);
+  int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA>, grid1, dim3(WAVES * 64),
                         smem1, st, ev, p);
   if (rc != SWIMBA_OK) return rc;
   rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 0, st, ev ? ev + 2 : nullptr);
   if (rc != SWIMBA_OK) return rc;
   const int ncg3 = (p.nchunks - 1 + WAVES - 1) / WAVES;
   dim3 grid3((unsigned)((size_t)p.B * ncg3 * p.ntiles));
-  allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K>, smem3);
-  return launch_timed(mix_fixup_kernel<TIn, TOut, WAVES, K>, grid3, dim3(WAVES * 64), smem3, st,
+  allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K, SA>, smem3);
+  return launch_timed(mix_fixup_kernel<TIn, TOut, WAVES, K, SA>, grid3, dim3(WAVES * 64), smem3, st,
                       ev ? ev + 4 : nullptr, p);
 }
 
-template <typename TIn, typename TOut, int WAVES>
+template <typename TIn, typename TOut, int WAVES, bool SA>
 int launch_mixed_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   switch (a->k) {
     case 1:
-      return launch_mixed_t<TIn, TOut, WAVES, 1>(a, pl, ws, st);
+      return launch_mixed_t<TIn, TOut, WAVES, 1, SA>(a, pl, ws, st);
     case 2:
-      return launch_mixed_t<TIn, TOut, WAVES, 2>(a, pl, ws, st);
+      return launch_mixed_t<TIn, TOut, WAVES, 2, SA>(a, pl, ws, st);
     default:
-      return launch_mixed_t<TIn, TOut, WAVES, 0>(a, pl, ws, st);
+      return launch_mixed_t<TIn, TOut, WAVES, 0, SA>(a, pl, ws, st);
   }
 }
 
 template <typename TIn, typename TOut>
 int launch_mixed_w(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
-  if (pl.waves == 8) return launch_mixed_k<TIn, TOut, 8>(a, pl, ws, st);
-  return launch_mixed_k<TIn, TOut, 4>(a, pl, ws, st);
+  if (a->a_form == SWIMBA_A_SCALAR) {
+    if (pl.waves == 8) return launch_mixed_k<TIn, TOut, 8, true>(a, pl, ws, st);
+    return launch_mixed_k<TIn, TOut, 4, true>(a, pl, ws, st);
+  }
+  if (pl.waves == 8) return launch_mixed_k<TIn, TOut, 8, false>(a, pl, ws, st);
+  return launch_mixed_k<TIn, TOut, 4, false>(a, pl, ws, st);
 }
 
 }  // namespace mixed

@@ -29,6 +29,7 @@ constexpr int kStepChan = kStepThreads / 4;  // channels per workgroup iteration
 
 struct StepParams {
   int B, D, E, k, slices;
+  int scalar_a;  // A is [E][D]: one transition per expert and channel
   const void* x;
   const void* dt;
   const void* Bm;
@@ -241,12 +242,15 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
         beta = fmaf(gj, p.bias[(size_t)e * p.D + dd], beta);
         delta = fmaf(gj, p.Dsk[(size_t)e * p.D + dd], delta);
         const float4 a =
-            *reinterpret_cast<const float4*>(p.A + ((size_t)e * p.D + dd) * kN + 4 * q);
+            p.scalar_a
+                ? make_float4(p.A[(size_t)e * p.D + dd], 0.f, 0.f, 0.f)
+                : *reinterpret_cast<const float4*>(p.A + ((size_t)e * p.D + dd) * kN + 4 * q);
         m[0] = fmaf(gj, a.x, m[0]);
         m[1] = fmaf(gj, a.y, m[1]);
         m[2] = fmaf(gj, a.z, m[2]);
         m[3] = fmaf(gj, a.w, m[3]);
       }
+      if (p.scalar_a) m[1] = m[2] = m[3] = m[0];
       const float dlt = softplus_f32(rv + beta);
       const float dl2 = dlt * kLog2e, dx = dlt * xv;
       float hv[4] = {cur[u].h.x, cur[u].h.y, cur[u].h.z, cur[u].h.w};
@@ -293,6 +297,7 @@ int launch_step_t(const swimba_step_args* a, hipStream_t s) {
   p.idx_out = a->idx_out;
   p.gate_out = a->gate_out;
   p.A = a->A;
+  p.scalar_a = a->a_form == SWIMBA_A_SCALAR;
   p.bias = a->dt_bias;
   p.Dsk = a->Dskip;
   p.state = a->state;

@@ -29,6 +29,7 @@ int validate_scan(const swimba_scan_args* a, int separate) {
   if (a->carry != SWIMBA_CARRY_AUTO && a->carry != SWIMBA_CARRY_REWALK &&
       a->carry != SWIMBA_CARRY_FIXUP)
     return SWIMBA_EINVAL;
+  if (a->a_form != SWIMBA_A_DIAGONAL && a->a_form != SWIMBA_A_SCALAR) return SWIMBA_EINVAL;
   if (a->N != SWIMBA_STATE_N) return SWIMBA_EUNSUPPORTED;
   if (a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
   if (separate && a->E > 16) return SWIMBA_EUNSUPPORTED;
@@ -300,6 +301,7 @@ int swimba_step(const swimba_step_args* a, hipStream_t stream) {
   if (a->B < 0 || a->D < 1 || a->N < 1 || a->E < 1 || a->k < 1 || a->k > a->E)
     return SWIMBA_EINVAL;
   if (!dtype_ok(a->in_dtype) || !dtype_ok(a->y_dtype)) return SWIMBA_EINVAL;
+  if (a->a_form != SWIMBA_A_DIAGONAL && a->a_form != SWIMBA_A_SCALAR) return SWIMBA_EINVAL;
   if (a->N != SWIMBA_STATE_N || a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
   if (a->B == 0) return SWIMBA_OK;
   if (a->x == nullptr || a->dt_raw == nullptr || a->Bm == nullptr || a->Cm == nullptr ||
@@ -308,8 +310,9 @@ int swimba_step(const swimba_step_args* a, hipStream_t stream) {
     return SWIMBA_EINVAL;
   if (a->idx == nullptr && a->Wr == nullptr) return SWIMBA_EINVAL;
   if (a->idx != nullptr && a->gate == nullptr) return SWIMBA_EINVAL;
-  // state and A are read as 16-byte vectors
-  if ((reinterpret_cast<uintptr_t>(a->state) & 15) || (reinterpret_cast<uintptr_t>(a->A) & 15))
+  // state (and a diagonal A) are read as 16-byte vectors
+  if ((reinterpret_cast<uintptr_t>(a->state) & 15) ||
+      (a->a_form == SWIMBA_A_DIAGONAL && (reinterpret_cast<uintptr_t>(a->A) & 15)))
     return SWIMBA_EINVAL;
   return launch_step(a, stream);
 }

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libswimba.so")
 F32, BF16 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 CARRY = {"auto": 0, "rewalk": 1, "fixup": 2}
+A_DIAGONAL, A_SCALAR = 0, 1  # A [E, D, N] or [E, D] (one transition per channel)
 N_STATE = 16
 
 _vp = ctypes.c_void_p
@@ -29,7 +30,7 @@ class ScanArgs(ctypes.Structure):
                 ("x", _vp), ("dt_raw", _vp), ("Bm", _vp), ("Cm", _vp),
                 ("idx", _vp), ("gate", _vp), ("A", _vp), ("dt_bias", _vp), ("Dskip", _vp),
                 ("h0", _vp), ("y", _vp), ("h_final", _vp),
-                ("chunk", _ci), ("carry", _ci), ("phase_events", _vp)]
+                ("chunk", _ci), ("carry", _ci), ("phase_events", _vp), ("a_form", _ci)]
 
 
 class StepArgs(ctypes.Structure):
@@ -37,7 +38,8 @@ class StepArgs(ctypes.Structure):
                 ("in_dtype", _ci), ("y_dtype", _ci),
                 ("x", _vp), ("dt_raw", _vp), ("Bm", _vp), ("Cm", _vp),
                 ("Wr", _vp), ("idx", _vp), ("gate", _vp), ("idx_out", _vp), ("gate_out", _vp),
-                ("A", _vp), ("dt_bias", _vp), ("Dskip", _vp), ("state", _vp), ("y", _vp)]
+                ("A", _vp), ("dt_bias", _vp), ("Dskip", _vp), ("state", _vp), ("y", _vp),
+                ("a_form", _ci)]
 
 
 class StreamArgs(ctypes.Structure):
@@ -162,7 +164,7 @@ def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, 
         raise ValueError("x must be [B, L, D]")
     B, L, D = x.shape
     E = A.shape[0]
-    N = A.shape[2] if A.dim() == 3 else -1
+    N = Bm.shape[2] if Bm.dim() == 3 else -1
     k = idx.shape[2] if idx.dim() == 3 else -1
     dev = x.device
     _need(dt_raw, "dt_raw", (B, L, D), x.dtype, dev)
@@ -170,7 +172,8 @@ def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, 
     _need(Cm, "Cm", (B, L, N), x.dtype, dev)
     _need(idx, "idx", (B, L, k), torch.int32, dev)
     _need(gate, "gate", (B, L, k), torch.float32, dev)
-    _need(A, "A", (E, D, N), torch.float32, dev)
+    scalar_a = A.dim() == 2
+    _need(A, "A", (E, D) if scalar_a else (E, D, N), torch.float32, dev)
     _need(dt_bias, "dt_bias", (E, D), torch.float32, dev)
     _need(Dskip, "Dskip", (E, D), torch.float32, dev)
     sshape = (B, E, D, N) if separate else (B, D, N)
@@ -189,6 +192,7 @@ def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, 
     a.chunk = int(chunk)
     a.carry = CARRY[carry] if isinstance(carry, str) else int(carry)
     a.phase_events = phase_events
+    a.a_form = A_SCALAR if scalar_a else A_DIAGONAL
     return a
 
 
@@ -219,8 +223,9 @@ def _scan(separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, y=
 
 
 def scan(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
-    """Parameter-space-mixed scan (include/swimba.h: swimba_scan).  Returns
-    (y [B,L,D], h_final [B,D,16] or None)."""
+    """Parameter-space-mixed scan (include/swimba.h: swimba_scan).  A is
+    [E,D,16], or [E,D] for one transition per channel (the scalar form).
+    Returns (y [B,L,D], h_final [B,D,16] or None)."""
     return _scan(False, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
 
 
@@ -233,7 +238,8 @@ def scan_separate(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw
 def _shape_args(x, A, idx, chunk, y_dtype):
     B, L, D = x.shape
     a = ScanArgs()
-    a.B, a.L, a.D, a.N, a.E, a.k = B, L, D, A.shape[2], A.shape[0], idx.shape[2]
+    a.B, a.L, a.D, a.N, a.E, a.k = B, L, D, N_STATE, A.shape[0], idx.shape[2]
+    a.a_form = A_SCALAR if A.dim() == 2 else A_DIAGONAL
     a.in_dtype = _dt(x)
     a.y_dtype = a.in_dtype if y_dtype is None else (BF16 if y_dtype == torch.bfloat16 else F32)
     a.chunk = chunk
@@ -398,12 +404,14 @@ def _step_args(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, k, idx, gate, y,
                gate_out, y_dtype):
     _need(x, "x")
     B, D = x.shape
-    E, N = A.shape[0], A.shape[2]
+    E = A.shape[0]
+    N = Bm.shape[1] if Bm.dim() == 2 else -1
     dev = x.device
     _need(dt_raw, "dt_raw", (B, D), x.dtype, dev)
     _need(Bm, "Bm", (B, N), x.dtype, dev)
     _need(Cm, "Cm", (B, N), x.dtype, dev)
-    _need(A, "A", (E, D, N), torch.float32, dev)
+    scalar_a = A.dim() == 2
+    _need(A, "A", (E, D) if scalar_a else (E, D, N), torch.float32, dev)
     _need(dt_bias, "dt_bias", (E, D), torch.float32, dev)
     _need(Dskip, "Dskip", (E, D), torch.float32, dev)
     _need(state, "state", (B, D, N), torch.float32, dev)
@@ -430,6 +438,7 @@ def _step_args(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, k, idx, gate, y,
     a.idx_out, a.gate_out = _ptr(idx_out), _ptr(gate_out)
     a.A, a.dt_bias, a.Dskip, a.state, a.y = _ptr(A), _ptr(dt_bias), _ptr(Dskip), _ptr(state), \
         _ptr(y)
+    a.a_form = A_SCALAR if scalar_a else A_DIAGONAL
     return a, y
 
 

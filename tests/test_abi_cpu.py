@@ -100,7 +100,7 @@ def scan_args(**kw):
     ("B", -1, sw.EINVAL), ("L", -1, sw.EINVAL), ("chunk", -1, sw.EINVAL), ("carry", 7, sw.EINVAL),
     ("in_dtype", 5, sw.EINVAL), ("N", 8, sw.EUNSUPPORTED), ("E", 65, sw.EUNSUPPORTED),
     ("E", 17, sw.EUNSUPPORTED), ("x", None, sw.EINVAL), ("A", None, sw.EINVAL),
-    ("idx", None, sw.EINVAL),
+    ("idx", None, sw.EINVAL), ("a_form", 2, sw.EINVAL),
 ])
 def test_scan_rejects(lib, field, value, status):
     a = scan_args(**{field: value})
