@@ -54,10 +54,11 @@ def load(path: str | None = None):
     lib.ref_scan_separate.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7
     lib.ref_mamba_scan.argtypes = [ci] * 4 + [_f64p] * 9
     lib.ref_scan_streams.argtypes = [ci] * 5 + [_f64p] * 10
+    lib.ref_scan_backward.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 16
     lib.ref_step.argtypes = [ci] * 5 + [_f64p] * 5 + [_i32p] + [_f64p] * 6 + [_i32p, _f64p]
     lib.ref_num_threads.restype = ci
     for f in (lib.ref_route, lib.ref_scan, lib.ref_scan_separate, lib.ref_mamba_scan,
-              lib.ref_scan_streams, lib.ref_step):
+              lib.ref_scan_streams, lib.ref_scan_backward, lib.ref_step):
         f.restype = None
     if path is None:
         _lib = lib
@@ -137,6 +138,34 @@ def scan_separate(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, lib=
     lib = lib or load()
     return _scan_common(lib.ref_scan_separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias,
                         Dskip, h0, lambda B, E, D, N: (B, E, D, N))
+
+
+def scan_backward(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0=None, dh_final=None,
+                  lib=None):
+    """Gradients of the mixed scan.  Inputs as ``scan`` plus dy [B,L,D] and
+    dh_final [B,D,N] (None = 0).  Returns a dict of fp64 arrays: dx, ddt_raw
+    [B,L,D]; dBm, dCm [B,L,N]; dgate [B,L,k]; dA [E,D,N]; dbias, dDskip [E,D];
+    dh0 [B,D,N]."""
+    lib = lib or load()
+    x, dt_raw, Bm, Cm = _d(x), _d(dt_raw), _d(Bm), _d(Cm)
+    idx, gate = _i(idx), _d(gate)
+    A, dt_bias, Dskip, dy = _d(A), _d(dt_bias), _d(Dskip), _d(dy)
+    B, L, D = x.shape
+    N = Bm.shape[2]
+    E = A.shape[0]
+    k = idx.shape[2]
+    assert dy.shape == x.shape and A.shape == (E, D, N) and idx.shape == (B, L, k)
+    h0 = None if h0 is None else _d(h0)
+    dh_final = None if dh_final is None else _d(dh_final)
+    out = dict(dx=np.zeros((B, L, D)), ddt_raw=np.zeros((B, L, D)), dBm=np.zeros((B, L, N)),
+               dCm=np.zeros((B, L, N)), dgate=np.zeros((B, L, k)), dA=np.zeros((E, D, N)),
+               dbias=np.zeros((E, D)), dDskip=np.zeros((E, D)), dh0=np.zeros((B, D, N)))
+    lib.ref_scan_backward(B, L, D, N, E, k, _p(x), _p(dt_raw), _p(Bm), _p(Cm), _p(idx),
+                          _p(gate), _p(A), _p(dt_bias), _p(Dskip), _p(h0), _p(dy),
+                          _p(dh_final), *[_p(out[n]) for n in ("dx", "ddt_raw", "dBm", "dCm",
+                                                                 "dgate", "dA", "dbias",
+                                                                 "dDskip", "dh0")])
+    return out
 
 
 def mamba_scan(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, h0=None, lib=None):

@@ -44,6 +44,9 @@
  */
 #include <math.h>
 #include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -306,6 +309,150 @@ void ref_mamba_scan(int B, int L, int D, int N, const double* x,
   }
 }
 
+/* ------------------------------------------------------- mixed backward */
+/*
+ * ref_scan_backward: gradients of the mixed scan (ref_scan) for training
+ * ([SW] French summary, "Résultats Expérimentaux": the Swimba layers are
+ * trained).  Given dL/dy [B,L,D] and dL/dh_final [B,D,N] (NULL = 0), returns
+ * dL/d of every input: dx, ddt_raw [B,L,D]; dBm, dCm [B,L,N] (summed over
+ * channels); dgate [B,L,k] (summed over channels; the gates are taken as
+ * free inputs); dA [E,D,N], dbias, dDskip [E,D] (summed over batch and
+ * tokens); dh0 [B,D,N].
+ * The adjoint of the state, lam_t = dL/dh_t, obeys the reverse recurrence
+ *   lam_t = C_t dy_t + a_{t+1} lam_{t+1},   lam_{L-1} starts from dh_final,
+ * and each forward quantity receives the chain rule of its one use:
+ *   h_t = a_t h_{t-1} + Delta B_t x   ->  dx += lam Delta B, dB += lam Delta x,
+ *                                          dDelta += lam (a Abar h_{t-1} + B x),
+ *                                          dAbar += lam a Delta h_{t-1}
+ *   y_t = C_t . h_t + delta x        ->  dC += dy h_t, dx += delta dy,
+ *                                          ddelta = dy x
+ *   Delta = softplus(z), z = dt_raw + beta  ->  dz = dDelta sigmoid(z)
+ *   beta, delta, Abar = sum_j g_j (bias, Dskip, A)[e_j]  ->  per slot j:
+ *     dbias[e_j] += g_j dz, dDskip[e_j] += g_j ddelta, dA[e_j] += g_j dAbar,
+ *     dgate_j += bias[e_j] dz + Dskip[e_j] ddelta + A[e_j] . dAbar.
+ * OpenMP splits the channels d (each thread owns the parameter gradients of
+ * its channels, summed over b in order); the sums over channels are added
+ * per thread and then in thread order.
+ */
+void ref_scan_backward(int B, int L, int D, int N, int E, int k,
+                       const double* x, const double* dt_raw, const double* Bm,
+                       const double* Cm, const int32_t* idx, const double* gate,
+                       const double* A, const double* dt_bias,
+                       const double* Dskip, const double* h0, const double* dy,
+                       const double* dh_final, double* dx, double* ddt_raw,
+                       double* dBm, double* dCm, double* dgate, double* dA,
+                       double* dbias, double* dDskip, double* dh0) {
+  const int64_t BL = (int64_t)B * L;
+  const int64_t red = BL * (2 * N + k); /* per-thread sums over channels */
+#ifdef _OPENMP
+  const int nth = omp_get_max_threads();
+#else
+  const int nth = 1;
+#endif
+  double* part = (double*)calloc((size_t)nth * (size_t)red, sizeof(double));
+  for (int64_t i = 0; i < (int64_t)E * D * N; ++i) dA[i] = 0.0;
+  for (int64_t i = 0; i < (int64_t)E * D; ++i) dbias[i] = dDskip[i] = 0.0;
+#pragma omp parallel
+  {
+#ifdef _OPENMP
+    double* my = part + (size_t)omp_get_thread_num() * (size_t)red;
+#else
+    double* my = part;
+#endif
+    double* Dt = (double*)malloc(sizeof(double) * (size_t)L);
+    double* zz = (double*)malloc(sizeof(double) * (size_t)L);
+    double* Ab = (double*)malloc(sizeof(double) * (size_t)L * N);
+    double* aa = (double*)malloc(sizeof(double) * (size_t)L * N);
+    double* hh = (double*)malloc(sizeof(double) * (size_t)(L + 1) * N);
+    double* lam = (double*)malloc(sizeof(double) * (size_t)N);
+    double* dAbar = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(static)
+    for (int d = 0; d < D; ++d) {
+      for (int b = 0; b < B; ++b) {
+        /* forward, keeping every state: hh[(t+1)N + n] = h_t, hh[n] = h_{-1} */
+        for (int n = 0; n < N; ++n)
+          hh[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.0;
+        for (int t = 0; t < L; ++t) {
+          int64_t bt = (int64_t)b * L + t;
+          double beta = 0.0;
+          for (int j = 0; j < k; ++j)
+            beta += gate[bt * k + j] * dt_bias[(int64_t)idx[bt * k + j] * D + d];
+          zz[t] = dt_raw[bt * D + d] + beta;
+          Dt[t] = softplus(zz[t]);
+          for (int n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int j = 0; j < k; ++j)
+              s += gate[bt * k + j] * A[((int64_t)idx[bt * k + j] * D + d) * N + n];
+            Ab[(int64_t)t * N + n] = s;
+            aa[(int64_t)t * N + n] = exp(Dt[t] * s);
+            hh[(int64_t)(t + 1) * N + n] = aa[(int64_t)t * N + n] * hh[(int64_t)t * N + n] +
+                                           Dt[t] * Bm[bt * N + n] * x[bt * D + d];
+          }
+        }
+        /* reverse */
+        for (int n = 0; n < N; ++n)
+          lam[n] = dh_final ? dh_final[((int64_t)b * D + d) * N + n] : 0.0;
+        for (int t = L - 1; t >= 0; --t) {
+          int64_t bt = (int64_t)b * L + t;
+          double xv = x[bt * D + d], g_dy = dy[bt * D + d];
+          double delta = 0.0;
+          for (int j = 0; j < k; ++j)
+            delta += gate[bt * k + j] * Dskip[(int64_t)idx[bt * k + j] * D + d];
+          double dxv = delta * g_dy, dDt = 0.0;
+          for (int n = 0; n < N; ++n) {
+            const double ht = hh[(int64_t)(t + 1) * N + n], hp = hh[(int64_t)t * N + n];
+            const double a = aa[(int64_t)t * N + n];
+            lam[n] += Cm[bt * N + n] * g_dy;
+            my[bt * (2 * N + k) + N + n] += g_dy * ht;                  /* dC */
+            my[bt * (2 * N + k) + n] += lam[n] * Dt[t] * xv;            /* dB */
+            dxv += lam[n] * Dt[t] * Bm[bt * N + n];
+            dDt += lam[n] * (a * Ab[(int64_t)t * N + n] * hp + Bm[bt * N + n] * xv);
+            dAbar[n] = lam[n] * a * Dt[t] * hp;
+          }
+          double sig = 1.0 / (1.0 + exp(-zz[t]));
+          double dz = dDt * sig, ddelta = g_dy * xv;
+          dx[bt * D + d] = dxv;
+          ddt_raw[bt * D + d] = dz;
+          for (int j = 0; j < k; ++j) {
+            int e = idx[bt * k + j];
+            double gj = gate[bt * k + j], s = 0.0;
+            dbias[(int64_t)e * D + d] += gj * dz;
+            dDskip[(int64_t)e * D + d] += gj * ddelta;
+            for (int n = 0; n < N; ++n) {
+              dA[((int64_t)e * D + d) * N + n] += gj * dAbar[n];
+              s += A[((int64_t)e * D + d) * N + n] * dAbar[n];
+            }
+            my[bt * (2 * N + k) + 2 * N + j] +=
+                dt_bias[(int64_t)e * D + d] * dz + Dskip[(int64_t)e * D + d] * ddelta + s;
+          }
+          for (int n = 0; n < N; ++n) lam[n] *= aa[(int64_t)t * N + n];
+        }
+        for (int n = 0; n < N; ++n) dh0[((int64_t)b * D + d) * N + n] = lam[n];
+      }
+    }
+    free(Dt);
+    free(zz);
+    free(Ab);
+    free(aa);
+    free(hh);
+    free(lam);
+    free(dAbar);
+  }
+  for (int64_t i = 0; i < BL * N; ++i) dBm[i] = dCm[i] = 0.0;
+  for (int64_t i = 0; i < BL * k; ++i) dgate[i] = 0.0;
+  for (int th = 0; th < nth; ++th) {
+    const double* p = part + (size_t)th * (size_t)red;
+    for (int64_t bt = 0; bt < BL; ++bt) {
+      for (int n = 0; n < N; ++n) {
+        dBm[bt * N + n] += p[bt * (2 * N + k) + n];
+        dCm[bt * N + n] += p[bt * (2 * N + k) + N + n];
+      }
+      for (int j = 0; j < k; ++j) dgate[bt * k + j] += p[bt * (2 * N + k) + 2 * N + j];
+    }
+  }
+  free(part);
+}
+
 /* ------------------------------------------------------------ decode step */
 /*
  * ref_step: one decoding step on a persistent state ([MB] Figure 2: the
@@ -343,7 +490,6 @@ void ref_step(int B, int D, int N, int E, int k, const double* x,
 
 /* Threads the parallel loops above use (for reporting the CPU baseline). */
 #ifdef _OPENMP
-#include <omp.h>
 int ref_num_threads(void) { return omp_get_max_threads(); }
 #else
 int ref_num_threads(void) { return 1; }

@@ -15,6 +15,8 @@ and the mathematics fix:
     linearity in x; the two designs differ under time-varying routing,
     Theorem 4);
   * brute-force sorting for the router;
+  * the backward of the mixed scan against central differences of the
+    forward, and the support of its gradients for a single-token loss;
   * for the stream-mixed form (shared A, mixed B X injection and C readout):
     one slot or identical slots reduce to the plain Mamba scan, a zero-weight
     slot drops out, slots permute freely, the state superposes over slots
@@ -672,6 +674,62 @@ def pin_streams_split_composition(lib):
     y2, h2 = oracle.scan_streams(**c2, lib=lib)
     _close(np.concatenate([y1, y2], axis=1), y, 1e-13, "stream split y")
     _close(h2, hf, 1e-13, "stream split h")
+
+
+# ------------------------------------------------------------- backward
+def pin_backward_finite_differences(lib):
+    """Every gradient of the mixed scan against central differences of the
+    forward oracle, for L = sum(dy * y) + sum(dh_final * h_final): an
+    independent derivative of the pinned forward (step 1e-6 in fp64, error
+    ~1e-10 relative)."""
+    rng = np.random.default_rng(40)
+    c = _rand_case(rng, B=2, L=6, D=3, N=4, E=3, k=2)
+    dy = rng.standard_normal(c["x"].shape)
+    dhf = rng.standard_normal(c["h0"].shape)
+    g = oracle.scan_backward(**c, dy=dy, dh_final=dhf, lib=lib)
+
+    def loss(**kw):
+        a = dict(c)
+        a.update(kw)
+        y, hf = oracle.scan(**a, lib=lib)
+        return float(np.sum(y * dy) + np.sum(hf * dhf))
+
+    eps = 1e-6
+    for name, key in (("x", "dx"), ("dt_raw", "ddt_raw"), ("Bm", "dBm"), ("Cm", "dCm"),
+                      ("gate", "dgate"), ("A", "dA"), ("dt_bias", "dbias"), ("Dskip", "dDskip"),
+                      ("h0", "dh0")):
+        arr = c[name]
+        fd = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[i] += eps
+            m[i] -= eps
+            fd[i] = (loss(**{name: p}) - loss(**{name: m})) / (2 * eps)
+        _close(g[key], fd, 1e-7, "backward d%s" % name)
+
+
+def pin_backward_without_final_gradient(lib):
+    """dh_final = 0 (None) and dy = 0 except one token: the adjoint starts at
+    that token, so every gradient of later tokens is zero, dC is nonzero only
+    there, and dh0 equals the finite difference of that single output."""
+    rng = np.random.default_rng(41)
+    c = _rand_case(rng, B=1, L=8, D=2, N=3, E=3, k=2)
+    dy = np.zeros(c["x"].shape)
+    dy[0, 4] = rng.standard_normal(2)
+    g = oracle.scan_backward(**c, dy=dy, lib=lib)
+    assert np.all(g["dx"][0, 5:] == 0) and np.all(g["ddt_raw"][0, 5:] == 0)
+    assert np.all(g["dCm"][0, :4] == 0) and np.all(g["dCm"][0, 5:] == 0)
+    assert np.all(g["dBm"][0, 5:] == 0) and np.all(g["dgate"][0, 5:] == 0)
+    eps = 1e-6
+    fd = np.zeros_like(c["h0"])
+    for i in np.ndindex(c["h0"].shape):
+        p, m = c["h0"].copy(), c["h0"].copy()
+        p[i] += eps
+        m[i] -= eps
+        yp, _ = oracle.scan(**dict(c, h0=p), lib=lib)
+        ym, _ = oracle.scan(**dict(c, h0=m), lib=lib)
+        fd[i] = np.sum((yp - ym) * dy) / (2 * eps)
+    _close(g["dh0"], fd, 1e-7, "dh0 single token")
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -68,6 +68,19 @@ MUTATIONS = [
     ("streams_h0_ignored",
      "h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.0;\n      for (int t = 0; t < L; ++t) {\n        int64_t bt = (int64_t)b * L + t;\n        const double* g",
      "h[n] = 0.0;\n      for (int t = 0; t < L; ++t) {\n        int64_t bt = (int64_t)b * L + t;\n        const double* g"),
+    ("bwd_no_decay_of_adjoint", "          for (int n = 0; n < N; ++n) lam[n] *= aa[(int64_t)t * N + n];\n",
+     ""),
+    ("bwd_sigmoid_sign", "double sig = 1.0 / (1.0 + exp(-zz[t]));", "double sig = 1.0 / (1.0 + exp(zz[t]));"),
+    ("bwd_dC_previous_state", "+= g_dy * ht;", "+= g_dy * hp;"),
+    ("bwd_dB_no_delta", "+= lam[n] * Dt[t] * xv;", "+= lam[n] * xv;"),
+    ("bwd_dgate_no_A_term", "Dskip[(int64_t)e * D + d] * ddelta + s;", "Dskip[(int64_t)e * D + d] * ddelta;"),
+    ("bwd_dA_ungated", "dA[((int64_t)e * D + d) * N + n] += gj * dAbar[n];",
+     "dA[((int64_t)e * D + d) * N + n] += dAbar[n];"),
+    ("bwd_dx_no_D_term", "double dxv = delta * g_dy, dDt = 0.0;", "double dxv = 0.0, dDt = 0.0;"),
+    ("bwd_dDelta_no_injection", "(a * Ab[(int64_t)t * N + n] * hp + Bm[bt * N + n] * xv)",
+     "(a * Ab[(int64_t)t * N + n] * hp)"),
+    ("bwd_adjoint_from_next_C", "lam[n] += Cm[bt * N + n] * g_dy;",
+     "lam[n] += Cm[(t + 1 < L ? bt + 1 : bt) * N + n] * g_dy;"),
 ]
 
 
