@@ -172,6 +172,46 @@ int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
                          hipStream_t stream);
 
 typedef struct {
+  swimba_scan_args fwd;         /* the forward call's arguments; its y, h_final,
+                                   chunk and phase_events are not used            */
+  const void* dy;               /* [B, L, D]  dL/dy, dtype dy_dtype               */
+  swimba_dtype dy_dtype;
+  const float* dh_final;        /* [B, D, N]  dL/dh_final, or NULL for zero        */
+  float* dx;                    /* [B, L, D]  out                                  */
+  float* ddt_raw;               /* [B, L, D]  out                                  */
+  float* dBm;                   /* [B, L, N]  out, summed over channels            */
+  float* dCm;                   /* [B, L, N]  out, summed over channels            */
+  float* dgate;                 /* [B, L, k]  out, summed over channels            */
+  float* dA;                    /* [E, D, N]  out, summed over batch and tokens    */
+  float* ddt_bias;              /* [E, D]     out                                  */
+  float* dDskip;                /* [E, D]     out                                  */
+  float* dh0;                   /* [B, D, N]  out, or NULL                         */
+} swimba_scan_grad_args;
+
+/*
+ * swimba_scan_backward -- gradients of swimba_scan for training ([SW] French
+ * summary "Résultats Expérimentaux": the Swimba layers are trained; [MB]
+ * "Mamba": the selective recurrence).  With lam_t = dL/dh_t obeying
+ * lam_t = C_t dy_t + a_{t+1} lam_{t+1} (lam_{L-1} from dh_final), returns
+ * dL/d of x, dt_raw, B_t, C_t, the gates (as free inputs: the router's own
+ * backward is not part of this call), A, dt_bias, Dskip and h0, all fp32.
+ * The forward is recomputed inside from the same arguments (same chunking
+ * as swimba_scan).  dA, ddt_bias and dDskip take their per-workgroup
+ * partials in a fixed order, but the partials themselves are LDS sums whose
+ * order varies, so those three may differ between runs in the last bits.
+ *   ws, ws_bytes: device workspace of at least
+ *   swimba_scan_backward_workspace_size(g) bytes, 256-byte aligned.  It
+ *   holds every state h_t (64 bytes per token and channel) besides the
+ *   chunk records.
+ * Constraints: those of swimba_scan (E <= 16) with a_form DIAGONAL (SCALAR
+ * returns SWIMBA_EUNSUPPORTED).  B == 0 or L == 0 writes zero parameter
+ * gradients and dh0 = dh_final (or zeros).
+ */
+size_t swimba_scan_backward_workspace_size(const swimba_scan_grad_args* g);
+int swimba_scan_backward(const swimba_scan_grad_args* g, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+typedef struct {
   int B, D, N, E, k;
   swimba_dtype in_dtype, y_dtype;
   const void* x;                /* [B, D]                                        */

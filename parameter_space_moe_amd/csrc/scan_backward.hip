@@ -1,0 +1,102 @@
+// Backward pass of the mixed scan: the passes that do not depend on the
+// dtypes (reverse carry, reductions), the argument plan and the dispatch.
+// Kernels of the dtype-dependent passes: scan_backward.hpp.
+#include "scan_backward.hpp"
+
+namespace swimba {
+namespace bwd {
+
+// ---------------------------------------------------------------- pass 3
+// Incoming adjoint of every chunk, backward over chunks; one thread per
+// (b, n, d).
+__global__ __launch_bounds__(256) void bwd_reverse_carry_kernel(int B, int C, int D,
+                                                                const float* __restrict__ P,
+                                                                float* __restrict__ K,
+                                                                const float* __restrict__ dhf,
+                                                                float* __restrict__ dh0) {
+  const size_t total = (size_t)B * kN * D;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int d = (int)(i % D);
+  const int n = (int)((i / D) % kN);
+  const int b = (int)(i / ((size_t)D * kN));
+  const size_t stride = (size_t)kN * D;
+  const size_t base = (size_t)b * C * stride + (size_t)n * D + d;
+  float kap = dhf != nullptr ? dhf[((size_t)b * D + d) * kN + n] : 0.f;
+  for (int c = C - 1; c >= 0; --c) {
+    const float seed = K[base + (size_t)c * stride];
+    const float pc = P[base + (size_t)c * stride];
+    K[base + (size_t)c * stride] = kap;
+    kap = fmaf(pc, kap, seed);
+  }
+  if (dh0 != nullptr) dh0[((size_t)b * D + d) * kN + n] = kap;
+}
+
+int reverse_carry(const BwdParams& p, hipStream_t st) {
+  const size_t total = (size_t)p.B * kN * p.D;
+  hipLaunchKernelGGL(bwd_reverse_carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, st, p.B, p.nchunks, p.D, p.P, p.adj, p.dhf, p.dh0);
+  return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
+}
+
+// ---------------------------------------------------------------- pass 5
+// dB, dC and dgate: the per-tile channel sums added over tiles.
+__global__ __launch_bounds__(256) void bwd_reduce_tiles_kernel(const float* __restrict__ red,
+                                                               int ntiles, size_t tokens, int k,
+                                                               float* __restrict__ dB,
+                                                               float* __restrict__ dC,
+                                                               float* __restrict__ dgate) {
+  const int kr = kRed + k;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= tokens * kr) return;
+  float s = 0.f;
+  for (int t = 0; t < ntiles; ++t) s += red[(size_t)t * tokens * kr + i];
+  const size_t bt = i / kr;
+  const int c = (int)(i % kr);
+  if (c < kN)
+    dB[bt * kN + c] = s;
+  else if (c < kRed)
+    dC[bt * kN + c - kN] = s;
+  else
+    dgate[bt * k + c - kRed] = s;
+}
+
+// dA, dbias and dDskip: the per-workgroup partials added in order.
+__global__ __launch_bounds__(256) void bwd_reduce_params_kernel(const float* __restrict__ pA,
+                                                                const float* __restrict__ pBD,
+                                                                int slots, int E, int D,
+                                                                float* __restrict__ dA,
+                                                                float* __restrict__ dbias,
+                                                                float* __restrict__ dDsk) {
+  const size_t na = (size_t)E * D * kN, nb = (size_t)E * D;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < na) {
+    float s = 0.f;
+    for (int w = 0; w < slots; ++w) s += pA[(size_t)w * na + i];
+    dA[i] = s;
+  } else if (i < na + 2 * nb) {
+    const size_t j = i - na;                  // [which][e][d]
+    const int which = (int)(j / nb);
+    const size_t ed = j % nb;
+    const int e = (int)(ed / D), dd = (int)(ed % D);
+    float s = 0.f;
+    for (int w = 0; w < slots; ++w) s += pBD[(((size_t)w * E + e) * 2 + which) * D + dd];
+    (which == 0 ? dbias : dDsk)[ed] = s;
+  }
+}
+
+int reduce_outputs(const BwdParams& p, float* dB, float* dC, float* dgate, float* dA,
+                   float* dbias, float* dDsk, hipStream_t st) {
+  const size_t tokens = (size_t)p.B * p.L;
+  const size_t n1 = tokens * (kRed + p.k);
+  hipLaunchKernelGGL(bwd_reduce_tiles_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0,
+                     st, p.red, p.ntiles, tokens, p.k, dB, dC, dgate);
+  if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
+  const size_t n2 = (size_t)p.E * p.D * (kN + 2);
+  hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0,
+                     st, p.pA, p.pBD, p.B * p.ncg, p.E, p.D, dA, dbias, dDsk);
+  return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
+}
+
+}  // namespace bwd
+}  // namespace swimba

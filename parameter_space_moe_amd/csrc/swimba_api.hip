@@ -38,12 +38,12 @@ int validate_scan(const swimba_scan_args* a, int separate) {
   return SWIMBA_OK;
 }
 
-// Pointers the launch will dereference.
-int validate_scan_pointers(const swimba_scan_args* a) {
+// Pointers the launch will dereference (the backward reads no y).
+int validate_scan_pointers(const swimba_scan_args* a, bool need_y = true) {
   if (a->A == nullptr || a->dt_bias == nullptr || a->Dskip == nullptr) return SWIMBA_EINVAL;
   if (a->B > 0 && a->L > 0) {
     if (a->x == nullptr || a->dt_raw == nullptr || a->Bm == nullptr || a->Cm == nullptr ||
-        a->idx == nullptr || a->gate == nullptr || a->y == nullptr)
+        a->idx == nullptr || a->gate == nullptr || (need_y && a->y == nullptr))
       return SWIMBA_EINVAL;
     // B_t and C_t rows are staged as 16-byte vectors
     if ((reinterpret_cast<uintptr_t>(a->Bm) & 15) || (reinterpret_cast<uintptr_t>(a->Cm) & 15))
@@ -145,6 +145,55 @@ int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p) {
   return SWIMBA_OK;
 }
 
+int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p) {
+  if (g == nullptr) return SWIMBA_EINVAL;
+  const swimba_scan_args* a = &g->fwd;
+  ScanPlan sp;
+  int rc = plan_scan(a, 0, &sp);
+  if (rc != SWIMBA_OK) return rc;
+  if (!dtype_ok(g->dy_dtype)) return SWIMBA_EINVAL;
+  if (a->a_form != SWIMBA_A_DIAGONAL) return SWIMBA_EUNSUPPORTED;
+  *p = BwdPlan();
+  p->waves = backward_lds_bytes(a->E, a->k, 8) <= 160 * 1024 ? 8 : 4;
+  if (backward_lds_bytes(a->E, a->k, p->waves) > 160 * 1024) return SWIMBA_EUNSUPPORTED;
+  p->ntiles = sp.ntiles;
+  if (a->B == 0 || a->L == 0) return SWIMBA_OK;
+  // Own chunking (the forward is recomputed here): about two waves per SIMD
+  // over all chunks, a whole number of workgroups per (sequence, tile), and
+  // chunks of at least 64 tokens; a caller's chunk size is kept.
+  if (a->chunk > 0) {
+    p->chunk = sp.chunk;
+  } else {
+    const long long cus = device_cus();
+    const long long base = (long long)a->B * sp.ntiles;
+    long long want = (8 * cus + base - 1) / base;
+    want = (want + p->waves - 1) / p->waves * p->waves;
+    const long long maxc = (a->L + 63) / 64;
+    if (want > maxc) want = maxc;
+    if (want < 1) want = 1;
+    p->chunk = (int)((a->L + want - 1) / want);
+  }
+  p->nchunks = (int)(((long long)a->L + p->chunk - 1) / p->chunk);
+  p->ncg = (p->nchunks + p->waves - 1) / p->waves;
+  const size_t B = (size_t)a->B, L = (size_t)a->L, D = (size_t)a->D, E = (size_t)a->E;
+  const size_t arr = B * p->nchunks * SWIMBA_STATE_N * D * sizeof(float);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  p->off_P = take(arr);
+  p->off_H = take(arr);
+  p->off_adj = take(arr);
+  p->off_hs = take(B * L * D * SWIMBA_STATE_N * sizeof(float));
+  p->off_red = take((size_t)p->ntiles * B * L * (2 * SWIMBA_STATE_N + a->k) * sizeof(float));
+  p->off_pA = take(B * p->ncg * E * D * SWIMBA_STATE_N * sizeof(float));
+  p->off_pBD = take(B * p->ncg * E * 2 * D * sizeof(float));
+  p->bytes = o;
+  return SWIMBA_OK;
+}
+
 int plan_streams(const swimba_stream_args* a, ScanPlan* p) {
   if (a == nullptr) return SWIMBA_EINVAL;
   if (a->B < 0 || a->L < 0 || a->D < 1 || a->N < 1 || a->k < 1 || a->chunk < 0)
@@ -236,6 +285,47 @@ int run_streams(const swimba_stream_args* a, void* ws, size_t ws_bytes, hipStrea
   return launch_streams_ff(a, p, ws, s);
 }
 
+int run_backward(const swimba_scan_grad_args* g, void* ws, size_t ws_bytes, hipStream_t s) {
+  BwdPlan p;
+  int rc = plan_backward(g, &p);
+  if (rc != SWIMBA_OK) return rc;
+  const swimba_scan_args* a = &g->fwd;
+  if (a->A == nullptr || a->dt_bias == nullptr || a->Dskip == nullptr || g->dA == nullptr ||
+      g->ddt_bias == nullptr || g->dDskip == nullptr)
+    return SWIMBA_EINVAL;
+  const bool work = a->B > 0 && a->L > 0;
+  if (work) {
+    rc = validate_scan_pointers(a, false);
+    if (rc != SWIMBA_OK) return rc;
+    if (g->dy == nullptr || g->dx == nullptr || g->ddt_raw == nullptr || g->dBm == nullptr ||
+        g->dCm == nullptr || g->dgate == nullptr)
+      return SWIMBA_EINVAL;
+    if (ws == nullptr || ws_bytes < p.bytes || (reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+      return SWIMBA_EWORKSPACE;
+  }
+  if (!work) {
+    // no tokens: the parameter gradients are zero and dh0 = dh_final
+    const size_t na = (size_t)a->E * a->D * SWIMBA_STATE_N, nb = (size_t)a->E * a->D;
+    hipLaunchKernelGGL(fill_initial_state, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, s,
+                       nullptr, g->dA, na);
+    hipLaunchKernelGGL(fill_initial_state, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
+                       nullptr, g->ddt_bias, nb);
+    hipLaunchKernelGGL(fill_initial_state, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
+                       nullptr, g->dDskip, nb);
+    if (g->dh0 != nullptr && a->B > 0) {
+      const size_t nh = (size_t)a->B * a->D * SWIMBA_STATE_N;
+      hipLaunchKernelGGL(fill_initial_state, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0,
+                         s, g->dh_final, g->dh0, nh);
+    }
+    return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
+  }
+  const bool in_bf = a->in_dtype == SWIMBA_BF16, dy_bf = g->dy_dtype == SWIMBA_BF16;
+  if (in_bf && dy_bf) return launch_backward_bb(g, p, ws, s);
+  if (in_bf) return launch_backward_bf(g, p, ws, s);
+  if (dy_bf) return launch_backward_fb(g, p, ws, s);
+  return launch_backward_ff(g, p, ws, s);
+}
+
 }  // namespace
 }  // namespace swimba
 
@@ -274,6 +364,17 @@ int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_
 int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
   return run_scan(a, ws, ws_bytes, stream, 1);
+}
+
+size_t swimba_scan_backward_workspace_size(const swimba_scan_grad_args* g) {
+  BwdPlan p;
+  if (plan_backward(g, &p) != SWIMBA_OK) return 0;
+  return p.bytes;
+}
+
+int swimba_scan_backward(const swimba_scan_grad_args* g, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  return run_backward(g, ws, ws_bytes, stream);
 }
 
 size_t swimba_scan_streams_workspace_size(const swimba_stream_args* a) {

@@ -21,8 +21,23 @@ struct ScanPlan {
   size_t off_P = 0, off_H = 0, off_flags = 0, bytes = 0;  // workspace layout
 };
 
+// Plan of a backward call: the forward's chunking plus the workspace of the
+// backward passes (all offsets 256-byte aligned).
+struct BwdPlan {
+  int ntiles = 0, chunk = 0, nchunks = 0, ncg = 0, waves = 4;
+  size_t off_P = 0, off_H = 0, off_adj = 0, off_hs = 0, off_red = 0, off_pA = 0, off_pBD = 0;
+  size_t bytes = 0;
+};
+
 // Fills `p` for these arguments; returns a status.  Pure host arithmetic.
 int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p);
+int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p);
+// LDS of the backward's gradient pass: expert table, per-expert gradient
+// accumulators and one staging ring per wave.
+inline size_t backward_lds_bytes(int E, int k, int waves) {
+  return (size_t)E * (4 * 64 * 16 + 64 * 8) * 2 +
+         (size_t)waves * ((size_t)2 * 8 * 32 * 4 + (size_t)2 * 2 * 8 * k * 4);
+}
 int plan_streams(const swimba_stream_args* a, ScanPlan* p);
 
 // Kernel launchers (validated arguments only).
@@ -31,6 +46,11 @@ int launch_route(const void* x, swimba_dtype xd, const float* Wr, int64_t T, int
 int launch_scan(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_scan_separate(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_step(const swimba_step_args* a, hipStream_t s);
+// Backward of the mixed scan, one launcher per (input, dL/dy) dtype pair.
+int launch_backward_ff(const swimba_scan_grad_args* g, const BwdPlan& p, void* ws, hipStream_t s);
+int launch_backward_fb(const swimba_scan_grad_args* g, const BwdPlan& p, void* ws, hipStream_t s);
+int launch_backward_bf(const swimba_scan_grad_args* g, const BwdPlan& p, void* ws, hipStream_t s);
+int launch_backward_bb(const swimba_scan_grad_args* g, const BwdPlan& p, void* ws, hipStream_t s);
 // Stream-mixed scan, one launcher per (input, output) dtype pair.
 int launch_streams_ff(const swimba_stream_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_streams_fb(const swimba_stream_args* a, const ScanPlan& p, void* ws, hipStream_t s);

@@ -42,6 +42,12 @@ class StepArgs(ctypes.Structure):
                 ("a_form", _ci)]
 
 
+class GradArgs(ctypes.Structure):
+    _fields_ = [("fwd", ScanArgs), ("dy", _vp), ("dy_dtype", _ci), ("dh_final", _vp),
+                ("dx", _vp), ("ddt_raw", _vp), ("dBm", _vp), ("dCm", _vp), ("dgate", _vp),
+                ("dA", _vp), ("ddt_bias", _vp), ("dDskip", _vp), ("dh0", _vp)]
+
+
 class StreamArgs(ctypes.Structure):
     _fields_ = [("B", _ci), ("L", _ci), ("D", _ci), ("N", _ci), ("k", _ci),
                 ("in_dtype", _ci), ("y_dtype", _ci),
@@ -86,6 +92,10 @@ def load(path: str | None = None):
     lib.swimba_scan_streams_plan.restype = _ci
     lib.swimba_scan_streams.argtypes = [ctypes.POINTER(StreamArgs), _vp, ctypes.c_size_t, _vp]
     lib.swimba_scan_streams.restype = _ci
+    lib.swimba_scan_backward_workspace_size.argtypes = [ctypes.POINTER(GradArgs)]
+    lib.swimba_scan_backward_workspace_size.restype = ctypes.c_size_t
+    lib.swimba_scan_backward.argtypes = [ctypes.POINTER(GradArgs), _vp, ctypes.c_size_t, _vp]
+    lib.swimba_scan_backward.restype = _ci
     lib.swimba_step.argtypes = [ctypes.POINTER(StepArgs), _vp]
     lib.swimba_step.restype = _ci
     lib.swimba_status_string.argtypes = [_ci]
@@ -158,7 +168,7 @@ def route(x: torch.Tensor, Wr: torch.Tensor, k: int, idx=None, gate=None, stream
 
 
 def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, chunk, carry,
-               separate, phase_events):
+               separate, phase_events, need_y=True):
     _need(x, "x")
     if x.dim() != 3:
         raise ValueError("x must be [B, L, D]")
@@ -179,12 +189,13 @@ def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, 
     sshape = (B, E, D, N) if separate else (B, D, N)
     if h0 is not None:
         _need(h0, "h0", sshape, torch.float32, dev)
-    _need(y, "y", (B, L, D), None, dev)
+    if need_y:
+        _need(y, "y", (B, L, D), None, dev)
     if h_final is not None:
         _need(h_final, "h_final", sshape, torch.float32, dev)
     a = ScanArgs()
     a.B, a.L, a.D, a.N, a.E, a.k = B, L, D, N, E, k
-    a.in_dtype, a.y_dtype = _dt(x), _dt(y)
+    a.in_dtype, a.y_dtype = _dt(x), (_dt(y) if y is not None else _dt(x))
     a.x, a.dt_raw, a.Bm, a.Cm = _ptr(x), _ptr(dt_raw), _ptr(Bm), _ptr(Cm)
     a.idx, a.gate, a.A, a.dt_bias, a.Dskip = _ptr(idx), _ptr(gate), _ptr(A), _ptr(dt_bias), \
         _ptr(Dskip)
@@ -233,6 +244,83 @@ def scan_separate(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw
     """Separate design (include/swimba.h: swimba_scan_separate).  Returns
     (y [B,L,D], h_final [B,E,D,16] or None)."""
     return _scan(True, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
+
+
+def _grad_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0, dh_final, chunk,
+               out):
+    a = _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, None, None, chunk,
+                   "auto", False, None, need_y=False)
+    B, L, D = x.shape
+    E, k = A.shape[0], idx.shape[2]
+    N = Bm.shape[2]
+    dev = x.device
+    _need(dy, "dy", (B, L, D), None, dev)
+    if dh_final is not None:
+        _need(dh_final, "dh_final", (B, D, N), torch.float32, dev)
+    shapes = {"dx": (B, L, D), "ddt_raw": (B, L, D), "dBm": (B, L, N), "dCm": (B, L, N),
+              "dgate": (B, L, k), "dA": tuple(A.shape), "ddt_bias": (E, D), "dDskip": (E, D),
+              "dh0": (B, D, N)}
+    for name, shape in shapes.items():
+        if out.get(name) is not None:
+            _need(out[name], name, shape, torch.float32, dev)
+    g = GradArgs()
+    g.fwd = a
+    g.dy, g.dy_dtype, g.dh_final = _ptr(dy), _dt(dy), _ptr(dh_final)
+    for name in shapes:
+        setattr(g, name, _ptr(out.get(name)))
+    return g
+
+
+def scan_backward(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0=None, dh_final=None,
+                  chunk=0, want_dh0=True, out=None, workspace=None, stream=None):
+    """Gradients of the mixed scan (include/swimba.h: swimba_scan_backward) for
+    dL/dy = dy (and dL/dh_final).  Returns a dict of fp32 tensors: dx,
+    ddt_raw [B,L,D]; dBm, dCm [B,L,16]; dgate [B,L,k]; dA [E,D,16]; ddt_bias,
+    dDskip [E,D]; dh0 [B,D,16] (when want_dh0)."""
+    B, L, D = x.shape
+    E, k, N = A.shape[0], idx.shape[2], N_STATE
+    dev = x.device
+    out = dict(out or {})
+    shapes = {"dx": (B, L, D), "ddt_raw": (B, L, D), "dBm": (B, L, N), "dCm": (B, L, N),
+              "dgate": (B, L, k), "dA": tuple(A.shape), "ddt_bias": (E, D), "dDskip": (E, D)}
+    if want_dh0:
+        shapes["dh0"] = (B, D, N)
+    for name, shape in shapes.items():
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=torch.float32, device=dev)
+    g = _grad_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0, dh_final, chunk, out)
+    lib = load()
+    need = int(lib.swimba_scan_backward_workspace_size(ctypes.byref(g)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib.swimba_scan_backward(ctypes.byref(g), _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    _check("swimba_scan_backward", rc)
+    return out
+
+
+class PreparedBackward:
+    """swimba_scan_backward marshalled once (see PreparedScan)."""
+
+    def __init__(self, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, out, h0=None,
+                 dh_final=None, chunk=0, workspace=None, stream=None):
+        self.args = _grad_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0, dh_final,
+                               chunk, out)
+        lib = load()
+        need = int(lib.swimba_scan_backward_workspace_size(ctypes.byref(self.args)))
+        self.workspace = workspace if workspace is not None else torch.empty(
+            max(need, 1), dtype=torch.uint8, device=x.device)
+        self._keep = (x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0, dh_final, out)
+        self._fn = lib.swimba_scan_backward
+        self._ref = ctypes.byref(self.args)
+        self._ws = self.workspace.data_ptr()
+        self._wsn = self.workspace.numel()
+        self.stream = _stream(stream)
+
+    def __call__(self):
+        rc = self._fn(self._ref, self._ws, self._wsn, self.stream)
+        if rc != OK:
+            raise SwimbaError("swimba_scan_backward", rc)
 
 
 def _shape_args(x, A, idx, chunk, y_dtype):

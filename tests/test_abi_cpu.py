@@ -42,7 +42,7 @@ def test_exports_nothing_but_the_abi():
 
 
 STRUCTS = (("swimba_scan_args", sw.ScanArgs), ("swimba_step_args", sw.StepArgs),
-           ("swimba_stream_args", sw.StreamArgs))
+           ("swimba_stream_args", sw.StreamArgs), ("swimba_scan_grad_args", sw.GradArgs))
 
 LAYOUT_SRC = r"""
 #include <cstddef>
@@ -53,6 +53,7 @@ int main() {
   std::printf("swimba_scan_args sizeof %zu\n", sizeof(swimba_scan_args));
   std::printf("swimba_step_args sizeof %zu\n", sizeof(swimba_step_args));
   std::printf("swimba_stream_args sizeof %zu\n", sizeof(swimba_stream_args));
+  std::printf("swimba_scan_grad_args sizeof %zu\n", sizeof(swimba_scan_grad_args));
   %FIELDS%
   return 0;
 }
@@ -200,3 +201,33 @@ def test_streams_workspace_and_plan(lib):
     assert lib.swimba_scan_streams_workspace_size(ctypes.byref(a)) == 0
     a = stream_args(k=9)
     assert lib.swimba_scan_streams_workspace_size(ctypes.byref(a)) == 0
+
+
+def grad_args(**kw):
+    g = sw.GradArgs()
+    g.fwd = scan_args(B=2, L=1000, D=256, E=8, k=2)
+    fake = 0x100000
+    for f in ("dy", "dx", "ddt_raw", "dBm", "dCm", "dgate", "dA", "ddt_bias", "dDskip"):
+        setattr(g, f, fake)
+    g.dy_dtype = sw.BF16
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g
+
+
+def test_backward_rejects_and_workspace(lib):
+    g = grad_args()
+    need = lib.swimba_scan_backward_workspace_size(ctypes.byref(g))
+    # the states of every token and channel dominate: 64 B per token-channel
+    assert need >= 2 * 1000 * 256 * 16 * 4
+    assert lib.swimba_scan_backward(ctypes.byref(g), None, 0, None) == sw.EWORKSPACE
+    for field, value, status in (("dy", None, sw.EINVAL), ("dA", None, sw.EINVAL),
+                                 ("dy_dtype", 7, sw.EINVAL)):
+        assert lib.swimba_scan_backward(ctypes.byref(grad_args(**{field: value})), None, 0,
+                                        None) == status
+    g = grad_args()
+    g.fwd.a_form = 1
+    assert lib.swimba_scan_backward(ctypes.byref(g), None, 0, None) == sw.EUNSUPPORTED
+    g = grad_args()
+    g.fwd.E = 17
+    assert lib.swimba_scan_backward(ctypes.byref(g), None, 0, None) == sw.EUNSUPPORTED
