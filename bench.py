@@ -9,8 +9,9 @@ inputs resident in HBM.  Printed as one JSON line (rank 0):
   modes    = the separate design, the dense single-expert scan (E = 1), the
              scan alone, and the decode step, for the "mixed vs separate" and
              "mixed vs dense" ratios; the stream-mixed form (shared A, mixed
-             B X injection and C readout) and the scalar-transition (Mamba-2)
-             form of the mixed scan at the same shape
+             B X injection and C readout), the scalar-transition (Mamba-2)
+             form of the mixed scan and the mixed scan's backward at the same
+             shape
   cpu_baseline = the fp64 oracle timed on this host on the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -329,6 +330,33 @@ def expert_sweep(swimba, dev, reps):
     return out
 
 
+def backward_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, reps, ms_mixed):
+    """Gradients of the mixed scan for a seeded dL/dy at the same shape (the
+    whole backward call: forward recompute with the chunk records, the two
+    carries, the gradient pass and the reductions), against the forward scan."""
+    import torch
+    dev = x.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    dy = torch.randn(x.shape, generator=g, device=dev).to(x.dtype)
+    B, L, D, E, k = w.B, w.L, w.D, w.E, w.k
+    f32 = torch.float32
+    out = {"dx": torch.empty((B, L, D), dtype=f32, device=dev),
+           "ddt_raw": torch.empty((B, L, D), dtype=f32, device=dev),
+           "dBm": torch.empty((B, L, N_STATE), dtype=f32, device=dev),
+           "dCm": torch.empty((B, L, N_STATE), dtype=f32, device=dev),
+           "dgate": torch.empty((B, L, k), dtype=f32, device=dev),
+           "dA": torch.empty_like(A), "ddt_bias": torch.empty_like(bias),
+           "dDskip": torch.empty_like(Dsk),
+           "dh0": torch.empty((B, D, N_STATE), dtype=f32, device=dev)}
+    call = swimba.PreparedBackward(x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, dy, out)
+    ms = _time(call, reps)
+    return {"ms": round(ms, 4), "G_tc_per_s": round(w.tc / ms / 1e6, 3),
+            "over_forward_scan": round(ms / ms_mixed, 3),
+            "workspace_MB": round(call.workspace.numel() / 1e6, 1),
+            "note": "fp32 gradients of x, dt_raw, B, C, gates, A, dt_bias, Dskip, h0"}
+
+
 def scalar_a_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y, hf, reps, ms_mixed):
     """The mixed scan with one transition per (expert, channel), the Mamba-2
     form A_t = a_t I, on the same inputs (A[e, d] = the n = 0 entry of the
@@ -470,6 +498,8 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
     del flush
     res["expert_sweep"] = expert_sweep(swimba, dev, reps)
     res["stream_mixed"] = stream_mode(swimba, workloads, w, x, Wr, idx, gate, reps)
+    res["backward"] = backward_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, reps,
+                                    ms_mixed)
     res["scalar_a"] = scalar_a_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y, hf,
                                     reps, ms_mixed)
     # decode workload: 128 routed steps on a persistent fp32 state

@@ -196,16 +196,14 @@ typedef struct {
  * dL/d of x, dt_raw, B_t, C_t, the gates (as free inputs: the router's own
  * backward is not part of this call), A, dt_bias, Dskip and h0, all fp32.
  * The forward is recomputed inside from the same arguments (same chunking
- * as swimba_scan).  dA, ddt_bias and dDskip take their per-workgroup
- * partials in a fixed order, but the partials themselves are LDS sums whose
- * order varies, so those three may differ between runs in the last bits.
+ * as swimba_scan).
  *   ws, ws_bytes: device workspace of at least
  *   swimba_scan_backward_workspace_size(g) bytes, 256-byte aligned.  It
  *   holds every state h_t (64 bytes per token and channel) besides the
  *   chunk records.
  * Constraints: those of swimba_scan (E <= 16) with a_form DIAGONAL (SCALAR
- * returns SWIMBA_EUNSUPPORTED).  B == 0 or L == 0 writes zero parameter
- * gradients and dh0 = dh_final (or zeros).
+ * returns SWIMBA_EUNSUPPORTED).  B == 0 or L == 0 writes zero parameter gradients
+ * and dh0 = dh_final (or zeros).  Every output is deterministic.
  */
 size_t swimba_scan_backward_workspace_size(const swimba_scan_grad_args* g);
 int swimba_scan_backward(const swimba_scan_grad_args* g, void* ws, size_t ws_bytes,

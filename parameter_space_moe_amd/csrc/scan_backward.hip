@@ -39,29 +39,35 @@ int reverse_carry(const BwdParams& p, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
 }
 
-// ---------------------------------------------------------------- pass 5
-// dB, dC and dgate: the per-tile channel sums added over tiles.
-__global__ __launch_bounds__(256) void bwd_reduce_tiles_kernel(const float* __restrict__ red,
-                                                               int ntiles, size_t tokens, int k,
-                                                               float* __restrict__ dB,
-                                                               float* __restrict__ dC,
-                                                               float* __restrict__ dgate) {
-  const int kr = kRed + k;
+// ---------------------------------------------------------------- pass 6
+// dB, dC and dgate: the per-tile (dC) and per-wave (dB, dgate) channel sums
+// added in order.
+__global__ __launch_bounds__(256) void bwd_reduce_tokens_kernel(const float* __restrict__ redC,
+                                                                const float* __restrict__ redB,
+                                                                int ntiles, size_t tokens, int k,
+                                                                float* __restrict__ dB,
+                                                                float* __restrict__ dC,
+                                                                float* __restrict__ dgate) {
+  const int kr = kN + k;
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= tokens * kr) return;
-  float s = 0.f;
-  for (int t = 0; t < ntiles; ++t) s += red[(size_t)t * tokens * kr + i];
-  const size_t bt = i / kr;
-  const int c = (int)(i % kr);
-  if (c < kN)
-    dB[bt * kN + c] = s;
-  else if (c < kRed)
-    dC[bt * kN + c - kN] = s;
-  else
-    dgate[bt * k + c - kRed] = s;
+  if (i < tokens * kN) {
+    float s = 0.f;
+    for (int t = 0; t < ntiles; ++t) s += redC[(size_t)t * tokens * kN + i];
+    dC[i] = s;
+  }
+  if (i < tokens * kr) {
+    float s = 0.f;
+    for (int w = 0; w < ntiles * 4; ++w) s += redB[(size_t)w * tokens * kr + i];
+    const size_t bt = i / kr;
+    const int c = (int)(i % kr);
+    if (c < kN)
+      dB[bt * kN + c] = s;
+    else
+      dgate[bt * k + c - kN] = s;
+  }
 }
 
-// dA, dbias and dDskip: the per-workgroup partials added in order.
+// dA, dbias and dDskip: the per-(sequence, chunk) partials added in order.
 __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(const float* __restrict__ pA,
                                                                 const float* __restrict__ pBD,
                                                                 int slots, int E, int D,
@@ -88,13 +94,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(const float* __r
 int reduce_outputs(const BwdParams& p, float* dB, float* dC, float* dgate, float* dA,
                    float* dbias, float* dDsk, hipStream_t st) {
   const size_t tokens = (size_t)p.B * p.L;
-  const size_t n1 = tokens * (kRed + p.k);
-  hipLaunchKernelGGL(bwd_reduce_tiles_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0,
-                     st, p.red, p.ntiles, tokens, p.k, dB, dC, dgate);
+  const size_t n1 = tokens * (kN + p.k);
+  hipLaunchKernelGGL(bwd_reduce_tokens_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0,
+                     st, p.redC, p.redB, p.ntiles, tokens, p.k, dB, dC, dgate);
   if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
   const size_t n2 = (size_t)p.E * p.D * (kN + 2);
   hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0,
-                     st, p.pA, p.pBD, p.B * p.ncg, p.E, p.D, dA, dbias, dDsk);
+                     st, p.pA, p.pBD, p.B * p.nchunks, p.E, p.D, dA, dbias, dDsk);
   return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
 }
 

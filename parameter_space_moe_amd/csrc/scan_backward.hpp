@@ -18,18 +18,19 @@
 //  2. forward carry (shared kernel): carried-in state of every chunk;
 //  3. reverse carry: incoming adjoint of every chunk, kappa_{c-1} =
 //     P(c) kappa_c + S_c from kappa_last = dL/dh_final; dh0 = kappa_{-1};
-//  4. gradient pass, one wave per chunk: walk the chunk forward from its
-//     carried-in state writing every state h_t to the workspace, then walk it
-//     backward from its incoming adjoint, reading h_{t-1}, and form the
-//     gradients.  Per-channel gradients (dx, ddt_raw) are stored directly;
-//     sums over channels (dB, dC, dgate) are reduced across the wave with a
-//     lane butterfly and stored per 64-channel tile; per-expert parameter
-//     gradients (dA, dbias, dDskip) are added into the workgroup's LDS
-//     accumulators and stored per workgroup;
-//  5. reductions over tiles and over workgroups, in a fixed order.
-// The LDS accumulators take adds from the four waves of a workgroup in no
-// fixed order, so dA, dbias and dDskip may differ between runs in the last
-// bits; every other output is deterministic.
+//  4. state pass (a lane per channel, a wave per chunk): walk each chunk
+//     forward from its carried-in state, store every state h_t to the
+//     workspace, and sum dy_t h_t over the tile's channels (dC);
+//  5. gradient pass (four lanes per channel, four states each; a workgroup
+//     per (sequence, chunk, 64-channel tile)): walk the chunk backward from
+//     its incoming adjoint, reading h_{t-1}, and form the gradients.
+//     dx and ddt_raw are stored per channel; sums over channels (dB, dgate)
+//     are reduced across the wave and stored per wave; the per-expert
+//     parameter gradients (dA, dbias, dDskip) accumulate in registers over
+//     all experts with each token's dense gate vector (zero for unselected
+//     experts), branch-free, and are stored per (sequence, chunk);
+//  6. reductions over tiles, waves and chunks, in a fixed order.
+// Every output is deterministic.
 #pragma once
 #include "scan_common.hpp"
 #include "swimba_device.hpp"
@@ -68,31 +69,27 @@ struct BwdParams {
   float* H;       // [B][C][16][D] chunk end states, then carried-in states
   float* adj;     // [B][C][16][D] adjoint seeds, then incoming adjoints
   float* hs;      // [B][L][D][16] states of the gradient pass
-  float* red;     // [ntiles][B*L][kRed + k] per-tile channel sums
-  float* pA;      // [B*ncg][E][D][16] per-workgroup dA
-  float* pBD;     // [B*ncg][E][2][D] per-workgroup dbias, dDskip
+  float* redC;    // [ntiles][B*L][16] per-tile sums of dy h_t
+  float* redB;    // [ntiles*4][B*L][16 + k] per-wave sums of the dB terms and the gate terms
+  float* pA;      // [B*C][E][D][16] per-(sequence, chunk) dA
+  float* pBD;     // [B*C][E][2][D] per-(sequence, chunk) dbias, dDskip
 };
 
-// LDS of a workgroup: the tile's expert table, the per-wave rings and either
-// the chunk pass's decay sums or the gradient pass's accumulators.
+// LDS of a chunk-pass or state-pass workgroup: the tile's expert table, the
+// chunk pass's per-wave decay sums and the per-wave rings.
 struct Smem {
   float4* A;      // [E][4][64]
   float2* BD;     // [E][64]
-  float* U;       // chunk pass: [waves][E][64]
-  float* accA;    // gradient pass: [E][16][64]
-  float* accB;    // gradient pass: [E][2][64] (dbias, dDskip)
+  float* U;       // [waves][E][64]
   Ring ring;
 };
 
 __host__ __device__ inline size_t table_bytes(int E) { return (size_t)E * (4 * 64 * 16 + 64 * 8); }
-__host__ __device__ inline size_t extra_bytes(int E, bool grad, int waves) {
-  return grad ? (size_t)E * (16 * 64 * 4 + 2 * 64 * 4) : (size_t)waves * E * 64 * 4;
-}
-__host__ inline size_t smem_bytes(int E, int k, bool grad, int waves) {
-  return table_bytes(E) + extra_bytes(E, grad, waves) + ring_bytes(k) * waves;
+__host__ inline size_t smem_bytes(int E, int k, int waves) {
+  return table_bytes(E) + (size_t)waves * E * 64 * 4 + ring_bytes(k) * waves;
 }
 
-__device__ __forceinline__ Smem smem_layout(int E, int k, bool grad, int waves, int wave) {
+__device__ __forceinline__ Smem smem_layout(int E, int k, int waves, int wave) {
   extern __shared__ float4 smem_bwd[];
   char* p = reinterpret_cast<char*>(smem_bwd);
   Smem s;
@@ -101,9 +98,7 @@ __device__ __forceinline__ Smem smem_layout(int E, int k, bool grad, int waves, 
   s.BD = reinterpret_cast<float2*>(p);
   p += (size_t)E * 64 * 8;
   s.U = reinterpret_cast<float*>(p);
-  s.accA = reinterpret_cast<float*>(p);
-  s.accB = reinterpret_cast<float*>(p + (size_t)E * 16 * 64 * 4);
-  p += extra_bytes(E, grad, waves);
+  p += (size_t)waves * E * 64 * 4;
   p += ring_bytes(k) * wave;
   s.ring.bc = reinterpret_cast<float*>(p);
   s.ring.e = reinterpret_cast<int32_t*>(p + 2 * kTB * 32 * 4);
@@ -207,8 +202,13 @@ __device__ __forceinline__ void wave_transpose_sum(float* v, int lane) {
     const bool upper = (lane & mask) != 0;
 #pragma unroll
     for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[half + i];
-      const float keep = upper ? v[half + i] : v[i];
+      // take both values first: otherwise the compiler turns the two selects
+      // into a lane-dependent index into v, i.e. a compare-and-select chain
+      // over the whole array
+      float lo = v[i], hi = v[half + i];
+      asm("" : "+v"(lo), "+v"(hi));
+      const float send = upper ? lo : hi;
+      const float keep = upper ? hi : lo;
       v[i] = keep + __shfl_xor(send, mask, 64);
     }
   }
@@ -243,7 +243,7 @@ template <typename TIn, typename TDy, int WAVES, int K>
 __global__ __launch_bounds__(WAVES * 64) void bwd_chunk_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = uniform((int)(threadIdx.x >> 6));
   const int k = K > 0 ? K : p.k;
-  const Smem s = smem_layout(p.E, k, false, WAVES, wave);
+  const Smem s = smem_layout(p.E, k, WAVES, wave);
   const Task tk = task<WAVES>(p);
   const int d0 = tk.tile * 64, d = d0 + lane;
   const bool active = d < p.D;
@@ -350,247 +350,370 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_chunk_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- pass 4
 template <typename TIn, typename TDy, int WAVES, int K>
-__global__ __launch_bounds__(WAVES * 64) void bwd_grad_kernel(BwdParams p) {
+__global__ __launch_bounds__(WAVES * 64) void bwd_state_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = uniform((int)(threadIdx.x >> 6));
   const int k = K > 0 ? K : p.k;
   constexpr int KM = K > 0 ? K : 16;
-  const Smem s = smem_layout(p.E, k, true, WAVES, wave);
+  const Smem s = smem_layout(p.E, k, WAVES, wave);
   const Task tk = task<WAVES>(p);
   const int d0 = tk.tile * 64, d = d0 + lane;
   const bool active = d < p.D;
   stage::load_table(p, s.A, s.BD, d0, false);
-  for (int i = threadIdx.x; i < p.E * (16 + 2) * 64; i += blockDim.x) s.accA[i] = 0.f;
+  __syncthreads();
+  if (tk.c >= p.nchunks) return;  // no barrier below
+  const int t0 = tk.c * p.chunk, t1 = min(p.L, t0 + p.chunk);
+  const size_t row = (size_t)tk.b * p.L;
+  const size_t total = (size_t)p.B * p.L;
+  constexpr int KW = (kTB * KM + 63) / 64;
+  const uint32_t off_in = active ? (uint32_t)d * (uint32_t)sizeof(TIn) : stage::kOffNone;
+  const uint32_t off_dy = active ? (uint32_t)d * (uint32_t)sizeof(TDy) : stage::kOffNone;
+  auto valid_at = [&](int t) { return (int)min((size_t)kTB, total - (row + t)); };
+  stage::Stager<TIn, KW> st;
+  st.init(lane);
+  int gate_bad = 0;
+  float h[kN];
+  const size_t cbase = (((size_t)tk.b * p.nchunks + tk.c) * kN) * p.D + (active ? d : 0);
+#pragma unroll
+  for (int n = 0; n < kN; ++n) {
+    float v = 0.f;
+    if (active) {
+      if (tk.c > 0)
+        v = p.H[cbase + (size_t)n * p.D];
+      else if (p.h0 != nullptr)
+        v = p.h0[((size_t)tk.b * p.D + d) * kN + n];
+    }
+    h[n] = v;
+  }
+  float4* hs4 = reinterpret_cast<float4*>(p.hs);
+  float* redC = p.redC + (size_t)tk.tile * total * kN;
+  BlockRows<TIn, TDy> cur, nxt;
+  st.issue(p, row + t0, valid_at(t0), k);
+  load_rows<TIn, TDy>(p, row + t0, valid_at(t0), off_in, off_dy, true, cur);
+  st.commit(s.ring, 0, min(kTB, t1 - t0), k, p.E, lane, gate_bad);
+  int slot = 0;
+  for (int tb = t0; tb < t1; tb += kTB, slot ^= 1) {
+    const int n = min(kTB, t1 - tb), tn = tb + kTB;
+    const bool more = tn < t1;
+    if (more) {
+      st.issue(p, row + tn, valid_at(tn), k);
+      load_rows<TIn, TDy>(p, row + tn, valid_at(tn), off_in, off_dy, true, nxt);
+    }
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < kTB; ++i) {
+      if (i >= n) break;
+      int e[KM];
+      float gw[KM];
+      read_routing(s.ring, slot, i, k, e, gw, KM);
+      const float xv = active ? to_f32(cur.x[i]) : 0.f, rv = active ? to_f32(cur.r[i]) : 0.f;
+      const Mix<K> mx = mix_scalars<K>(s, e, gw, k, lane, rv);
+      float ab[kN];
+      mix_abar<K>(s, e, gw, k, lane, ab);
+      const float dl2 = mx.dlt * kLog2e, dx = mx.dlt * xv;
+      const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 b4 = bc[q];
+        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int nn = 4 * q + r;
+          h[nn] = fmaf(hw_exp2(dl2 * ab[nn]), h[nn], dx * bv[r]);
+        }
+      }
+      const size_t bt = row + tb + i;
+      if (active) {
+        float4* dst = hs4 + (bt * (size_t)p.D + d) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dst[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+      }
+      // dC terms dy h_t, summed over the tile's channels
+      const float gy = active ? to_f32(cur.g[i]) : 0.f;
+      float v[kN];
+#pragma unroll
+      for (int nn = 0; nn < kN; ++nn) v[nn] = gy * h[nn];
+      wave_transpose_sum<kN>(v, lane);
+      if ((lane & 3) == 0) redC[bt * kN + (lane >> 2)] = v[0];
+    }
+    if (more) {
+      st.commit(s.ring, slot ^ 1, min(kTB, t1 - tn), k, p.E, lane, gate_bad);
+      cur = nxt;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pass 5
+// LDS of the gradient pass: the tile's A as [E][64 channels][16] floats, the
+// (dt_bias, Dskip) table [E][64], and per wave its ring plus the dense gate
+// vectors of the ring's tokens ([2][kTB][EMAX]).
+template <int EMAX>
+__host__ __device__ inline size_t rev_smem_bytes(int E, int k) {
+  return (size_t)E * 64 * 16 * 4 + (size_t)E * 64 * 8 +
+         4 * (ring_bytes(k) + (size_t)2 * kTB * EMAX * 4);
+}
+
+template <typename TIn, typename TDy, int K, int EMAX>
+__global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
+  extern __shared__ float4 smem_rev[];
+  const int lane = threadIdx.x & 63, wave = uniform((int)(threadIdx.x >> 6));
+  const int k = K > 0 ? K : p.k;
+  constexpr int KM = K > 0 ? K : 16;
+  float* sA = reinterpret_cast<float*>(smem_rev);                    // [E][64][16]
+  float2* sBD = reinterpret_cast<float2*>(sA + (size_t)p.E * 64 * 16);  // [E][64]
+  char* wp = reinterpret_cast<char*>(sBD + (size_t)p.E * 64) +
+             (ring_bytes(k) + (size_t)2 * kTB * EMAX * 4) * wave;
+  float* ringG = reinterpret_cast<float*>(wp);  // [2][kTB][EMAX]
+  char* rp = wp + (size_t)2 * kTB * EMAX * 4;
+  Ring ring;
+  ring.bc = reinterpret_cast<float*>(rp);
+  ring.e = reinterpret_cast<int32_t*>(rp + 2 * kTB * 32 * 4);
+  ring.g = reinterpret_cast<float*>(rp + 2 * kTB * 32 * 4 + 2 * kTB * k * 4);
+
+  int bid = blockIdx.x;
+  const int tile = bid % p.ntiles;
+  bid /= p.ntiles;
+  const int c = bid % p.nchunks;
+  const int b = bid / p.nchunks;
+  const int q = lane & 3, cl = wave * 16 + (lane >> 2);  // channel within the tile
+  const int d0 = tile * 64, d = d0 + cl;
+  const bool active = d < p.D;
+  // the tile's tables (zeros past D)
+  for (int i = threadIdx.x; i < p.E * 64 * 4; i += blockDim.x) {
+    const int e = i / 256, dl = (i / 4) % 64, qq = i % 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (d0 + dl < p.D) v = *reinterpret_cast<const float4*>(p.A + ((size_t)e * p.D + d0 + dl) * kN + 4 * qq);
+    reinterpret_cast<float4*>(sA)[i] = v;
+  }
+  for (int i = threadIdx.x; i < p.E * 64; i += blockDim.x) {
+    const int e = i / 64, dl = i % 64;
+    float2 v = make_float2(0.f, 0.f);
+    if (d0 + dl < p.D) v = make_float2(p.bias[(size_t)e * p.D + d0 + dl], p.Dsk[(size_t)e * p.D + d0 + dl]);
+    sBD[i] = v;
+  }
   __syncthreads();
 
-  if (tk.c < p.nchunks) {
-    const int t0 = tk.c * p.chunk, t1 = min(p.L, t0 + p.chunk);
-    const size_t row = (size_t)tk.b * p.L;
-    const size_t total = (size_t)p.B * p.L;
-    constexpr int KW = (kTB * KM + 63) / 64;
-    const uint32_t off_in = active ? (uint32_t)d * (uint32_t)sizeof(TIn) : stage::kOffNone;
-    const uint32_t off_dy = active ? (uint32_t)d * (uint32_t)sizeof(TDy) : stage::kOffNone;
-    const int dd = active ? d : 0;
-    auto valid_at = [&](int t) { return (int)min((size_t)kTB, total - (row + t)); };
-    stage::Stager<TIn, KW> st;
-    st.init(lane);
-    int gate_bad = 0;
-    const size_t cbase = (((size_t)tk.b * p.nchunks + tk.c) * kN) * p.D + dd;
-    auto load_hin = [&](float* h) {
+  const int t0 = c * p.chunk, t1 = min(p.L, t0 + p.chunk);
+  const size_t row = (size_t)b * p.L;
+  const size_t total = (size_t)p.B * p.L;
+  constexpr int KW = (kTB * KM + 63) / 64;
+  const uint32_t off_in = active ? (uint32_t)d * (uint32_t)sizeof(TIn) : stage::kOffNone;
+  const uint32_t off_dy = active ? (uint32_t)d * (uint32_t)sizeof(TDy) : stage::kOffNone;
+  auto valid_at = [&](int t) { return (int)min((size_t)kTB, total - (row + t)); };
+  stage::Stager<TIn, KW> st;
+  st.init(lane);
+  int gate_bad = 0;
+  const size_t cbase = (((size_t)b * p.nchunks + c) * kN) * p.D + (active ? d : 0);
+  float mu[4];
 #pragma unroll
-      for (int n = 0; n < kN; ++n) {
-        float v = 0.f;
-        if (active) {
-          if (tk.c > 0)
-            v = p.H[cbase + (size_t)n * p.D];
-          else if (p.h0 != nullptr)
-            v = p.h0[((size_t)tk.b * p.D + d) * kN + n];
-        }
-        h[n] = v;
-      }
-    };
-    float4* hs4 = reinterpret_cast<float4*>(p.hs);
-
-    // ---- forward: every state of the chunk, from its carried-in state
-    float h[kN];
-    load_hin(h);
-    {
-      BlockRows<TIn, TDy> cur, nxt;
-      st.issue(p, row + t0, valid_at(t0), k);
-      load_rows<TIn, TDy>(p, row + t0, valid_at(t0), off_in, off_dy, true, cur);
-      st.commit(s.ring, 0, min(kTB, t1 - t0), k, p.E, lane, gate_bad);
-      int slot = 0;
-      for (int tb = t0; tb < t1; tb += kTB, slot ^= 1) {
-        const int n = min(kTB, t1 - tb), tn = tb + kTB;
-        const bool more = tn < t1;
-        if (more) {
-          st.issue(p, row + tn, valid_at(tn), k);
-          load_rows<TIn, TDy>(p, row + tn, valid_at(tn), off_in, off_dy, true, nxt);
-        }
-        wave_sync();
+  for (int r = 0; r < 4; ++r) mu[r] = active ? p.adj[cbase + (size_t)(4 * q + r) * p.D] : 0.f;
+  float accA[EMAX][4], accB[EMAX][2];
 #pragma unroll
-        for (int i = 0; i < kTB; ++i) {
-          if (i >= n) break;
-          int e[KM];
-          float gw[KM];
-          read_routing(s.ring, slot, i, k, e, gw, KM);
-          const float xv = active ? to_f32(cur.x[i]) : 0.f, rv = active ? to_f32(cur.r[i]) : 0.f;
-          const Mix<K> mx = mix_scalars<K>(s, e, gw, k, lane, rv);
-          float ab[kN];
-          mix_abar<K>(s, e, gw, k, lane, ab);
-          const float dl2 = mx.dlt * kLog2e, dx = mx.dlt * xv;
-          const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
+  for (int e = 0; e < EMAX; ++e) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 b4 = bc[q];
-            const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+    for (int r = 0; r < 4; ++r) accA[e][r] = 0.f;
+    accB[e][0] = accB[e][1] = 0.f;
+  }
+  // dense gate vectors of a committed ring slot: G[t][e] = sum of the gates
+  // of the slots of token t that chose expert e
+  auto dense_gates = [&](int sl) {
+    wave_sync();
+    for (int l = lane; l < kTB * EMAX; l += 64) {
+      const int tt = l / EMAX, ee = l % EMAX;
+      float gsum = 0.f;
+      for (int j = 0; j < k; ++j)
+        if (ring.e[(sl * kTB + tt) * k + j] == ee) gsum += ring.g[(sl * kTB + tt) * k + j];
+      ringG[(sl * kTB + tt) * EMAX + ee] = gsum;
+    }
+  };
+  const float4* hs4 = reinterpret_cast<const float4*>(p.hs);
+  const int kr = kN + k;
+  float* redB = p.redB + ((size_t)tile * 4 + wave) * total * kr;
+  const int nblk = (t1 - t0 + kTB - 1) / kTB;
+  BlockRows<TIn, TDy> cur, nxt;
+  {
+    const int tb = t0 + (nblk - 1) * kTB;
+    st.issue(p, row + tb, valid_at(tb), k);
+    load_rows<TIn, TDy>(p, row + tb, valid_at(tb), off_in, off_dy, true, cur);
+    st.commit(ring, 0, min(kTB, t1 - tb), k, p.E, lane, gate_bad);
+    dense_gates(0);
+  }
+  int slot = 0;
+  for (int blk = nblk - 1; blk >= 0; --blk, slot ^= 1) {
+    const int tb = t0 + blk * kTB;
+    const int n = min(kTB, t1 - tb);
+    const bool more = blk > 0;
+    if (more) {
+      st.issue(p, row + tb - kTB, kTB, k);
+      load_rows<TIn, TDy>(p, row + tb - kTB, kTB, off_in, off_dy, true, nxt);
+    }
+    // this block's previous states h_{t-1}, all issued before the first is used
+    float4 hpb[kTB];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int nn = 4 * q + r;
-              h[nn] = fmaf(hw_exp2(dl2 * ab[nn]), h[nn], dx * bv[r]);
-            }
-          }
-          if (active) {
-            float4* dst = hs4 + ((row + tb + i) * (size_t)p.D + d) * 4;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              dst[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
-          }
-          // dC partials dy h_t, summed over the tile's channels
-          const float gy = active ? to_f32(cur.g[i]) : 0.f;
-          float v[kN];
-#pragma unroll
-          for (int nn = 0; nn < kN; ++nn) v[nn] = gy * h[nn];
-          wave_transpose_sum<kN>(v, lane);
-          if ((lane & 3) == 0) p.red[((size_t)tk.tile * total + row + tb + i) * (kRed + k) + kN +
-                                     (lane >> 2)] = v[0];
-        }
-        if (more) {
-          st.commit(s.ring, slot ^ 1, min(kTB, t1 - tn), k, p.E, lane, gate_bad);
-          cur = nxt;
-        }
+    for (int i = 0; i < kTB; ++i) {
+      hpb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int t = tb + i;
+      if (active && i < n) {
+        if (t > t0)
+          hpb[i] = hs4[((row + t - 1) * (size_t)p.D + d) * 4 + q];
+        else if (c > 0)
+          hpb[i] = make_float4(p.H[cbase + (size_t)(4 * q) * p.D],
+                               p.H[cbase + (size_t)(4 * q + 1) * p.D],
+                               p.H[cbase + (size_t)(4 * q + 2) * p.D],
+                               p.H[cbase + (size_t)(4 * q + 3) * p.D]);
+        else if (p.h0 != nullptr)
+          hpb[i] = *reinterpret_cast<const float4*>(p.h0 + ((size_t)b * p.D + d) * kN + 4 * q);
       }
     }
-
-    // ---- backward: blocks from the last, tokens from the last
-    float mu[kN];
+    wave_sync();
 #pragma unroll
-    for (int n = 0; n < kN; ++n) mu[n] = active ? p.adj[cbase + (size_t)n * p.D] : 0.f;
-    const int nblk = (t1 - t0 + kTB - 1) / kTB;
-    const int kr = kRed + k;
-    float* red = p.red + (size_t)tk.tile * total * kr;
-    BlockRows<TIn, TDy> cur;
-    {
-      const int tb = t0 + (nblk - 1) * kTB;
-      st.issue(p, row + tb, valid_at(tb), k);
-      load_rows<TIn, TDy>(p, row + tb, valid_at(tb), off_in, off_dy, true, cur);
-      st.commit(s.ring, 0, min(kTB, t1 - tb), k, p.E, lane, gate_bad);
-    }
-    int slot = 0;
-    for (int blk = nblk - 1; blk >= 0; --blk, slot ^= 1) {
-      const int tb = t0 + blk * kTB;
-      const int n = min(kTB, t1 - tb);
-      const bool more = blk > 0;
-      if (more) st.issue(p, row + tb - kTB, kTB, k);
-      wave_sync();
-#pragma unroll
-      for (int ii = 0; ii < kTB; ++ii) {
-        const int i = kTB - 1 - ii;
-        if (i < n) {
+    for (int ii = 0; ii < kTB; ++ii) {
+      const int i = kTB - 1 - ii;
+      if (i < n) {
         const int t = tb + i;
         const size_t bt = row + t;
         int e[KM];
         float gw[KM];
-        read_routing(s.ring, slot, i, k, e, gw, KM);
+        read_routing(ring, slot, i, k, e, gw, KM);
         const float xv = active ? to_f32(cur.x[i]) : 0.f, rv = active ? to_f32(cur.r[i]) : 0.f;
         const float gy = active ? to_f32(cur.g[i]) : 0.f;
-        // h_{t-1}
-        float hp[kN];
-        if (active && t > t0) {
-          const float4* sp = hs4 + ((bt - 1) * (size_t)p.D + d) * 4;
+        const float hp[4] = {hpb[i].x, hpb[i].y, hpb[i].z, hpb[i].w};
+        // mixed per-channel parameters (the four lanes of a channel agree)
+        float beta = 0.f, delta = 0.f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 v = sp[q];
-            hp[4 * q] = v.x;
-            hp[4 * q + 1] = v.y;
-            hp[4 * q + 2] = v.z;
-            hp[4 * q + 3] = v.w;
-          }
-        } else {
-          load_hin(hp);  // zeros on inactive lanes
+        for (int j = 0; j < KM; ++j) {
+          if (j >= k) break;
+          const float2 bd = sBD[e[j] * 64 + cl];
+          beta = fmaf(gw[j], bd.x, beta);
+          delta = fmaf(gw[j], bd.y, delta);
         }
-        float* rr = red + bt * kr;
-        const Mix<K> mx = mix_scalars<K>(s, e, gw, k, lane, rv);
-        const float dl2 = mx.dlt * kLog2e;
-        const float dxs = mx.dlt * xv;
-        const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
-        float ab[kN], w[kN], vb[kN];
-        mix_abar<K>(s, e, gw, k, lane, ab);
+        const float z = rv + beta;
+        const float dlt = softplus_f32(z);
+        const float dl2 = dlt * kLog2e, dxs = dlt * xv;
+        const float4 b4 = reinterpret_cast<const float4*>(ring.bc + (slot * kTB + i) * 32)[q];
+        const float4 c4 = reinterpret_cast<const float4*>(ring.bc + (slot * kTB + i) * 32)[4 + q];
+        const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, cv[4] = {c4.x, c4.y, c4.z, c4.w};
+        float aj[KM][4];
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          if (j < k) {
+            const float4 a4 = reinterpret_cast<const float4*>(sA)[(e[j] * 64 + cl) * 4 + q];
+            aj[j][0] = a4.x;
+            aj[j][1] = a4.y;
+            aj[j][2] = a4.z;
+            aj[j][3] = a4.w;
+          }
+        }
+        float w[4], vb[4], sa[KM];
+#pragma unroll
+        for (int j = 0; j < KM; ++j) sa[j] = 0.f;
         float slb = 0.f, swa = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 b4 = bc[q], c4 = bc[4 + q];
-          const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, cv[4] = {c4.x, c4.y, c4.z, c4.w};
+        for (int r = 0; r < 4; ++r) {
+          float abn = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int nn = 4 * q + r;
-            const float a = hw_exp2(dl2 * ab[nn]);
-            const float lam = fmaf(cv[r], gy, mu[nn]);
-            vb[nn] = lam * dxs;
-            slb = fmaf(lam, bv[r], slb);
-            w[nn] = lam * a * hp[nn];
-            swa = fmaf(w[nn], ab[nn], swa);
-            mu[nn] = a * lam;
-          }
+          for (int j = 0; j < KM; ++j)
+            if (j < k) abn = fmaf(gw[j], aj[j][r], abn);
+          const float a = hw_exp2(dl2 * abn);
+          const float lam = fmaf(cv[r], gy, mu[r]);
+          vb[r] = lam * dxs;
+          slb = fmaf(lam, bv[r], slb);
+          w[r] = lam * a * hp[r];
+          swa = fmaf(w[r], abn, swa);
+#pragma unroll
+          for (int j = 0; j < KM; ++j)
+            if (j < k) sa[j] = fmaf(aj[j][r], w[r], sa[j]);
+          mu[r] = a * lam;
         }
-        const float ddelta_dt = fmaf(xv, slb, swa);              // dL/dDelta
-        const float sig = hw_exp2((mx.z - mx.dlt) * kLog2e);     // sigmoid(z)
-        const float dz = ddelta_dt * sig;
+        // sums over the channel's four lanes
+        slb += __shfl_xor(slb, 1, 64);
+        slb += __shfl_xor(slb, 2, 64);
+        swa += __shfl_xor(swa, 1, 64);
+        swa += __shfl_xor(swa, 2, 64);
+        const float dz = fmaf(xv, slb, swa) * hw_exp2((z - dlt) * kLog2e);  // dDelta sigmoid(z)
         const float gyx = gy * xv;
-        if (active) {
-          p.dx[bt * p.D + d] = fmaf(mx.delta, gy, mx.dlt * slb);
+        if (active && q == 0) {
+          p.dx[bt * p.D + d] = fmaf(delta, gy, dlt * slb);
           p.ddt[bt * p.D + d] = dz;
         }
-        // per expert: dA += g Delta w, dbias, dDskip, and the gates' partials
-        float dgp[KM];
+        float* rr = redB + bt * kr;
+        // per-expert parameter gradients, all experts, with the dense gates
+        {
+          const float4* G4 = reinterpret_cast<const float4*>(ringG + (slot * kTB + i) * EMAX);
 #pragma unroll
-        for (int j = 0; j < KM; ++j) {
-          if (j >= k) break;
-          const int ej = e[j];
-          const float gd = gw[j] * mx.dlt;
-          float sa = 0.f;
+          for (int e4 = 0; e4 < EMAX / 4; ++e4) {
+            const float4 gv4 = G4[e4];
+            const float gv[4] = {gv4.x, gv4.y, gv4.z, gv4.w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 a4 = s.A[(ej * 4 + q) * 64 + lane];
-            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+            for (int u = 0; u < 4; ++u) {
+              const int ee = 4 * e4 + u;
+              const float gd = gv[u] * dlt;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int nn = 4 * q + r;
-              sa = fmaf(av[r], w[nn], sa);
-              __hip_atomic_fetch_add(&s.accA[(ej * kN + nn) * 64 + lane], gd * w[nn],
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              for (int r = 0; r < 4; ++r) accA[ee][r] = fmaf(gd, w[r], accA[ee][r]);
+              accB[ee][0] = fmaf(gv[u], dz, accB[ee][0]);
+              accB[ee][1] = fmaf(gv[u], gyx, accB[ee][1]);
             }
           }
-          const float2 bd = s.BD[ej * 64 + lane];
-          __hip_atomic_fetch_add(&s.accB[(ej * 2) * 64 + lane], gw[j] * dz, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-          __hip_atomic_fetch_add(&s.accB[(ej * 2 + 1) * 64 + lane], gw[j] * gyx,
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          dgp[j] = fmaf(bd.x, dz, fmaf(bd.y, gyx, mx.dlt * sa));
         }
-        // dB partials over the tile's channels (inactive lanes hold zeros)
-        wave_transpose_sum<kN>(vb, lane);
-        if ((lane & 3) == 0) rr[lane >> 2] = vb[0];
-        // the gates' sums over the tile's channels
 #pragma unroll
         for (int j = 0; j < KM; ++j) {
           if (j >= k) break;
-          const float sj = wave_sum(dgp[j]);
-          if (lane == j) rr[kRed + j] = sj;
+              const int ej = e[j];
+          const float2 bd = sBD[ej * 64 + cl];
+          const float part = fmaf(dlt, sa[j], q == 0 ? fmaf(bd.x, dz, bd.y * gyx) : 0.f);
+          const float sj = wave_sum(part);
+          if (lane == j) rr[kN + j] = sj;
         }
+        // dB terms summed over the wave's 16 channels: lanes of equal q hold
+        // the same states; after two halving exchanges (masks 32, 16) and two
+        // sums (8, 4) lane l holds state 4q + 2 bit5 + bit4
+        {
+          int mask = 32;
+#pragma unroll
+          for (int cnt = 4; cnt > 1; cnt >>= 1, mask >>= 1) {
+            const int half = cnt / 2;
+            const bool upper = (lane & mask) != 0;
+#pragma unroll
+            for (int r = 0; r < half; ++r) {
+              float lo = vb[r], hi = vb[half + r];
+              asm("" : "+v"(lo), "+v"(hi));
+              const float send = upper ? lo : hi;
+              const float keep = upper ? hi : lo;
+              vb[r] = keep + __shfl_xor(send, mask, 64);
+            }
+          }
+          vb[0] += __shfl_xor(vb[0], 8, 64);
+          vb[0] += __shfl_xor(vb[0], 4, 64);
+          if ((lane & 12) == 0) rr[4 * q + 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1)] = vb[0];
         }
       }
-      if (more) {
-        st.commit(s.ring, slot ^ 1, kTB, k, p.E, lane, gate_bad);
-        load_rows<TIn, TDy>(p, row + tb - kTB, kTB, off_in, off_dy, true, cur);
+    }
+    if (more) {
+      st.commit(ring, slot ^ 1, kTB, k, p.E, lane, gate_bad);
+      dense_gates(slot ^ 1);
+      cur = nxt;
+    }
+  }
+  // per-(sequence, chunk) parameter-gradient partials (the four lanes of a
+  // channel hold the same dbias and dDskip sums; lane q = 0 stores them)
+  if (active) {
+    const size_t slotbc = (size_t)b * p.nchunks + c;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < p.E) {
+        reinterpret_cast<float4*>(p.pA)[((slotbc * p.E + e) * p.D + d) * 4 + q] =
+            make_float4(accA[e][0], accA[e][1], accA[e][2], accA[e][3]);
+        if (q == 0) {
+          p.pBD[((slotbc * p.E + e) * 2) * p.D + d] = accB[e][0];
+          p.pBD[((slotbc * p.E + e) * 2 + 1) * p.D + d] = accB[e][1];
+        }
       }
     }
   }
-  __syncthreads();
-  // the workgroup's parameter-gradient partials
-  const size_t slotwg = (size_t)tk.b * p.ncg + tk.cg;
-  for (int i = threadIdx.x; i < p.E * kN * 64; i += blockDim.x) {
-    const int e = i / (kN * 64), nn = (i / 64) % kN, l = i % 64;
-    if (d0 + l < p.D)
-      p.pA[((slotwg * p.E + e) * p.D + d0 + l) * kN + nn] = s.accA[(e * kN + nn) * 64 + l];
-  }
-  for (int i = threadIdx.x; i < p.E * 2 * 64; i += blockDim.x) {
-    const int e = i / 128, w2 = (i / 64) % 2, l = i % 64;
-    if (d0 + l < p.D) p.pBD[((slotwg * p.E + e) * 2 + w2) * p.D + d0 + l] = s.accB[i];
-  }
 }
 
-// Passes 3 and 5 (scan_backward.hip): the reverse carry, and the reductions
-// over tiles and workgroups into dB, dC, dgate, dA, dbias and dDskip.
+// Passes 3 and 6 (scan_backward.hip): the reverse carry, and the reductions
+// over tiles, waves and chunks into dB, dC, dgate, dA, dbias and dDskip.
 int reverse_carry(const BwdParams& p, hipStream_t st);
 int reduce_outputs(const BwdParams& p, float* dB, float* dC, float* dgate, float* dA,
                    float* dbias, float* dDsk, hipStream_t st);
@@ -628,13 +751,13 @@ int launch_bwd_t(const swimba_scan_grad_args* g, const BwdPlan& pl, void* ws, hi
   p.H = reinterpret_cast<float*>(w + pl.off_H);
   p.adj = reinterpret_cast<float*>(w + pl.off_adj);
   p.hs = reinterpret_cast<float*>(w + pl.off_hs);
-  p.red = reinterpret_cast<float*>(w + pl.off_red);
+  p.redC = reinterpret_cast<float*>(w + pl.off_redC);
+  p.redB = reinterpret_cast<float*>(w + pl.off_redB);
   p.pA = reinterpret_cast<float*>(w + pl.off_pA);
   p.pBD = reinterpret_cast<float*>(w + pl.off_pBD);
 
   const dim3 grid((unsigned)((size_t)p.B * p.ncg * p.ntiles)), block(WAVES * 64);
-  const size_t smem1 = smem_bytes(p.E, p.k, false, WAVES);
-  const size_t smem4 = smem_bytes(p.E, p.k, true, WAVES);
+  const size_t smem1 = smem_bytes(p.E, p.k, WAVES);
   allow_dynamic_lds(bwd_chunk_kernel<TIn, TDy, WAVES, K>, smem1);
   hipLaunchKernelGGL((bwd_chunk_kernel<TIn, TDy, WAVES, K>), grid, block, smem1, st, p);
   if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
@@ -642,8 +765,24 @@ int launch_bwd_t(const swimba_scan_grad_args* g, const BwdPlan& pl, void* ws, hi
   if (rc != SWIMBA_OK) return rc;
   rc = reverse_carry(p, st);
   if (rc != SWIMBA_OK) return rc;
-  allow_dynamic_lds(bwd_grad_kernel<TIn, TDy, WAVES, K>, smem4);
-  hipLaunchKernelGGL((bwd_grad_kernel<TIn, TDy, WAVES, K>), grid, block, smem4, st, p);
+  // the state pass uses the chunk pass's layout (its decay sums unused)
+  allow_dynamic_lds(bwd_state_kernel<TIn, TDy, WAVES, K>, smem1);
+  hipLaunchKernelGGL((bwd_state_kernel<TIn, TDy, WAVES, K>), grid, block, smem1, st, p);
+  if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
+  const dim3 grid5((unsigned)((size_t)p.B * p.nchunks * p.ntiles));
+  if (p.E <= 4) {
+    const size_t smem5 = rev_smem_bytes<4>(p.E, p.k);
+    allow_dynamic_lds(bwd_grad_kernel<TIn, TDy, K, 4>, smem5);
+    hipLaunchKernelGGL((bwd_grad_kernel<TIn, TDy, K, 4>), grid5, dim3(256), smem5, st, p);
+  } else if (p.E <= 8) {
+    const size_t smem5 = rev_smem_bytes<8>(p.E, p.k);
+    allow_dynamic_lds(bwd_grad_kernel<TIn, TDy, K, 8>, smem5);
+    hipLaunchKernelGGL((bwd_grad_kernel<TIn, TDy, K, 8>), grid5, dim3(256), smem5, st, p);
+  } else {
+    const size_t smem5 = rev_smem_bytes<16>(p.E, p.k);
+    allow_dynamic_lds(bwd_grad_kernel<TIn, TDy, K, 16>, smem5);
+    hipLaunchKernelGGL((bwd_grad_kernel<TIn, TDy, K, 16>), grid5, dim3(256), smem5, st, p);
+  }
   if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
   return reduce_outputs(p, g->dBm, g->dCm, g->dgate, g->dA, g->ddt_bias, g->dDskip, st);
 }
@@ -660,8 +799,8 @@ int launch_bwd_w(const swimba_scan_grad_args* g, const BwdPlan& pl, void* ws, hi
   }
 }
 
-// Eight chunks (waves) share a workgroup's expert table and accumulators when
-// the LDS allows it, four otherwise (E > 8).
+// Eight chunks (waves) share a workgroup's expert table in the chunk and
+// state passes when the LDS allows it, four otherwise.
 template <typename TIn, typename TDy>
 int launch_bwd_k(const swimba_scan_grad_args* g, const BwdPlan& pl, void* ws, hipStream_t st) {
   if (pl.waves == 8) return launch_bwd_w<TIn, TDy, 8>(g, pl, ws, st);

@@ -154,8 +154,10 @@ int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p) {
   if (!dtype_ok(g->dy_dtype)) return SWIMBA_EINVAL;
   if (a->a_form != SWIMBA_A_DIAGONAL) return SWIMBA_EUNSUPPORTED;
   *p = BwdPlan();
-  p->waves = backward_lds_bytes(a->E, a->k, 8) <= 160 * 1024 ? 8 : 4;
-  if (backward_lds_bytes(a->E, a->k, p->waves) > 160 * 1024) return SWIMBA_EUNSUPPORTED;
+  p->waves = backward_lds_bytes(a->E, a->k, 8) <= 80 * 1024 ? 8 : 4;
+  if (backward_lds_bytes(a->E, a->k, p->waves) > 160 * 1024 ||
+      backward_grad_lds_bytes(a->E, a->k) > 160 * 1024)
+    return SWIMBA_EUNSUPPORTED;
   p->ntiles = sp.ntiles;
   if (a->B == 0 || a->L == 0) return SWIMBA_OK;
   // Own chunking (the forward is recomputed here): about two waves per SIMD
@@ -187,9 +189,10 @@ int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p) {
   p->off_H = take(arr);
   p->off_adj = take(arr);
   p->off_hs = take(B * L * D * SWIMBA_STATE_N * sizeof(float));
-  p->off_red = take((size_t)p->ntiles * B * L * (2 * SWIMBA_STATE_N + a->k) * sizeof(float));
-  p->off_pA = take(B * p->ncg * E * D * SWIMBA_STATE_N * sizeof(float));
-  p->off_pBD = take(B * p->ncg * E * 2 * D * sizeof(float));
+  p->off_redC = take((size_t)p->ntiles * B * L * SWIMBA_STATE_N * sizeof(float));
+  p->off_redB = take((size_t)p->ntiles * 4 * B * L * (SWIMBA_STATE_N + a->k) * sizeof(float));
+  p->off_pA = take(B * p->nchunks * E * D * SWIMBA_STATE_N * sizeof(float));
+  p->off_pBD = take(B * p->nchunks * E * 2 * D * sizeof(float));
   p->bytes = o;
   return SWIMBA_OK;
 }

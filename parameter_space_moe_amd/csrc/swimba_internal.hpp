@@ -25,17 +25,25 @@ struct ScanPlan {
 // backward passes (all offsets 256-byte aligned).
 struct BwdPlan {
   int ntiles = 0, chunk = 0, nchunks = 0, ncg = 0, waves = 4;
-  size_t off_P = 0, off_H = 0, off_adj = 0, off_hs = 0, off_red = 0, off_pA = 0, off_pBD = 0;
+  size_t off_P = 0, off_H = 0, off_adj = 0, off_hs = 0, off_redC = 0, off_redB = 0;
+  size_t off_pA = 0, off_pBD = 0;
   size_t bytes = 0;
 };
 
 // Fills `p` for these arguments; returns a status.  Pure host arithmetic.
 int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p);
 int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p);
-// LDS of the backward's gradient pass: expert table, per-expert gradient
-// accumulators and one staging ring per wave.
+// LDS of the backward's gradient pass (four waves): the tile's expert tables,
+// and per wave a staging ring and the dense gate vectors of its tokens.
+inline size_t backward_grad_lds_bytes(int E, int k) {
+  const size_t emax = E <= 4 ? 4 : (E <= 8 ? 8 : 16);
+  return (size_t)E * 64 * 16 * 4 + (size_t)E * 64 * 8 +
+         4 * ((size_t)2 * 8 * 32 * 4 + (size_t)2 * 2 * 8 * k * 4 + (size_t)2 * 8 * emax * 4);
+}
+// LDS of the backward's chunk and state passes: expert table, per-wave decay
+// sums and one staging ring per wave.
 inline size_t backward_lds_bytes(int E, int k, int waves) {
-  return (size_t)E * (4 * 64 * 16 + 64 * 8) * 2 +
+  return (size_t)E * (4 * 64 * 16 + 64 * 8) + (size_t)waves * E * 64 * 4 +
          (size_t)waves * ((size_t)2 * 8 * 32 * 4 + (size_t)2 * 2 * 8 * k * 4);
 }
 int plan_streams(const swimba_stream_args* a, ScanPlan* p);

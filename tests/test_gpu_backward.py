@@ -81,8 +81,9 @@ def test_backward_optional_state_gradients(with_h0, with_dhf):
 @pytest.mark.parametrize("E,k", [(5, 3), (8, 2), (16, 2), (3, 1)])
 def test_backward_ragged_and_expert_counts(chunk, E, k):
     """A ragged channel tile (D = 130), the runtime-k path (k = 3), the
-    4-wave workgroups for E = 16, a length that is not a whole number of
-    chunks or staging blocks."""
+    4-wave chunk and state workgroups and 16-expert accumulators for
+    E = 16, a length that is not a
+    whole number of chunks or staging blocks."""
     w, inp, t = case(B=2, L=301, D=130, E=E, k=k, seed=10 * E + k)
     idx, gate, g = run(t, w, chunk=chunk)
     check(g, reference(inp, idx, gate), TOL_F32)
@@ -128,10 +129,8 @@ def test_backward_chunking_agrees_and_is_deterministic():
     w, inp, t = case(B=1, L=2048, D=128, E=8, k=2, dtype="bf16", seed=11)
     _, _, g0 = run(t, w, chunk=0)
     _, _, g1 = run(t, w, chunk=0)
-    for n in ("dx", "ddt_raw", "dBm", "dCm", "dgate", "dh0"):
+    for n in NAMES:
         assert torch.equal(g0[n], g1[n]), n
-    for n in ("dA", "ddt_bias", "dDskip"):
-        assert rel_err(host(g1[n]), host(g0[n])) < 1e-5, n
     _, _, g2 = run(t, w, chunk=96)
     for n in NAMES:
         assert rel_err(host(g2[n]), host(g0[n])) < 1e-4, n
@@ -162,5 +161,5 @@ def test_prepared_backward():
                                    dh_final=t["dhf"])
     call()
     torch.cuda.synchronize()
-    for n in ("dx", "ddt_raw", "dBm", "dCm", "dgate", "dh0"):
+    for n in NAMES:
         assert torch.equal(out[n], g[n]), n
