@@ -50,12 +50,12 @@ def load(path: str | None = None):
     lib = ctypes.CDLL(so)
     i64, ci = ctypes.c_int64, ctypes.c_int
     lib.ref_route.argtypes = [i64, ci, ci, ci, _f64p, _f64p, _i32p, _f64p, _f64p, _f64p]
-    lib.ref_scan.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7
-    lib.ref_scan_separate.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7
-    lib.ref_mamba_scan.argtypes = [ci] * 4 + [_f64p] * 9
+    lib.ref_scan.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7 + [ci]
+    lib.ref_scan_separate.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7 + [ci]
+    lib.ref_mamba_scan.argtypes = [ci] * 4 + [_f64p] * 10 + [ci]
     lib.ref_scan_streams.argtypes = [ci] * 5 + [_f64p] * 10
     lib.ref_scan_backward.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 16
-    lib.ref_step.argtypes = [ci] * 5 + [_f64p] * 5 + [_i32p] + [_f64p] * 6 + [_i32p, _f64p]
+    lib.ref_step.argtypes = [ci] * 5 + [_f64p] * 5 + [_i32p] + [_f64p] * 6 + [_i32p, _f64p, ci]
     lib.ref_num_threads.restype = ci
     for f in (lib.ref_route, lib.ref_scan, lib.ref_scan_separate, lib.ref_mamba_scan,
               lib.ref_scan_streams, lib.ref_scan_backward, lib.ref_step):
@@ -101,7 +101,7 @@ def route(x, Wr, k, lib=None):
     return idx, gate, logits, absdot
 
 
-def _scan_common(fn, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, state_shape):
+def _scan_common(fn, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, state_shape, zoh):
     x, dt_raw, Bm, Cm = _d(x), _d(dt_raw), _d(Bm), _d(Cm)
     idx, gate = _i(idx), _d(gate)
     A, dt_bias, Dskip = _d(A), _d(dt_bias), _d(Dskip)
@@ -120,24 +120,26 @@ def _scan_common(fn, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, state_
     y = np.zeros((B, L, D))
     hf = np.zeros(shape)
     fn(B, L, D, N, E, k, _p(x), _p(dt_raw), _p(Bm), _p(Cm), _p(idx), _p(gate), _p(A),
-       _p(dt_bias), _p(Dskip), _p(h0), _p(y), _p(hf))
+       _p(dt_bias), _p(Dskip), _p(h0), _p(y), _p(hf), 1 if zoh else 0)
     return y, hf
 
 
-def scan(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, lib=None):
+def scan(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, lib=None, zoh=False):
     """Mixed (parameter-space) scan.  Shapes: x, dt_raw [B,L,D]; Bm, Cm [B,L,N];
     idx, gate [B,L,k]; A [E,D,N]; dt_bias, Dskip [E,D]; h0 [B,D,N] or None.
+    zoh: zero-order-hold input term instead of Euler.
     Returns y [B,L,D], h_final [B,D,N] (fp64)."""
     lib = lib or load()
     return _scan_common(lib.ref_scan, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0,
-                        lambda B, E, D, N: (B, D, N))
+                        lambda B, E, D, N: (B, D, N), zoh)
 
 
-def scan_separate(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, lib=None):
+def scan_separate(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, lib=None,
+                  zoh=False):
     """Separate design: one state per expert.  h0, h_final [B,E,D,N]."""
     lib = lib or load()
     return _scan_common(lib.ref_scan_separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias,
-                        Dskip, h0, lambda B, E, D, N: (B, E, D, N))
+                        Dskip, h0, lambda B, E, D, N: (B, E, D, N), zoh)
 
 
 def scan_backward(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0=None, dh_final=None,
@@ -168,7 +170,7 @@ def scan_backward(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0=None, 
     return out
 
 
-def mamba_scan(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, h0=None, lib=None):
+def mamba_scan(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, h0=None, lib=None, zoh=False):
     """Plain single-expert selective scan.  A [D,N], dt_bias, Dskip [D]."""
     lib = lib or load()
     x, dt_raw, Bm, Cm = _d(x), _d(dt_raw), _d(Bm), _d(Cm)
@@ -180,7 +182,7 @@ def mamba_scan(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, h0=None, lib=None):
     y = np.zeros((B, L, D))
     hf = np.zeros((B, D, N))
     lib.ref_mamba_scan(B, L, D, N, _p(x), _p(dt_raw), _p(Bm), _p(Cm), _p(A), _p(dt_bias),
-                       _p(Dskip), _p(h0), _p(y), _p(hf))
+                       _p(Dskip), _p(h0), _p(y), _p(hf), 1 if zoh else 0)
     return y, hf
 
 
@@ -207,7 +209,7 @@ def scan_streams(X, dt_raw, Bs, Cs, gate, A, dt_bias, h0=None, lib=None):
 
 
 def step(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None, gate=None,
-         lib=None):
+         lib=None, zoh=False):
     """One decode step.  x, dt_raw [B,D]; Bm, Cm [B,N]; state [B,D,N] fp64,
     updated IN PLACE.  Routing from Wr [D,E] with top-k, or forced idx/gate
     [B,k].  Returns y [B,D], idx [B,k], gate [B,k]."""
@@ -230,5 +232,6 @@ def step(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None,
     idx_out = np.zeros((B, k), np.int32)
     gate_out = np.zeros((B, k))
     lib.ref_step(B, D, N, E, k, _p(x), _p(dt_raw), _p(Bm), _p(Cm), Wr_p, _p(idx), _p(gate),
-                 _p(A), _p(dt_bias), _p(Dskip), _p(state), _p(y), _p(idx_out), _p(gate_out))
+                 _p(A), _p(dt_bias), _p(Dskip), _p(state), _p(y), _p(idx_out), _p(gate_out),
+                 1 if zoh else 0)
     return y, idx_out, gate_out

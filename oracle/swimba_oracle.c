@@ -26,7 +26,9 @@
  *              delta = sum_j g_j Dskip[e_j,d]      (parameters mixed, [SW])
  *   discretise Delta = softplus(dt_raw + beta); a[n] = exp(Delta Abar[n])
  *              ([MB] "Mamba": transition exp(Delta A)); injection
- *              Delta * B[t,n] * x (Euler form of the input term)
+ *              Delta * B[t,n] * x (Euler form of the input term), or with
+ *              zoh = 1 the zero-order hold (exp(Delta Abar) - 1)/Abar * B x
+ *              ([MB] "Mamba": B_bar = A^{-1}(exp(Delta A) - I) B)
  *   recurrence h[n] <- a[n] h[n] + Delta B[t,n] x      ([MB], [SW])
  *   readout    y = sum_n C[t,n] h[n] + delta x          (after the update)
  * The separate design keeps one state per expert and advances only the
@@ -53,6 +55,20 @@
 /* Stable softplus, log(1 + exp(z)) = max(z,0) + log1p(exp(-|z|)). */
 static double softplus(double z) {
   return (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z)));
+}
+
+/*
+ * Coefficient of B_t x in the discretised input term of one state entry with
+ * transition Abar:
+ *   zoh == 0: Euler, Delta (the form the scans use by default);
+ *   zoh == 1: zero-order hold, B_bar = A^{-1}(exp(Delta A) - I) B ([MB]
+ *             "Mamba", the discretised state equations), i.e. the coefficient
+ *             (exp(Delta Abar) - 1) / Abar, which tends to Delta as Abar -> 0.
+ */
+static double input_coeff(double Dt, double Abar, int zoh) {
+  if (!zoh) return Dt;
+  double z = Dt * Abar;
+  return z == 0.0 ? Dt : expm1(z) / Abar;
 }
 
 /* ---------------------------------------------------------------- router */
@@ -119,12 +135,13 @@ void ref_route(int64_t T, int D, int E, int k, const double* x,
  *   h0        [B, D, N]     initial state, or NULL for zeros
  *   y         [B, L, D]     out
  *   h_final   [B, D, N]     out, or NULL
+ *   zoh       0: Euler input term Delta B x; 1: zero-order hold (input_coeff)
  */
 void ref_scan(int B, int L, int D, int N, int E, int k, const double* x,
               const double* dt_raw, const double* Bm, const double* Cm,
               const int32_t* idx, const double* gate, const double* A,
               const double* dt_bias, const double* Dskip, const double* h0,
-              double* y, double* h_final) {
+              double* y, double* h_final, int zoh) {
   (void)E;
 #pragma omp parallel for collapse(2) schedule(static)
   for (int b = 0; b < B; ++b) {
@@ -150,7 +167,7 @@ void ref_scan(int B, int L, int D, int N, int E, int k, const double* x,
           for (int j = 0; j < k; ++j)
             Abar += g[j] * A[((int64_t)e[j] * D + d) * N + n];
           double a = exp(Dt * Abar);
-          double bb = Dt * Bm[bt * N + n] * xv;
+          double bb = input_coeff(Dt, Abar, zoh) * Bm[bt * N + n] * xv;
           h[n] = a * h[n] + bb;
           yv += Cm[bt * N + n] * h[n];
         }
@@ -179,7 +196,7 @@ void ref_scan_separate(int B, int L, int D, int N, int E, int k,
                        const double* Bm, const double* Cm, const int32_t* idx,
                        const double* gate, const double* A,
                        const double* dt_bias, const double* Dskip,
-                       const double* h0, double* y, double* h_final) {
+                       const double* h0, double* y, double* h_final, int zoh) {
 #pragma omp parallel for collapse(2) schedule(static)
   for (int b = 0; b < B; ++b) {
     for (int d = 0; d < D; ++d) {
@@ -196,8 +213,9 @@ void ref_scan_separate(int B, int L, int D, int N, int E, int k,
           double Dt = softplus(dt_raw[bt * D + d] + dt_bias[(int64_t)e * D + d]);
           double ye = 0.0;
           for (int n = 0; n < N; ++n) {
-            double a = exp(Dt * A[((int64_t)e * D + d) * N + n]);
-            H[e * N + n] = a * H[e * N + n] + Dt * Bm[bt * N + n] * xv;
+            double Ae = A[((int64_t)e * D + d) * N + n];
+            double a = exp(Dt * Ae);
+            H[e * N + n] = a * H[e * N + n] + input_coeff(Dt, Ae, zoh) * Bm[bt * N + n] * xv;
             ye += Cm[bt * N + n] * H[e * N + n];
           }
           ye += Dskip[(int64_t)e * D + d] * xv;
@@ -284,7 +302,7 @@ void ref_mamba_scan(int B, int L, int D, int N, const double* x,
                     const double* dt_raw, const double* Bm, const double* Cm,
                     const double* A, const double* dt_bias,
                     const double* Dskip, const double* h0, double* y,
-                    double* h_final) {
+                    double* h_final, int zoh) {
 #pragma omp parallel for collapse(2) schedule(static)
   for (int b = 0; b < B; ++b) {
     for (int d = 0; d < D; ++d) {
@@ -297,7 +315,8 @@ void ref_mamba_scan(int B, int L, int D, int N, const double* x,
         double Dt = softplus(dt_raw[bt * D + d] + dt_bias[d]);
         double out = Dskip[d] * u;
         for (int n = 0; n < N; ++n) {
-          h[n] = exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * Bm[bt * N + n] * u;
+          double An = A[(int64_t)d * N + n];
+          h[n] = exp(Dt * An) * h[n] + input_coeff(Dt, An, zoh) * Bm[bt * N + n] * u;
           out += Cm[bt * N + n] * h[n];
         }
         y[bt * D + d] = out;
@@ -466,7 +485,8 @@ void ref_step(int B, int D, int N, int E, int k, const double* x,
               const double* dt_raw, const double* Bm, const double* Cm,
               const double* Wr, const int32_t* idx_in, const double* gate_in,
               const double* A, const double* dt_bias, const double* Dskip,
-              double* state, double* y, int32_t* idx_out, double* gate_out) {
+              double* state, double* y, int32_t* idx_out, double* gate_out,
+              int zoh) {
   int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)B * k);
   double* gate = (double*)malloc(sizeof(double) * (size_t)B * k);
   if (idx_in) {
@@ -479,7 +499,7 @@ void ref_step(int B, int D, int N, int E, int k, const double* x,
   }
   /* a step is the scan over a sequence of length one, state carried */
   ref_scan(B, 1, D, N, E, k, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip,
-           state, y, state);
+           state, y, state, zoh);
   if (idx_out)
     for (int64_t i = 0; i < (int64_t)B * k; ++i) idx_out[i] = idx[i];
   if (gate_out)

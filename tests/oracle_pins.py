@@ -15,6 +15,9 @@ and the mathematics fix:
     linearity in x; the two designs differ under time-varying routing,
     Theorem 4);
   * brute-force sorting for the router;
+  * the zero-order-hold option: the continuous equilibrium under constant
+    input, the semigroup property (two half steps = one step), and the
+    small-A limit where it meets Euler;
   * the backward of the mixed scan against central differences of the
     forward, and the support of its gradients for a single-token loss;
   * for the stream-mixed form (shared A, mixed B X injection and C readout):
@@ -674,6 +677,80 @@ def pin_streams_split_composition(lib):
     y2, h2 = oracle.scan_streams(**c2, lib=lib)
     _close(np.concatenate([y1, y2], axis=1), y, 1e-13, "stream split y")
     _close(h2, hf, 1e-13, "stream split h")
+
+
+# --------------------------------------------------------- zero-order hold
+def _softplus_inv(v):
+    return math.log(math.expm1(v))
+
+
+def pin_zoh_equilibrium(lib):
+    """With constant inputs the zero-order-hold recurrence has the fixed point
+    of the continuous system, h* = -B x / Abar, whatever the step size:
+    h_t = a^t h0 + (1 - a^t) h* exactly (Euler's fixed point is
+    Delta B x / (1 - a) instead)."""
+    B, L, D, N, E, k = 1, 30, 2, 3, 3, 2
+    x = np.broadcast_to(np.array([0.8, -1.6]), (B, L, D)).copy()
+    dt_raw = np.broadcast_to(np.array([0.5, -0.7]), (B, L, D)).copy()
+    Bv, Cv = np.array([1.0, -0.5, 2.0]), np.array([0.5, 1.5, -1.0])
+    Bm = np.broadcast_to(Bv, (B, L, N)).copy()
+    Cm = np.broadcast_to(Cv, (B, L, N)).copy()
+    A = -np.array([[[0.5, 2.0, 8.0], [1.0, 3.0, 0.25]],
+                   [[4.0, 1.0, 0.5], [2.0, 0.75, 6.0]],
+                   [[1.5, 1.5, 1.5], [0.5, 0.5, 0.5]]])
+    dt_bias = np.array([[0.1, -0.2], [0.0, 0.3], [-0.3, 0.1]])
+    Dskip = np.array([[0.5, 1.0], [-1.0, 0.0], [2.0, -0.5]])
+    g = np.array([0.65, 0.35])
+    idx = np.broadcast_to(np.array([1, 2], np.int32), (B, L, k)).copy()
+    gate = np.broadcast_to(g, (B, L, k)).copy()
+    h0 = np.array([[[1.0, -2.0, 0.5], [0.0, 1.0, -1.0]]])
+    y, hf = oracle.scan(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, lib=lib, zoh=True)
+    t = np.arange(1, L + 1)[:, None]
+    for d in range(D):
+        beta = g[0] * dt_bias[1, d] + g[1] * dt_bias[2, d]
+        delta = g[0] * Dskip[1, d] + g[1] * Dskip[2, d]
+        Dt = math.log1p(math.exp(dt_raw[0, 0, d] + beta))
+        Abar = g[0] * A[1, d] + g[1] * A[2, d]
+        a = np.exp(Dt * Abar)
+        hstar = -Bv * x[0, 0, d] / Abar
+        h = a ** t * h0[0, d] + (1 - a ** t) * hstar
+        _close(y[0, :, d], h @ Cv + delta * x[0, 0, d], 1e-12, "zoh equilibrium y d=%d" % d)
+        _close(hf[0, d], h[-1], 1e-12, "zoh equilibrium h d=%d" % d)
+
+
+def pin_zoh_semigroup(lib):
+    """Zero-order hold is exact for an input held constant: two steps of
+    Delta with the same B, x and routing equal one step of 2 Delta (Euler
+    does not compose so)."""
+    rng = np.random.default_rng(42)
+    c = _rand_case(rng, B=1, L=2, D=3, N=4, E=2, k=2)
+    for key in ("x", "Bm", "Cm"):
+        c[key][:, 1] = c[key][:, 0]
+    c["idx"][:, 1] = c["idx"][:, 0]
+    c["gate"][:, 1] = c["gate"][:, 0]
+    c["dt_raw"][:, 1] = c["dt_raw"][:, 0]
+    _, h2 = oracle.scan(**c, lib=lib, zoh=True)
+    one = {k_: (v[:, :1].copy() if k_ in ("x", "dt_raw", "Bm", "Cm", "idx", "gate") else v)
+           for k_, v in c.items()}
+    idx0, g0 = c["idx"][0, 0], c["gate"][0, 0]
+    for d in range(3):
+        beta = g0[0] * c["dt_bias"][idx0[0], d] + g0[1] * c["dt_bias"][idx0[1], d]
+        Dt = math.log1p(math.exp(c["dt_raw"][0, 0, d] + beta))
+        one["dt_raw"][0, 0, d] = _softplus_inv(2 * Dt) - beta
+    _, h1 = oracle.scan(**one, lib=lib, zoh=True)
+    _close(h1, h2, 1e-12, "zoh semigroup")
+
+
+def pin_zoh_small_transition_is_euler(lib):
+    """As A -> 0 the zero-order-hold coefficient (exp(Delta A) - 1)/A tends
+    to Delta: with |A| ~ 1e-9 the two discretisations agree to ~1e-9."""
+    rng = np.random.default_rng(43)
+    c = _rand_case(rng, B=2, L=9, D=3, N=4, E=3, k=2)
+    c["A"] = c["A"] * 1e-9
+    yz, hz = oracle.scan(**c, lib=lib, zoh=True)
+    ye, he = oracle.scan(**c, lib=lib)
+    _close(yz, ye, 1e-7, "zoh small A y")
+    _close(hz, he, 1e-7, "zoh small A h")
 
 
 # ------------------------------------------------------------- backward

@@ -25,7 +25,13 @@ MUTATIONS = [
     ("A_first_gate_only", "Abar += g[j] * A[", "Abar += g[0] * A["),
     ("A_transposed", "Abar += g[j] * A[((int64_t)e[j] * D + d) * N + n];",
      "Abar += g[j] * A[((int64_t)e[j] * N + n) * D + d];"),
-    ("injection_no_delta", "double bb = Dt * Bm[bt * N + n] * xv;", "double bb = Bm[bt * N + n] * xv;"),
+    ("injection_no_delta", "double bb = input_coeff(Dt, Abar, zoh) * Bm[bt * N + n] * xv;",
+     "double bb = Bm[bt * N + n] * xv;"),
+    ("zoh_divides_by_delta", "return z == 0.0 ? Dt : expm1(z) / Abar;",
+     "return z == 0.0 ? Dt : expm1(z) / Dt;"),
+    ("zoh_exp_for_expm1", "return z == 0.0 ? Dt : expm1(z) / Abar;",
+     "return z == 0.0 ? Dt : exp(z) / Abar;"),
+    ("zoh_ignored", "  if (!zoh) return Dt;\n", "  return Dt;\n"),
     ("B_C_swapped", "yv += Cm[bt * N + n] * h[n];", "yv += Bm[bt * N + n] * h[n];"),
     ("h0_ignored", "h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.0;\n      for (int t = 0; t < L; ++t) {\n        int64_t bt = (int64_t)b * L + t;\n        const int32_t* e",
      "h[n] = 0.0;\n      for (int t = 0; t < L; ++t) {\n        int64_t bt = (int64_t)b * L + t;\n        const int32_t* e"),
@@ -33,16 +39,15 @@ MUTATIONS = [
     ("route_softmax_all", "for (int j = 0; j < k; ++j) z += exp(l[idx[t * k + j]] - m);",
      "for (int j = 0; j < E; ++j) z += exp(l[j] - m);"),
     ("route_absdot_signed", "sa += fabs(p);", "sa += p;"),
-    ("separate_wrong_expert_A", "double a = exp(Dt * A[((int64_t)e * D + d) * N + n]);",
-     "double a = exp(Dt * A[((int64_t)0 * D + d) * N + n]);"),
+    ("separate_wrong_expert_A", "double Ae = A[((int64_t)e * D + d) * N + n];",
+     "double Ae = A[((int64_t)0 * D + d) * N + n];"),
     ("separate_ungated", "yv += gate[bt * k + j] * ye;", "yv += ye;"),
     ("separate_bias_of_slot0", "softplus(dt_raw[bt * D + d] + dt_bias[(int64_t)e * D + d]);",
      "softplus(dt_raw[bt * D + d] + dt_bias[(int64_t)idx[bt * k] * D + d]);"),
     ("separate_decays_all",
      "          ye += Dskip[(int64_t)e * D + d] * xv;",
      "          for (int o = 0; o < E; ++o) if (o != e) for (int n = 0; n < N; ++n) H[o * N + n] *= 0.5;\n          ye += Dskip[(int64_t)e * D + d] * xv;"),
-    ("mamba_wrong_A_index", "exp(Dt * A[(int64_t)d * N + n]) * h[n] + Dt * Bm",
-     "exp(Dt * A[(int64_t)n]) * h[n] + Dt * Bm"),
+    ("mamba_wrong_A_index", "double An = A[(int64_t)d * N + n];", "double An = A[(int64_t)n];"),
     ("mamba_no_D", "double out = Dskip[d] * u;", "double out = 0.0;"),
     ("step_routes_first_token_only", "ref_route(B, D, E, k, x, Wr, idx, gate, NULL, NULL);",
      "ref_route(1, D, E, k, x, Wr, idx, gate, NULL, NULL);\n    for (int64_t i = k; i < (int64_t)B * k; ++i) { idx[i] = idx[i % k]; gate[i] = gate[i % k]; }"),
