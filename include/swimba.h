@@ -20,7 +20,8 @@
  *   mixed:   Abar = sum_j g_j A[e_j,d,:], beta = sum_j g_j dt_bias[e_j,d],
  *            delta = sum_j g_j Dskip[e_j,d]; Delta = softplus(dt_raw + beta);
  *            h <- exp(Delta Abar) * h + Delta * B_t * x;  y = C_t . h + delta x
- *            (y reads the updated state).
+ *            (y reads the updated state).  Options: A one scalar per channel
+ *            (a_form), zero-order-hold input term (disc).
  *   separate: each expert keeps its own state; at token t each selected
  *            expert e_j advances with its own A, bias, Dskip and emits y_j;
  *            y = sum_j g_j y_j; unselected experts' states do not change.
@@ -105,6 +106,14 @@ typedef enum {
  */
 typedef enum { SWIMBA_A_DIAGONAL = 0, SWIMBA_A_SCALAR = 1 } swimba_a_form;
 
+/*
+ * Discretisation of the input term.  EULER: Delta B_t x.  ZOH: zero-order
+ * hold, B_bar = A^{-1}(exp(Delta A) - I) B_t ([MB] "Mamba": the discretised
+ * state equations), i.e. the coefficient (exp(Delta Abar) - 1)/Abar per state
+ * entry in place of Delta.
+ */
+typedef enum { SWIMBA_DISC_EULER = 0, SWIMBA_DISC_ZOH = 1 } swimba_disc;
+
 typedef struct {
   int B, L, D, N, E, k;         /* batch, length, channels, states (16), experts, active */
   swimba_dtype in_dtype;        /* dtype of x, dt_raw, Bm, Cm                            */
@@ -130,6 +139,7 @@ typedef struct {
                                    (no extra packets on `stream`); a pass that does not
                                    run has both events recorded where it would run      */
   swimba_a_form a_form;         /* A is [E, D, N] (DIAGONAL, 0) or [E, D] (SCALAR)        */
+  swimba_disc disc;             /* input term: EULER (0) or ZOH                          */
 } swimba_scan_args;
 
 /*
@@ -198,7 +208,8 @@ typedef struct {
  * The forward is recomputed inside from the same arguments (same chunking
  * as swimba_scan).
  *   ws, ws_bytes: device workspace of at least
- *   swimba_scan_backward_workspace_size(g) bytes, 256-byte aligned.  It
+ *   swimba_scan_backward_workspace_size(g) bytes, 256-byte aligned (the
+ *   forward's disc must be EULER; ZOH returns SWIMBA_EUNSUPPORTED).  It
  *   holds every state h_t (64 bytes per token and channel) besides the
  *   chunk records.
  * Constraints: those of swimba_scan (E <= 16) with a_form DIAGONAL (SCALAR
@@ -227,6 +238,7 @@ typedef struct {
   float* state;                 /* [B, D, N] fp32, read and updated in place     */
   void* y;                      /* [B, D] out                                    */
   swimba_a_form a_form;         /* A is [E, D, N] (DIAGONAL, 0) or [E, D] (SCALAR) */
+  swimba_disc disc;             /* input term: EULER (0) or ZOH                  */
 } swimba_step_args;
 
 /*

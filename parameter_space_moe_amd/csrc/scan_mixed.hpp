@@ -115,7 +115,8 @@ __host__ inline size_t smem_bytes(int E, int k, bool with_u, int waves, bool sca
 //   ACC_U: accumulate the gate-weighted Delta per expert (chunk pass).
 //   SA: one transition per (expert, channel), shared by the 16 states (the
 //       Mamba-2 form A = a I): one exponential per token instead of 16.
-template <int K, bool TRACK, bool ACC_U, bool SA>
+//   ZOH: zero-order-hold input term, zoh_phi(a) times the Euler term.
+template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
 __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, float* U,
                                            const int* e, const float* gw, int slot, int i,
                                            int lane, float xv, float rv, float* h, float* g) {
@@ -152,7 +153,7 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
     }
     const float a = hw_exp2(m);
     const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
-    const float dx = dlt * xv;
+    const float dx = ZOH ? dlt * xv * zoh_phi(a, m) : dlt * xv;
     float yv = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -212,7 +213,8 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
     for (int r = 0; r < 4; ++r) {
       const int n = 4 * q + r;
       const float a = hw_exp2(m[n]);
-      h[n] = fmaf(a, h[n], dx * bv[r]);
+      const float inj = ZOH ? (dx * bv[r]) * zoh_phi(a, m[n]) : dx * bv[r];
+      h[n] = fmaf(a, h[n], inj);
       yv = fmaf(cv[r], h[n], yv);
       if (TRACK) g[n] *= a;
     }
@@ -226,7 +228,7 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
 // x, dt_raw and y go through per-block buffer resources (scalar token offsets,
 // a fixed per-lane channel offset); the prefetch of the next block is issued
 // before the current one computes and is waited on only when it is used.
-template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA>
+template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
 __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U, int b, int t0,
                                      int t1, int d, bool active, bool full_tile, int lane,
                                      bool truncate, float* h, float* g, int& gate_bad) {
@@ -289,7 +291,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
             ev[j] = s.ring.e[(slot * kTB + i) * K + j];
             gv[j] = s.ring.g[(slot * kTB + i) * K + j];
           }
-          const float yv = mix_token<K, TRACK, ACC_U, SA>(p, s, U, ev, gv, slot, i, lane,
+          const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, U, ev, gv, slot, i, lane,
                                                       to_f32(xc[i]), to_f32(rc[i]), h, g);
           stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
@@ -305,7 +307,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
               gv[j] = s.ring.g[(slot * kTB + i) * K + j];
             }
             const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
-            const float yv = mix_token<K, TRACK, ACC_U, SA>(p, s, U, ev, gv, slot, i, lane, xv, rv,
+            const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, U, ev, gv, slot, i, lane, xv, rv,
                                                         h, g);
             if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
           }
@@ -322,7 +324,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
             gb[j] = s.ring.g[(slot * kTB + i) * k + j];
           }
           const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
-          const float yv = mix_token<K, TRACK, ACC_U, SA>(p, s, U, eb, gb, slot, i, lane, xv, rv, h,
+          const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, U, eb, gb, slot, i, lane, xv, rv, h,
                                                       g);
           if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
@@ -354,7 +356,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
 }
 
 // Pass 1 (or the only pass when CHUNKED is false).
-template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA>
+template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA, bool ZOH>
 __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const Smem s = smem_layout(p.E, K > 0 ? K : p.k, CHUNKED, WAVES, wave, SA);
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   // every chunk writes y (provisional for chunks >= 1, recomputed by the
   // fix-up pass where the carried-in state still matters)
   int gate_bad = 0;
-  walk<TIn, TOut, K, false, CHUNKED, SA>(p, s, U, b, t0, t1, d, active, d0 + 64 <= p.D, lane, false,
+  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH>(p, s, U, b, t0, t1, d, active, d0 + 64 <= p.D, lane, false,
                                      h, nullptr, gate_bad);
 
   if (CHUNKED) {
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
 
 // Pass 3: chunks 1.. re-run from their carried-in state until the carried part
 // has decayed away (or to the chunk's end).
-template <typename TIn, typename TOut, int WAVES, int K, bool SA>
+template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH>
 __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const Smem s = smem_layout(p.E, K > 0 ? K : p.k, false, WAVES, wave, SA);
@@ -468,11 +470,11 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const bool truncate = p.carry == SWIMBA_CARRY_FIXUP &&
                         p.flags[((size_t)b * p.nchunks + c) * p.ntiles + tile] == 0;
   int gate_bad = 0;
-  walk<TIn, TOut, K, true, false, SA>(p, s, nullptr, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
+  walk<TIn, TOut, K, true, false, SA, ZOH>(p, s, nullptr, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
                                   truncate, h, g, gate_bad);
 }
 
-template <typename TIn, typename TOut, int WAVES, int K, bool SA>
+template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH>
 int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   MixParams p;
   p.B = a->B;
@@ -507,8 +509,8 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   if (pl.nchunks <= 1) {
     p.nchunks = 1;
     dim3 grid((unsigned)((size_t)p.B * p.ntiles));
-    allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA>, smem3);
-    const int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA>, grid,
+    allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH>, smem3);
+    const int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH>, grid,
                                 dim3(WAVES * 64), smem3, st, ev, p);
     if (rc != SWIMBA_OK) return rc;
     record_skipped(ev ? ev + 2 : nullptr, st);
@@ -517,39 +519,45 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   }
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   dim3 grid1((unsigned)((size_t)p.B * ncg * p.ntiles));
-  allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA>, smem1);
-  int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA>, grid1, dim3(WAVES * 64),
+  allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH>, smem1);
+  int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH>, grid1, dim3(WAVES * 64),
                         smem1, st, ev, p);
   if (rc != SWIMBA_OK) return rc;
   rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 0, st, ev ? ev + 2 : nullptr);
   if (rc != SWIMBA_OK) return rc;
   const int ncg3 = (p.nchunks - 1 + WAVES - 1) / WAVES;
   dim3 grid3((unsigned)((size_t)p.B * ncg3 * p.ntiles));
-  allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K, SA>, smem3);
-  return launch_timed(mix_fixup_kernel<TIn, TOut, WAVES, K, SA>, grid3, dim3(WAVES * 64), smem3, st,
+  allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH>, smem3);
+  return launch_timed(mix_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH>, grid3, dim3(WAVES * 64), smem3, st,
                       ev ? ev + 4 : nullptr, p);
 }
 
-template <typename TIn, typename TOut, int WAVES, bool SA>
+template <typename TIn, typename TOut, int WAVES, bool SA, bool ZOH>
 int launch_mixed_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   switch (a->k) {
     case 1:
-      return launch_mixed_t<TIn, TOut, WAVES, 1, SA>(a, pl, ws, st);
+      return launch_mixed_t<TIn, TOut, WAVES, 1, SA, ZOH>(a, pl, ws, st);
     case 2:
-      return launch_mixed_t<TIn, TOut, WAVES, 2, SA>(a, pl, ws, st);
+      return launch_mixed_t<TIn, TOut, WAVES, 2, SA, ZOH>(a, pl, ws, st);
     default:
-      return launch_mixed_t<TIn, TOut, WAVES, 0, SA>(a, pl, ws, st);
+      return launch_mixed_t<TIn, TOut, WAVES, 0, SA, ZOH>(a, pl, ws, st);
   }
+}
+
+template <typename TIn, typename TOut, int WAVES, bool SA>
+int launch_mixed_z(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
+  if (a->disc == SWIMBA_DISC_ZOH) return launch_mixed_k<TIn, TOut, WAVES, SA, true>(a, pl, ws, st);
+  return launch_mixed_k<TIn, TOut, WAVES, SA, false>(a, pl, ws, st);
 }
 
 template <typename TIn, typename TOut>
 int launch_mixed_w(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   if (a->a_form == SWIMBA_A_SCALAR) {
-    if (pl.waves == 8) return launch_mixed_k<TIn, TOut, 8, true>(a, pl, ws, st);
-    return launch_mixed_k<TIn, TOut, 4, true>(a, pl, ws, st);
+    if (pl.waves == 8) return launch_mixed_z<TIn, TOut, 8, true>(a, pl, ws, st);
+    return launch_mixed_z<TIn, TOut, 4, true>(a, pl, ws, st);
   }
-  if (pl.waves == 8) return launch_mixed_k<TIn, TOut, 8, false>(a, pl, ws, st);
-  return launch_mixed_k<TIn, TOut, 4, false>(a, pl, ws, st);
+  if (pl.waves == 8) return launch_mixed_z<TIn, TOut, 8, false>(a, pl, ws, st);
+  return launch_mixed_z<TIn, TOut, 4, false>(a, pl, ws, st);
 }
 
 }  // namespace mixed

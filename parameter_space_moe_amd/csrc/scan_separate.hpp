@@ -126,14 +126,15 @@ __device__ __forceinline__ void stage_round(const SepParams& p, const SepSmem<TI
 
 // Advance this wave's expert by one selected token; returns the expert's
 // output C_t . h + Dskip x (READOUT) or 0.  SA: one transition Ae[0] shared
-// by the 16 states.
-template <bool READOUT, bool SA>
+// by the 16 states.  ZOH: zero-order-hold input term (zoh_phi times Euler).
+template <bool READOUT, bool SA, bool ZOH>
 __device__ __forceinline__ float expert_step(float* h, float& S, const float* Ae, float bias,
                                              float dsk, float xv, float rv, const float4* bc) {
   const float dlt = softplus_f32(rv + bias);
   S += dlt;
   const float dx = dlt * xv;
   const float a0 = SA ? hw_exp2(dlt * Ae[0]) : 0.f;
+  const float dx0 = (SA && ZOH) ? dx * zoh_phi(a0, dlt * Ae[0]) : dx;
   float ye = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -143,7 +144,8 @@ __device__ __forceinline__ float expert_step(float* h, float& S, const float* Ae
     for (int r = 0; r < 4; ++r) {
       const int n = 4 * q + r;
       const float a = SA ? a0 : hw_exp2(dlt * Ae[n]);
-      h[n] = fmaf(a, h[n], dx * bv[r]);
+      const float inj = (ZOH && !SA) ? (dx * bv[r]) * zoh_phi(a, dlt * Ae[n]) : dx0 * bv[r];
+      h[n] = fmaf(a, h[n], inj);
       if (READOUT) ye = fmaf(cv[r], h[n], ye);
     }
   }
@@ -155,14 +157,14 @@ __device__ __forceinline__ float expert_step(float* h, float& S, const float* Ae
 // time the wave first takes one ballot per slot (which staged tokens chose its
 // expert there) and then visits only the selected tokens, so the scan over
 // the round costs scalar bit operations only.
-template <typename TIn, int K, bool READOUT, bool SA>
+template <typename TIn, int K, bool READOUT, bool SA, bool ZOH>
 __device__ __forceinline__ void walk_round(const SepSmem<TIn>& s, int n, int k, int ex, int lane,
                                            float* h, float& S, const float* Ae, float bias,
                                            float dsk) {
   auto select = [&](int i, int j) {
     const float xv = to_f32(s.xs[i * 64 + lane]), rv = to_f32(s.rs[i * 64 + lane]);
     const float4* bc = reinterpret_cast<const float4*>(s.bc + i * 32);
-    const float ye = expert_step<READOUT, SA>(h, S, Ae, bias, dsk, xv, rv, bc);
+    const float ye = expert_step<READOUT, SA, ZOH>(h, S, Ae, bias, dsk, xv, rv, bc);
     if (READOUT) s.yb[(i * k + j) * 64 + lane] = s.g[i * k + j] * ye;
   };
   if constexpr (K > 0) {
@@ -187,7 +189,7 @@ __device__ __forceinline__ void walk_round(const SepSmem<TIn>& s, int n, int k, 
   }
 }
 
-template <typename TIn, typename TOut, int PASS, int K, bool SA>
+template <typename TIn, typename TOut, int PASS, int K, bool SA, bool ZOH>
 __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   const int k = K > 0 ? K : p.k;
   const int R = round_tokens(k);
@@ -240,9 +242,9 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
     stage_round<TIn>(p, s, row, ts, n, k, d0);
     __syncthreads();
     if (readout)
-      walk_round<TIn, K, true, SA>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
+      walk_round<TIn, K, true, SA, ZOH>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
     else
-      walk_round<TIn, K, false, SA>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
+      walk_round<TIn, K, false, SA, ZOH>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
     __syncthreads();
     // every (token, slot) output was written by its expert's wave; add them in
     // slot order.  The next round's staging touches no output buffer, and its
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   }
 }
 
-template <typename TIn, typename TOut, int K, bool SA>
+template <typename TIn, typename TOut, int K, bool SA, bool ZOH>
 int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   SepParams p;
   p.B = a->B;
@@ -304,43 +306,47 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
   const dim3 block((unsigned)(p.E * 64));
   const size_t tiles = (size_t)p.B * p.ntiles;
   const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassSingle, K, SA>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFirst, K, SA>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFixup, K, SA>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH>, smem);
   if (pl.nchunks <= 1) {
-    const int rc = launch_timed(sep_kernel<TIn, TOut, kPassSingle, K, SA>, dim3((unsigned)tiles),
+    const int rc = launch_timed(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH>, dim3((unsigned)tiles),
                                 block, smem, st, ev, p);
     if (rc != SWIMBA_OK) return rc;
     record_skipped(ev ? ev + 2 : nullptr, st);
     record_skipped(ev ? ev + 4 : nullptr, st);
     return SWIMBA_OK;
   }
-  int rc = launch_timed(sep_kernel<TIn, TOut, kPassFirst, K, SA>,
+  int rc = launch_timed(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH>,
                         dim3((unsigned)(tiles * p.nchunks)), block, smem, st, ev, p);
   if (rc != SWIMBA_OK) return rc;
   rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 1, st, ev ? ev + 2 : nullptr);
   if (rc != SWIMBA_OK) return rc;
-  return launch_timed(sep_kernel<TIn, TOut, kPassFixup, K, SA>,
+  return launch_timed(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH>,
                       dim3((unsigned)(tiles * (p.nchunks - 1))), block, smem, st,
                       ev ? ev + 4 : nullptr, p);
 }
 
-template <typename TIn, typename TOut, bool SA>
+template <typename TIn, typename TOut, bool SA, bool ZOH>
 int launch_sep_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   switch (a->k) {
     case 1:
-      return launch_sep_t<TIn, TOut, 1, SA>(a, pl, ws, st);
+      return launch_sep_t<TIn, TOut, 1, SA, ZOH>(a, pl, ws, st);
     case 2:
-      return launch_sep_t<TIn, TOut, 2, SA>(a, pl, ws, st);
+      return launch_sep_t<TIn, TOut, 2, SA, ZOH>(a, pl, ws, st);
     default:
-      return launch_sep_t<TIn, TOut, 0, SA>(a, pl, ws, st);
+      return launch_sep_t<TIn, TOut, 0, SA, ZOH>(a, pl, ws, st);
   }
 }
 
 template <typename TIn, typename TOut>
 int launch_sep_e(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
-  if (a->a_form == SWIMBA_A_SCALAR) return launch_sep_k<TIn, TOut, true>(a, pl, ws, st);
-  return launch_sep_k<TIn, TOut, false>(a, pl, ws, st);
+  const bool zoh = a->disc == SWIMBA_DISC_ZOH;
+  if (a->a_form == SWIMBA_A_SCALAR)
+    return zoh ? launch_sep_k<TIn, TOut, true, true>(a, pl, ws, st)
+               : launch_sep_k<TIn, TOut, true, false>(a, pl, ws, st);
+  return zoh ? launch_sep_k<TIn, TOut, false, true>(a, pl, ws, st)
+             : launch_sep_k<TIn, TOut, false, false>(a, pl, ws, st);
 }
 
 }  // namespace sep

@@ -30,6 +30,7 @@ constexpr int kStepChan = kStepThreads / 4;  // channels per workgroup iteration
 struct StepParams {
   int B, D, E, k, slices;
   int scalar_a;  // A is [E][D]: one transition per expert and channel
+  int zoh;       // zero-order-hold input term
   const void* x;
   const void* dt;
   const void* Bm;
@@ -258,7 +259,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float a = hw_exp2(dl2 * m[i]);
-        hv[i] = fmaf(a, hv[i], dx * Bv[i]);
+        const float inj = p.zoh ? (dx * Bv[i]) * zoh_phi(a, dl2 * m[i]) : dx * Bv[i];
+        hv[i] = fmaf(a, hv[i], inj);
         yv = fmaf(Cv[i], hv[i], yv);
       }
       // quad sum of the readout (lanes 4c..4c+3 hold one channel)
@@ -298,6 +300,7 @@ int launch_step_t(const swimba_step_args* a, hipStream_t s) {
   p.gate_out = a->gate_out;
   p.A = a->A;
   p.scalar_a = a->a_form == SWIMBA_A_SCALAR;
+  p.zoh = a->disc == SWIMBA_DISC_ZOH;
   p.bias = a->dt_bias;
   p.Dsk = a->Dskip;
   p.state = a->state;

@@ -30,6 +30,7 @@ int validate_scan(const swimba_scan_args* a, int separate) {
       a->carry != SWIMBA_CARRY_FIXUP)
     return SWIMBA_EINVAL;
   if (a->a_form != SWIMBA_A_DIAGONAL && a->a_form != SWIMBA_A_SCALAR) return SWIMBA_EINVAL;
+  if (a->disc != SWIMBA_DISC_EULER && a->disc != SWIMBA_DISC_ZOH) return SWIMBA_EINVAL;
   if (a->N != SWIMBA_STATE_N) return SWIMBA_EUNSUPPORTED;
   if (a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
   if (separate && a->E > 16) return SWIMBA_EUNSUPPORTED;
@@ -152,7 +153,7 @@ int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p) {
   int rc = plan_scan(a, 0, &sp);
   if (rc != SWIMBA_OK) return rc;
   if (!dtype_ok(g->dy_dtype)) return SWIMBA_EINVAL;
-  if (a->a_form != SWIMBA_A_DIAGONAL) return SWIMBA_EUNSUPPORTED;
+  if (a->a_form != SWIMBA_A_DIAGONAL || a->disc != SWIMBA_DISC_EULER) return SWIMBA_EUNSUPPORTED;
   *p = BwdPlan();
   p->waves = backward_lds_bytes(a->E, a->k, 8) <= 80 * 1024 ? 8 : 4;
   if (backward_lds_bytes(a->E, a->k, p->waves) > 160 * 1024 ||
@@ -406,6 +407,7 @@ int swimba_step(const swimba_step_args* a, hipStream_t stream) {
     return SWIMBA_EINVAL;
   if (!dtype_ok(a->in_dtype) || !dtype_ok(a->y_dtype)) return SWIMBA_EINVAL;
   if (a->a_form != SWIMBA_A_DIAGONAL && a->a_form != SWIMBA_A_SCALAR) return SWIMBA_EINVAL;
+  if (a->disc != SWIMBA_DISC_EULER && a->disc != SWIMBA_DISC_ZOH) return SWIMBA_EINVAL;
   if (a->N != SWIMBA_STATE_N || a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
   if (a->B == 0) return SWIMBA_OK;
   if (a->x == nullptr || a->dt_raw == nullptr || a->Bm == nullptr || a->Cm == nullptr ||

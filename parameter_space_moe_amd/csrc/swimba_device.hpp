@@ -33,10 +33,28 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// softplus(z) = max(z, 0) + ln(1 + exp(-|z|)), in two hardware transcendentals.
+// softplus(z) = max(z, 0) + log1p(exp(-|z|)).  log1p(e) is formed as
+// e * ln(u) / (u - 1) with u = 1 + e rounded, so that the rounding of u
+// cancels (Goldberg, "What every computer scientist should know about
+// floating-point arithmetic"): accurate to a few ulps also for e << 1, where
+// ln(1 + e) alone would keep only the bits of e that survive the add.
 __device__ __forceinline__ float softplus_f32(float z) {
-  float e = hw_exp2(-fabsf(z) * kLog2e);
-  return fmaxf(z, 0.0f) + hw_log2(1.0f + e) * kLn2;
+  const float e = hw_exp2(-fabsf(z) * kLog2e);
+  const float u = 1.0f + e;
+  const float l = u == 1.0f ? e : e * (hw_log2(u) * kLn2) * __builtin_amdgcn_rcpf(u - 1.0f);
+  return fmaxf(z, 0.0f) + l;
+}
+
+// Zero-order-hold factor phi = (exp(z) - 1) / z of the decay a = exp(z) =
+// exp2(m): the zero-order-hold input term is phi times the Euler term
+// Delta B x.  For a >= 1/2 it is (a - 1) / ln(a) with the computed log of a,
+// so that the rounding of a cancels between numerator and denominator
+// (Kahan's expm1 method, as given in Goldberg, "What every computer scientist
+// should know about floating-point arithmetic"); below 1/2 there is no
+// cancellation and z itself divides; phi = 1 when a rounds to 1.
+__device__ __forceinline__ float zoh_phi(float a, float m) {
+  const float lg = a < 0.5f ? m : hw_log2(a);
+  return lg == 0.f ? 1.f : (a - 1.f) * __builtin_amdgcn_rcpf(lg) * kLog2e;
 }
 
 // Element `i` of a wave-uniform base with a 32-bit byte offset: lets the

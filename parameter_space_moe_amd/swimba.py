@@ -18,6 +18,7 @@ F32, BF16 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 CARRY = {"auto": 0, "rewalk": 1, "fixup": 2}
 A_DIAGONAL, A_SCALAR = 0, 1  # A [E, D, N] or [E, D] (one transition per channel)
+DISC_EULER, DISC_ZOH = 0, 1  # input term Delta B x, or zero-order hold
 N_STATE = 16
 
 _vp = ctypes.c_void_p
@@ -30,7 +31,8 @@ class ScanArgs(ctypes.Structure):
                 ("x", _vp), ("dt_raw", _vp), ("Bm", _vp), ("Cm", _vp),
                 ("idx", _vp), ("gate", _vp), ("A", _vp), ("dt_bias", _vp), ("Dskip", _vp),
                 ("h0", _vp), ("y", _vp), ("h_final", _vp),
-                ("chunk", _ci), ("carry", _ci), ("phase_events", _vp), ("a_form", _ci)]
+                ("chunk", _ci), ("carry", _ci), ("phase_events", _vp), ("a_form", _ci),
+                ("disc", _ci)]
 
 
 class StepArgs(ctypes.Structure):
@@ -39,7 +41,7 @@ class StepArgs(ctypes.Structure):
                 ("x", _vp), ("dt_raw", _vp), ("Bm", _vp), ("Cm", _vp),
                 ("Wr", _vp), ("idx", _vp), ("gate", _vp), ("idx_out", _vp), ("gate_out", _vp),
                 ("A", _vp), ("dt_bias", _vp), ("Dskip", _vp), ("state", _vp), ("y", _vp),
-                ("a_form", _ci)]
+                ("a_form", _ci), ("disc", _ci)]
 
 
 class GradArgs(ctypes.Structure):
@@ -168,7 +170,7 @@ def route(x: torch.Tensor, Wr: torch.Tensor, k: int, idx=None, gate=None, stream
 
 
 def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, chunk, carry,
-               separate, phase_events, need_y=True):
+               separate, phase_events, need_y=True, zoh=False):
     _need(x, "x")
     if x.dim() != 3:
         raise ValueError("x must be [B, L, D]")
@@ -204,6 +206,7 @@ def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, 
     a.carry = CARRY[carry] if isinstance(carry, str) else int(carry)
     a.phase_events = phase_events
     a.a_form = A_SCALAR if scalar_a else A_DIAGONAL
+    a.disc = DISC_ZOH if zoh else DISC_EULER
     return a
 
 
@@ -213,7 +216,7 @@ def workspace_size(args: ScanArgs, separate: bool) -> int:
 
 def _scan(separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, y=None,
           h_final=None, y_dtype=None, want_state=True, chunk=0, carry="auto", workspace=None,
-          stream=None, phase_events=None):
+          stream=None, phase_events=None, zoh=False):
     if y is None:
         y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
     if h_final is None and want_state:
@@ -222,7 +225,7 @@ def _scan(separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, y=
             (x.shape[0], x.shape[2], N_STATE)
         h_final = torch.empty(shape, dtype=torch.float32, device=x.device)
     a = _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, chunk, carry,
-                   separate, phase_events)
+                   separate, phase_events, zoh=zoh)
     lib = load()
     need = workspace_size(a, separate)
     if workspace is None:
@@ -353,9 +356,10 @@ class PreparedScan:
     that issue the same call repeatedly; __call__ goes straight to the C ABI."""
 
     def __init__(self, separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None,
-                 y=None, h_final=None, chunk=0, carry="auto", workspace=None, stream=None):
+                 y=None, h_final=None, chunk=0, carry="auto", workspace=None, stream=None,
+                 zoh=False):
         self.args = _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final,
-                               chunk, carry, separate, None)
+                               chunk, carry, separate, None, zoh=zoh)
         need = workspace_size(self.args, separate)
         self.workspace = workspace if workspace is not None else torch.empty(
             max(need, 1), dtype=torch.uint8, device=x.device)
@@ -489,7 +493,7 @@ class PreparedRoute:
 
 
 def _step_args(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, k, idx, gate, y, idx_out,
-               gate_out, y_dtype):
+               gate_out, y_dtype, zoh=False):
     _need(x, "x")
     B, D = x.shape
     E = A.shape[0]
@@ -527,16 +531,17 @@ def _step_args(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, k, idx, gate, y,
     a.A, a.dt_bias, a.Dskip, a.state, a.y = _ptr(A), _ptr(dt_bias), _ptr(Dskip), _ptr(state), \
         _ptr(y)
     a.a_form = A_SCALAR if scalar_a else A_DIAGONAL
+    a.disc = DISC_ZOH if zoh else DISC_EULER
     return a, y
 
 
 def step(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None, gate=None,
-         y=None, idx_out=None, gate_out=None, y_dtype=None, stream=None):
+         y=None, idx_out=None, gate_out=None, y_dtype=None, stream=None, zoh=False):
     """One decode step (include/swimba.h: swimba_step).  x, dt_raw [B,D];
     Bm, Cm [B,16]; state [B,D,16] f32 updated in place.  Routing from Wr [D,E]
     with top-k, or forced idx/gate [B,k].  Returns y [B,D]."""
     a, y = _step_args(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, k, idx, gate, y, idx_out,
-                      gate_out, y_dtype)
+                      gate_out, y_dtype, zoh)
     rc = load().swimba_step(ctypes.byref(a), _stream(stream))
     _check("swimba_step", rc)
     return y
@@ -547,9 +552,10 @@ class PreparedStep:
     its buffers calls the C ABI directly, without per-call checks)."""
 
     def __init__(self, x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr=None, k=None, idx=None,
-                 gate=None, y=None, idx_out=None, gate_out=None, y_dtype=None, stream=None):
+                 gate=None, y=None, idx_out=None, gate_out=None, y_dtype=None, stream=None,
+                 zoh=False):
         self.args, self.y = _step_args(x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, k, idx,
-                                       gate, y, idx_out, gate_out, y_dtype)
+                                       gate, y, idx_out, gate_out, y_dtype, zoh)
         self._keep = (x, dt_raw, Bm, Cm, A, dt_bias, Dskip, state, Wr, idx, gate, idx_out,
                       gate_out)
         self._ref = ctypes.byref(self.args)

@@ -101,7 +101,7 @@ def scan_args(**kw):
     ("B", -1, sw.EINVAL), ("L", -1, sw.EINVAL), ("chunk", -1, sw.EINVAL), ("carry", 7, sw.EINVAL),
     ("in_dtype", 5, sw.EINVAL), ("N", 8, sw.EUNSUPPORTED), ("E", 65, sw.EUNSUPPORTED),
     ("E", 17, sw.EUNSUPPORTED), ("x", None, sw.EINVAL), ("A", None, sw.EINVAL),
-    ("idx", None, sw.EINVAL), ("a_form", 2, sw.EINVAL),
+    ("idx", None, sw.EINVAL), ("a_form", 2, sw.EINVAL), ("disc", 2, sw.EINVAL),
 ])
 def test_scan_rejects(lib, field, value, status):
     a = scan_args(**{field: value})
@@ -227,6 +227,9 @@ def test_backward_rejects_and_workspace(lib):
                                         None) == status
     g = grad_args()
     g.fwd.a_form = 1
+    assert lib.swimba_scan_backward(ctypes.byref(g), None, 0, None) == sw.EUNSUPPORTED
+    g = grad_args()
+    g.fwd.disc = 1
     assert lib.swimba_scan_backward(ctypes.byref(g), None, 0, None) == sw.EUNSUPPORTED
     for E in (17,):
         g = grad_args()
