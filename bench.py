@@ -330,6 +330,26 @@ def expert_sweep(swimba, dev, reps):
     return out
 
 
+def theorem4_mode(swimba, workloads, w, x, dtr, Bm, Cm, A, bias, Dsk):
+    """Theorem 4 ("Fondements Théoriques"): relative difference between the
+    mixed and separate designs' outputs under top-1 routing that switches
+    expert with probability p per token (p = 0: constant routing, where they
+    coincide)."""
+    import torch
+    dev = x.device
+    out = {"shape": "B=%d L=%d D=%d E=%d top-1" % (w.B, w.L, w.D, w.E)}
+    for p in (0.0, 0.01, 0.1, 0.5, 1.0):
+        i, g = workloads.switching_routing(w.B, w.L, w.E, p, seed=7)
+        idx = torch.from_numpy(i).to(dev)
+        gate = torch.from_numpy(g).to(dev)
+        a = (x, dtr, Bm, Cm, idx, gate, A, bias, Dsk)
+        ym, _ = swimba.scan(*a, y_dtype=torch.float32, want_state=False)
+        ys, _ = swimba.scan_separate(*a, y_dtype=torch.float32, want_state=False)
+        d = torch.linalg.vector_norm(ym - ys) / torch.linalg.vector_norm(ys)
+        out["p%g" % p] = round(float(d), 5)
+    return out
+
+
 def backward_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, reps, ms_mixed):
     """Gradients of the mixed scan for a seeded dL/dy at the same shape (the
     whole backward call: forward recompute with the chunk records, the two
@@ -498,6 +518,7 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
     del flush
     res["expert_sweep"] = expert_sweep(swimba, dev, reps)
     res["stream_mixed"] = stream_mode(swimba, workloads, w, x, Wr, idx, gate, reps)
+    res["theorem4"] = theorem4_mode(swimba, workloads, w, x, dtr, Bm, Cm, A, bias, Dsk)
     res["backward"] = backward_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, reps,
                                     ms_mixed)
     res["scalar_a"] = scalar_a_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y, hf,
@@ -521,6 +542,22 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
             c()
 
     ms_dec = _time(run_decode, 2, warm=1)
+    # the same 128 steps captured once in a HIP graph and replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gcalls = [swimba.PreparedStep(s["x"], s["dt_raw"], s["Bm"], s["Cm"], P["A"],
+                                      P["dt_bias"], P["Dskip"], state, Wr=P["Wr"], k=wd.k, y=yd,
+                                      stream=side) for s in S]
+        for c in gcalls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for c in gcalls:
+            c()
+    ms_graph = _time(graph.replay, 3, warm=1)
     esz = 2 if wd.dtype == "bf16" else 4
     per_step_bytes = wd.B * wd.D * (2 * N_STATE * 4 + 3 * esz)
     gbs = per_step_bytes * len(S) / (ms_dec * 1e-3) / 1e9
@@ -528,7 +565,9 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
                      "us_per_step": round(ms_dec * 1e3 / len(S), 2),
                      "G_channel_steps_per_s": round(wd.B * wd.D * len(S) / ms_dec / 1e6, 3),
                      "hbm_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "note": "state (84 MB) fits the 256 MB Infinity Cache in steady state"}
+                     "graph_us_per_step": round(ms_graph * 1e3 / len(S), 2),
+                     "note": "state (84 MB) fits the 256 MB Infinity Cache in steady state; "
+                             "graph = the 128 steps captured once and replayed"}
     return res
 
 

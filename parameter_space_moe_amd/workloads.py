@@ -163,3 +163,18 @@ def generate_streams(w: Workload, k: int | None = None, B: int | None = None,
         out[name] = bf16_round(v) if w.dtype == "bf16" else v
     out["gate"] = rng.dirichlet(np.ones(k), size=(B, L)).astype(np.float32)
     return out
+
+
+def switching_routing(B: int, L: int, E: int, p: float, seed: int):
+    """Top-1 routing that switches expert with probability p per token: the
+    first token's expert is uniform over E; afterwards each token keeps the
+    previous expert with probability 1 - p, else takes one of the other
+    E - 1 uniformly.  Returns idx [B, L, 1] int32 and gate [B, L, 1] = 1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = np.empty((B, L), np.int32)
+    idx[:, 0] = rng.integers(0, E, size=B)
+    switch = rng.random((B, L)) < p
+    step = rng.integers(1, E, size=(B, L)) if E > 1 else np.zeros((B, L), np.int64)
+    for t in range(1, L):
+        idx[:, t] = np.where(switch[:, t], (idx[:, t - 1] + step[:, t]) % E, idx[:, t - 1])
+    return idx[:, :, None].copy(), np.ones((B, L, 1), np.float32)

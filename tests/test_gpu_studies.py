@@ -1,0 +1,130 @@
+"""GPU studies and variants built from the library's entry points:
+
+* Theorem 4 of "Swimba: Switch Mamba Model Scales State Space Models"
+  (French summary, "Fondements Théoriques"): the one-trajectory (mixed) and
+  per-expert (separate) designs coincide under constant top-1 routing and
+  drift apart as routing varies over time -- measured as the relative
+  difference of their outputs against the switching rate;
+* the separate-design reading in which all E experts advance at every token
+  (gates zero for the unselected), run as swimba_scan_separate with k = E and
+  dense routing, against the oracle with the same dense routing;
+* a decode loop captured once in a HIP graph and replayed, against the same
+  steps run eagerly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL_F32, dev_tensors, host, rel_err
+from parameter_space_moe_amd import swimba, workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def inputs(B, L, D, E, seed, dtype="f32"):
+    w = workloads.Workload("study", B=B, L=L, D=D, N=16, E=E, k=1, dtype=dtype, seed=seed)
+    inp = workloads.generate(w)
+    return w, inp, dev_tensors(inp, dtype, DEV)
+
+
+def divergence(t, idx, gate):
+    a = (t["x"], t["dt_raw"], t["Bm"], t["Cm"], idx, gate, t["A"], t["dt_bias"], t["Dskip"])
+    ym, _ = swimba.scan(*a, y_dtype=torch.float32)
+    ys, _ = swimba.scan_separate(*a, y_dtype=torch.float32)
+    return float(torch.linalg.vector_norm(ym - ys) / torch.linalg.vector_norm(ys))
+
+
+def test_theorem4_designs_diverge_with_switching():
+    B, L, D, E = 2, 1024, 256, 8
+    w, inp, t = inputs(B, L, D, E, seed=61)
+    d = {}
+    for p in (0.0, 0.01, 0.1, 0.5):
+        i, g = workloads.switching_routing(B, L, E, p, seed=62)
+        d[p] = divergence(t, torch.from_numpy(i).to(DEV), torch.from_numpy(g).to(DEV))
+    # constant top-1 routing: one expert runs alone in both designs
+    assert d[0.0] < 1e-5, d
+    assert d[0.01] > 1e-3 and d[0.01] < d[0.1] < d[0.5], d
+
+
+def test_theorem4_divergence_matches_oracle():
+    """The divergence itself, on a small case, from the oracle's two designs."""
+    B, L, D, E = 1, 300, 64, 4
+    w, inp, t = inputs(B, L, D, E, seed=63)
+    i, g = workloads.switching_routing(B, L, E, 0.2, seed=64)
+    got = divergence(t, torch.from_numpy(i).to(DEV), torch.from_numpy(g).to(DEV))
+    args = (inp["x"], inp["dt_raw"], inp["Bm"], inp["Cm"], i, g.astype(np.float64), inp["A"],
+            inp["dt_bias"], inp["Dskip"])
+    ym, _ = oracle.scan(*args)
+    ys, _ = oracle.scan_separate(*args)
+    want = np.linalg.norm(ym - ys) / np.linalg.norm(ys)
+    assert abs(got - want) < 1e-4 * want + 1e-6, (got, want)
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_separate_all_experts_advance(chunk):
+    """Every expert advances at every token, weighted by its gate (zero when
+    not selected): k = E with dense routing."""
+    B, L, D, E, k = 2, 300, 96, 4, 2
+    w, inp, t = inputs(B, L, D, E, seed=65)
+    idx, gate = swimba.route(t["x"], t["Wr"], k)
+    gi, gg = host(idx).astype(np.int64), host(gate)
+    dense = np.zeros((B, L, E))
+    np.put_along_axis(dense, gi, gg, axis=2)
+    didx = np.broadcast_to(np.arange(E, dtype=np.int32), (B, L, E)).copy()
+    a = (t["x"], t["dt_raw"], t["Bm"], t["Cm"], torch.from_numpy(didx).to(DEV),
+         torch.from_numpy(dense.astype(np.float32)).to(DEV), t["A"], t["dt_bias"], t["Dskip"])
+    y, hf = swimba.scan_separate(*a, chunk=chunk)
+    ry, rh = oracle.scan_separate(inp["x"], inp["dt_raw"], inp["Bm"], inp["Cm"], didx, dense,
+                                  inp["A"], inp["dt_bias"], inp["Dskip"])
+    assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
+    # differs from the design that advances only the selected experts
+    ys, _ = swimba.scan_separate(t["x"], t["dt_raw"], t["Bm"], t["Cm"], idx, gate, t["A"],
+                                 t["dt_bias"], t["Dskip"], chunk=chunk)
+    assert rel_err(host(ys), host(y)) > 1e-2
+
+
+def test_decode_graph_replay_matches_eager():
+    """16 routed decode steps captured in one graph; three replays, each from
+    the same initial state with eager work in between, against the eager run."""
+    B, D, E, k, S = 64, 512, 8, 2, 16
+    w = workloads.Workload("decode_graph", B=B, L=1, D=D, N=16, E=E, k=k, dtype="bf16", seed=66)
+    p, steps = workloads.decode_steps(w, steps=S)
+    P = {n: torch.from_numpy(v).to(DEV) for n, v in p.items()}
+    X = [{n: torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).to(DEV)
+          for n, v in s_.items()} for s_ in steps]
+    s0 = torch.randn((B, D, 16), device=DEV)
+    # eager reference
+    st = s0.clone()
+    ys = []
+    for s_ in X:
+        ys.append(swimba.step(s_["x"], s_["dt_raw"], s_["Bm"], s_["Cm"], P["A"], P["dt_bias"],
+                              P["Dskip"], st, Wr=P["Wr"], k=k).clone())
+    st_eager = st.clone()
+    # capture
+    state = s0.clone()
+    yg = [torch.empty((B, D), dtype=torch.bfloat16, device=DEV) for _ in range(S)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls = [swimba.PreparedStep(s_["x"], s_["dt_raw"], s_["Bm"], s_["Cm"], P["A"],
+                                     P["dt_bias"], P["Dskip"], state, Wr=P["Wr"], k=k, y=yg[i],
+                                     stream=side) for i, s_ in enumerate(X)]
+        for c in calls:      # warm-up on the capture stream
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for c in calls:
+            c()
+    for r in range(3):
+        state.copy_(s0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(state, st_eager), r
+        for i in range(S):
+            assert torch.equal(yg[i], ys[i]), (r, i)
+        _ = (s0 * 2).sum().item()   # eager work between replays
