@@ -33,15 +33,16 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// softplus(z) = max(z, 0) + log1p(exp(-|z|)).  log1p(e) is formed as
-// e * ln(u) / (u - 1) with u = 1 + e rounded, so that the rounding of u
-// cancels (Goldberg, "What every computer scientist should know about
-// floating-point arithmetic"): accurate to a few ulps also for e << 1, where
-// ln(1 + e) alone would keep only the bits of e that survive the add.
+// softplus(z) = max(z, 0) + log1p(exp(-|z|)).  With u = 1 + e rounded,
+// 1 + e = u - c where c = (u - 1) - e is the rounding error of u, computed
+// exactly; log1p(e) = ln(u - c) = ln(u) - c/u, and ln(u) - c is within
+// |c| e of it.  So the result keeps full relative accuracy also for e << 1,
+// where ln(u) alone would keep only the bits of e that survive the add (and
+// for e below half an ulp of 1 it returns e itself).
 __device__ __forceinline__ float softplus_f32(float z) {
   const float e = hw_exp2(-fabsf(z) * kLog2e);
   const float u = 1.0f + e;
-  const float l = u == 1.0f ? e : e * (hw_log2(u) * kLn2) * __builtin_amdgcn_rcpf(u - 1.0f);
+  const float l = fmaf(hw_log2(u), kLn2, e - (u - 1.0f));
   return fmaxf(z, 0.0f) + l;
 }
 
