@@ -518,6 +518,12 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
     del flush
     res["expert_sweep"] = expert_sweep(swimba, dev, reps)
     res["stream_mixed"] = stream_mode(swimba, workloads, w, x, Wr, idx, gate, reps)
+    zoh = swimba.PreparedScan(False, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y=y, h_final=hf,
+                              chunk=w.chunk, zoh=True)
+    ms_zoh = _time(zoh, reps)
+    res["zoh_scan"] = {"ms": round(ms_zoh, 4), "G_tc_per_s": round(tc / ms_zoh / 1e6, 3),
+                       "over_euler": round(ms_zoh / ms_mixed, 3),
+                       "note": "zero-order-hold input term, B_bar = A^-1 (exp(Delta A) - I) B"}
     res["theorem4"] = theorem4_mode(swimba, workloads, w, x, dtr, Bm, Cm, A, bias, Dsk)
     res["backward"] = backward_mode(swimba, w, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, reps,
                                     ms_mixed)
