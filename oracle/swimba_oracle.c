@@ -232,6 +232,59 @@ void ref_scan_separate(int B, int L, int D, int N, int E, int k,
   }
 }
 
+/*
+ * ref_scan_slots: the other reading of separate trajectories: one state per
+ * routing slot instead of per expert.  Slot j's state advances at every token
+ * with the parameters of the expert selected in that slot, e = idx[t,j]
+ * (its own A, dt_bias and Dskip, unmixed), and keeps its value across a change
+ * of expert; y = sum_j g_j (C_t . h_j + Dskip[e,d] x).  The gates weight the
+ * outputs only, never the states.  Where a slot keeps its expert for the whole
+ * sequence this equals the per-expert trajectories of ref_scan_separate
+ * ([SW] Spanish summary "Distinción de Diseños", French "Distinction des deux
+ * designs": the designs differ in which state a selected expert advances).
+ *   h0, h_final [B, k, D, N] (NULL allowed); other arrays as ref_scan.
+ */
+void ref_scan_slots(int B, int L, int D, int N, int E, int k,
+                    const double* x, const double* dt_raw,
+                    const double* Bm, const double* Cm, const int32_t* idx,
+                    const double* gate, const double* A,
+                    const double* dt_bias, const double* Dskip,
+                    const double* h0, double* y, double* h_final, int zoh) {
+  (void)E;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int d = 0; d < D; ++d) {
+      double* H = (double*)malloc(sizeof(double) * (size_t)k * N);
+      for (int j = 0; j < k; ++j)
+        for (int n = 0; n < N; ++n)
+          H[j * N + n] = h0 ? h0[(((int64_t)b * k + j) * D + d) * N + n] : 0.0;
+      for (int t = 0; t < L; ++t) {
+        int64_t bt = (int64_t)b * L + t;
+        double xv = x[bt * D + d];
+        double yv = 0.0;
+        for (int j = 0; j < k; ++j) {
+          const int64_t ed = (int64_t)idx[bt * k + j] * D + d;  /* (expert, channel) */
+          double Dt = softplus(dt_raw[bt * D + d] + dt_bias[ed]);
+          double yj = 0.0;
+          for (int n = 0; n < N; ++n) {
+            double Aj = A[ed * N + n];
+            H[j * N + n] = exp(Dt * Aj) * H[j * N + n] +
+                           input_coeff(Dt, Aj, zoh) * Bm[bt * N + n] * xv;
+            yj += Cm[bt * N + n] * H[j * N + n];
+          }
+          yv += gate[bt * k + j] * (yj + Dskip[ed] * xv);
+        }
+        y[bt * D + d] = yv;
+      }
+      if (h_final)
+        for (int j = 0; j < k; ++j)
+          for (int n = 0; n < N; ++n)
+            h_final[(((int64_t)b * k + j) * D + d) * N + n] = H[j * N + n];
+      free(H);
+    }
+  }
+}
+
 /* ------------------------------------------------- stream-mixed scan */
 /*
  * ref_scan_streams: the pages' own form of the mixed layer ([SW] Dutch

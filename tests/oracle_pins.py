@@ -18,6 +18,10 @@ and the mathematics fix:
   * the zero-order-hold option: the continuous equilibrium under constant
     input, the semigroup property (two half steps = one step), and the
     small-A limit where it meets Euler;
+  * per-slot trajectories (the other separate reading): each slot is the
+    mixed scan's gate-1 top-1 form of that slot's routing, its state carries
+    across expert switches, gates weight only the outputs, and constant
+    routing meets the per-expert trajectories;
   * the backward of the mixed scan against central differences of the
     forward, and the support of its gradients for a single-token loss;
   * for the stream-mixed form (shared A, mixed B X injection and C readout):
@@ -419,6 +423,88 @@ def pin_designs_differ_when_routing_varies(lib):
     # from the second token on, the mixed trajectory carries expert 0's state
     # into expert 1's update, while expert 1's own trajectory starts at zero
     assert np.min(np.max(np.abs(ys[0, 1:] - ym[0, 1:]), axis=-1)) > 1e-6, "designs should differ"
+
+
+# ----------------------------------------------------- per-slot trajectories
+def _slot_as_top1(c, j):
+    """The case routed by slot j alone, gate 1: the mixed scan's top-1 form."""
+    return {**c, "idx": np.ascontiguousarray(c["idx"][:, :, j:j + 1]),
+            "gate": np.ones(c["gate"].shape[:2] + (1,))}
+
+
+def pin_slots_are_gated_top1_scans(lib):
+    """Slot j's trajectory is the mixed scan routed by slot j alone with gate 1
+    (mixing one expert with weight 1 gives that expert's A, dt_bias and Dskip,
+    including across expert switches), and y adds the slots' outputs weighted
+    by their gates; for both input terms and with an initial state."""
+    rng = np.random.default_rng(23)
+    B, L, D, N, E, k = 2, 9, 3, 4, 4, 3
+    c = _rand_case(rng, B=B, L=L, D=D, N=N, E=E, k=k, h0=False)
+    H0 = rng.standard_normal((B, k, D, N))
+    for zoh in (False, True):
+        y, hf = oracle.scan_slots(**{**c, "h0": H0}, lib=lib, zoh=zoh)
+        want = np.zeros((B, L, D))
+        for j in range(k):
+            yj, hj = oracle.scan(**{**_slot_as_top1(c, j), "h0": H0[:, j]}, lib=lib, zoh=zoh)
+            want += c["gate"][:, :, j:j + 1] * yj
+            _close(hf[:, j], hj, 1e-13, "slot %d state (zoh=%d)" % (j, zoh))
+        _close(y, want, 1e-12, "slots y (zoh=%d)" % zoh)
+
+
+def pin_slots_state_carries_across_switch(lib):
+    """Top-1 routing e0 | e1 | e0 in blocks: the one slot's state passes from
+    each block to the next (unlike the per-expert trajectories, where e0
+    resumes its own state in block 3) -- a chain of plain scans."""
+    rng = np.random.default_rng(24)
+    B, L, D, N, E = 1, 12, 2, 3, 2
+    c = _rand_case(rng, B=B, L=L, D=D, N=N, E=E, k=1, h0=True)
+    c["gate"][:] = 1.0
+    c["idx"][:] = 0
+    c["idx"][:, 4:8] = 1
+    y, hf = oracle.scan_slots(**{**c, "h0": c["h0"][:, None]}, lib=lib)
+    h = c["h0"]
+    ys = []
+    for e, a, b in ((0, 0, 4), (1, 4, 8), (0, 8, 12)):
+        yb, h = oracle.mamba_scan(c["x"][:, a:b], c["dt_raw"][:, a:b], c["Bm"][:, a:b],
+                                  c["Cm"][:, a:b], c["A"][e], c["dt_bias"][e], c["Dskip"][e], h,
+                                  lib=lib)
+        ys.append(yb)
+    _close(y, np.concatenate(ys, 1), 1e-13, "slot switch y")
+    _close(hf[:, 0], h, 1e-13, "slot switch h")
+
+
+def pin_slots_gates_weight_outputs_only(lib):
+    """The states do not depend on the gates: scaling every gate by 3 scales y
+    by 3 and leaves h_final unchanged; a zero gate removes that slot from y
+    while its state still advances."""
+    rng = np.random.default_rng(25)
+    c = _rand_case(rng, B=1, L=8, D=3, N=4, E=3, k=2, h0=False)
+    y1, h1 = oracle.scan_slots(**c, lib=lib)
+    y3, h3 = oracle.scan_slots(**{**c, "gate": 3.0 * c["gate"]}, lib=lib)
+    _close(y3, 3.0 * y1, 1e-13, "gate scaling y")
+    _close(h3, h1, 0.0, "gate scaling h")
+    g0 = c["gate"].copy()
+    g0[:, :, 1] = 0.0
+    yz, hz = oracle.scan_slots(**{**c, "gate": g0}, lib=lib)
+    y_one, _ = oracle.scan_slots(**{**c, "idx": c["idx"][:, :, :1].copy(),
+                                    "gate": g0[:, :, :1].copy()}, lib=lib)
+    _close(yz, y_one, 1e-13, "zero-gate slot drops out of y")
+    _close(hz, h1, 0.0, "zero-gate slot still advances")
+    assert np.max(np.abs(h1[:, 1])) > 1e-3
+
+
+def pin_slots_constant_routing_equals_separate(lib):
+    """Each slot keeps one expert for the whole sequence (distinct experts):
+    slot j's trajectory is expert idx[j]'s own, so the two separate readings
+    agree on y and on those experts' states."""
+    rng = np.random.default_rng(26)
+    c = _rand_case(rng, B=2, L=9, D=3, N=4, E=4, k=2, h0=False)
+    c["idx"][:] = np.array([3, 1], np.int32)
+    ys, hs = oracle.scan_slots(**c, lib=lib)
+    ye, he = oracle.scan_separate(**c, lib=lib)
+    _close(ys, ye, 1e-13, "constant routing y")
+    _close(hs[:, 0], he[:, 3], 1e-13, "constant routing slot 0")
+    _close(hs[:, 1], he[:, 1], 1e-13, "constant routing slot 1")
 
 
 # ------------------------------------------------------------------ router

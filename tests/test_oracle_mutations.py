@@ -47,6 +47,17 @@ MUTATIONS = [
     ("separate_decays_all",
      "          ye += Dskip[(int64_t)e * D + d] * xv;",
      "          for (int o = 0; o < E; ++o) if (o != e) for (int n = 0; n < N; ++n) H[o * N + n] *= 0.5;\n          ye += Dskip[(int64_t)e * D + d] * xv;"),
+    ("slots_expert_of_slot0", "const int64_t ed = (int64_t)idx[bt * k + j] * D + d;",
+     "const int64_t ed = (int64_t)idx[bt * k + 0] * D + d;"),
+    ("slots_gate_in_state", "input_coeff(Dt, Aj, zoh)", "gate[bt * k + j] * input_coeff(Dt, Aj, zoh)"),
+    ("slots_no_Dskip", "(yj + Dskip[ed] * xv)", "(yj)"),
+    ("slots_readout_before_update",
+     "            H[j * N + n] = exp(Dt * Aj) * H[j * N + n] +\n                           input_coeff(Dt, Aj, zoh) * Bm[bt * N + n] * xv;\n            yj += Cm[bt * N + n] * H[j * N + n];",
+     "            yj += Cm[bt * N + n] * H[j * N + n];\n            H[j * N + n] = exp(Dt * Aj) * H[j * N + n] +\n                           input_coeff(Dt, Aj, zoh) * Bm[bt * N + n] * xv;"),
+    ("slots_h0_layout", "h0[(((int64_t)b * k + j) * D + d) * N + n]",
+     "h0[(((int64_t)b * D + d) * k + j) * N + n]"),
+    ("slots_reset_on_switch", "H[j * N + n] = exp(Dt * Aj) * H[j * N + n] +",
+     "H[j * N + n] = (t > 0 && idx[bt * k + j] != idx[(bt - 1) * k + j] ? 0.0 : exp(Dt * Aj) * H[j * N + n]) +"),
     ("mamba_wrong_A_index", "double An = A[(int64_t)d * N + n];", "double An = A[(int64_t)n];"),
     ("mamba_no_D", "double out = Dskip[d] * u;", "double out = 0.0;"),
     ("step_routes_first_token_only", "ref_route(B, D, E, k, x, Wr, idx, gate, NULL, NULL);",
