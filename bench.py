@@ -6,7 +6,8 @@ inputs resident in HBM.  Printed as one JSON line (rank 0):
   value    = tokens x channels per second of the whole step (G tc/s)
   roofline = the dominant kernel (the scan's chunk pass) against the VALU issue
              ceiling that bounds it, with its HBM rate against 8 TB/s beside it
-  modes    = the separate design, the dense single-expert scan (E = 1), the
+  modes    = the separate design (per expert, and per routing slot), the
+             dense single-expert scan (E = 1), the
              scan alone, and the decode step, for the "mixed vs separate" and
              "mixed vs dense" ratios; the stream-mixed form (shared A, mixed
              B X injection and C readout), the scalar-transition (Mamba-2)
@@ -488,6 +489,15 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
     res["separate_scan"] = {"ms": round(ms_sep, 4), "G_tc_per_s": round(tc / ms_sep / 1e6, 3),
                             "separate_over_mixed": round(ms_sep / ms_mixed, 3)}
     del hfs, sep
+    # separate trajectories per routing slot: k states per (b, d), each slot
+    # advancing at every token with its own expert (library's chunking)
+    hfk = torch.empty((w.B, w.k, w.D, N_STATE), dtype=torch.float32, device=dev)
+    slots = swimba.PreparedScan(swimba.DESIGN_SLOTS, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk,
+                                y=y, h_final=hfk)
+    ms_slots = _time(slots, reps)
+    res["slots_scan"] = {"ms": round(ms_slots, 4), "G_tc_per_s": round(tc / ms_slots / 1e6, 3),
+                         "slots_over_mixed": round(ms_slots / ms_mixed, 3)}
+    del hfk, slots
     # dense single-expert scan (E = 1): the plain Mamba scan on the same shapes
     idx1 = torch.zeros((w.B, w.L, 1), dtype=torch.int32, device=dev)
     gate1 = torch.ones((w.B, w.L, 1), dtype=torch.float32, device=dev)

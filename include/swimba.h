@@ -25,6 +25,9 @@
  *   separate: each expert keeps its own state; at token t each selected
  *            expert e_j advances with its own A, bias, Dskip and emits y_j;
  *            y = sum_j g_j y_j; unselected experts' states do not change.
+ *   slots:   each routing slot j keeps its own state, which advances at every
+ *            token with the parameters of the expert in slot j (unmixed) and
+ *            keeps its value when that expert changes; y = sum_j g_j y_j.
  *   streams: A shared by the experts; each selected expert's B, C and X
  *            streams arrive per routing slot; the injection
  *            Delta sum_j g_j B_j X_j and the readout vector sum_j g_j C_j
@@ -128,9 +131,11 @@ typedef struct {
                                    [E, D] with a_form SCALAR                            */
   const float* dt_bias;         /* [E, D]                                                 */
   const float* Dskip;           /* [E, D]     per-expert feed-through D                   */
-  const float* h0;              /* NULL = zeros; [B, D, N] (separate: [B, E, D, N])       */
+  const float* h0;              /* NULL = zeros; [B, D, N] (separate: [B, E, D, N];
+                                   slots: [B, k, D, N])                                   */
   void* y;                      /* [B, L, D]  out                                         */
-  float* h_final;               /* NULL = not written; [B, D, N] (separate: [B, E, D, N]) */
+  float* h_final;               /* NULL = not written; [B, D, N] (separate: [B, E, D, N];
+                                   slots: [B, k, D, N])                                   */
   int chunk;                    /* tokens per chunk; 0 = library's choice                 */
   swimba_carry carry;           /* chunk join method                                      */
   hipEvent_t* phase_events;     /* NULL, or 6 timing events: start and end of the chunk
@@ -142,21 +147,28 @@ typedef struct {
   swimba_disc disc;             /* input term: EULER (0) or ZOH                          */
 } swimba_scan_args;
 
-/*
- * swimba_scan_workspace_size -- bytes of device workspace the scan needs for
- * these arguments (0 when the sequence is one chunk).  `separate` selects
- * swimba_scan_separate's layout.  Returns 0 as well for invalid arguments;
- * the scan call itself reports those.
- */
-size_t swimba_scan_workspace_size(const swimba_scan_args* a, int separate);
+/* Which scan a workspace or plan query is for. */
+enum {
+  SWIMBA_DESIGN_MIXED = 0,    /* swimba_scan          */
+  SWIMBA_DESIGN_SEPARATE = 1, /* swimba_scan_separate */
+  SWIMBA_DESIGN_SLOTS = 2     /* swimba_scan_slots    */
+};
 
 /*
- * swimba_scan_plan -- the chunking the scan will use for these arguments:
+ * swimba_scan_workspace_size -- bytes of device workspace the scan named by
+ * `design` (SWIMBA_DESIGN_*) needs for these arguments (0 when the sequence
+ * is one chunk).  Returns 0 as well for invalid arguments or an unknown
+ * design; the scan call itself reports those.
+ */
+size_t swimba_scan_workspace_size(const swimba_scan_args* a, int design);
+
+/*
+ * swimba_scan_plan -- the chunking the scan named by `design` will use for these arguments:
  * tokens per chunk and number of chunks (both 0 when B or L is 0).  Reads
  * sizes and options only; returns the status the scan's size validation
  * would return.
  */
-int swimba_scan_plan(const swimba_scan_args* a, int separate, int* chunk, int* nchunks);
+int swimba_scan_plan(const swimba_scan_args* a, int design, int* chunk, int* nchunks);
 
 /*
  * swimba_scan -- the parameter-space-mixed selective scan: one state
@@ -180,6 +192,20 @@ int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_
  */
 int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/*
+ * swimba_scan_slots -- separate trajectories per routing slot, the other
+ * reading of the separate design ([SW] Spanish "Distinción de Diseños",
+ * French "Distinction des deux designs"): h0/h_final [B, k, D, N]; slot j's
+ * state advances at every token with the A, dt_bias and Dskip of expert
+ * idx[t, j] (not mixed) and carries over when that expert changes; y adds
+ * the slots' outputs C_t . h_j + Dskip x weighted by the gates, which never
+ * enter a state.  Where every slot keeps one expert for the whole sequence
+ * this equals swimba_scan_separate.  Workspace: swimba_scan_workspace_size
+ * with SWIMBA_DESIGN_SLOTS.  Same constraints as swimba_scan, plus k <= 4
+ * (the k x N states of a channel are held in registers).
+ */
+int swimba_scan_slots(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 
 typedef struct {
   swimba_scan_args fwd;         /* the forward call's arguments; its y, h_final,

@@ -19,9 +19,11 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 bool dtype_ok(swimba_dtype d) { return d == SWIMBA_F32 || d == SWIMBA_BF16; }
 
-// Sizes and options only (enough for the workspace query).
-int validate_scan(const swimba_scan_args* a, int separate) {
-  if (a == nullptr) return SWIMBA_EINVAL;
+// Sizes and options only (enough for the workspace query).  `design`:
+// 0 mixed, 1 separate (per expert), 2 separate per routing slot.
+int validate_scan(const swimba_scan_args* a, int design) {
+  if (a == nullptr || design < 0 || design > 2) return SWIMBA_EINVAL;
+  const bool separate = design == 1;
   if (a->B < 0 || a->L < 0 || a->D < 1 || a->N < 1 || a->E < 1 || a->k < 1 || a->k > a->E ||
       a->chunk < 0)
     return SWIMBA_EINVAL;
@@ -34,8 +36,11 @@ int validate_scan(const swimba_scan_args* a, int separate) {
   if (a->N != SWIMBA_STATE_N) return SWIMBA_EUNSUPPORTED;
   if (a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
   if (separate && a->E > 16) return SWIMBA_EUNSUPPORTED;
-  // the mixed scan stages E tables of 4.5 KiB (plus per-wave sums) in LDS
+  // the mixed and per-slot scans stage E tables of 4.5 KiB (plus per-wave
+  // sums) in LDS
   if (!separate && a->E > 16) return SWIMBA_EUNSUPPORTED;
+  // per-slot scan: k x 16 states per lane in registers
+  if (design == 2 && a->k > 4) return SWIMBA_EUNSUPPORTED;
   return SWIMBA_OK;
 }
 
@@ -125,24 +130,27 @@ void plan_layout(const ScanPlan& in, int B, int L, int D, int chunk, size_t rows
 
 }  // namespace
 
-int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p) {
-  int rc = validate_scan(a, separate);
+int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p) {
+  int rc = validate_scan(a, design);
   if (rc != SWIMBA_OK) return rc;
+  const bool separate = design == 1, slots = design == 2;
   ScanPlan q;
   q.ntiles = (a->D + 63) / 64;
-  q.waves = (!separate && a->E > 8) ? 8 : 4;
+  q.waves = (!separate && !slots && a->E > 8) ? 8 : 4;
   if (a->L == 0 || a->B == 0) {
     *p = q;
     return SWIMBA_OK;
   }
   bool small = false;  // mixed scan with too little work for four waves per SIMD
-  const int chunk = a->chunk > 0 ? a->chunk
-                                 : auto_chunk(a->B, a->L, q.ntiles, separate, a->E <= 8, &small);
-  const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N : SWIMBA_STATE_N;
+  const int chunk =
+      a->chunk > 0 ? a->chunk
+                   : auto_chunk(a->B, a->L, q.ntiles, separate, slots || a->E <= 8, &small);
+  const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N
+                               : (slots ? (size_t)a->k * SWIMBA_STATE_N : SWIMBA_STATE_N);
   plan_layout(q, a->B, a->L, a->D, chunk, rows, true, p);
   // chunks of one tile share the workgroup's expert table: 8 waves when there
   // are enough chunks to fill them (and the problem is not the small case)
-  if (!separate && p->nchunks >= 8 && !small) p->waves = 8;
+  if (!separate && !slots && p->nchunks >= 8 && !small) p->waves = 8;
   return SWIMBA_OK;
 }
 
@@ -227,17 +235,18 @@ __global__ void fill_initial_state(const float* h0, float* h, size_t n) {
   if (i < n) h[i] = h0 ? h0[i] : 0.f;
 }
 
-int empty_sequence(const swimba_scan_args* a, int separate, hipStream_t s) {
+int empty_sequence(const swimba_scan_args* a, int design, hipStream_t s) {
   if (a->h_final == nullptr || a->B == 0) return SWIMBA_OK;
-  const size_t n = (size_t)a->B * (separate ? a->E : 1) * a->D * SWIMBA_STATE_N;
+  const size_t per = design == 1 ? a->E : (design == 2 ? a->k : 1);  // trajectories
+  const size_t n = (size_t)a->B * per * a->D * SWIMBA_STATE_N;
   hipLaunchKernelGGL(fill_initial_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      a->h0, a->h_final, n);
   return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
 }
 
-int run_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t s, int separate) {
+int run_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t s, int design) {
   ScanPlan p;
-  int rc = plan_scan(a, separate, &p);
+  int rc = plan_scan(a, design, &p);
   if (rc != SWIMBA_OK) return rc;
   rc = validate_scan_pointers(a);
   if (rc != SWIMBA_OK) return rc;
@@ -248,9 +257,11 @@ int run_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t s
   if (a->B == 0 || a->L == 0) {
     if (a->phase_events)
       for (int i = 0; i < 6; ++i) (void)hipEventRecord(a->phase_events[i], s);
-    return empty_sequence(a, separate, s);
+    return empty_sequence(a, design, s);
   }
-  return separate ? launch_scan_separate(a, p, ws, s) : launch_scan(a, p, ws, s);
+  if (design == 1) return launch_scan_separate(a, p, ws, s);
+  if (design == 2) return launch_scan_slots(a, p, ws, s);
+  return launch_scan(a, p, ws, s);
 }
 
 int run_streams(const swimba_stream_args* a, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -346,15 +357,15 @@ int swimba_route(const void* x, swimba_dtype x_dtype, const float* Wr, int64_t T
   return launch_route(x, x_dtype, Wr, T, D, E, k, idx, gate, stream);
 }
 
-size_t swimba_scan_workspace_size(const swimba_scan_args* a, int separate) {
+size_t swimba_scan_workspace_size(const swimba_scan_args* a, int design) {
   ScanPlan p;
-  if (plan_scan(a, separate ? 1 : 0, &p) != SWIMBA_OK) return 0;
+  if (plan_scan(a, design, &p) != SWIMBA_OK) return 0;
   return p.bytes;
 }
 
-int swimba_scan_plan(const swimba_scan_args* a, int separate, int* chunk, int* nchunks) {
+int swimba_scan_plan(const swimba_scan_args* a, int design, int* chunk, int* nchunks) {
   ScanPlan p;
-  const int rc = plan_scan(a, separate ? 1 : 0, &p);
+  const int rc = plan_scan(a, design, &p);
   if (rc != SWIMBA_OK) return rc;
   if (chunk) *chunk = p.chunk;
   if (nchunks) *nchunks = p.nchunks;
@@ -368,6 +379,10 @@ int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_
 int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
   return run_scan(a, ws, ws_bytes, stream, 1);
+}
+
+int swimba_scan_slots(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_scan(a, ws, ws_bytes, stream, 2);
 }
 
 size_t swimba_scan_backward_workspace_size(const swimba_scan_grad_args* g) {

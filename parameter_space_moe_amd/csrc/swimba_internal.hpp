@@ -31,7 +31,8 @@ struct BwdPlan {
 };
 
 // Fills `p` for these arguments; returns a status.  Pure host arithmetic.
-int plan_scan(const swimba_scan_args* a, int separate, ScanPlan* p);
+// design: 0 mixed, 1 separate per expert, 2 separate per routing slot.
+int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p);
 int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p);
 // LDS of the backward's gradient pass (four waves): the tile's expert tables,
 // and per wave a staging ring and the dense gate vectors of its tokens.
@@ -53,6 +54,7 @@ int launch_route(const void* x, swimba_dtype xd, const float* Wr, int64_t T, int
                  int k, int32_t* idx, float* gate, hipStream_t s);
 int launch_scan(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_scan_separate(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
+int launch_scan_slots(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_step(const swimba_step_args* a, hipStream_t s);
 // Backward of the mixed scan, one launcher per (input, dL/dy) dtype pair.
 int launch_backward_ff(const swimba_scan_grad_args* g, const BwdPlan& p, void* ws, hipStream_t s);
@@ -64,7 +66,9 @@ int launch_streams_ff(const swimba_stream_args* a, const ScanPlan& p, void* ws, 
 int launch_streams_fb(const swimba_stream_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_streams_bf(const swimba_stream_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_streams_bb(const swimba_stream_args* a, const ScanPlan& p, void* ws, hipStream_t s);
-// Pass 2 of the chunked scans: carried-in state per chunk (rows = 16 or E*16).
+// Pass 2 of the chunked scans: carried-in state per chunk (rows = 16, or 16 per
+// trajectory: E * 16 per expert, k * 16 per routing slot, with E passed as the
+// trajectory count).
 int launch_carry(int B, int C, int D, int E, const float* P, float* H, float* h_final,
                  int separate, hipStream_t st, const hipEvent_t* ev);
 

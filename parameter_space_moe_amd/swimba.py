@@ -81,7 +81,7 @@ def load(path: str | None = None):
     lib.swimba_route.restype = _ci
     lib.swimba_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs), _ci]
     lib.swimba_scan_workspace_size.restype = ctypes.c_size_t
-    for fn in (lib.swimba_scan, lib.swimba_scan_separate):
+    for fn in (lib.swimba_scan, lib.swimba_scan_separate, lib.swimba_scan_slots):
         fn.argtypes = [ctypes.POINTER(ScanArgs), _vp, ctypes.c_size_t, _vp]
         fn.restype = _ci
     lib.swimba_scan_plan.argtypes = [ctypes.POINTER(ScanArgs), _ci, ctypes.POINTER(_ci),
@@ -170,7 +170,7 @@ def route(x: torch.Tensor, Wr: torch.Tensor, k: int, idx=None, gate=None, stream
 
 
 def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, chunk, carry,
-               separate, phase_events, need_y=True, zoh=False):
+               design, phase_events, need_y=True, zoh=False):
     _need(x, "x")
     if x.dim() != 3:
         raise ValueError("x must be [B, L, D]")
@@ -188,7 +188,7 @@ def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, 
     _need(A, "A", (E, D) if scalar_a else (E, D, N), torch.float32, dev)
     _need(dt_bias, "dt_bias", (E, D), torch.float32, dev)
     _need(Dskip, "Dskip", (E, D), torch.float32, dev)
-    sshape = (B, E, D, N) if separate else (B, D, N)
+    sshape = _state_shape(design, B, E, k, D, N)
     if h0 is not None:
         _need(h0, "h0", sshape, torch.float32, dev)
     if need_y:
@@ -210,29 +210,46 @@ def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, 
     return a
 
 
-def workspace_size(args: ScanArgs, separate: bool) -> int:
-    return int(load().swimba_scan_workspace_size(ctypes.byref(args), 1 if separate else 0))
+# Which scan (SWIMBA_DESIGN_* in include/swimba.h); a bool `separate` reads as
+# MIXED (False) or SEPARATE (True).
+DESIGN_MIXED, DESIGN_SEPARATE, DESIGN_SLOTS = 0, 1, 2
+_SCAN_FN = {DESIGN_MIXED: "swimba_scan", DESIGN_SEPARATE: "swimba_scan_separate",
+            DESIGN_SLOTS: "swimba_scan_slots"}
 
 
-def _scan(separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, y=None,
+def _state_shape(design, B, E, k, D, N=N_STATE):
+    """h0 / h_final shape: one state per (b, d), per (b, expert, d) or per
+    (b, slot, d)."""
+    design = int(design)
+    if design == DESIGN_SEPARATE:
+        return (B, E, D, N)
+    if design == DESIGN_SLOTS:
+        return (B, k, D, N)
+    return (B, D, N)
+
+
+def workspace_size(args: ScanArgs, design) -> int:
+    return int(load().swimba_scan_workspace_size(ctypes.byref(args), int(design)))
+
+
+def _scan(design, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, y=None,
           h_final=None, y_dtype=None, want_state=True, chunk=0, carry="auto", workspace=None,
           stream=None, phase_events=None, zoh=False):
+    design = int(design)
     if y is None:
         y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
     if h_final is None and want_state:
-        E = A.shape[0]
-        shape = (x.shape[0], E, x.shape[2], N_STATE) if separate else \
-            (x.shape[0], x.shape[2], N_STATE)
+        shape = _state_shape(design, x.shape[0], A.shape[0], idx.shape[-1], x.shape[2])
         h_final = torch.empty(shape, dtype=torch.float32, device=x.device)
     a = _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, chunk, carry,
-                   separate, phase_events, zoh=zoh)
+                   design, phase_events, zoh=zoh)
     lib = load()
-    need = workspace_size(a, separate)
+    need = workspace_size(a, design)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    fn = lib.swimba_scan_separate if separate else lib.swimba_scan
-    rc = fn(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream))
-    _check("swimba_scan_separate" if separate else "swimba_scan", rc)
+    name = _SCAN_FN[design]
+    rc = getattr(lib, name)(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(name, rc)
     return y, h_final
 
 
@@ -246,7 +263,13 @@ def scan(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
 def scan_separate(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
     """Separate design (include/swimba.h: swimba_scan_separate).  Returns
     (y [B,L,D], h_final [B,E,D,16] or None)."""
-    return _scan(True, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
+    return _scan(DESIGN_SEPARATE, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
+
+
+def scan_slots(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
+    """Separate trajectories per routing slot (include/swimba.h:
+    swimba_scan_slots).  Returns (y [B,L,D], h_final [B,k,D,16] or None)."""
+    return _scan(DESIGN_SLOTS, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
 
 
 def _grad_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0, dh_final, chunk,
@@ -338,15 +361,17 @@ def _shape_args(x, A, idx, chunk, y_dtype):
 
 
 def scan_workspace_bytes(x, A, idx, separate=False, chunk=0, y_dtype=None):
-    """Workspace bytes swimba_scan(_separate) needs for these shapes."""
+    """Workspace bytes the scan named by `separate` (a DESIGN_* value, or a
+    bool for mixed / separate) needs for these shapes."""
     return workspace_size(_shape_args(x, A, idx, chunk, y_dtype), separate)
 
 
 def scan_plan(x, A, idx, separate=False, chunk=0):
-    """(tokens per chunk, number of chunks) the scan will use (swimba_scan_plan)."""
+    """(tokens per chunk, number of chunks) the scan will use (swimba_scan_plan);
+    `separate` as in scan_workspace_bytes."""
     c, n = _ci(), _ci()
     rc = load().swimba_scan_plan(ctypes.byref(_shape_args(x, A, idx, chunk, None)),
-                                 1 if separate else 0, ctypes.byref(c), ctypes.byref(n))
+                                 int(separate), ctypes.byref(c), ctypes.byref(n))
     _check("swimba_scan_plan", rc)
     return c.value, n.value
 
@@ -358,14 +383,17 @@ class PreparedScan:
     def __init__(self, separate, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None,
                  y=None, h_final=None, chunk=0, carry="auto", workspace=None, stream=None,
                  zoh=False):
+        # separate: a DESIGN_* value, or a bool for mixed / separate
+        design = int(separate)
         self.args = _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final,
-                               chunk, carry, separate, None, zoh=zoh)
-        need = workspace_size(self.args, separate)
+                               chunk, carry, design, None, zoh=zoh)
+        need = workspace_size(self.args, design)
         self.workspace = workspace if workspace is not None else torch.empty(
             max(need, 1), dtype=torch.uint8, device=x.device)
         self._keep = (x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final)
         lib = load()
-        self._fn = lib.swimba_scan_separate if separate else lib.swimba_scan
+        self._name = _SCAN_FN[design]
+        self._fn = getattr(lib, self._name)
         self._ref = ctypes.byref(self.args)
         self._ws = self.workspace.data_ptr()
         self._wsn = self.workspace.numel()
@@ -375,7 +403,7 @@ class PreparedScan:
         self.args.phase_events = phase_events
         rc = self._fn(self._ref, self._ws, self._wsn, self.stream)
         if rc != OK:
-            raise SwimbaError("swimba_scan", rc)
+            raise SwimbaError(self._name, rc)
 
 
 def _stream_args(X, dt_raw, Bs, Cs, gate, A, dt_bias, h0, y, h_final, chunk, carry,

@@ -27,7 +27,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert {"swimba_route", "swimba_scan", "swimba_scan_separate", "swimba_step",
+    assert {"swimba_route", "swimba_scan", "swimba_scan_separate", "swimba_scan_slots",
+            "swimba_step",
             "swimba_scan_workspace_size", "swimba_status_string"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -111,6 +112,29 @@ def test_scan_rejects(lib, field, value, status):
 def test_separate_rejects_many_experts(lib):
     a = scan_args(E=17)
     assert lib.swimba_scan_separate(ctypes.byref(a), None, 0, None) == sw.EUNSUPPORTED
+
+
+def test_slots_rejects_and_workspace(lib):
+    # k slot states per lane live in registers: k <= 4
+    a = scan_args(E=8, k=5)
+    assert lib.swimba_scan_slots(ctypes.byref(a), None, 0, None) == sw.EUNSUPPORTED
+    assert lib.swimba_scan_slots(ctypes.byref(scan_args(E=17)), None, 0, None) == \
+        sw.EUNSUPPORTED
+    assert lib.swimba_scan_slots(ctypes.byref(scan_args(x=None)), None, 0, None) == sw.EINVAL
+    # workspace: k x 16 state rows per (sequence, chunk, channel), plus flags
+    a = scan_args(B=2, L=4096, D=256, E=8, k=3, chunk=512)
+    arr = 2 * 8 * 3 * 16 * 256 * 4
+    flags = 2 * 8 * 4 * 4
+    assert lib.swimba_scan_workspace_size(ctypes.byref(a), sw.DESIGN_SLOTS) == 2 * arr + flags
+    assert lib.swimba_scan_slots(ctypes.byref(a), None, 0, None) == sw.EWORKSPACE
+    # an unknown design
+    assert lib.swimba_scan_workspace_size(ctypes.byref(a), 3) == 0
+    c, n = ctypes.c_int(), ctypes.c_int()
+    assert lib.swimba_scan_plan(ctypes.byref(a), 3, ctypes.byref(c), ctypes.byref(n)) == \
+        sw.EINVAL
+    assert lib.swimba_scan_plan(ctypes.byref(a), sw.DESIGN_SLOTS, ctypes.byref(c),
+                                ctypes.byref(n)) == sw.OK
+    assert (c.value, n.value) == (512, 8)
 
 
 def test_workspace_checked_before_launch(lib):
