@@ -105,11 +105,119 @@ __host__ inline size_t smem_bytes(int E, int k, bool with_u, int waves, bool sca
          (with_u ? (size_t)waves * E * 64 * 4 : 0) + ring_bytes(k) * waves;
 }
 
+// State update and readout of one token for one lane, given the per-state
+// exponents m[n] = Delta Abar[n] log2(e) (SA: one exponent m[0]) and the
+// Euler input dx = Delta x; B_t/C_t come from ring slot `slot`, position `i`.
+template <bool TRACK, bool SA, bool ZOH>
+__device__ __forceinline__ float update_readout(const Smem& s, int slot, int i, const float* m,
+                                                float dx, float* h, float* g) {
+  const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
+  const float a0 = SA ? hw_exp2(m[0]) : 0.f;
+  const float dx0 = (SA && ZOH) ? dx * zoh_phi(a0, m[0]) : dx;
+  float yv = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 b4 = bc[q], c4 = bc[4 + q];
+    const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = 4 * q + r;
+      const float a = SA ? a0 : hw_exp2(m[n]);
+      const float inj = (ZOH && !SA) ? (dx * bv[r]) * zoh_phi(a, m[n]) : dx0 * bv[r];
+      h[n] = fmaf(a, h[n], inj);
+      yv = fmaf(cv[r], h[n], yv);
+      if (TRACK && !SA) g[n] *= a;
+    }
+  }
+  if (TRACK && SA) g[0] *= a0;
+  return yv;
+}
+
+// One token of the mixed recurrence for one lane with k == K known at compile
+// time.  Routing (experts e[j], gates gw[j]) is wave-uniform.  All of the
+// token's table reads (dt_bias/Dskip, A rows, and in the chunk pass the
+// per-expert Delta sums U) are issued first, and U is written back last:
+// the LDS write would otherwise order the A-row reads behind the softplus
+// chain, since the compiler cannot tell the two LDS regions apart.
+template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
+__device__ __forceinline__ float mix_token_k(const Smem& s, float* U, const int* e,
+                                             const float* gw, int slot, int i, int lane,
+                                             float xv, float rv, float* h, float* g) {
+  float2 bd[K];
+  float4 ar[SA ? 1 : K][4];
+  float as[K], uo[K];
+  const float* Asc = reinterpret_cast<const float*>(s.A);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    bd[j] = s.BD[e[j] * 64 + lane];
+    if constexpr (SA) {
+      as[j] = Asc[e[j] * 64 + lane];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ar[j][q] = s.A[(e[j] * 4 + q) * 64 + lane];
+    }
+    if (ACC_U) uo[j] = U[e[j] * 64 + lane];
+  }
+  // mixed dt_bias and Dskip
+  float beta = 0.f, delta = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    beta = fmaf(gw[j], bd[j].x, beta);
+    delta = fmaf(gw[j], bd[j].y, delta);
+  }
+  const float dlt = softplus_f32(rv + beta);
+  const float dl2 = dlt * kLog2e;
+  float u[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) u[j] = dl2 * gw[j];
+  // mixed exponents m[n] = sum_j u_j A[e_j, d, n]
+  float m[SA ? 1 : kN];
+  if constexpr (SA) {
+    m[0] = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) m[0] = fmaf(u[j], as[j], m[0]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 a = ar[0][q];
+      m[4 * q + 0] = u[0] * a.x;
+      m[4 * q + 1] = u[0] * a.y;
+      m[4 * q + 2] = u[0] * a.z;
+      m[4 * q + 3] = u[0] * a.w;
+    }
+#pragma unroll
+    for (int j = 1; j < K; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = ar[j][q];
+        m[4 * q + 0] = fmaf(u[j], a.x, m[4 * q + 0]);
+        m[4 * q + 1] = fmaf(u[j], a.y, m[4 * q + 1]);
+        m[4 * q + 2] = fmaf(u[j], a.z, m[4 * q + 2]);
+        m[4 * q + 3] = fmaf(u[j], a.w, m[4 * q + 3]);
+      }
+  }
+  const float yv = update_readout<TRACK, SA, ZOH>(s, slot, i, m, dlt * xv, h, g);
+  if (ACC_U) {
+    // each lane owns its column of U; an expert selected in two slots of the
+    // token takes both contributions, in slot order
+    float un[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      float base = uo[j];
+#pragma unroll
+      for (int jj = 0; jj < j; ++jj) base = e[jj] == e[j] ? un[jj] : base;
+      un[j] = base + u[j];
+      U[e[j] * 64 + lane] = un[j];
+    }
+  }
+  return fmaf(delta, xv, yv);
+}
+
 // One token of the mixed recurrence for one lane.  Routing (experts e[j],
 // gates g[j], j < k) is wave-uniform; B_t/C_t come from ring slot `slot`,
 // position `i`.  Every LDS address below depends only on (e, lane), so all of
 // a token's reads can be in flight together.
-//   K > 0: k == K known at compile time; K == 0: runtime k.
+//   K > 0: k == K known at compile time (mix_token_k); K == 0: runtime k.
 //   TRACK: also decay the carried part g (fix-up pass; with SA, g[0] is the
 //          carried part's common decay factor).
 //   ACC_U: accumulate the gate-weighted Delta per expert (chunk pass).
@@ -120,6 +228,8 @@ template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
 __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, float* U,
                                            const int* e, const float* gw, int slot, int i,
                                            int lane, float xv, float rv, float* h, float* g) {
+  if constexpr (K > 0)
+    return mix_token_k<K, TRACK, ACC_U, SA, ZOH>(s, U, e, gw, slot, i, lane, xv, rv, h, g);
   const int k = K > 0 ? K : p.k;
   // mixed dt_bias and Dskip
   float beta = 0.f, delta = 0.f;

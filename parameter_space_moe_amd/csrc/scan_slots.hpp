@@ -121,15 +121,22 @@ __device__ __forceinline__ float slot_token(const Smem& s, float* U, int E, cons
     cv[4 * q + 2] = c4.z;
     cv[4 * q + 3] = c4.w;
   }
+  // the token's table reads first; the U sums are written back last, so that
+  // no LDS write orders the A-row reads behind the softplus chain
+  float2 bdv[K];
+  float uo[K], du[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    bdv[j] = s.BD[e[j] * 64 + lane];
+    if (ACC_U) uo[j] = U[(j * E + e[j]) * 64 + lane];
+  }
   float y = 0.f;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const float2 bd = s.BD[e[j] * 64 + lane];
+    const float2 bd = bdv[j];
     const float dlt = softplus_f32(rv + bd.x);
     const float dl2 = dlt * kLog2e;
-    // each lane owns its column of U; LDS operations of a wave complete in
-    // order, so a plain read-modify-write accumulates correctly
-    if (ACC_U) U[(j * E + e[j]) * 64 + lane] += dl2;
+    du[j] = dl2;
     const float dx = dlt * xv;
     float yj = 0.f;
     if constexpr (SA) {
@@ -161,6 +168,11 @@ __device__ __forceinline__ float slot_token(const Smem& s, float* U, int E, cons
     }
     y = fmaf(gw[j], fmaf(bd.y, xv, yj), y);
   }
+  // each lane owns its column of U, and (slot, expert) rows differ between
+  // slots, so a plain read-modify-write accumulates correctly
+  if (ACC_U)
+#pragma unroll
+    for (int j = 0; j < K; ++j) U[(j * E + e[j]) * 64 + lane] = uo[j] + du[j];
   return y;
 }
 
