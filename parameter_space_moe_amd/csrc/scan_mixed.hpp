@@ -22,8 +22,8 @@
 // are joined in three passes, all exact up to fp32 rounding:
 //   1. chunk pass: every chunk from a zero state (chunk 0 from h0); it writes
 //      provisional y, its end state, and its total decay
-//      P[n] = prod_t exp(Delta_t Abar_t[n]) = exp2(sum_e U_e A[e,n] log2 e),
-//      with U_e the gate-weighted Delta of expert e summed over the chunk;
+//      P[n] = prod_t exp(Delta_t Abar_t[n]) = exp2(sum_t m_t[n]), with m_t the
+//      token's mixed exponent Delta_t Abar_t[n] log2 e, summed in registers;
 //   2. carry pass: h_in(c+1) = P(c) * h_in(c) + h_end(c), sequential over chunks;
 //   3. fix-up pass: chunk c >= 1 re-runs from h_in(c), tracking the carried part
 //      g = (prod of decays) * h_in.  With A < 0 and gates >= 0 every decay is in
@@ -68,13 +68,11 @@ struct MixParams {
   int32_t* flags;     // [B][C][ntiles] 1 = contraction not guaranteed
 };
 
-// LDS: the workgroup's expert table (64 channels), per-wave decay sums, and
-// per-wave staging rings.  With a scalar transition per (expert, channel) the
-// A table is [E][64] floats.
+// LDS: the workgroup's expert table (64 channels) and per-wave staging rings.
+// With a scalar transition per (expert, channel) the A table is [E][64] floats.
 struct Smem {
   float4* A;   // [E][4][64]  A[e, d0+lane, 4q..4q+3]  (scalar A: [E][64] floats)
   float2* BD;  // [E][64]     (dt_bias, Dskip)
-  float* U;    // [waves][E][64] (chunk pass only)
   Ring ring;   // this wave's ring
 };
 
@@ -82,8 +80,7 @@ __host__ __device__ inline size_t a_table_bytes(int E, bool scalar_a) {
   return scalar_a ? (size_t)E * 64 * 4 : (size_t)E * 4 * 64 * 16;
 }
 
-__device__ __forceinline__ Smem smem_layout(int E, int k, bool with_u, int waves, int wave,
-                                            bool scalar_a) {
+__device__ __forceinline__ Smem smem_layout(int E, int k, int wave, bool scalar_a) {
   extern __shared__ float4 smem_raw[];
   Smem s;
   char* p = reinterpret_cast<char*>(smem_raw);
@@ -91,8 +88,6 @@ __device__ __forceinline__ Smem smem_layout(int E, int k, bool with_u, int waves
   p += a_table_bytes(E, scalar_a);
   s.BD = reinterpret_cast<float2*>(p);
   p += (size_t)E * 64 * 8;
-  s.U = reinterpret_cast<float*>(p);
-  if (with_u) p += (size_t)waves * E * 64 * 4;
   p += ring_bytes(k) * wave;
   s.ring.bc = reinterpret_cast<float*>(p);
   s.ring.e = reinterpret_cast<int32_t*>(p + 2 * kTB * 32 * 4);
@@ -100,9 +95,8 @@ __device__ __forceinline__ Smem smem_layout(int E, int k, bool with_u, int waves
   return s;
 }
 
-__host__ inline size_t smem_bytes(int E, int k, bool with_u, int waves, bool scalar_a) {
-  return a_table_bytes(E, scalar_a) + (size_t)E * 64 * 8 +
-         (with_u ? (size_t)waves * E * 64 * 4 : 0) + ring_bytes(k) * waves;
+__host__ inline size_t smem_bytes(int E, int k, int waves, bool scalar_a) {
+  return a_table_bytes(E, scalar_a) + (size_t)E * 64 * 8 + ring_bytes(k) * waves;
 }
 
 // State update and readout of one token for one lane, given the per-state
@@ -135,17 +129,15 @@ __device__ __forceinline__ float update_readout(const Smem& s, int slot, int i, 
 
 // One token of the mixed recurrence for one lane with k == K known at compile
 // time.  Routing (experts e[j], gates gw[j]) is wave-uniform.  All of the
-// token's table reads (dt_bias/Dskip, A rows, and in the chunk pass the
-// per-expert Delta sums U) are issued first, and U is written back last:
-// the LDS write would otherwise order the A-row reads behind the softplus
-// chain, since the compiler cannot tell the two LDS regions apart.
+// token's table reads (dt_bias/Dskip and the A rows) are issued together.
+// ACC_U: add the token's exponents m[n] to the chunk's sums ms[n] (registers).
 template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ float mix_token_k(const Smem& s, float* U, const int* e,
+__device__ __forceinline__ float mix_token_k(const Smem& s, float* ms, const int* e,
                                              const float* gw, int slot, int i, int lane,
                                              float xv, float rv, float* h, float* g) {
   float2 bd[K];
   float4 ar[SA ? 1 : K][4];
-  float as[K], uo[K];
+  float as[K];
   const float* Asc = reinterpret_cast<const float*>(s.A);
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -156,7 +148,6 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, float* U, const int*
 #pragma unroll
       for (int q = 0; q < 4; ++q) ar[j][q] = s.A[(e[j] * 4 + q) * 64 + lane];
     }
-    if (ACC_U) uo[j] = U[e[j] * 64 + lane];
   }
   // mixed dt_bias and Dskip
   float beta = 0.f, delta = 0.f;
@@ -196,20 +187,10 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, float* U, const int*
         m[4 * q + 3] = fmaf(u[j], a.w, m[4 * q + 3]);
       }
   }
+  if (ACC_U)
+#pragma unroll
+    for (int n = 0; n < (SA ? 1 : kN); ++n) ms[n] += m[n];
   const float yv = update_readout<TRACK, SA, ZOH>(s, slot, i, m, dlt * xv, h, g);
-  if (ACC_U) {
-    // each lane owns its column of U; an expert selected in two slots of the
-    // token takes both contributions, in slot order
-    float un[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      float base = uo[j];
-#pragma unroll
-      for (int jj = 0; jj < j; ++jj) base = e[jj] == e[j] ? un[jj] : base;
-      un[j] = base + u[j];
-      U[e[j] * 64 + lane] = un[j];
-    }
-  }
   return fmaf(delta, xv, yv);
 }
 
@@ -220,16 +201,16 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, float* U, const int*
 //   K > 0: k == K known at compile time (mix_token_k); K == 0: runtime k.
 //   TRACK: also decay the carried part g (fix-up pass; with SA, g[0] is the
 //          carried part's common decay factor).
-//   ACC_U: accumulate the gate-weighted Delta per expert (chunk pass).
+//   ACC_U: add the token's exponents to the chunk's sums ms (chunk pass).
 //   SA: one transition per (expert, channel), shared by the 16 states (the
 //       Mamba-2 form A = a I): one exponential per token instead of 16.
 //   ZOH: zero-order-hold input term, zoh_phi(a) times the Euler term.
 template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, float* U,
+__device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, float* ms,
                                            const int* e, const float* gw, int slot, int i,
                                            int lane, float xv, float rv, float* h, float* g) {
   if constexpr (K > 0)
-    return mix_token_k<K, TRACK, ACC_U, SA, ZOH>(s, U, e, gw, slot, i, lane, xv, rv, h, g);
+    return mix_token_k<K, TRACK, ACC_U, SA, ZOH>(s, ms, e, gw, slot, i, lane, xv, rv, h, g);
   const int k = K > 0 ? K : p.k;
   // mixed dt_bias and Dskip
   float beta = 0.f, delta = 0.f;
@@ -252,7 +233,6 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
     float m = 0.f;
     auto a_slot = [&](int j) {
       const float u = dl2 * gw[j];
-      if (ACC_U) U[e[j] * 64 + lane] += u;
       m = fmaf(u, As[e[j] * 64 + lane], m);
     };
     if constexpr (K > 0) {
@@ -261,6 +241,7 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
     } else {
       for (int j = 0; j < k; ++j) a_slot(j);
     }
+    if (ACC_U) ms[0] += m;
     const float a = hw_exp2(m);
     const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
     const float dx = ZOH ? dlt * xv * zoh_phi(a, m) : dlt * xv;
@@ -286,10 +267,6 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
   const float dl2 = dlt * kLog2e;
   auto a_slot = [&](int j) {
     const float u = dl2 * gw[j];
-    // each lane owns its column of U, so a plain read-modify-write suffices
-    // (LDS atomics cost far more on this path); LDS operations of one wave
-    // complete in order, so repeated experts within a token still add up
-    if (ACC_U) U[e[j] * 64 + lane] += u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 a = s.A[(e[j] * 4 + q) * 64 + lane];
@@ -312,6 +289,9 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
   } else {
     for (int j = 0; j < k; ++j) a_slot(j);
   }
+  if (ACC_U)
+#pragma unroll
+    for (int n = 0; n < kN; ++n) ms[n] += m[n];
   const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
   const float dx = dlt * xv;
   float yv = 0.f;
@@ -339,7 +319,7 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
 // a fixed per-lane channel offset); the prefetch of the next block is issued
 // before the current one computes and is waited on only when it is used.
 template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U, int b, int t0,
+__device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* ms, int b, int t0,
                                      int t1, int d, bool active, bool full_tile, int lane,
                                      bool truncate, float* h, float* g, int& gate_bad) {
   constexpr int KW = (kTB * (K > 0 ? K : 16) + 63) / 64;
@@ -401,7 +381,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
             ev[j] = s.ring.e[(slot * kTB + i) * K + j];
             gv[j] = s.ring.g[(slot * kTB + i) * K + j];
           }
-          const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, U, ev, gv, slot, i, lane,
+          const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, ms, ev, gv, slot, i, lane,
                                                       to_f32(xc[i]), to_f32(rc[i]), h, g);
           stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
@@ -417,7 +397,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
               gv[j] = s.ring.g[(slot * kTB + i) * K + j];
             }
             const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
-            const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, U, ev, gv, slot, i, lane, xv, rv,
+            const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, ms, ev, gv, slot, i, lane, xv, rv,
                                                         h, g);
             if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
           }
@@ -434,7 +414,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
             gb[j] = s.ring.g[(slot * kTB + i) * k + j];
           }
           const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
-          const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, U, eb, gb, slot, i, lane, xv, rv, h,
+          const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, ms, eb, gb, slot, i, lane, xv, rv, h,
                                                       g);
           if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
         }
@@ -469,7 +449,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* U
 template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA, bool ZOH>
 __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, CHUNKED, WAVES, wave, SA);
+  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, wave, SA);
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
   const int tile = bid % p.ntiles;
@@ -480,9 +460,6 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   const bool active = d < p.D;
 
   int bad = stage::load_table(p, s.A, s.BD, d0, SA);
-  float* U = s.U + wave * p.E * 64;
-  if (CHUNKED)
-    for (int e = 0; e < p.E; ++e) U[e * 64 + lane] = 0.f;
   bad = __syncthreads_or(bad);
 
   const int c = cg * WAVES + wave;
@@ -498,37 +475,21 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   // every chunk writes y (provisional for chunks >= 1, recomputed by the
   // fix-up pass where the carried-in state still matters)
   int gate_bad = 0;
-  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH>(p, s, U, b, t0, t1, d, active, d0 + 64 <= p.D, lane, false,
-                                     h, nullptr, gate_bad);
+  // the chunk's summed exponents (SA: ms[0] only)
+  float ms[kN];
+#pragma unroll
+  for (int n = 0; n < kN; ++n) ms[n] = 0.f;
+  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH>(p, s, ms, b, t0, t1, d, active, d0 + 64 <= p.D,
+                                              lane, false, h, nullptr, gate_bad);
 
   if (CHUNKED) {
-    // total decay of the chunk: P[n] = exp2(sum_e U_e A[e, d, n])
-    float m[kN];
-#pragma unroll
-    for (int n = 0; n < kN; ++n) m[n] = 0.f;
-    if (SA) {
-      // one decay per channel, written to every state row for the carry pass
-      const float* As = reinterpret_cast<const float*>(s.A);
-      for (int e = 0; e < p.E; ++e) m[0] = fmaf(U[e * 64 + lane], As[e * 64 + lane], m[0]);
-#pragma unroll
-      for (int n = 1; n < kN; ++n) m[n] = m[0];
-    }
-    for (int e = 0; e < (SA ? 0 : p.E); ++e) {
-      float u = U[e * 64 + lane];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float4 a = s.A[(e * 4 + q) * 64 + lane];
-        m[4 * q + 0] = fmaf(u, a.x, m[4 * q + 0]);
-        m[4 * q + 1] = fmaf(u, a.y, m[4 * q + 1]);
-        m[4 * q + 2] = fmaf(u, a.z, m[4 * q + 2]);
-        m[4 * q + 3] = fmaf(u, a.w, m[4 * q + 3]);
-      }
-    }
+    // total decay of the chunk: P[n] = exp2(sum_t m_t[n]); with SA one decay
+    // per channel, written to every state row for the carry pass
     if (active) {
       const size_t base = (((size_t)b * p.nchunks + c) * kN) * p.D + d;
 #pragma unroll
       for (int n = 0; n < kN; ++n) {
-        p.P[base + (size_t)n * p.D] = hw_exp2(m[n]);
+        p.P[base + (size_t)n * p.D] = hw_exp2(ms[SA ? 0 : n]);
         p.H[base + (size_t)n * p.D] = h[n];
       }
     }
@@ -545,7 +506,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
 template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH>
 __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, false, WAVES, wave, SA);
+  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, wave, SA);
   const int nfix = p.nchunks - 1;
   const int ncg = (nfix + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
@@ -613,8 +574,8 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
   p.flags = pl.nchunks > 1 ? reinterpret_cast<int32_t*>(w + pl.off_flags) : nullptr;
 
-  const size_t smem1 = smem_bytes(p.E, p.k, true, WAVES, SA);
-  const size_t smem3 = smem_bytes(p.E, p.k, false, WAVES, SA);
+  const size_t smem1 = smem_bytes(p.E, p.k, WAVES, SA);
+  const size_t smem3 = smem1;
   const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
   if (pl.nchunks <= 1) {
     p.nchunks = 1;
