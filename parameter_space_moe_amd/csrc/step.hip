@@ -59,7 +59,10 @@ struct ChanLoads {
   TIn x, r;
 };
 
-template <typename TIn, typename TOut>
+// K > 0: k == K known at compile time (the parameter loads of a whole batch
+// are issued together); K == 0: runtime k.  SA: A is [E][D] (K > 0 only; the
+// runtime-k path reads p.scalar_a).
+template <typename TIn, typename TOut, int K, bool SA>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
   __shared__ float s_part[kStepWaves][64];
   __shared__ int s_idx[64];
@@ -225,6 +228,79 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     Cv[i] = to_f32(Cp[i]);
   }
   TOut* Y = reinterpret_cast<TOut*>(p.y) + (size_t)b * p.D;
+  if constexpr (K > 0) {
+    int ev[K];
+    float gv[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      ev[j] = s_idx[j];
+      gv[j] = s_gate[j];
+    }
+    for (int dc = dbeg; dc < dend; dc += kBatch * kStepChan) {
+      // the selected experts' parameters of this batch's channels (L2): all
+      // issued together and before the next batch's state loads, so that
+      // waiting for them leaves the state loads in flight
+      float4 av[kBatch][K];
+      float bz[kBatch][K], dk[kBatch][K];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int d = dc + u * kStepChan + cl;
+        const int dd = d < dend ? d : dbeg;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const size_t ed = (size_t)ev[j] * p.D + dd;
+          bz[u][j] = p.bias[ed];
+          dk[u][j] = p.Dsk[ed];
+          av[u][j] = SA ? make_float4(p.A[ed], 0.f, 0.f, 0.f)
+                        : *reinterpret_cast<const float4*>(p.A + ed * kN + 4 * q);
+        }
+      }
+      // the next batch (past the end: a valid, unused reload of the first
+      // channels), issued on every iteration so every path has the same
+      // loads in flight
+      ChanLoads<TIn> nxt[kBatch];
+      issue(dc + kBatch * kStepChan, nxt);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int d = dc + u * kStepChan + cl;
+        const bool active = d < dend;
+        const float xv = to_f32(cur[u].x), rv = to_f32(cur[u].r);
+        float beta = 0.f, delta = 0.f;
+        float m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          beta = fmaf(gv[j], bz[u][j], beta);
+          delta = fmaf(gv[j], dk[u][j], delta);
+          m[0] = fmaf(gv[j], av[u][j].x, m[0]);
+          m[1] = fmaf(gv[j], av[u][j].y, m[1]);
+          m[2] = fmaf(gv[j], av[u][j].z, m[2]);
+          m[3] = fmaf(gv[j], av[u][j].w, m[3]);
+        }
+        if (SA) m[1] = m[2] = m[3] = m[0];
+        const float dlt = softplus_f32(rv + beta);
+        const float dl2 = dlt * kLog2e, dx = dlt * xv;
+        float hv[4] = {cur[u].h.x, cur[u].h.y, cur[u].h.z, cur[u].h.w};
+        float yv = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = hw_exp2(dl2 * m[i]);
+          const float inj = p.zoh ? (dx * Bv[i]) * zoh_phi(a, dl2 * m[i]) : dx * Bv[i];
+          hv[i] = fmaf(a, hv[i], inj);
+          yv = fmaf(Cv[i], hv[i], yv);
+        }
+        // quad sum of the readout (lanes 4c..4c+3 hold one channel)
+        yv += __shfl_xor(yv, 1, 64);
+        yv += __shfl_xor(yv, 2, 64);
+        if (active) {
+          St[(size_t)d * 4 + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+          if (q == 0) Y[d] = from_f32<TOut>(fmaf(delta, xv, yv));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) cur[u] = nxt[u];
+    }
+    return;
+  }
   for (int dc = dbeg; dc < dend; dc += kBatch * kStepChan) {
     ChanLoads<TIn> nxt[kBatch];
     const int dn = dc + kBatch * kStepChan;
@@ -305,8 +381,17 @@ int launch_step_t(const swimba_step_args* a, hipStream_t s) {
   p.Dsk = a->Dskip;
   p.state = a->state;
   p.y = a->y;
-  hipLaunchKernelGGL((step_kernel<TIn, TOut>), dim3((unsigned)((size_t)a->B * slices)),
-                     dim3(kStepThreads), 0, s, p);
+  const dim3 grid((unsigned)((size_t)a->B * slices)), block(kStepThreads);
+  if (a->k == 1 && p.scalar_a)
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 1, true>), grid, block, 0, s, p);
+  else if (a->k == 1)
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 1, false>), grid, block, 0, s, p);
+  else if (a->k == 2 && p.scalar_a)
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 2, true>), grid, block, 0, s, p);
+  else if (a->k == 2)
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 2, false>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 0, false>), grid, block, 0, s, p);
   return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
 }
 

@@ -124,9 +124,10 @@ def test_scalar_a_separate(chunk, k):
     assert rel_err(host(hf), rh) < TOL_F32
 
 
+@pytest.mark.parametrize("k", [1, 2])
 @pytest.mark.parametrize("routed", [True, False])
-def test_scalar_a_step(routed):
-    w, inp, t = case(B=8, L=6, D=300, E=6, k=2, seed=11)
+def test_scalar_a_step(routed, k):
+    w, inp, t = case(B=8, L=6, D=300, E=6, k=k, seed=11)
     state = torch.zeros((8, 300, 16), dtype=torch.float32, device=DEV)
     rstate = np.zeros((8, 300, 16))
     Ad = diag(inp["A"])
@@ -135,16 +136,16 @@ def test_scalar_a_step(routed):
         Bs, Cs = t["Bm"][:, s].contiguous(), t["Cm"][:, s].contiguous()
         if routed:
             # the scan part is compared on the routing the GPU chose
-            io = torch.empty((8, 2), dtype=torch.int32, device=DEV)
-            go = torch.empty((8, 2), dtype=torch.float32, device=DEV)
+            io = torch.empty((8, k), dtype=torch.int32, device=DEV)
+            go = torch.empty((8, k), dtype=torch.float32, device=DEV)
             y = swimba.step(xs, rs, Bs, Cs, t["A"], t["dt_bias"], t["Dskip"], state, Wr=t["Wr"],
-                            k=2, idx_out=io, gate_out=go)
+                            k=k, idx_out=io, gate_out=go)
             ry, _, _ = oracle.step(inp["x"][:, s], inp["dt_raw"][:, s], inp["Bm"][:, s],
                                    inp["Cm"][:, s], Ad, inp["dt_bias"], inp["Dskip"], rstate,
                                    idx=host(io).astype(np.int32), gate=host(go))
         else:
-            idx = torch.from_numpy(np.array([[s % 6, (s + 1) % 6]] * 8, np.int32)).to(DEV)
-            gate = torch.from_numpy(np.array([[0.6, 0.4]] * 8, np.float32)).to(DEV)
+            idx = torch.from_numpy(np.array([[s % 6, (s + 1) % 6][:k]] * 8, np.int32)).to(DEV)
+            gate = torch.from_numpy(np.array([[0.6, 0.4][:k]] * 8, np.float32)).to(DEV)
             y = swimba.step(xs, rs, Bs, Cs, t["A"], t["dt_bias"], t["Dskip"], state, idx=idx,
                             gate=gate)
             ry, _, _ = oracle.step(inp["x"][:, s], inp["dt_raw"][:, s], inp["Bm"][:, s],
