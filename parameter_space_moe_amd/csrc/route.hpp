@@ -239,9 +239,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
 
   // transpose-reduce: at level m (32, 16, ..., 1) a lane keeps the half of its
   // values selected by its bit m and adds its partner's copy of that half; at
-  // the end lane l holds the full sum of value l.
+  // the end lane l holds the full sum of value l.  Levels 32 and 16 use the
+  // lane swap instructions (xchg_add), the others the LDS-crossbar shuffle.
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
+  for (int i = 0; i < 32; ++i) acc[i] = xchg_add<32>(acc[i], acc[i + 32]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = xchg_add<16>(acc[i], acc[i + 16]);
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) {
     const bool hi = (lane & m) != 0;
 #pragma unroll
     for (int i = 0; i < m; ++i) {

@@ -202,24 +202,26 @@ __device__ __forceinline__ void wave_transpose_sum(float* v, int lane) {
     const bool upper = (lane & mask) != 0;
 #pragma unroll
     for (int i = 0; i < half; ++i) {
-      // take both values first: otherwise the compiler turns the two selects
-      // into a lane-dependent index into v, i.e. a compare-and-select chain
-      // over the whole array
-      float lo = v[i], hi = v[half + i];
-      asm("" : "+v"(lo), "+v"(hi));
-      const float send = upper ? lo : hi;
-      const float keep = upper ? hi : lo;
-      v[i] = keep + __shfl_xor(send, mask, 64);
+      if (mask == 32) {
+        v[i] = xchg_add<32>(v[i], v[half + i]);
+      } else if (mask == 16) {
+        v[i] = xchg_add<16>(v[i], v[half + i]);
+      } else {
+        // take both values first: otherwise the compiler turns the two
+        // selects into a lane-dependent index into v, i.e. a compare-and-
+        // select chain over the whole array
+        float lo = v[i], hi = v[half + i];
+        asm("" : "+v"(lo), "+v"(hi));
+        const float send = upper ? lo : hi;
+        const float keep = upper ? hi : lo;
+        v[i] = keep + __shfl_xor(send, mask, 64);
+      }
     }
   }
   for (; mask >= 1; mask >>= 1) v[0] += __shfl_xor(v[0], mask, 64);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return wave_sum64(v); }
 
 // Grid of the chunk and gradient passes: (sequence, chunk group, tile), tile
 // fastest; wave w of a WAVES-wave workgroup takes chunk cg * WAVES + w.
@@ -675,11 +677,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
             const bool upper = (lane & mask) != 0;
 #pragma unroll
             for (int r = 0; r < half; ++r) {
-              float lo = vb[r], hi = vb[half + r];
-              asm("" : "+v"(lo), "+v"(hi));
-              const float send = upper ? lo : hi;
-              const float keep = upper ? hi : lo;
-              vb[r] = keep + __shfl_xor(send, mask, 64);
+              // masks 32 and 16 only: the lane swap exchanges
+              (void)upper;
+              vb[r] = mask == 32 ? xchg_add<32>(vb[r], vb[half + r])
+                                 : xchg_add<16>(vb[r], vb[half + r]);
             }
           }
           vb[0] += __shfl_xor(vb[0], 8, 64);

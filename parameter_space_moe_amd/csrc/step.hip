@@ -161,8 +161,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float v = part[i];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        v = wave_sum64(v);
         if (lane == 0 && eb + i < p.E) s_part[wave][eb + i] = v;
       }
     }
@@ -183,9 +182,21 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
         bool bc = free_e;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-          const float ov = __shfl_xor(bv, off, 64);
-          const int oe = __shfl_xor(be, off, 64);
-          const bool oc = __shfl_xor((int)bc, off, 64) != 0;
+          float ov;
+          int oe, oci;
+          if (off >= 16) {
+            // lane swaps (bit moves, exact for the integer fields too)
+            ov = off == 32 ? partner<32>(bv, lane) : partner<16>(bv, lane);
+            oe = __float_as_int(off == 32 ? partner<32>(__int_as_float(be), lane)
+                                          : partner<16>(__int_as_float(be), lane));
+            oci = __float_as_int(off == 32 ? partner<32>(__int_as_float((int)bc), lane)
+                                           : partner<16>(__int_as_float((int)bc), lane));
+          } else {
+            ov = __shfl_xor(bv, off, 64);
+            oe = __shfl_xor(be, off, 64);
+            oci = __shfl_xor((int)bc, off, 64);
+          }
+          const bool oc = oci != 0;
           bool take;
           if (!bc)
             take = oc;

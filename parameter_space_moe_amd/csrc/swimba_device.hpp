@@ -58,6 +58,53 @@ __device__ __forceinline__ float zoh_phi(float a, float m) {
   return lg == 0.f ? 1.f : (a - 1.f) * __builtin_amdgcn_rcpf(lg) * kLog2e;
 }
 
+// Cross-lane exchanges at lane distance M = 32 or 16 on gfx950's lane-half
+// and row swap instructions (VALU, no LDS round trip).  permlane32_swap(x, y)
+// exchanges the upper 32 lanes of x with the lower 32 lanes of y;
+// permlane16_swap(x, y) exchanges the odd 16-lane rows of x with the even
+// rows of y.
+template <int M>
+__device__ __forceinline__ void lane_swap(float x, float y, float& r0, float& r1) {
+  static_assert(M == 32 || M == 16, "swap distances are 32 and 16 lanes");
+  const uint32_t a = __float_as_uint(x), b = __float_as_uint(y);
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    r0 = __uint_as_float(r[0]);
+    r1 = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    r0 = __uint_as_float(r[0]);
+    r1 = __uint_as_float(r[1]);
+  }
+}
+
+// One transpose-reduce exchange at distance M: a lane whose bit M is clear
+// keeps `lo` and sends `hi`, the others keep `hi` and send `lo`; returns
+// keep + the partner's sent value (the two swap results hold exactly those
+// two values on every lane; the sum is the same in either order).
+template <int M>
+__device__ __forceinline__ float xchg_add(float lo, float hi) {
+  float r0, r1;
+  lane_swap<M>(lo, hi, r0, r1);
+  return r0 + r1;
+}
+
+// The value of lane (lane ^ M) for M = 32 or 16.
+template <int M>
+__device__ __forceinline__ float partner(float v, int lane) {
+  float r0, r1;
+  lane_swap<M>(v, v, r0, r1);
+  return (lane & M) ? r0 : r1;
+}
+// Sum over the 64 lanes of a wave, the same on every lane.
+__device__ __forceinline__ float wave_sum64(float v) {
+  v = xchg_add<32>(v, v);
+  v = xchg_add<16>(v, v);
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
 // Element `i` of a wave-uniform base with a 32-bit byte offset: lets the
 // backend address it as SGPR base + unsigned VGPR offset (no 64-bit math).
 template <typename T>
