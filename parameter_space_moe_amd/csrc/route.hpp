@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
   // transpose-reduce: at level m (32, 16, ..., 1) a lane keeps the half of its
   // values selected by its bit m and adds its partner's copy of that half; at
   // the end lane l holds the full sum of value l.  Levels 32 and 16 use the
-  // lane swap instructions (xchg_add), the others the LDS-crossbar shuffle.
+  // lane swap instructions (xchg_add), the others DPP permutes (xor_lane).
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = xchg_add<32>(acc[i], acc[i + 32]);
 #pragma unroll
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
     for (int i = 0; i < m; ++i) {
       const float send = hi ? acc[i] : acc[i + m];
       const float keep = hi ? acc[i + m] : acc[i];
-      acc[i] = keep + __shfl_xor(send, m, 64);
+      acc[i] = keep + xor_lane_any(send, m, lane);
     }
   }
   const int r = lane / EC, e = lane % EC;
@@ -271,9 +271,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
     int be = e;
 #pragma unroll
     for (int o = 1; o < EC; o <<= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      const bool oc = __shfl_xor((int)cand, o, 64) != 0;
+      const float ov = xor_lane_any(bv, o, lane);
+      const int oe = xor_lane_any(be, o, lane);
+      const bool oc = xor_lane_any((int)cand, o, lane) != 0;
       // the lower expert index wins unless the higher one is strictly larger
       bool take_other;
       if (!cand)

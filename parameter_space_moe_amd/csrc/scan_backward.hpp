@@ -214,11 +214,11 @@ __device__ __forceinline__ void wave_transpose_sum(float* v, int lane) {
         asm("" : "+v"(lo), "+v"(hi));
         const float send = upper ? lo : hi;
         const float keep = upper ? hi : lo;
-        v[i] = keep + __shfl_xor(send, mask, 64);
+        v[i] = keep + xor_lane_any(send, mask, lane);
       }
     }
   }
-  for (; mask >= 1; mask >>= 1) v[0] += __shfl_xor(v[0], mask, 64);
+  for (; mask >= 1; mask >>= 1) v[0] += xor_lane_any(v[0], mask, lane);
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return wave_sum64(v); }
@@ -628,10 +628,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
           mu[r] = a * lam;
         }
         // sums over the channel's four lanes
-        slb += __shfl_xor(slb, 1, 64);
-        slb += __shfl_xor(slb, 2, 64);
-        swa += __shfl_xor(swa, 1, 64);
-        swa += __shfl_xor(swa, 2, 64);
+        slb += xor_lane<1>(slb, lane);
+        slb += xor_lane<2>(slb, lane);
+        swa += xor_lane<1>(swa, lane);
+        swa += xor_lane<2>(swa, lane);
         const float dz = fmaf(xv, slb, swa) * hw_exp2((z - dlt) * kLog2e);  // dDelta sigmoid(z)
         const float gyx = gy * xv;
         if (active && q == 0) {
@@ -683,8 +683,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
                                  : xchg_add<16>(vb[r], vb[half + r]);
             }
           }
-          vb[0] += __shfl_xor(vb[0], 8, 64);
-          vb[0] += __shfl_xor(vb[0], 4, 64);
+          vb[0] += xor_lane<8>(vb[0], lane);
+          vb[0] += xor_lane<4>(vb[0], lane);
           if ((lane & 12) == 0) rr[4 * q + 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1)] = vb[0];
         }
       }

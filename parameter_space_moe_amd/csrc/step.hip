@@ -192,9 +192,9 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
             oci = __float_as_int(off == 32 ? partner<32>(__int_as_float((int)bc), lane)
                                            : partner<16>(__int_as_float((int)bc), lane));
           } else {
-            ov = __shfl_xor(bv, off, 64);
-            oe = __shfl_xor(be, off, 64);
-            oci = __shfl_xor((int)bc, off, 64);
+            ov = xor_lane_any(bv, off, lane);
+            oe = xor_lane_any(be, off, lane);
+            oci = xor_lane_any((int)bc, off, lane);
           }
           const bool oc = oci != 0;
           bool take;
@@ -300,8 +300,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
           yv = fmaf(Cv[i], hv[i], yv);
         }
         // quad sum of the readout (lanes 4c..4c+3 hold one channel)
-        yv += __shfl_xor(yv, 1, 64);
-        yv += __shfl_xor(yv, 2, 64);
+        yv += xor_lane<1>(yv, lane);
+        yv += xor_lane<2>(yv, lane);
         if (active) {
           St[(size_t)d * 4 + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
           if (q == 0) Y[d] = from_f32<TOut>(fmaf(delta, xv, yv));
@@ -351,8 +351,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
         yv = fmaf(Cv[i], hv[i], yv);
       }
       // quad sum of the readout (lanes 4c..4c+3 hold one channel)
-      yv += __shfl_xor(yv, 1, 64);
-      yv += __shfl_xor(yv, 2, 64);
+      yv += xor_lane<1>(yv, lane);
+      yv += xor_lane<2>(yv, lane);
       if (active) {
         St[(size_t)d * 4 + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
         if (q == 0) Y[d] = from_f32<TOut>(fmaf(delta, xv, yv));

@@ -96,12 +96,48 @@ __device__ __forceinline__ float partner(float v, int lane) {
   lane_swap<M>(v, v, r0, r1);
   return (lane & M) ? r0 : r1;
 }
+// A DPP lane permute of v (CTRL: the DPP control code, all rows and banks).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// The value of lane (lane ^ M), M a power of two below 64, without an LDS
+// round trip: DPP quad permutes for 1 and 2, a half-row mirror followed by a
+// quad reverse for 4, a 16-lane row rotate by 8 for 8, the lane swaps for 16
+// and 32.
+template <int M>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "xor distance");
+  if constexpr (M == 1) return dpp_mov<0xB1>(v);         // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));  // half-mirror, reverse
+  else if constexpr (M == 8) return dpp_mov<0x128>(v);   // row_ror:8
+  else return partner<M>(v, lane);
+}
+// The same for a distance known only after unrolling (constant-folded).
+__device__ __forceinline__ float xor_lane_any(float v, int m, int lane) {
+  switch (m) {
+    case 1: return xor_lane<1>(v, lane);
+    case 2: return xor_lane<2>(v, lane);
+    case 4: return xor_lane<4>(v, lane);
+    case 8: return xor_lane<8>(v, lane);
+    case 16: return xor_lane<16>(v, lane);
+    default: return xor_lane<32>(v, lane);
+  }
+}
+__device__ __forceinline__ int xor_lane_any(int v, int m, int lane) {
+  return __float_as_int(xor_lane_any(__int_as_float(v), m, lane));
+}
+
 // Sum over the 64 lanes of a wave, the same on every lane.
 __device__ __forceinline__ float wave_sum64(float v) {
   v = xchg_add<32>(v, v);
   v = xchg_add<16>(v, v);
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  v += xor_lane<8>(v, 0);
+  v += xor_lane<4>(v, 0);
+  v += xor_lane<2>(v, 0);
+  v += xor_lane<1>(v, 0);
   return v;
 }
 
