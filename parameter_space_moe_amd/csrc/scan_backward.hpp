@@ -132,6 +132,54 @@ __device__ __forceinline__ void load_rows(const BwdParams& p, size_t tok, int va
   }
 }
 
+// The same rows for a wave whose four lanes of a quad share one channel: lane
+// q of the quad holds tokens q and q + 4 of the block, and the quad exchanges
+// them through DPP broadcasts when they are used, so each lane keeps a quarter
+// of the block in registers.
+template <typename TIn, typename TDy>
+struct QuadRows {
+  static constexpr int kH = kTB / 4;
+  TIn x[kH], r[kH];
+  TDy g[kH];
+};
+
+template <typename TIn, typename TDy>
+__device__ __forceinline__ void load_quad_rows(const BwdParams& p, size_t tok, int valid,
+                                               bool active, int d, int q,
+                                               QuadRows<TIn, TDy>& o) {
+  const rsrc_t rx = stage::rows_rsrc<TIn>(p.x, tok, valid, p.D);
+  const rsrc_t rr = stage::rows_rsrc<TIn>(p.dt, tok, valid, p.D);
+  const rsrc_t rg = stage::rows_rsrc<TDy>(p.dy, tok, valid, p.D);
+#pragma unroll
+  for (int h = 0; h < QuadRows<TIn, TDy>::kH; ++h) {
+    // rows past the block's valid ones are out of the buffer's range: 0
+    const uint32_t ii = (uint32_t)(q + 4 * h);
+    const uint32_t vin = active ? ((uint32_t)d + ii * (uint32_t)p.D) * (uint32_t)sizeof(TIn)
+                                : stage::kOffNone;
+    const uint32_t vdy = active ? ((uint32_t)d + ii * (uint32_t)p.D) * (uint32_t)sizeof(TDy)
+                                : stage::kOffNone;
+    o.x[h] = stage::buf_load<TIn>(rx, vin, 0);
+    o.r[h] = stage::buf_load<TIn>(rr, vin, 0);
+    o.g[h] = stage::buf_load<TDy>(rg, vdy, 0);
+  }
+}
+
+// Token i of a QuadRows block, broadcast from the quad lane that holds it
+// (quad_perm [s,s,s,s]; i is a constant once the token loop is unrolled).
+// The half is chosen by a select, not an index: an index into the array
+// before unrolling keeps the rows in scratch memory.
+template <typename T>
+__device__ __forceinline__ float quad_token(const T* v, int i) {
+  static_assert(kTB == 8, "two tokens per quad lane");
+  const float f = to_f32(i < 4 ? v[0] : v[1]);
+  switch (i & 3) {
+    case 0: return dpp_mov<0x00>(f);
+    case 1: return dpp_mov<0x55>(f);
+    case 2: return dpp_mov<0xAA>(f);
+    default: return dpp_mov<0xFF>(f);
+  }
+}
+
 // Mixed parameters of one token for one lane: Delta, delta, beta, and the
 // mixed transition Abar[n] (natural units).
 template <int K>
@@ -499,8 +547,6 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
   const size_t row = (size_t)b * p.L;
   const size_t total = (size_t)p.B * p.L;
   constexpr int KW = (kTB * KM + 63) / 64;
-  const uint32_t off_in = active ? (uint32_t)d * (uint32_t)sizeof(TIn) : stage::kOffNone;
-  const uint32_t off_dy = active ? (uint32_t)d * (uint32_t)sizeof(TDy) : stage::kOffNone;
   auto valid_at = [&](int t) { return (int)min((size_t)kTB, total - (row + t)); };
   stage::Stager<TIn, KW> st;
   st.init(lane);
@@ -509,13 +555,16 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
   float mu[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) mu[r] = active ? p.adj[cbase + (size_t)(4 * q + r) * p.D] : 0.f;
-  float accA[EMAX][4], accB[EMAX][2];
+  // dA of every expert for this lane's four states; dbias and dDskip are the
+  // same on the four lanes of a channel, so lane q keeps them for the experts
+  // e = q, q + 4, ... only
+  float accA[EMAX][4], accB[EMAX / 4][2];
 #pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
+  for (int e = 0; e < EMAX; ++e)
 #pragma unroll
     for (int r = 0; r < 4; ++r) accA[e][r] = 0.f;
-    accB[e][0] = accB[e][1] = 0.f;
-  }
+#pragma unroll
+  for (int e4 = 0; e4 < EMAX / 4; ++e4) accB[e4][0] = accB[e4][1] = 0.f;
   // dense gate vectors of a committed ring slot: G[t][e] = sum of the gates
   // of the slots of token t that chose expert e
   auto dense_gates = [&](int sl) {
@@ -532,11 +581,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
   const int kr = kN + k;
   float* redB = p.redB + ((size_t)tile * 4 + wave) * total * kr;
   const int nblk = (t1 - t0 + kTB - 1) / kTB;
-  BlockRows<TIn, TDy> cur, nxt;
+  QuadRows<TIn, TDy> cur, nxt;
   {
     const int tb = t0 + (nblk - 1) * kTB;
     st.issue(p, row + tb, valid_at(tb), k);
-    load_rows<TIn, TDy>(p, row + tb, valid_at(tb), off_in, off_dy, true, cur);
+    load_quad_rows<TIn, TDy>(p, row + tb, valid_at(tb), active, d, q, cur);
     st.commit(ring, 0, min(kTB, t1 - tb), k, p.E, lane, gate_bad);
     dense_gates(0);
   }
@@ -547,7 +596,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
     const bool more = blk > 0;
     if (more) {
       st.issue(p, row + tb - kTB, kTB, k);
-      load_rows<TIn, TDy>(p, row + tb - kTB, kTB, off_in, off_dy, true, nxt);
+      load_quad_rows<TIn, TDy>(p, row + tb - kTB, kTB, active, d, q, nxt);
     }
     // this block's previous states h_{t-1}, all issued before the first is used
     float4 hpb[kTB];
@@ -577,17 +626,19 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
         int e[KM];
         float gw[KM];
         read_routing(ring, slot, i, k, e, gw, KM);
-        const float xv = active ? to_f32(cur.x[i]) : 0.f, rv = active ? to_f32(cur.r[i]) : 0.f;
-        const float gy = active ? to_f32(cur.g[i]) : 0.f;
+        // (inactive channels load zeros)
+        const float xv = quad_token(cur.x, i), rv = quad_token(cur.r, i);
+        const float gy = quad_token(cur.g, i);
         const float hp[4] = {hpb[i].x, hpb[i].y, hpb[i].z, hpb[i].w};
         // mixed per-channel parameters (the four lanes of a channel agree)
         float beta = 0.f, delta = 0.f;
 #pragma unroll
         for (int j = 0; j < KM; ++j) {
-          if (j >= k) break;
-          const float2 bd = sBD[e[j] * 64 + cl];
-          beta = fmaf(gw[j], bd.x, beta);
-          delta = fmaf(gw[j], bd.y, delta);
+          if (j < k) {
+            const float2 bd = sBD[e[j] * 64 + cl];
+            beta = fmaf(gw[j], bd.x, beta);
+            delta = fmaf(gw[j], bd.y, delta);
+          }
         }
         const float z = rv + beta;
         const float dlt = softplus_f32(z);
@@ -652,19 +703,21 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
               const float gd = gv[u] * dlt;
 #pragma unroll
               for (int r = 0; r < 4; ++r) accA[ee][r] = fmaf(gd, w[r], accA[ee][r]);
-              accB[ee][0] = fmaf(gv[u], dz, accB[ee][0]);
-              accB[ee][1] = fmaf(gv[u], gyx, accB[ee][1]);
             }
+            // this lane's expert of the group: e = 4 e4 + q
+            const float gq = q == 0 ? gv[0] : (q == 1 ? gv[1] : (q == 2 ? gv[2] : gv[3]));
+            accB[e4][0] = fmaf(gq, dz, accB[e4][0]);
+            accB[e4][1] = fmaf(gq, gyx, accB[e4][1]);
           }
         }
 #pragma unroll
         for (int j = 0; j < KM; ++j) {
-          if (j >= k) break;
-              const int ej = e[j];
-          const float2 bd = sBD[ej * 64 + cl];
-          const float part = fmaf(dlt, sa[j], q == 0 ? fmaf(bd.x, dz, bd.y * gyx) : 0.f);
-          const float sj = wave_sum(part);
-          if (lane == j) rr[kN + j] = sj;
+          if (j < k) {
+            const float2 bd = sBD[e[j] * 64 + cl];
+            const float part = fmaf(dlt, sa[j], q == 0 ? fmaf(bd.x, dz, bd.y * gyx) : 0.f);
+            const float sj = wave_sum(part);
+            if (lane == j) rr[kN + j] = sj;
+          }
         }
         // dB terms summed over the wave's 16 channels: lanes of equal q hold
         // the same states; after two halving exchanges (masks 32, 16) and two
@@ -695,8 +748,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
       cur = nxt;
     }
   }
-  // per-(sequence, chunk) parameter-gradient partials (the four lanes of a
-  // channel hold the same dbias and dDskip sums; lane q = 0 stores them)
+  // per-(sequence, chunk) parameter-gradient partials (lane q stores the dbias
+  // and dDskip sums of the experts it kept)
   if (active) {
     const size_t slotbc = (size_t)b * p.nchunks + c;
 #pragma unroll
@@ -704,10 +757,14 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
       if (e < p.E) {
         reinterpret_cast<float4*>(p.pA)[((slotbc * p.E + e) * p.D + d) * 4 + q] =
             make_float4(accA[e][0], accA[e][1], accA[e][2], accA[e][3]);
-        if (q == 0) {
-          p.pBD[((slotbc * p.E + e) * 2) * p.D + d] = accB[e][0];
-          p.pBD[((slotbc * p.E + e) * 2 + 1) * p.D + d] = accB[e][1];
-        }
+      }
+    }
+#pragma unroll
+    for (int e4 = 0; e4 < EMAX / 4; ++e4) {
+      const int e = 4 * e4 + q;
+      if (e < p.E) {
+        p.pBD[((slotbc * p.E + e) * 2) * p.D + d] = accB[e4][0];
+        p.pBD[((slotbc * p.E + e) * 2 + 1) * p.D + d] = accB[e4][1];
       }
     }
   }
