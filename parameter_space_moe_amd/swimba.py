@@ -148,6 +148,15 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def _hold(stream, *tensors):
+    """Temporaries allocated here for a call on the caller's stream: the
+    caching allocator must not hand them out again before that stream's
+    work has run (allocation is ordered on the current stream only)."""
+    if stream is not None:
+        for t in tensors:
+            t.record_stream(stream)
+
+
 def route(x: torch.Tensor, Wr: torch.Tensor, k: int, idx=None, gate=None, stream=None):
     """Top-k router: x [..., D] (f32/bf16), Wr [D, E] f32 -> idx [..., k] int32,
     gate [..., k] f32 (include/swimba.h: swimba_route)."""
@@ -247,6 +256,7 @@ def _scan(design, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, y=No
     need = workspace_size(a, design)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        _hold(stream, workspace)
     name = _SCAN_FN[design]
     rc = getattr(lib, name)(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(name, rc)
@@ -319,6 +329,7 @@ def scan_backward(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0=None, 
     need = int(lib.swimba_scan_backward_workspace_size(ctypes.byref(g)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        _hold(stream, workspace)
     rc = lib.swimba_scan_backward(ctypes.byref(g), _ptr(workspace), workspace.numel(),
                                   _stream(stream))
     _check("swimba_scan_backward", rc)
@@ -454,6 +465,7 @@ def scan_streams(X, dt_raw, Bs, Cs, gate, A, dt_bias, h0=None, y=None, h_final=N
     need = int(lib.swimba_scan_streams_workspace_size(ctypes.byref(a)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+        _hold(stream, workspace)
     rc = lib.swimba_scan_streams(ctypes.byref(a), _ptr(workspace), workspace.numel(),
                                  _stream(stream))
     _check("swimba_scan_streams", rc)
