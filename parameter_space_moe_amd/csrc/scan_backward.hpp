@@ -472,11 +472,13 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_state_kernel(BwdParams p) {
         }
       }
       const size_t bt = row + tb + i;
+      // stored as [token][4][D] float4 (plane q: states 4q..4q+3), so that
+      // each store of the wave covers 1 KiB of consecutive channels
       if (active) {
-        float4* dst = hs4 + (bt * (size_t)p.D + d) * 4;
+        float4* dst = hs4 + bt * 4 * (size_t)p.D + d;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          dst[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+          dst[(size_t)q * p.D] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
       }
       // dC terms dy h_t, summed over the tile's channels
       const float gy = active ? to_f32(cur.g[i]) : 0.f;
@@ -606,7 +608,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
       const int t = tb + i;
       if (active && i < n) {
         if (t > t0)
-          hpb[i] = hs4[((row + t - 1) * (size_t)p.D + d) * 4 + q];
+          hpb[i] = hs4[((row + t - 1) * 4 + q) * (size_t)p.D + d];
         else if (c > 0)
           hpb[i] = make_float4(p.H[cbase + (size_t)(4 * q) * p.D],
                                p.H[cbase + (size_t)(4 * q + 1) * p.D],
