@@ -85,9 +85,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     for (int u = 0; u < kBatch; ++u) {
       const int d = dc + u * kStepChan + cl;
       const int dd = d < dend ? d : dbeg;
-      L[u].h = St[(size_t)dd * 4 + q];
-      L[u].x = X[dd];
-      L[u].r = R[dd];
+      // 32-bit offsets from the row's base (no 64-bit address arithmetic)
+      L[u].h = at32(St, (uint32_t)dd * 4 + q);
+      L[u].x = at32(X, (uint32_t)dd);
+      L[u].r = at32(R, (uint32_t)dd);
     }
   };
   ChanLoads<TIn> cur[kBatch];
@@ -244,8 +245,20 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     float gv[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      ev[j] = s_idx[j];
-      gv[j] = s_gate[j];
+      ev[j] = uniform(s_idx[j]);
+      gv[j] = uniform(s_gate[j]);
+    }
+    // the selected experts' rows (wave-uniform bases)
+    const float* bzr[K];
+    const float* dkr[K];
+    const float* asr[K];
+    const float4* avr[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      bzr[j] = p.bias + (size_t)ev[j] * p.D;
+      dkr[j] = p.Dsk + (size_t)ev[j] * p.D;
+      asr[j] = p.A + (size_t)ev[j] * p.D;
+      avr[j] = reinterpret_cast<const float4*>(p.A + (size_t)ev[j] * p.D * kN);
     }
     for (int dc = dbeg; dc < dend; dc += kBatch * kStepChan) {
       // the selected experts' parameters of this batch's channels (L2): all
@@ -259,11 +272,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
         const int dd = d < dend ? d : dbeg;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-          const size_t ed = (size_t)ev[j] * p.D + dd;
-          bz[u][j] = p.bias[ed];
-          dk[u][j] = p.Dsk[ed];
-          av[u][j] = SA ? make_float4(p.A[ed], 0.f, 0.f, 0.f)
-                        : *reinterpret_cast<const float4*>(p.A + ed * kN + 4 * q);
+          bz[u][j] = at32(bzr[j], (uint32_t)dd);
+          dk[u][j] = at32(dkr[j], (uint32_t)dd);
+          av[u][j] = SA ? make_float4(at32(asr[j], (uint32_t)dd), 0.f, 0.f, 0.f)
+                        : at32(avr[j], (uint32_t)dd * 4 + q);
         }
       }
       // the next batch (past the end: a valid, unused reload of the first
@@ -292,19 +304,27 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
         const float dl2 = dlt * kLog2e, dx = dlt * xv;
         float hv[4] = {cur[u].h.x, cur[u].h.y, cur[u].h.z, cur[u].h.w};
         float yv = 0.f;
+        // the input term is chosen once per channel, not per state
+        if (p.zoh) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = hw_exp2(dl2 * m[i]);
-          const float inj = p.zoh ? (dx * Bv[i]) * zoh_phi(a, dl2 * m[i]) : dx * Bv[i];
-          hv[i] = fmaf(a, hv[i], inj);
-          yv = fmaf(Cv[i], hv[i], yv);
+          for (int i = 0; i < 4; ++i) {
+            const float a = hw_exp2(dl2 * m[i]);
+            hv[i] = fmaf(a, hv[i], (dx * Bv[i]) * zoh_phi(a, dl2 * m[i]));
+            yv = fmaf(Cv[i], hv[i], yv);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[i] = fmaf(hw_exp2(dl2 * m[i]), hv[i], dx * Bv[i]);
+            yv = fmaf(Cv[i], hv[i], yv);
+          }
         }
         // quad sum of the readout (lanes 4c..4c+3 hold one channel)
         yv += xor_lane<1>(yv, lane);
         yv += xor_lane<2>(yv, lane);
         if (active) {
-          St[(size_t)d * 4 + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
-          if (q == 0) Y[d] = from_f32<TOut>(fmaf(delta, xv, yv));
+          at32(St, (uint32_t)d * 4 + q) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+          if (q == 0) at32(Y, (uint32_t)d) = from_f32<TOut>(fmaf(delta, xv, yv));
         }
       }
 #pragma unroll
