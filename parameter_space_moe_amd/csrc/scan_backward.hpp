@@ -75,18 +75,17 @@ struct BwdParams {
   float* pBD;     // [B*C][E][2][D] per-(sequence, chunk) dbias, dDskip
 };
 
-// LDS of a chunk-pass or state-pass workgroup: the tile's expert table, the
-// chunk pass's per-wave decay sums and the per-wave rings.
+// LDS of a chunk-pass or state-pass workgroup: the tile's expert table and
+// the per-wave rings.
 struct Smem {
   float4* A;      // [E][4][64]
   float2* BD;     // [E][64]
-  float* U;       // [waves][E][64]
   Ring ring;
 };
 
 __host__ __device__ inline size_t table_bytes(int E) { return (size_t)E * (4 * 64 * 16 + 64 * 8); }
 __host__ inline size_t smem_bytes(int E, int k, int waves) {
-  return table_bytes(E) + (size_t)waves * E * 64 * 4 + ring_bytes(k) * waves;
+  return table_bytes(E) + ring_bytes(k) * waves;
 }
 
 __device__ __forceinline__ Smem smem_layout(int E, int k, int waves, int wave) {
@@ -97,8 +96,6 @@ __device__ __forceinline__ Smem smem_layout(int E, int k, int waves, int wave) {
   p += (size_t)E * 4 * 64 * 16;
   s.BD = reinterpret_cast<float2*>(p);
   p += (size_t)E * 64 * 8;
-  s.U = reinterpret_cast<float*>(p);
-  p += (size_t)waves * E * 64 * 4;
   p += ring_bytes(k) * wave;
   s.ring.bc = reinterpret_cast<float*>(p);
   s.ring.e = reinterpret_cast<int32_t*>(p + 2 * kTB * 32 * 4);
@@ -180,8 +177,8 @@ __device__ __forceinline__ float quad_token(const T* v, int i) {
   }
 }
 
-// Mixed parameters of one token for one lane: Delta, delta, beta, and the
-// mixed transition Abar[n] (natural units).
+// Mixed scalars of one token for one lane: Delta, its argument z, and delta
+// (the mixed transition exponents come from mix_abar).
 template <int K>
 struct Mix {
   float dlt, z, delta;
@@ -206,6 +203,8 @@ __device__ __forceinline__ Mix<K> mix_scalars(const Smem& s, const int* e, const
   return m;
 }
 
+// ab[n] = sum_j w_j A[e_j, d, n] for one lane's channel d; the callers pass
+// w_j = Delta log2(e) g_j, so ab is the exponent of the token's decays.
 template <int K>
 __device__ __forceinline__ void mix_abar(const Smem& s, const int* e, const float* gw, int k,
                                          int lane, float* ab) {
@@ -298,8 +297,6 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_chunk_kernel(BwdParams p) {
   const int d0 = tk.tile * 64, d = d0 + lane;
   const bool active = d < p.D;
   int bad = stage::load_table(p, s.A, s.BD, d0, false);
-  float* U = s.U + wave * p.E * 64;
-  for (int e = 0; e < p.E; ++e) U[e * 64 + lane] = 0.f;
   bad = __syncthreads_or(bad);
   (void)bad;
   if (tk.c >= p.nchunks) return;  // no barrier below
@@ -344,14 +341,13 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_chunk_kernel(BwdParams p) {
       const float xv = active ? to_f32(cur.x[i]) : 0.f, rv = active ? to_f32(cur.r[i]) : 0.f;
       const float gy = active ? to_f32(cur.g[i]) : 0.f;
       const Mix<K> mx = mix_scalars<K>(s, e, gw, k, lane, rv);
-      float ab[kN];
-      mix_abar<K>(s, e, gw, k, lane, ab);
+      // mixed exponents m[n] = sum_j (Delta log2(e) g_j) A[e_j, d, n]
       const float dl2 = mx.dlt * kLog2e;
+      float u[K > 0 ? K : 16];
 #pragma unroll
-      for (int j = 0; j < (K > 0 ? K : 16); ++j) {
-        if (j >= k) break;
-        U[e[j] * 64 + lane] += dl2 * gw[j];
-      }
+      for (int j = 0; j < (K > 0 ? K : 16); ++j) u[j] = dl2 * gw[j];
+      float mexp[kN];
+      mix_abar<K>(s, e, u, k, lane, mexp);
       const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
       const float dx = mx.dlt * xv;
 #pragma unroll
@@ -361,7 +357,7 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int nn = 4 * q + r;
-          const float a = hw_exp2(dl2 * ab[nn]);
+          const float a = hw_exp2(mexp[nn]);
           h[nn] = fmaf(a, h[nn], dx * bv[r]);
           G[nn] *= a;
           S[nn] = fmaf(G[nn], cv[r] * gy, S[nn]);
@@ -374,25 +370,11 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_chunk_kernel(BwdParams p) {
     }
   }
   if (!active) return;
-  // chunk decay exp2(sum_e U_e A[e, d, n])
-  float m[kN];
-#pragma unroll
-  for (int nn = 0; nn < kN; ++nn) m[nn] = 0.f;
-  for (int e = 0; e < p.E; ++e) {
-    const float u = U[e * 64 + lane];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 a = s.A[(e * 4 + q) * 64 + lane];
-      m[4 * q + 0] = fmaf(u, a.x, m[4 * q + 0]);
-      m[4 * q + 1] = fmaf(u, a.y, m[4 * q + 1]);
-      m[4 * q + 2] = fmaf(u, a.z, m[4 * q + 2]);
-      m[4 * q + 3] = fmaf(u, a.w, m[4 * q + 3]);
-    }
-  }
+  // the chunk decay P = prod_t a_t is the running product G
   const size_t base = (((size_t)tk.b * p.nchunks + tk.c) * kN) * p.D + d;
 #pragma unroll
   for (int nn = 0; nn < kN; ++nn) {
-    p.P[base + (size_t)nn * p.D] = hw_exp2(m[nn]);
+    p.P[base + (size_t)nn * p.D] = G[nn];
     p.H[base + (size_t)nn * p.D] = h[nn];
     p.adj[base + (size_t)nn * p.D] = S[nn];
   }
@@ -457,9 +439,13 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_state_kernel(BwdParams p) {
       read_routing(s.ring, slot, i, k, e, gw, KM);
       const float xv = active ? to_f32(cur.x[i]) : 0.f, rv = active ? to_f32(cur.r[i]) : 0.f;
       const Mix<K> mx = mix_scalars<K>(s, e, gw, k, lane, rv);
-      float ab[kN];
-      mix_abar<K>(s, e, gw, k, lane, ab);
+      // mixed exponents m[n] = sum_j (Delta log2(e) g_j) A[e_j, d, n]
       const float dl2 = mx.dlt * kLog2e, dx = mx.dlt * xv;
+      float u[KM];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) u[j] = dl2 * gw[j];
+      float mexp[kN];
+      mix_abar<K>(s, e, u, k, lane, mexp);
       const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -468,7 +454,7 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int nn = 4 * q + r;
-          h[nn] = fmaf(hw_exp2(dl2 * ab[nn]), h[nn], dx * bv[r]);
+          h[nn] = fmaf(hw_exp2(mexp[nn]), h[nn], dx * bv[r]);
         }
       }
       const size_t bt = row + tb + i;

@@ -41,10 +41,10 @@ inline size_t backward_grad_lds_bytes(int E, int k) {
   return (size_t)E * 64 * 16 * 4 + (size_t)E * 64 * 8 +
          4 * ((size_t)2 * 8 * 32 * 4 + (size_t)2 * 2 * 8 * k * 4 + (size_t)2 * 8 * emax * 4);
 }
-// LDS of the backward's chunk and state passes: expert table, per-wave decay
-// sums and one staging ring per wave.
+// LDS of the backward's chunk and state passes: expert table and one staging
+// ring per wave.
 inline size_t backward_lds_bytes(int E, int k, int waves) {
-  return (size_t)E * (4 * 64 * 16 + 64 * 8) + (size_t)waves * E * 64 * 4 +
+  return (size_t)E * (4 * 64 * 16 + 64 * 8) +
          (size_t)waves * ((size_t)2 * 8 * 32 * 4 + (size_t)2 * 2 * 8 * k * 4);
 }
 int plan_streams(const swimba_stream_args* a, ScanPlan* p);
