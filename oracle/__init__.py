@@ -53,13 +53,14 @@ def load(path: str | None = None):
     lib.ref_scan.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7 + [ci]
     lib.ref_scan_separate.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7 + [ci]
     lib.ref_scan_slots.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7 + [ci]
+    lib.ref_scan_all_experts.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 7 + [ci]
     lib.ref_mamba_scan.argtypes = [ci] * 4 + [_f64p] * 10 + [ci]
     lib.ref_scan_streams.argtypes = [ci] * 5 + [_f64p] * 10
     lib.ref_scan_backward.argtypes = [ci] * 6 + [_f64p] * 4 + [_i32p] + [_f64p] * 16
     lib.ref_step.argtypes = [ci] * 5 + [_f64p] * 5 + [_i32p] + [_f64p] * 6 + [_i32p, _f64p, ci]
     lib.ref_num_threads.restype = ci
     for f in (lib.ref_route, lib.ref_scan, lib.ref_scan_separate, lib.ref_scan_slots,
-              lib.ref_mamba_scan,
+              lib.ref_scan_all_experts, lib.ref_mamba_scan,
               lib.ref_scan_streams, lib.ref_scan_backward, lib.ref_step):
         f.restype = None
     if path is None:
@@ -151,6 +152,15 @@ def scan_slots(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, lib=Non
     k = np.shape(idx)[2]
     return _scan_common(lib.ref_scan_slots, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias,
                         Dskip, h0, lambda B, E, D, N: (B, k, D, N), zoh)
+
+
+def scan_all_experts(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, lib=None,
+                     zoh=False):
+    """Separate trajectories where every expert advances at every token; the
+    routing picks whose outputs are mixed.  h0, h_final [B,E,D,N]."""
+    lib = lib or load()
+    return _scan_common(lib.ref_scan_all_experts, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias,
+                        Dskip, h0, lambda B, E, D, N: (B, E, D, N), zoh)
 
 
 def scan_backward(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0=None, dh_final=None,

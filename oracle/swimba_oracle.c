@@ -285,6 +285,63 @@ void ref_scan_slots(int B, int L, int D, int N, int E, int k,
   }
 }
 
+/*
+ * ref_scan_all_experts: the third reading of separate trajectories: every
+ * expert keeps a state per channel and advances it at every token with its
+ * own parameters, whether or not the router selected it; the router only
+ * chooses whose outputs the token mixes, y = sum_j g_j y_{idx[t,j]} with
+ * y_e = C_t . h_e + Dskip[e,d] x.  Each expert's trajectory is therefore a
+ * plain selective scan with that expert's parameters, independent of the
+ * routing, and the cost is E state updates per token instead of k
+ * ([SW] Spanish summary "Distinción de Diseños", French "Distinction des
+ * deux designs": separate SSMs, one per expert).
+ *   h0, h_final [B, E, D, N] (NULL allowed); other arrays as ref_scan.
+ */
+void ref_scan_all_experts(int B, int L, int D, int N, int E, int k,
+                          const double* x, const double* dt_raw,
+                          const double* Bm, const double* Cm, const int32_t* idx,
+                          const double* gate, const double* A,
+                          const double* dt_bias, const double* Dskip,
+                          const double* h0, double* y, double* h_final, int zoh) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int d = 0; d < D; ++d) {
+      double* S = (double*)malloc(sizeof(double) * (size_t)E * N);  /* states [E][N] */
+      double* out = (double*)malloc(sizeof(double) * (size_t)E);     /* y_e of token t */
+      for (int e = 0; e < E; ++e)
+        for (int n = 0; n < N; ++n)
+          S[e * N + n] = h0 ? h0[(((int64_t)b * E + e) * D + d) * N + n] : 0.0;
+      for (int t = 0; t < L; ++t) {
+        const int64_t bt = (int64_t)b * L + t;
+        const double u = x[bt * D + d];
+        /* every expert advances */
+        for (int e = 0; e < E; ++e) {
+          const int64_t ed = (int64_t)e * D + d;
+          const double step = softplus(dt_raw[bt * D + d] + dt_bias[ed]);
+          double acc = Dskip[ed] * u;
+          for (int n = 0; n < N; ++n) {
+            const double an = A[ed * N + n];
+            S[e * N + n] = exp(step * an) * S[e * N + n] +
+                           input_coeff(step, an, zoh) * Bm[bt * N + n] * u;
+            acc += Cm[bt * N + n] * S[e * N + n];
+          }
+          out[e] = acc;
+        }
+        /* the selected outputs, gate-weighted, in slot order */
+        double yv = 0.0;
+        for (int j = 0; j < k; ++j) yv += gate[bt * k + j] * out[idx[bt * k + j]];
+        y[bt * D + d] = yv;
+      }
+      if (h_final)
+        for (int e = 0; e < E; ++e)
+          for (int n = 0; n < N; ++n)
+            h_final[(((int64_t)b * E + e) * D + d) * N + n] = S[e * N + n];
+      free(out);
+      free(S);
+    }
+  }
+}
+
 /* ------------------------------------------------- stream-mixed scan */
 /*
  * ref_scan_streams: the pages' own form of the mixed layer ([SW] Dutch

@@ -507,6 +507,66 @@ def pin_slots_constant_routing_equals_separate(lib):
     _close(hs[:, 1], he[:, 1], 1e-13, "constant routing slot 1")
 
 
+# ----------------------------------------------- every expert advances
+def _plain_scans(c, H0, lib, zoh):
+    """Each expert's plain selective scan over the whole sequence (the
+    independently written ref_mamba_scan): outputs [B,L,D,E], states [B,E,D,N]."""
+    E = c["A"].shape[0]
+    ys, hs = [], []
+    for e in range(E):
+        ye, he = oracle.mamba_scan(c["x"], c["dt_raw"], c["Bm"], c["Cm"], c["A"][e],
+                                   c["dt_bias"][e], c["Dskip"][e], H0[:, e], lib=lib, zoh=zoh)
+        ys.append(ye)
+        hs.append(he)
+    return np.stack(ys, -1), np.stack(hs, 1)
+
+
+def pin_all_experts_are_plain_scans(lib):
+    """Every expert's trajectory is the plain scan with that expert's own
+    parameters over all tokens, and y gathers the selected experts' outputs
+    of those scans weighted by the gates (repeated experts add up); both
+    input terms, with an initial state."""
+    rng = np.random.default_rng(27)
+    B, L, D, N, E, k = 2, 9, 3, 4, 4, 3
+    c = _rand_case(rng, B=B, L=L, D=D, N=N, E=E, k=k, h0=False)
+    c["idx"][0, 2] = np.array([1, 1, 3], np.int32)   # a repeated expert
+    H0 = rng.standard_normal((B, E, D, N))
+    for zoh in (False, True):
+        y, hf = oracle.scan_all_experts(**{**c, "h0": H0}, lib=lib, zoh=zoh)
+        ye, he = _plain_scans(c, H0, lib, zoh)
+        want = np.zeros((B, L, D))
+        for j in range(k):
+            pick = np.take_along_axis(ye, c["idx"][:, :, None, j:j + 1].astype(np.int64), -1)[..., 0]
+            want += c["gate"][:, :, j:j + 1] * pick
+        _close(hf, he, 1e-13, "all-experts states (zoh=%d)" % zoh)
+        _close(y, want, 1e-12, "all-experts y (zoh=%d)" % zoh)
+
+
+def pin_all_experts_states_ignore_routing(lib):
+    """The routing decides only which outputs are mixed: two unrelated
+    routings give the same final states and different outputs."""
+    rng = np.random.default_rng(28)
+    c = _rand_case(rng, B=1, L=10, D=3, N=4, E=4, k=2, h0=False)
+    y1, h1 = oracle.scan_all_experts(**c, lib=lib)
+    c2 = _rand_case(np.random.default_rng(29), B=1, L=10, D=3, N=4, E=4, k=2, h0=False)
+    y2, h2 = oracle.scan_all_experts(**{**c, "idx": c2["idx"], "gate": c2["gate"]}, lib=lib)
+    _close(h2, h1, 0.0, "states independent of routing")
+    assert np.max(np.abs(y2 - y1)) > 1e-3
+
+
+def pin_all_experts_full_routing_equals_separate(lib):
+    """With k = E and every expert selected at every token, the per-expert
+    trajectories (advanced when selected) advance at every token too, so
+    the two readings agree on y and on every state."""
+    rng = np.random.default_rng(30)
+    c = _rand_case(rng, B=2, L=8, D=3, N=4, E=3, k=3, h0=False)
+    H0 = rng.standard_normal((2, 3, 3, 4))
+    ya, ha = oracle.scan_all_experts(**{**c, "h0": H0}, lib=lib)
+    ys, hs = oracle.scan_separate(**{**c, "h0": H0}, lib=lib)
+    _close(ya, ys, 1e-12, "k = E y")
+    _close(ha, hs, 1e-13, "k = E states")
+
+
 # ------------------------------------------------------------------ router
 def pin_route_bruteforce(lib):
     """Top-k equals a full sort by (-logit, index); gates are the softmax of

@@ -58,6 +58,19 @@ MUTATIONS = [
      "h0[(((int64_t)b * D + d) * k + j) * N + n]"),
     ("slots_reset_on_switch", "H[j * N + n] = exp(Dt * Aj) * H[j * N + n] +",
      "H[j * N + n] = (t > 0 && idx[bt * k + j] != idx[(bt - 1) * k + j] ? 0.0 : exp(Dt * Aj) * H[j * N + n]) +"),
+    ("all_only_selected_advance", "        /* every expert advances */\n        for (int e = 0; e < E; ++e) {\n",
+     "        for (int e = 0; e < E; ++e) {\n          int sel = 0;\n          for (int j = 0; j < k; ++j) sel |= idx[bt * k + j] == e;\n          if (!sel) { out[e] = 0.0; continue; }\n"),
+    ("all_ungated", "yv += gate[bt * k + j] * out[idx[bt * k + j]];", "yv += out[idx[bt * k + j]];"),
+    ("all_output_of_slot0", "yv += gate[bt * k + j] * out[idx[bt * k + j]];",
+     "yv += gate[bt * k + j] * out[idx[bt * k]];"),
+    ("all_bias_of_expert0", "const double step = softplus(dt_raw[bt * D + d] + dt_bias[ed]);",
+     "const double step = softplus(dt_raw[bt * D + d] + dt_bias[d]);"),
+    ("all_no_Dskip", "double acc = Dskip[ed] * u;", "double acc = 0.0;"),
+    ("all_h0_layout", "S[e * N + n] = h0 ? h0[(((int64_t)b * E + e) * D + d) * N + n] : 0.0;",
+     "S[e * N + n] = h0 ? h0[(((int64_t)b * D + d) * E + e) * N + n] : 0.0;"),
+    ("all_readout_before_update",
+     "            S[e * N + n] = exp(step * an) * S[e * N + n] +\n                           input_coeff(step, an, zoh) * Bm[bt * N + n] * u;\n            acc += Cm[bt * N + n] * S[e * N + n];",
+     "            acc += Cm[bt * N + n] * S[e * N + n];\n            S[e * N + n] = exp(step * an) * S[e * N + n] +\n                           input_coeff(step, an, zoh) * Bm[bt * N + n] * u;"),
     ("mamba_wrong_A_index", "double An = A[(int64_t)d * N + n];", "double An = A[(int64_t)n];"),
     ("mamba_no_D", "double out = Dskip[d] * u;", "double out = 0.0;"),
     ("step_routes_first_token_only", "ref_route(B, D, E, k, x, Wr, idx, gate, NULL, NULL);",
