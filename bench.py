@@ -6,7 +6,8 @@ inputs resident in HBM.  Printed as one JSON line (rank 0):
   value    = tokens x channels per second of the whole step (G tc/s)
   roofline = the dominant kernel (the scan's chunk pass) against the VALU issue
              ceiling that bounds it, with its HBM rate against 8 TB/s beside it
-  modes    = the separate design (per expert, and per routing slot), the
+  modes    = the separate design (per expert, per routing slot, and every
+             expert advancing at every token), the
              dense single-expert scan (E = 1), the
              scan alone, and the decode step, for the "mixed vs separate" and
              "mixed vs dense" ratios; the stream-mixed form (shared A, mixed
@@ -499,6 +500,15 @@ def modes(args, w, swimba, workloads, x, dtr, Bm, Cm, Wr, A, bias, Dsk, idx, gat
     res["slots_scan"] = {"ms": round(ms_slots, 4), "G_tc_per_s": round(tc / ms_slots / 1e6, 3),
                          "slots_over_mixed": round(ms_slots / ms_mixed, 3)}
     del hfk, slots
+    # separate trajectories where every expert advances at every token (E
+    # updates per token; the routing only picks the outputs)
+    hfa = torch.empty((w.B, w.E, w.D, N_STATE), dtype=torch.float32, device=dev)
+    alle = swimba.PreparedScan(swimba.DESIGN_ALL_EXPERTS, x, dtr, Bm, Cm, idx, gate, A, bias,
+                               Dsk, y=y, h_final=hfa)
+    ms_all = _time(alle, reps)
+    res["all_experts_scan"] = {"ms": round(ms_all, 4), "G_tc_per_s": round(tc / ms_all / 1e6, 3),
+                               "all_experts_over_mixed": round(ms_all / ms_mixed, 3)}
+    del hfa, alle
     # dense single-expert scan (E = 1): the plain Mamba scan on the same shapes
     idx1 = torch.zeros((w.B, w.L, 1), dtype=torch.int32, device=dev)
     gate1 = torch.ones((w.B, w.L, 1), dtype=torch.float32, device=dev)

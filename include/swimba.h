@@ -28,6 +28,9 @@
  *   slots:   each routing slot j keeps its own state, which advances at every
  *            token with the parameters of the expert in slot j (unmixed) and
  *            keeps its value when that expert changes; y = sum_j g_j y_j.
+ *   all experts: each expert keeps its own state and advances it at every
+ *            token with its own parameters, selected or not; the routing
+ *            only picks whose outputs y = sum_j g_j y_{e_j} mixes.
  *   streams: A shared by the experts; each selected expert's B, C and X
  *            streams arrive per routing slot; the injection
  *            Delta sum_j g_j B_j X_j and the readout vector sum_j g_j C_j
@@ -131,11 +134,11 @@ typedef struct {
                                    [E, D] with a_form SCALAR                            */
   const float* dt_bias;         /* [E, D]                                                 */
   const float* Dskip;           /* [E, D]     per-expert feed-through D                   */
-  const float* h0;              /* NULL = zeros; [B, D, N] (separate: [B, E, D, N];
-                                   slots: [B, k, D, N])                                   */
+  const float* h0;              /* NULL = zeros; [B, D, N] (separate and all experts:
+                                   [B, E, D, N]; slots: [B, k, D, N])                    */
   void* y;                      /* [B, L, D]  out                                         */
-  float* h_final;               /* NULL = not written; [B, D, N] (separate: [B, E, D, N];
-                                   slots: [B, k, D, N])                                   */
+  float* h_final;               /* NULL = not written; [B, D, N] (separate and all
+                                   experts: [B, E, D, N]; slots: [B, k, D, N])           */
   int chunk;                    /* tokens per chunk; 0 = library's choice                 */
   swimba_carry carry;           /* chunk join method                                      */
   hipEvent_t* phase_events;     /* NULL, or 6 timing events: start and end of the chunk
@@ -151,7 +154,8 @@ typedef struct {
 enum {
   SWIMBA_DESIGN_MIXED = 0,    /* swimba_scan          */
   SWIMBA_DESIGN_SEPARATE = 1, /* swimba_scan_separate */
-  SWIMBA_DESIGN_SLOTS = 2     /* swimba_scan_slots    */
+  SWIMBA_DESIGN_SLOTS = 2,    /* swimba_scan_slots    */
+  SWIMBA_DESIGN_ALL_EXPERTS = 3 /* swimba_scan_all_experts */
 };
 
 /*
@@ -206,6 +210,21 @@ int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
  * (the k x N states of a channel are held in registers).
  */
 int swimba_scan_slots(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * swimba_scan_all_experts -- the third reading of the separate design ([SW]
+ * Spanish "Distinción de Diseños", French "Distinction des deux designs":
+ * separate SSMs, one per expert): h0/h_final [B, E, D, N]; every expert's
+ * state advances at every token with its own A, dt_bias and Dskip, whether
+ * or not the token selected it, so each trajectory is a plain selective scan
+ * and does not depend on the routing; y = sum_j g_j (C_t . h_{e_j} +
+ * Dskip[e_j] x).  E state updates per token instead of k.  With k = E and
+ * every expert selected at every token this equals swimba_scan_separate.
+ * Workspace: swimba_scan_workspace_size with SWIMBA_DESIGN_ALL_EXPERTS.
+ * Same constraints as swimba_scan_separate.
+ */
+int swimba_scan_all_experts(const swimba_scan_args* a, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 typedef struct {
   swimba_scan_args fwd;         /* the forward call's arguments; its y, h_final,

@@ -16,9 +16,15 @@
 // k slot outputs in slot order and stores y.  Each selection is done once, so
 // the work is k updates per token.
 //
+// ALL (the third reading of separate trajectories): every expert's wave
+// advances its state at every token, whether or not the token selected the
+// expert, and writes the gate-weighted output only to the slots that chose it;
+// that is E updates per token.
+//
 // Chunks are joined exactly: pass 1 runs every chunk from zero (chunk 0 from
 // h0) and records each expert's end state and decay P_e[n] = exp2(S_e A'[e,n]),
-// with S_e the Delta summed over the chunk's selections of e and A' = A log2 e;
+// with S_e the Delta summed over the chunk's selections of e (ALL: over all
+// its tokens) and A' = A log2 e;
 // pass 2 carries the states across chunks (shared with the mixed scan); pass 3
 // re-runs chunks 1.. from their carried-in states.
 #pragma once
@@ -157,10 +163,27 @@ __device__ __forceinline__ float expert_step(float* h, float& S, const float* Ae
 // time the wave first takes one ballot per slot (which staged tokens chose its
 // expert there) and then visits only the selected tokens, so the scan over
 // the round costs scalar bit operations only.
-template <typename TIn, int K, bool READOUT, bool SA, bool ZOH>
+template <typename TIn, int K, bool READOUT, bool SA, bool ZOH, bool ALL>
 __device__ __forceinline__ void walk_round(const SepSmem<TIn>& s, int n, int k, int ex, int lane,
                                            float* h, float& S, const float* Ae, float bias,
                                            float dsk) {
+  if constexpr (ALL) {
+    // every token advances the state; the output goes to the slots that
+    // selected this expert (none, one, or several)
+    for (int i = 0; i < n; ++i) {
+      const float xv = to_f32(s.xs[i * 64 + lane]), rv = to_f32(s.rs[i * 64 + lane]);
+      const float4* bc = reinterpret_cast<const float4*>(s.bc + i * 32);
+      const float ye = expert_step<READOUT, SA, ZOH>(h, S, Ae, bias, dsk, xv, rv, bc);
+      if (READOUT) {
+#pragma unroll
+        for (int j = 0; j < (K > 0 ? K : 16); ++j) {
+          if (K == 0 && j >= k) break;
+          if (uniform(s.e[i * k + j]) == ex) s.yb[(i * k + j) * 64 + lane] = s.g[i * k + j] * ye;
+        }
+      }
+    }
+    return;
+  }
   auto select = [&](int i, int j) {
     const float xv = to_f32(s.xs[i * 64 + lane]), rv = to_f32(s.rs[i * 64 + lane]);
     const float4* bc = reinterpret_cast<const float4*>(s.bc + i * 32);
@@ -189,7 +212,7 @@ __device__ __forceinline__ void walk_round(const SepSmem<TIn>& s, int n, int k, 
   }
 }
 
-template <typename TIn, typename TOut, int PASS, int K, bool SA, bool ZOH>
+template <typename TIn, typename TOut, int PASS, int K, bool SA, bool ZOH, bool ALL>
 __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   const int k = K > 0 ? K : p.k;
   const int R = round_tokens(k);
@@ -242,9 +265,9 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
     stage_round<TIn>(p, s, row, ts, n, k, d0);
     __syncthreads();
     if (readout)
-      walk_round<TIn, K, true, SA, ZOH>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
+      walk_round<TIn, K, true, SA, ZOH, ALL>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
     else
-      walk_round<TIn, K, false, SA, ZOH>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
+      walk_round<TIn, K, false, SA, ZOH, ALL>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
     __syncthreads();
     // every (token, slot) output was written by its expert's wave; add them in
     // slot order.  The next round's staging touches no output buffer, and its
@@ -276,7 +299,7 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   }
 }
 
-template <typename TIn, typename TOut, int K, bool SA, bool ZOH>
+template <typename TIn, typename TOut, int K, bool SA, bool ZOH, bool ALL>
 int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   SepParams p;
   p.B = a->B;
@@ -306,47 +329,55 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
   const dim3 block((unsigned)(p.E * 64));
   const size_t tiles = (size_t)p.B * p.ntiles;
   const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL>, smem);
   if (pl.nchunks <= 1) {
-    const int rc = launch_timed(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH>, dim3((unsigned)tiles),
+    const int rc = launch_timed(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL>, dim3((unsigned)tiles),
                                 block, smem, st, ev, p);
     if (rc != SWIMBA_OK) return rc;
     record_skipped(ev ? ev + 2 : nullptr, st);
     record_skipped(ev ? ev + 4 : nullptr, st);
     return SWIMBA_OK;
   }
-  int rc = launch_timed(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH>,
+  int rc = launch_timed(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL>,
                         dim3((unsigned)(tiles * p.nchunks)), block, smem, st, ev, p);
   if (rc != SWIMBA_OK) return rc;
   rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 1, st, ev ? ev + 2 : nullptr);
   if (rc != SWIMBA_OK) return rc;
-  return launch_timed(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH>,
+  return launch_timed(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL>,
                       dim3((unsigned)(tiles * (p.nchunks - 1))), block, smem, st,
                       ev ? ev + 4 : nullptr, p);
 }
 
-template <typename TIn, typename TOut, bool SA, bool ZOH>
+template <typename TIn, typename TOut, bool SA, bool ZOH, bool ALL>
 int launch_sep_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   switch (a->k) {
     case 1:
-      return launch_sep_t<TIn, TOut, 1, SA, ZOH>(a, pl, ws, st);
+      return launch_sep_t<TIn, TOut, 1, SA, ZOH, ALL>(a, pl, ws, st);
     case 2:
-      return launch_sep_t<TIn, TOut, 2, SA, ZOH>(a, pl, ws, st);
+      return launch_sep_t<TIn, TOut, 2, SA, ZOH, ALL>(a, pl, ws, st);
     default:
-      return launch_sep_t<TIn, TOut, 0, SA, ZOH>(a, pl, ws, st);
+      return launch_sep_t<TIn, TOut, 0, SA, ZOH, ALL>(a, pl, ws, st);
   }
 }
 
-template <typename TIn, typename TOut>
-int launch_sep_e(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
+template <typename TIn, typename TOut, bool ALL>
+int launch_sep_z(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   const bool zoh = a->disc == SWIMBA_DISC_ZOH;
   if (a->a_form == SWIMBA_A_SCALAR)
-    return zoh ? launch_sep_k<TIn, TOut, true, true>(a, pl, ws, st)
-               : launch_sep_k<TIn, TOut, true, false>(a, pl, ws, st);
-  return zoh ? launch_sep_k<TIn, TOut, false, true>(a, pl, ws, st)
-             : launch_sep_k<TIn, TOut, false, false>(a, pl, ws, st);
+    return zoh ? launch_sep_k<TIn, TOut, true, true, ALL>(a, pl, ws, st)
+               : launch_sep_k<TIn, TOut, true, false, ALL>(a, pl, ws, st);
+  return zoh ? launch_sep_k<TIn, TOut, false, true, ALL>(a, pl, ws, st)
+             : launch_sep_k<TIn, TOut, false, false, ALL>(a, pl, ws, st);
+}
+
+// all: every expert advances at every token (the all-experts reading)
+template <typename TIn, typename TOut>
+int launch_sep_e(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st,
+                 bool all) {
+  return all ? launch_sep_z<TIn, TOut, true>(a, pl, ws, st)
+             : launch_sep_z<TIn, TOut, false>(a, pl, ws, st);
 }
 
 }  // namespace sep

@@ -2,7 +2,8 @@
 #include "scan_separate.hpp"
 
 namespace swimba {
-int launch_sep_bf(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
-  return sep::launch_sep_e<bf16_t, float>(a, pl, ws, st);
+int launch_sep_bf(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st,
+                 bool all) {
+  return sep::launch_sep_e<bf16_t, float>(a, pl, ws, st, all);
 }
 }  // namespace swimba

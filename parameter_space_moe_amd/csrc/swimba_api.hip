@@ -20,10 +20,11 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 bool dtype_ok(swimba_dtype d) { return d == SWIMBA_F32 || d == SWIMBA_BF16; }
 
 // Sizes and options only (enough for the workspace query).  `design`:
-// 0 mixed, 1 separate (per expert), 2 separate per routing slot.
+// 0 mixed, 1 separate (per expert), 2 separate per routing slot, 3 separate
+// per expert with every expert advancing at every token.
 int validate_scan(const swimba_scan_args* a, int design) {
-  if (a == nullptr || design < 0 || design > 2) return SWIMBA_EINVAL;
-  const bool separate = design == 1;
+  if (a == nullptr || design < 0 || design > 3) return SWIMBA_EINVAL;
+  const bool separate = design == 1 || design == 3;
   if (a->B < 0 || a->L < 0 || a->D < 1 || a->N < 1 || a->E < 1 || a->k < 1 || a->k > a->E ||
       a->chunk < 0)
     return SWIMBA_EINVAL;
@@ -133,7 +134,7 @@ void plan_layout(const ScanPlan& in, int B, int L, int D, int chunk, size_t rows
 int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p) {
   int rc = validate_scan(a, design);
   if (rc != SWIMBA_OK) return rc;
-  const bool separate = design == 1, slots = design == 2;
+  const bool separate = design == 1 || design == 3, slots = design == 2;
   ScanPlan q;
   q.ntiles = (a->D + 63) / 64;
   q.waves = (!separate && !slots && a->E > 8) ? 8 : 4;
@@ -237,7 +238,8 @@ __global__ void fill_initial_state(const float* h0, float* h, size_t n) {
 
 int empty_sequence(const swimba_scan_args* a, int design, hipStream_t s) {
   if (a->h_final == nullptr || a->B == 0) return SWIMBA_OK;
-  const size_t per = design == 1 ? a->E : (design == 2 ? a->k : 1);  // trajectories
+  // trajectories per (sequence, channel)
+  const size_t per = (design == 1 || design == 3) ? a->E : (design == 2 ? a->k : 1);
   const size_t n = (size_t)a->B * per * a->D * SWIMBA_STATE_N;
   hipLaunchKernelGGL(fill_initial_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      a->h0, a->h_final, n);
@@ -259,7 +261,7 @@ int run_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t s
       for (int i = 0; i < 6; ++i) (void)hipEventRecord(a->phase_events[i], s);
     return empty_sequence(a, design, s);
   }
-  if (design == 1) return launch_scan_separate(a, p, ws, s);
+  if (design == 1 || design == 3) return launch_scan_separate(a, p, ws, s, design == 3);
   if (design == 2) return launch_scan_slots(a, p, ws, s);
   return launch_scan(a, p, ws, s);
 }
@@ -383,6 +385,11 @@ int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
 
 int swimba_scan_slots(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   return run_scan(a, ws, ws_bytes, stream, 2);
+}
+
+int swimba_scan_all_experts(const swimba_scan_args* a, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  return run_scan(a, ws, ws_bytes, stream, 3);
 }
 
 size_t swimba_scan_backward_workspace_size(const swimba_scan_grad_args* g) {

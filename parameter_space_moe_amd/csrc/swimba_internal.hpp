@@ -31,7 +31,8 @@ struct BwdPlan {
 };
 
 // Fills `p` for these arguments; returns a status.  Pure host arithmetic.
-// design: 0 mixed, 1 separate per expert, 2 separate per routing slot.
+// design: 0 mixed, 1 separate per expert, 2 separate per routing slot, 3 separate
+// per expert with every expert advancing at every token.
 int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p);
 int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p);
 // LDS of the backward's gradient pass (four waves): the tile's expert tables,
@@ -53,7 +54,9 @@ int plan_streams(const swimba_stream_args* a, ScanPlan* p);
 int launch_route(const void* x, swimba_dtype xd, const float* Wr, int64_t T, int D, int E,
                  int k, int32_t* idx, float* gate, hipStream_t s);
 int launch_scan(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
-int launch_scan_separate(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
+// all: every expert advances at every token (else only when selected)
+int launch_scan_separate(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s,
+                         bool all);
 int launch_scan_slots(const swimba_scan_args* a, const ScanPlan& p, void* ws, hipStream_t s);
 int launch_step(const swimba_step_args* a, hipStream_t s);
 // Backward of the mixed scan, one launcher per (input, dL/dy) dtype pair.

@@ -81,7 +81,8 @@ def load(path: str | None = None):
     lib.swimba_route.restype = _ci
     lib.swimba_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs), _ci]
     lib.swimba_scan_workspace_size.restype = ctypes.c_size_t
-    for fn in (lib.swimba_scan, lib.swimba_scan_separate, lib.swimba_scan_slots):
+    for fn in (lib.swimba_scan, lib.swimba_scan_separate, lib.swimba_scan_slots,
+               lib.swimba_scan_all_experts):
         fn.argtypes = [ctypes.POINTER(ScanArgs), _vp, ctypes.c_size_t, _vp]
         fn.restype = _ci
     lib.swimba_scan_plan.argtypes = [ctypes.POINTER(ScanArgs), _ci, ctypes.POINTER(_ci),
@@ -221,16 +222,16 @@ def _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, 
 
 # Which scan (SWIMBA_DESIGN_* in include/swimba.h); a bool `separate` reads as
 # MIXED (False) or SEPARATE (True).
-DESIGN_MIXED, DESIGN_SEPARATE, DESIGN_SLOTS = 0, 1, 2
+DESIGN_MIXED, DESIGN_SEPARATE, DESIGN_SLOTS, DESIGN_ALL_EXPERTS = 0, 1, 2, 3
 _SCAN_FN = {DESIGN_MIXED: "swimba_scan", DESIGN_SEPARATE: "swimba_scan_separate",
-            DESIGN_SLOTS: "swimba_scan_slots"}
+            DESIGN_SLOTS: "swimba_scan_slots", DESIGN_ALL_EXPERTS: "swimba_scan_all_experts"}
 
 
 def _state_shape(design, B, E, k, D, N=N_STATE):
     """h0 / h_final shape: one state per (b, d), per (b, expert, d) or per
     (b, slot, d)."""
     design = int(design)
-    if design == DESIGN_SEPARATE:
+    if design in (DESIGN_SEPARATE, DESIGN_ALL_EXPERTS):
         return (B, E, D, N)
     if design == DESIGN_SLOTS:
         return (B, k, D, N)
@@ -280,6 +281,13 @@ def scan_slots(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
     """Separate trajectories per routing slot (include/swimba.h:
     swimba_scan_slots).  Returns (y [B,L,D], h_final [B,k,D,16] or None)."""
     return _scan(DESIGN_SLOTS, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
+
+
+def scan_all_experts(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
+    """Separate trajectories where every expert advances at every token
+    (include/swimba.h: swimba_scan_all_experts).  Returns (y [B,L,D],
+    h_final [B,E,D,16] or None)."""
+    return _scan(DESIGN_ALL_EXPERTS, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
 
 
 def _grad_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, dy, h0, dh_final, chunk,

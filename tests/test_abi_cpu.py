@@ -128,13 +128,30 @@ def test_slots_rejects_and_workspace(lib):
     assert lib.swimba_scan_workspace_size(ctypes.byref(a), sw.DESIGN_SLOTS) == 2 * arr + flags
     assert lib.swimba_scan_slots(ctypes.byref(a), None, 0, None) == sw.EWORKSPACE
     # an unknown design
-    assert lib.swimba_scan_workspace_size(ctypes.byref(a), 3) == 0
+    assert lib.swimba_scan_workspace_size(ctypes.byref(a), 4) == 0
     c, n = ctypes.c_int(), ctypes.c_int()
-    assert lib.swimba_scan_plan(ctypes.byref(a), 3, ctypes.byref(c), ctypes.byref(n)) == \
+    assert lib.swimba_scan_plan(ctypes.byref(a), 4, ctypes.byref(c), ctypes.byref(n)) == \
         sw.EINVAL
     assert lib.swimba_scan_plan(ctypes.byref(a), sw.DESIGN_SLOTS, ctypes.byref(c),
                                 ctypes.byref(n)) == sw.OK
     assert (c.value, n.value) == (512, 8)
+
+
+def test_all_experts_rejects_and_workspace(lib):
+    # one wave per expert in a workgroup: E <= 16, as the per-expert design
+    assert lib.swimba_scan_all_experts(ctypes.byref(scan_args(E=17)), None, 0, None) == \
+        sw.EUNSUPPORTED
+    assert lib.swimba_scan_all_experts(ctypes.byref(scan_args(x=None)), None, 0, None) == \
+        sw.EINVAL
+    # the same E x 16 state rows per (sequence, chunk, channel) as the
+    # per-expert design
+    a = scan_args(B=2, L=4096, D=256, E=8, k=3, chunk=512)
+    arr = 2 * 8 * 8 * 16 * 256 * 4
+    flags = 2 * 8 * 4 * 4
+    need = lib.swimba_scan_workspace_size(ctypes.byref(a), sw.DESIGN_ALL_EXPERTS)
+    assert need == lib.swimba_scan_workspace_size(ctypes.byref(a), sw.DESIGN_SEPARATE)
+    assert need == 2 * arr + 256 * ((flags + 255) // 256)
+    assert lib.swimba_scan_all_experts(ctypes.byref(a), None, 0, None) == sw.EWORKSPACE
 
 
 def test_workspace_checked_before_launch(lib):
