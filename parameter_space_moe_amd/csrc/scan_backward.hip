@@ -42,6 +42,22 @@ int reverse_carry(const BwdParams& p, hipStream_t st) {
 // ---------------------------------------------------------------- pass 6
 // dB, dC and dgate: the per-tile (dC) and per-wave (dB, dgate) channel sums
 // added in order.
+// sum_w src[w * stride] for w = 0 .. n-1, added in that order; the loads are
+// issued eight at a time so that one memory round trip serves eight terms.
+__device__ __forceinline__ float ordered_sum(const float* __restrict__ src, size_t stride, int n) {
+  float s = 0.f;
+  int w = 0;
+  for (; w + 8 <= n; w += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(w + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; w < n; ++w) s += src[(size_t)w * stride];
+  return s;
+}
+
 __global__ __launch_bounds__(256) void bwd_reduce_tokens_kernel(const float* __restrict__ redC,
                                                                 const float* __restrict__ redB,
                                                                 int ntiles, size_t tokens, int k,
@@ -50,14 +66,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_tokens_kernel(const float* __r
                                                                 float* __restrict__ dgate) {
   const int kr = kN + k;
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < tokens * kN) {
-    float s = 0.f;
-    for (int t = 0; t < ntiles; ++t) s += redC[(size_t)t * tokens * kN + i];
-    dC[i] = s;
-  }
+  if (i < tokens * kN) dC[i] = ordered_sum(redC + i, tokens * kN, ntiles);
   if (i < tokens * kr) {
-    float s = 0.f;
-    for (int w = 0; w < ntiles * 4; ++w) s += redB[(size_t)w * tokens * kr + i];
+    const float s = ordered_sum(redB + i, tokens * kr, ntiles * 4);
     const size_t bt = i / kr;
     const int c = (int)(i % kr);
     if (c < kN)
@@ -77,17 +88,15 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(const float* __r
   const size_t na = (size_t)E * D * kN, nb = (size_t)E * D;
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < na) {
-    float s = 0.f;
-    for (int w = 0; w < slots; ++w) s += pA[(size_t)w * na + i];
-    dA[i] = s;
+    dA[i] = ordered_sum(pA + i, na, slots);
   } else if (i < na + 2 * nb) {
     const size_t j = i - na;                  // [which][e][d]
     const int which = (int)(j / nb);
     const size_t ed = j % nb;
     const int e = (int)(ed / D), dd = (int)(ed % D);
-    float s = 0.f;
-    for (int w = 0; w < slots; ++w) s += pBD[(((size_t)w * E + e) * 2 + which) * D + dd];
-    (which == 0 ? dbias : dDsk)[ed] = s;
+    // pBD is [slot][E][2][D]: consecutive slots lie E * 2 * D floats apart
+    (which == 0 ? dbias : dDsk)[ed] = ordered_sum(pBD + ((size_t)e * 2 + which) * D + dd,
+                                                  (size_t)E * 2 * D, slots);
   }
 }
 

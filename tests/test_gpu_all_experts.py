@@ -172,3 +172,13 @@ def test_all_experts_degenerate():
         ry, rh = ref(inp, idx, gate, h0=inp["h0"])
         assert rel_err(host(y), ry) < TOL_F32, (B, L, D, E, k)
         assert rel_err(host(hf), rh) < TOL_F32, (B, L, D, E, k)
+
+
+def test_all_experts_sixteen_experts_runtime_k():
+    """E = 16 (the largest workgroup, one wave per expert) with k = 3 (the
+    runtime-k slot loop), scalar transition and zero-order hold."""
+    w, inp, t = case(B=1, L=200, D=70, E=16, k=3, seed=99, h0=True, scalar=True)
+    idx, gate = swimba.route(t["x"], t["Wr"], 3)
+    y, hf = swimba.scan_all_experts(*args(t, idx, gate), h0=t["h0"], chunk=64, zoh=True)
+    ry, rh = ref(inp, idx, gate, h0=inp["h0"], zoh=True)
+    assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
