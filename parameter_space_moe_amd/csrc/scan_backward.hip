@@ -23,11 +23,34 @@ __global__ __launch_bounds__(256) void bwd_reverse_carry_kernel(int B, int C, in
   const size_t stride = (size_t)kN * D;
   const size_t base = (size_t)b * C * stride + (size_t)n * D + d;
   float kap = dhf != nullptr ? dhf[((size_t)b * D + d) * kN + n] : 0.f;
-  for (int c = C - 1; c >= 0; --c) {
-    const float seed = K[base + (size_t)c * stride];
-    const float pc = P[base + (size_t)c * stride];
-    K[base + (size_t)c * stride] = kap;
-    kap = fmaf(pc, kap, seed);
+  // chunks C-1 .. 0 in batches of 8, each batch's loads issued a batch ahead
+  // of the current batch's stores (loads before chunk 0 read chunk 0, unused)
+  constexpr int U8 = 8;
+  float sd[U8], pc[U8];
+  auto load_batch = [&](int c0, float* sb, float* pb) {
+#pragma unroll
+    for (int u = 0; u < U8; ++u) {
+      const size_t o = base + (size_t)max(c0 - u, 0) * stride;
+      sb[u] = K[o];
+      pb[u] = P[o];
+    }
+  };
+  load_batch(C - 1, sd, pc);
+  for (int c0 = C - 1; c0 >= 0; c0 -= U8) {
+    float sn[U8], pn[U8];
+    load_batch(c0 - U8, sn, pn);
+#pragma unroll
+    for (int u = 0; u < U8; ++u) {
+      if (c0 - u >= 0) {
+        K[base + (size_t)(c0 - u) * stride] = kap;
+        kap = fmaf(pc[u], kap, sd[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U8; ++u) {
+      sd[u] = sn[u];
+      pc[u] = pn[u];
+    }
   }
   if (dh0 != nullptr) dh0[((size_t)b * D + d) * kN + n] = kap;
 }

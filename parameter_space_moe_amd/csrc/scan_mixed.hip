@@ -24,26 +24,35 @@ __global__ __launch_bounds__(256) void mix_carry_kernel(int B, int C, int D, int
   const size_t stride = (size_t)rows * D;
   const size_t base = (size_t)b * C * stride + (size_t)r * D + d;
   float h = H[base];  // chunk 0 started from h0: its end state is exact
-  int c = 1;
+  // chunks 1 .. C-1 in batches of 8; each batch's loads are issued a batch
+  // ahead, before the current batch's stores, so the chain waits for memory
+  // once per batch.  Loads past chunk C-1 read chunk C-1 again (unused).
   constexpr int U8 = 8;
-  for (; c + U8 <= C; c += U8) {
-    float he[U8], pc[U8];
+  float he[U8], pc[U8];
+  auto load_batch = [&](int c0, float* hb, float* pb) {
 #pragma unroll
     for (int u = 0; u < U8; ++u) {
-      he[u] = H[base + (size_t)(c + u) * stride];
-      pc[u] = P[base + (size_t)(c + u) * stride];
+      const size_t o = base + (size_t)min(c0 + u, C - 1) * stride;
+      hb[u] = H[o];
+      pb[u] = P[o];
+    }
+  };
+  load_batch(1, he, pc);
+  for (int c0 = 1; c0 < C; c0 += U8) {
+    float hn[U8], pn[U8];
+    load_batch(c0 + U8, hn, pn);
+#pragma unroll
+    for (int u = 0; u < U8; ++u) {
+      if (c0 + u < C) {
+        H[base + (size_t)(c0 + u) * stride] = h;
+        h = fmaf(pc[u], h, he[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U8; ++u) {
-      H[base + (size_t)(c + u) * stride] = h;
-      h = fmaf(pc[u], h, he[u]);
+      he[u] = hn[u];
+      pc[u] = pn[u];
     }
-  }
-  for (; c < C; ++c) {
-    float he = H[base + (size_t)c * stride];
-    float pc = P[base + (size_t)c * stride];
-    H[base + (size_t)c * stride] = h;
-    h = fmaf(pc, h, he);
   }
   if (h_final != nullptr) {
     if (separate) {
