@@ -586,23 +586,27 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
       st.issue(p, row + tb - kTB, kTB, k);
       load_quad_rows<TIn, TDy>(p, row + tb - kTB, kTB, active, d, q, nxt);
     }
-    // this block's previous states h_{t-1}, all issued before the first is used
+    // this block's previous states h_{t-1}, all issued before the first is
+    // used, without branches: the stored state of token t - 1 (the ragged
+    // tail and channels past D read valid rows whose values go unused; the
+    // latter have a zero adjoint); the chunk's first token then takes the
+    // carried-in state
     float4 hpb[kTB];
+    const int dq = active ? d : 0;
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
-      hpb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      const int t = tb + i;
-      if (active && i < n) {
-        if (t > t0)
-          hpb[i] = hs4[((row + t - 1) * 4 + q) * (size_t)p.D + d];
-        else if (c > 0)
-          hpb[i] = make_float4(p.H[cbase + (size_t)(4 * q) * p.D],
-                               p.H[cbase + (size_t)(4 * q + 1) * p.D],
-                               p.H[cbase + (size_t)(4 * q + 2) * p.D],
-                               p.H[cbase + (size_t)(4 * q + 3) * p.D]);
-        else if (p.h0 != nullptr)
-          hpb[i] = *reinterpret_cast<const float4*>(p.h0 + ((size_t)b * p.D + d) * kN + 4 * q);
-      }
+      const int tp = max(min(tb + i, t1 - 1) - 1, 0);
+      hpb[i] = hs4[((row + tp) * 4 + q) * (size_t)p.D + dq];
+    }
+    if (tb == t0) {  // the chunk's first block (wave-uniform)
+      float4 hin = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (active && c > 0)
+        hin = make_float4(p.H[cbase + (size_t)(4 * q) * p.D], p.H[cbase + (size_t)(4 * q + 1) * p.D],
+                          p.H[cbase + (size_t)(4 * q + 2) * p.D],
+                          p.H[cbase + (size_t)(4 * q + 3) * p.D]);
+      else if (active && p.h0 != nullptr)
+        hin = *reinterpret_cast<const float4*>(p.h0 + ((size_t)b * p.D + d) * kN + 4 * q);
+      hpb[0] = hin;
     }
     wave_sync();
 #pragma unroll
