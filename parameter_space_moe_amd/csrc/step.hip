@@ -50,8 +50,9 @@ struct StepParams {
 // Channels a thread handles per batch: all their loads are issued before any
 // of them is used, so each thread keeps 4 x 16 bytes of state in flight.
 constexpr int kBatch = 4;
-// Channels a thread reads per round of the fused router (loads first).
-constexpr int kRU = 4;
+// Channels a thread reads per round of the fused router (loads first): five
+// per thread cover rows of up to 5120 channels in one round of loads.
+constexpr int kRU = 5;
 
 template <typename TIn>
 struct ChanLoads {
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     }
   } else {
     // router for row b (E <= 64): each thread sums a strided subset of the
-    // channels (four at a time, loads first), then the wave adds with lane
+    // channels (five at a time, loads first), then the wave adds with lane
     // exchanges and the waves add through LDS in a fixed order.  Rows of Wr
     // are read as 16-byte vectors when E is a multiple of 4 (one cache-line
     // visit per row instead of one per expert).
