@@ -34,8 +34,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, public peak
 # VALU ceiling: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz issue slots per second;
-# a slot is one fp32 FMA (2 flops).  Packed fp32 is not used by this build, so
-# the non-packed FMA rate is the ceiling: 78.6 TFLOP/s.
+# a slot is one fp32 FMA (2 flops).  The kernels use no packed fp32, so the
+# non-packed FMA rate is the ceiling: 78.6 TFLOP/s.
 VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
 N_STATE = 16
 
@@ -159,7 +159,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the Swimba scan has no multi-GPU path in this build "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

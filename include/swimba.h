@@ -75,7 +75,7 @@ enum {
   SWIMBA_EHIP = -4          /* a kernel launch failed                         */
 };
 
-/* Largest expert count and the only state size this build supports. */
+/* Largest expert count and the only state size the library supports. */
 #define SWIMBA_MAX_EXPERTS 64
 #define SWIMBA_STATE_N 16
 
