@@ -162,7 +162,10 @@ enum {
  * swimba_scan_workspace_size -- bytes of device workspace the scan named by
  * `design` (SWIMBA_DESIGN_*) needs for these arguments (0 when the sequence
  * is one chunk).  Returns 0 as well for invalid arguments or an unknown
- * design; the scan call itself reports those.
+ * design; the scan call itself reports those.  The library's chunking
+ * depends on the device's compute-unit count: this query (and
+ * swimba_scan_plan) plans for the current device, a scan call for the device
+ * of its stream.
  */
 size_t swimba_scan_workspace_size(const swimba_scan_args* a, int design);
 

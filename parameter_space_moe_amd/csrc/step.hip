@@ -392,7 +392,7 @@ int launch_step_t(const swimba_step_args* a, hipStream_t s) {
   p.E = a->E;
   p.k = a->k;
   // one workgroup per row; small batches split rows so every CU has work
-  const int cus = device_cus();
+  const int cus = device_cus(stream_device(s));
   int slices = (cus + a->B - 1) / (a->B > 0 ? a->B : 1);
   const int maxs = (a->D + kStepChan - 1) / kStepChan;
   slices = slices < 1 ? 1 : (slices > maxs ? maxs : slices);

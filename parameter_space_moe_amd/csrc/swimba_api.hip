@@ -61,9 +61,16 @@ int validate_scan_pointers(const swimba_scan_args* a, bool need_y = true) {
 
 }  // namespace
 
-int device_cus() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+int stream_device(hipStream_t s) {
+  int dev = -1;
+  if (s != nullptr && hipStreamGetDevice(s, &dev) == hipSuccess) return dev;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  return dev;
+}
+
+int device_cus(int dev) {
+  if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev < 0 || dev >= kMaxDevices) return 256;
   int v = g_cus[dev].load(std::memory_order_relaxed);
   if (v <= 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -80,8 +87,9 @@ namespace {
 // lane-per-channel scan over B * ntiles independent recurrences of length L.
 // `small_ok`: the kernel may run the small-problem layout (two 4-wave
 // workgroups per CU); *small tells whether it was chosen.
-int auto_chunk(long long B, long long L, int ntiles, bool separate, bool small_ok, bool* small) {
-  const long long cus = device_cus();
+int auto_chunk(long long B, long long L, int ntiles, bool separate, bool small_ok, bool* small,
+               int dev) {
+  const long long cus = device_cus(dev);
   const long long base = B * ntiles;
   long long want, min_chunk = 128;
   *small = false;
@@ -131,7 +139,7 @@ void plan_layout(const ScanPlan& in, int B, int L, int D, int chunk, size_t rows
 
 }  // namespace
 
-int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p) {
+int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p, int dev) {
   int rc = validate_scan(a, design);
   if (rc != SWIMBA_OK) return rc;
   const bool separate = design == 1 || design == 3, slots = design == 2;
@@ -145,7 +153,7 @@ int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p) {
   bool small = false;  // mixed scan with too little work for four waves per SIMD
   const int chunk =
       a->chunk > 0 ? a->chunk
-                   : auto_chunk(a->B, a->L, q.ntiles, separate, slots || a->E <= 8, &small);
+                   : auto_chunk(a->B, a->L, q.ntiles, separate, slots || a->E <= 8, &small, dev);
   const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N
                                : (slots ? (size_t)a->k * SWIMBA_STATE_N : SWIMBA_STATE_N);
   plan_layout(q, a->B, a->L, a->D, chunk, rows, true, p);
@@ -155,11 +163,11 @@ int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p) {
   return SWIMBA_OK;
 }
 
-int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p) {
+int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p, int dev) {
   if (g == nullptr) return SWIMBA_EINVAL;
   const swimba_scan_args* a = &g->fwd;
   ScanPlan sp;
-  int rc = plan_scan(a, 0, &sp);
+  int rc = plan_scan(a, 0, &sp, dev);
   if (rc != SWIMBA_OK) return rc;
   if (!dtype_ok(g->dy_dtype)) return SWIMBA_EINVAL;
   if (a->a_form != SWIMBA_A_DIAGONAL || a->disc != SWIMBA_DISC_EULER) return SWIMBA_EUNSUPPORTED;
@@ -176,7 +184,7 @@ int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p) {
   if (a->chunk > 0) {
     p->chunk = sp.chunk;
   } else {
-    const long long cus = device_cus();
+    const long long cus = device_cus(dev);
     const long long base = (long long)a->B * sp.ntiles;
     long long want = (8 * cus + base - 1) / base;
     want = (want + p->waves - 1) / p->waves * p->waves;
@@ -207,7 +215,7 @@ int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p) {
   return SWIMBA_OK;
 }
 
-int plan_streams(const swimba_stream_args* a, ScanPlan* p) {
+int plan_streams(const swimba_stream_args* a, ScanPlan* p, int dev) {
   if (a == nullptr) return SWIMBA_EINVAL;
   if (a->B < 0 || a->L < 0 || a->D < 1 || a->N < 1 || a->k < 1 || a->chunk < 0)
     return SWIMBA_EINVAL;
@@ -224,7 +232,7 @@ int plan_streams(const swimba_stream_args* a, ScanPlan* p) {
   }
   // no expert table in LDS: every problem may take the small-problem layout
   bool small = false;
-  const int chunk = a->chunk > 0 ? a->chunk : auto_chunk(a->B, a->L, q.ntiles, false, true, &small);
+  const int chunk = a->chunk > 0 ? a->chunk : auto_chunk(a->B, a->L, q.ntiles, false, true, &small, dev);
   plan_layout(q, a->B, a->L, a->D, chunk, SWIMBA_STATE_N, false, p);
   return SWIMBA_OK;
 }
@@ -248,7 +256,7 @@ int empty_sequence(const swimba_scan_args* a, int design, hipStream_t s) {
 
 int run_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t s, int design) {
   ScanPlan p;
-  int rc = plan_scan(a, design, &p);
+  int rc = plan_scan(a, design, &p, stream_device(s));
   if (rc != SWIMBA_OK) return rc;
   rc = validate_scan_pointers(a);
   if (rc != SWIMBA_OK) return rc;
@@ -268,7 +276,7 @@ int run_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t s
 
 int run_streams(const swimba_stream_args* a, void* ws, size_t ws_bytes, hipStream_t s) {
   ScanPlan p;
-  int rc = plan_streams(a, &p);
+  int rc = plan_streams(a, &p, stream_device(s));
   if (rc != SWIMBA_OK) return rc;
   if (a->A == nullptr || a->dt_bias == nullptr) return SWIMBA_EINVAL;
   // each lane reads its A row as 16-byte vectors
@@ -304,7 +312,7 @@ int run_streams(const swimba_stream_args* a, void* ws, size_t ws_bytes, hipStrea
 
 int run_backward(const swimba_scan_grad_args* g, void* ws, size_t ws_bytes, hipStream_t s) {
   BwdPlan p;
-  int rc = plan_backward(g, &p);
+  int rc = plan_backward(g, &p, stream_device(s));
   if (rc != SWIMBA_OK) return rc;
   const swimba_scan_args* a = &g->fwd;
   if (a->A == nullptr || a->dt_bias == nullptr || a->Dskip == nullptr || g->dA == nullptr ||
@@ -361,13 +369,13 @@ int swimba_route(const void* x, swimba_dtype x_dtype, const float* Wr, int64_t T
 
 size_t swimba_scan_workspace_size(const swimba_scan_args* a, int design) {
   ScanPlan p;
-  if (plan_scan(a, design, &p) != SWIMBA_OK) return 0;
+  if (plan_scan(a, design, &p, -1) != SWIMBA_OK) return 0;
   return p.bytes;
 }
 
 int swimba_scan_plan(const swimba_scan_args* a, int design, int* chunk, int* nchunks) {
   ScanPlan p;
-  const int rc = plan_scan(a, design, &p);
+  const int rc = plan_scan(a, design, &p, -1);
   if (rc != SWIMBA_OK) return rc;
   if (chunk) *chunk = p.chunk;
   if (nchunks) *nchunks = p.nchunks;
@@ -394,7 +402,7 @@ int swimba_scan_all_experts(const swimba_scan_args* a, void* ws, size_t ws_bytes
 
 size_t swimba_scan_backward_workspace_size(const swimba_scan_grad_args* g) {
   BwdPlan p;
-  if (plan_backward(g, &p) != SWIMBA_OK) return 0;
+  if (plan_backward(g, &p, -1) != SWIMBA_OK) return 0;
   return p.bytes;
 }
 
@@ -405,13 +413,13 @@ int swimba_scan_backward(const swimba_scan_grad_args* g, void* ws, size_t ws_byt
 
 size_t swimba_scan_streams_workspace_size(const swimba_stream_args* a) {
   ScanPlan p;
-  if (plan_streams(a, &p) != SWIMBA_OK) return 0;
+  if (plan_streams(a, &p, -1) != SWIMBA_OK) return 0;
   return p.bytes;
 }
 
 int swimba_scan_streams_plan(const swimba_stream_args* a, int* chunk, int* nchunks) {
   ScanPlan p;
-  const int rc = plan_streams(a, &p);
+  const int rc = plan_streams(a, &p, -1);
   if (rc != SWIMBA_OK) return rc;
   if (chunk) *chunk = p.chunk;
   if (nchunks) *nchunks = p.nchunks;

@@ -30,11 +30,13 @@ struct BwdPlan {
   size_t bytes = 0;
 };
 
-// Fills `p` for these arguments; returns a status.  Pure host arithmetic.
+// Fills `p` for these arguments; returns a status.  Pure host arithmetic, with
+// the compute-unit count of device `dev` (-1: the current device); a call
+// plans for the device of its stream.
 // design: 0 mixed, 1 separate per expert, 2 separate per routing slot, 3 separate
 // per expert with every expert advancing at every token.
-int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p);
-int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p);
+int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p, int dev);
+int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p, int dev);
 // LDS of the backward's gradient pass (four waves): the tile's expert tables,
 // and per wave a staging ring and the dense gate vectors of its tokens.
 inline size_t backward_grad_lds_bytes(int E, int k) {
@@ -48,7 +50,7 @@ inline size_t backward_lds_bytes(int E, int k, int waves) {
   return (size_t)E * (4 * 64 * 16 + 64 * 8) +
          (size_t)waves * ((size_t)2 * 8 * 32 * 4 + (size_t)2 * 2 * 8 * k * 4);
 }
-int plan_streams(const swimba_stream_args* a, ScanPlan* p);
+int plan_streams(const swimba_stream_args* a, ScanPlan* p, int dev);
 
 // Kernel launchers (validated arguments only).
 int launch_route(const void* x, swimba_dtype xd, const float* Wr, int64_t T, int D, int E,
@@ -75,8 +77,11 @@ int launch_streams_bb(const swimba_stream_args* a, const ScanPlan& p, void* ws, 
 int launch_carry(int B, int C, int D, int E, const float* P, float* H, float* h_final,
                  int separate, hipStream_t st, const hipEvent_t* ev);
 
-// Compute units of the current device (cached per device).
-int device_cus();
+// Compute units of device `dev` (-1: the current device), cached per device.
+int device_cus(int dev);
+// The device a stream belongs to (the null stream: the current device); -1
+// when HIP cannot tell.
+int stream_device(hipStream_t s);
 
 // Kernels that stage more than 64 KiB of dynamic LDS must say so before launch
 // (gfx950 has 160 KiB per CU).
