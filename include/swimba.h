@@ -40,9 +40,10 @@
  *   - Every tensor argument is a DEVICE pointer owned by the caller, dense and
  *     row-major (last index fastest), and must stay valid until the work
  *     enqueued on `stream` has finished.  The library allocates no memory,
- *     keeps no state beyond a per-device cache of the compute-unit count, and
- *     never synchronises the stream; calls on different streams may run
- *     concurrently.
+ *     keeps no state beyond a per-device cache of the compute-unit count (and
+ *     the fixed buffer of swimba_scan_noalloc), and never synchronises the
+ *     stream; calls on different streams may run concurrently (except
+ *     swimba_scan_noalloc calls on one device).
  *   - Work is enqueued on `stream` (NULL = the null stream).  A return of
  *     SWIMBA_OK means the kernels were launched; execution errors surface in
  *     later HIP calls on that stream.
@@ -72,7 +73,9 @@ enum {
   SWIMBA_EINVAL = -1,       /* a null pointer, a negative size, k > E, ...   */
   SWIMBA_EUNSUPPORTED = -2, /* valid but not built: N != 16, E > 64, ...     */
   SWIMBA_EWORKSPACE = -3,   /* workspace smaller than the query, or unaligned */
-  SWIMBA_EHIP = -4          /* a kernel launch failed                         */
+  SWIMBA_EHIP = -4,         /* a kernel launch failed                         */
+  SWIMBA_ESCRATCH = -5      /* swimba_scan_noalloc: the chunk workspace would
+                               exceed SWIMBA_NOALLOC_SCRATCH_BYTES           */
 };
 
 /* Largest expert count and the only state size the library supports. */
@@ -189,6 +192,30 @@ int swimba_scan_plan(const swimba_scan_args* a, int design, int* chunk, int* nch
  * (or zeros).
  */
 int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * swimba_scan_noalloc -- swimba_scan for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same computation, kernels, constraints and outputs as
+ * swimba_scan; the chunk workspace lives in a buffer the library owns
+ * instead of a caller's `ws`.
+ *   - The buffer is a fixed device array of SWIMBA_NOALLOC_SCRATCH_BYTES
+ *     (64 MiB), one per device, which each device the library runs on holds
+ *     until the process ends.  The call makes no hipMalloc, hipFree
+ *     or other allocating call; its first chunked call on a device looks the
+ *     buffer's address up (hipGetSymbolAddress).
+ *   - A call whose swimba_scan_workspace_size(a, SWIMBA_DESIGN_MIXED) would
+ *     exceed the buffer returns SWIMBA_ESCRATCH and enqueues nothing (a
+ *     larger chunk, or swimba_scan with a caller workspace, avoids it).
+ *     The size is planned for the device of `stream`.
+ *   - Every call on one device shares that device's buffer, which keeps the
+ *     last call's contents: calls that overlap on one GPU (on different
+ *     streams, or from different host threads without ordering) race and
+ *     give wrong results.  Order them on one stream.  Nothing in the buffer
+ *     needs to start at zero: each call writes every entry it reads.
+ */
+#define SWIMBA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int swimba_scan_noalloc(const swimba_scan_args* a, hipStream_t stream);
 
 /*
  * swimba_scan_separate -- the separate design ([SW] "MoE of separate SSMs"):

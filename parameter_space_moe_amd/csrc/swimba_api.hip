@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "swimba.h"
 #include "swimba_internal.hpp"
@@ -351,6 +352,53 @@ int run_backward(const swimba_scan_grad_args* g, void* ws, size_t ws_bytes, hipS
   return launch_backward_ff(g, p, ws, s);
 }
 
+// Chunk workspace of swimba_scan_noalloc: a fixed array in device memory,
+// one copy per device, allocated with the code object and held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (its
+// name is a host-side stand-in there): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kScratchBytes = SWIMBA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch[kMaxDevices];  // nullptr = not yet looked up
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device `dev`, or nullptr if HIP fails.
+void* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* q = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || q == nullptr) return nullptr;
+  g_scratch[dev].store(q, std::memory_order_release);
+  return q;
+}
+
+int run_scan_noalloc(const swimba_scan_args* a, hipStream_t s) {
+  const int dev = stream_device(s);
+  ScanPlan p;
+  const int rc = plan_scan(a, 0, &p, dev);
+  if (rc != SWIMBA_OK) return rc;
+  if (p.bytes > kScratchBytes) return SWIMBA_ESCRATCH;
+  void* ws = nullptr;
+  if (p.bytes > 0) {
+    // the launch below needs valid arguments; look the buffer up only then
+    const int prc = validate_scan_pointers(a);
+    if (prc != SWIMBA_OK) return prc;
+    ws = scratch_ptr(dev);
+    if (ws == nullptr) return SWIMBA_EHIP;
+  }
+  return run_scan(a, ws, p.bytes > 0 ? kScratchBytes : 0, s, 0);
+}
+
 }  // namespace
 }  // namespace swimba
 
@@ -384,6 +432,10 @@ int swimba_scan_plan(const swimba_scan_args* a, int design, int* chunk, int* nch
 
 int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   return run_scan(a, ws, ws_bytes, stream, 0);
+}
+
+int swimba_scan_noalloc(const swimba_scan_args* a, hipStream_t stream) {
+  return run_scan_noalloc(a, stream);
 }
 
 int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
@@ -465,6 +517,8 @@ const char* swimba_status_string(int status) {
       return "workspace too small or not 256-byte aligned";
     case SWIMBA_EHIP:
       return "HIP launch failed";
+    case SWIMBA_ESCRATCH:
+      return "problem needs more workspace than the library's fixed scratch buffer holds";
     default:
       return "unknown status";
   }

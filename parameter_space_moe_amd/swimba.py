@@ -15,7 +15,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libswimba.so")
 
 F32, BF16 = 0, 1
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5
+# fixed chunk-workspace buffer of swimba_scan_noalloc (SWIMBA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 CARRY = {"auto": 0, "rewalk": 1, "fixup": 2}
 A_DIAGONAL, A_SCALAR = 0, 1  # A [E, D, N] or [E, D] (one transition per channel)
 DISC_EULER, DISC_ZOH = 0, 1  # input term Delta B x, or zero-order hold
@@ -85,6 +87,8 @@ def load(path: str | None = None):
                lib.swimba_scan_all_experts):
         fn.argtypes = [ctypes.POINTER(ScanArgs), _vp, ctypes.c_size_t, _vp]
         fn.restype = _ci
+    lib.swimba_scan_noalloc.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+    lib.swimba_scan_noalloc.restype = _ci
     lib.swimba_scan_plan.argtypes = [ctypes.POINTER(ScanArgs), _ci, ctypes.POINTER(_ci),
                                      ctypes.POINTER(_ci)]
     lib.swimba_scan_plan.restype = _ci
@@ -269,6 +273,25 @@ def scan(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
     [E,D,16], or [E,D] for one transition per channel (the scalar form).
     Returns (y [B,L,D], h_final [B,D,16] or None)."""
     return _scan(False, x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, **kw)
+
+
+def scan_noalloc(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, y=None,
+                 h_final=None, y_dtype=None, want_state=True, chunk=0, carry="auto",
+                 stream=None, zoh=False):
+    """The mixed scan with its chunk workspace in the library's fixed buffer
+    (include/swimba.h: swimba_scan_noalloc): no workspace is allocated for
+    the call.  Outputs y and h_final are allocated here unless given.
+    Returns (y [B,L,D], h_final [B,D,16] or None)."""
+    if y is None:
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
+    if h_final is None and want_state:
+        h_final = torch.empty((x.shape[0], x.shape[2], N_STATE), dtype=torch.float32,
+                              device=x.device)
+    a = _scan_args(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0, y, h_final, chunk, carry,
+                   DESIGN_MIXED, None, zoh=zoh)
+    rc = load().swimba_scan_noalloc(ctypes.byref(a), _stream(stream))
+    _check("swimba_scan_noalloc", rc)
+    return y, h_final
 
 
 def scan_separate(x, dt_raw, Bm, Cm, idx, gate, A, dt_bias, Dskip, h0=None, **kw):
