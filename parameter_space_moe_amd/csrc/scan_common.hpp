@@ -19,6 +19,7 @@ struct Ring {
   float* bc;    // [2][kTB][32]
   int32_t* e;   // [2][kTB][k]
   float* g;     // [2][kTB][k]
+  int32_t* uo = nullptr;  // [2][kTB][k] or null: a second scaled copy of e (commit)
 };
 
 __host__ __device__ constexpr size_t ring_bytes(int k) {
@@ -156,8 +157,12 @@ struct Stager {
 
   // Convert and write to ring slot `slot`; n = tokens of the block that are
   // used (their gates are checked for the contraction condition, g >= 0).
+  // The expert ids are clamped to [0, E) and written times e_scale; with
+  // ring.uo set, also times u_scale there (callers that address per-expert
+  // LDS rows store byte offsets instead of ids).
   __device__ __forceinline__ void commit(const Ring& ring, int slot, int n, int k, int E,
-                                         int lane, int& gate_bad) const {
+                                         int lane, int& gate_bad, int e_scale = 1,
+                                         int u_scale = 0) const {
     if (lane < kPieces) {
       constexpr int kVals = 16 / (int)sizeof(TIn);  // values per piece
       const int tok = lane * kVals / kN, col = lane * kVals % kN;
@@ -188,7 +193,8 @@ struct Stager {
       if (w < nw) {
         int e = wi[i];
         e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-        ring.e[slot * nw + w] = e;
+        ring.e[slot * nw + w] = e * e_scale;
+        if (ring.uo != nullptr) ring.uo[slot * nw + w] = e * u_scale;
         const float gv = __int_as_float(wg[i]);
         if (w / k < n) gate_bad |= !(gv >= 0.f);
         ring.g[slot * nw + w] = gv;

@@ -12,19 +12,26 @@
 // 16 fp32 states in VGPRs for a whole chunk of tokens.  The 64 lanes of a wave
 // are 64 consecutive channels of the same token, so everything per token
 // (routing, gates, B_t, C_t) is wave-uniform: a per-wave LDS ring stages it one
-// block of 8 tokens ahead, while x, dt_raw and y stream as coalesced 64-lane rows.  The expert tables
-// A[e, tile, :], dt_bias and Dskip of the wave's 64 channels are staged once in
-// LDS and read back as conflict-free 16-byte rows for the selected experts.
-// The waves of a workgroup are consecutive chunks of the same channel tile and
-// share that table.
+// block of 8 tokens ahead, while x, dt_raw and y stream as coalesced 64-lane
+// rows.  The expert parameters of the wave's 64 channels are staged once in LDS
+// as one block of 16-byte rows per expert -- A x log2(e) in four rows of four
+// states, then (dt_bias, Dskip) -- so each selected expert costs one address
+// and five conflict-free reads per token.  The waves of a workgroup are
+// consecutive chunks of the same channel tile and share that table.
+//
+// The walk runs pairs of 8-token blocks with the two ring slots and two x /
+// dt_raw buffers fixed in the code (no register copies between blocks); a
+// ragged tail block or a ragged tile takes a guarded path after the full
+// blocks.
 //
 // Long sequences are cut into chunks so that enough waves run at once.  Chunks
 // are joined in three passes, all exact up to fp32 rounding:
 //   1. chunk pass: every chunk from a zero state (chunk 0 from h0); it writes
 //      provisional y, its end state, and its total decay
-//      P[n] = prod_t exp(Delta_t Abar_t[n]) = exp2(sum_t m_t[n]), with m_t the
-//      token's mixed exponent Delta_t Abar_t[n] log2 e, summed in registers;
-//   2. carry pass: h_in(c+1) = P(c) * h_in(c) + h_end(c), sequential over chunks;
+//      P[n] = prod_t exp(Delta_t Abar_t[n]) = exp2(sum_e U_e A[e, d, n] log2 e),
+//      where U_e = sum over the chunk's tokens and slots that selected e of
+//      Delta_t g_j; the U_e are added up per wave in LDS;
+//   2. carry pass: h_in(c+1) = P(c) * h_in(c) + h_end(c) over the chunks;
 //   3. fix-up pass: chunk c >= 1 re-runs from h_in(c), tracking the carried part
 //      g = (prod of decays) * h_in.  With A < 0 and gates >= 0 every decay is in
 //      (0, 1], so once |g| is below 2^-24 of the state on every lane the rest of
@@ -32,6 +39,8 @@
 //      When the contraction does not hold (flagged by the chunk pass) or the
 //      caller asks for it, the whole chunk is recomputed.
 #pragma once
+#include <type_traits>
+
 #include "scan_common.hpp"
 #include "swimba_device.hpp"
 #include "swimba_internal.hpp"
@@ -46,6 +55,10 @@ using stage::wave_sync;
 
 constexpr float kFixupTol = 5.9604645e-08f;  // 2^-24
 constexpr float kTiny = 1e-30f;
+// 16-byte rows of 64 lanes per expert in the LDS table: diagonal A as four
+// rows of (A x log2 e) for states 4q..4q+3, then (dt_bias, Dskip, 0, 0);
+// scalar A: one row (A x log2 e, dt_bias, Dskip, 0).
+constexpr int kRowsDiag = 5;
 
 struct MixParams {
   int B, L, D, E, k;
@@ -68,44 +81,115 @@ struct MixParams {
   int32_t* flags;     // [B][C][ntiles] 1 = contraction not guaranteed
 };
 
-// LDS: the workgroup's expert table (64 channels) and per-wave staging rings.
-// With a scalar transition per (expert, channel) the A table is [E][64] floats.
-struct Smem {
-  float4* A;   // [E][4][64]  A[e, d0+lane, 4q..4q+3]  (scalar A: [E][64] floats)
-  float2* BD;  // [E][64]     (dt_bias, Dskip)
-  Ring ring;   // this wave's ring
-};
-
-__host__ __device__ inline size_t a_table_bytes(int E, bool scalar_a) {
-  return scalar_a ? (size_t)E * 64 * 4 : (size_t)E * 4 * 64 * 16;
+__host__ __device__ inline int table_rows(bool scalar_a) { return scalar_a ? 1 : kRowsDiag; }
+__host__ __device__ inline size_t table_bytes(int E, bool scalar_a) {
+  return (size_t)E * table_rows(scalar_a) * 64 * 16;
 }
+// A wave's ring: the shared staging layout plus, per (token, slot), the byte
+// offset of the selected expert's U column.
+__host__ __device__ inline size_t ring_bytes_u(int k) {
+  return ring_bytes(k) + (size_t)2 * kTB * k * 4;
+}
+// byte stride of one expert's rows in the table
+__host__ __device__ inline int expert_stride(bool scalar_a) {
+  return table_rows(scalar_a) * 64 * 16;
+}
+
+// LDS: the workgroup's expert table, then per wave a staging ring (dynamic
+// LDS); in the chunk pass also the wave's sums U_e as [EMAX][64] floats, in a
+// separate static LDS array so that the compiler knows the sums' stores do
+// not touch the table and may issue the next token's table reads before them.
+struct Smem {
+  const float4* T;  // [E][rows][64]
+  float* U;         // [EMAX][64], chunk pass only
+  Ring ring;        // this wave's ring
+};
 
 __device__ __forceinline__ Smem smem_layout(int E, int k, int wave, bool scalar_a) {
   extern __shared__ float4 smem_raw[];
   Smem s;
   char* p = reinterpret_cast<char*>(smem_raw);
-  s.A = reinterpret_cast<float4*>(p);
-  p += a_table_bytes(E, scalar_a);
-  s.BD = reinterpret_cast<float2*>(p);
-  p += (size_t)E * 64 * 8;
-  p += ring_bytes(k) * wave;
+  s.T = reinterpret_cast<const float4*>(p);
+  p += table_bytes(E, scalar_a);
+  p += ring_bytes_u(k) * wave;
   s.ring.bc = reinterpret_cast<float*>(p);
   s.ring.e = reinterpret_cast<int32_t*>(p + 2 * kTB * 32 * 4);
   s.ring.g = reinterpret_cast<float*>(p + 2 * kTB * 32 * 4 + 2 * kTB * k * 4);
+  s.ring.uo = reinterpret_cast<int32_t*>(p + ring_bytes(k));
+  s.U = nullptr;
   return s;
 }
 
+// dynamic LDS of the chunk and fix-up passes
 __host__ inline size_t smem_bytes(int E, int k, int waves, bool scalar_a) {
-  return a_table_bytes(E, scalar_a) + (size_t)E * 64 * 8 + ring_bytes(k) * waves;
+  return table_bytes(E, scalar_a) + ring_bytes_u(k) * waves;
+}
+
+// Stage the tile's expert parameters (A scaled by log2 e); returns 1 if any A
+// in the tile is not strictly negative (including NaN).  Lanes past D get
+// zeros.
+__device__ __forceinline__ int load_table(const MixParams& p, float4* T, int d0, bool scalar_a) {
+  int bad = 0;
+  const int nthr = blockDim.x;
+  if (scalar_a) {
+    for (int i = threadIdx.x; i < p.E * 64; i += nthr) {
+      const int e = i >> 6, d = d0 + (i & 63);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (d < p.D) {
+        const size_t o = (size_t)e * p.D + d;
+        const float a = p.A[o];
+        bad |= !(a < 0.f);
+        v = make_float4(a * kLog2e, p.bias[o], p.Dsk[o], 0.f);
+      }
+      T[i] = v;
+    }
+    return bad;
+  }
+  // consecutive threads read consecutive 16-byte pieces of A[e, d0:d0+64, :]
+  for (int i = threadIdx.x; i < p.E * 256; i += nthr) {
+    const int e = i >> 8, dl = (i >> 2) & 63, q = i & 3;
+    const int d = d0 + dl;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (d < p.D) {
+      const float* a = p.A + ((size_t)e * p.D + d) * kN + q * 4;
+      const float a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+      bad |= !(a0 < 0.f) | !(a1 < 0.f) | !(a2 < 0.f) | !(a3 < 0.f);
+      v = make_float4(a0 * kLog2e, a1 * kLog2e, a2 * kLog2e, a3 * kLog2e);
+    }
+    T[(e * kRowsDiag + q) * 64 + dl] = v;
+  }
+  for (int i = threadIdx.x; i < p.E * 64; i += nthr) {
+    const int e = i >> 6, dl = i & 63, d = d0 + dl;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (d < p.D) {
+      const size_t o = (size_t)e * p.D + d;
+      v = make_float4(p.bias[o], p.Dsk[o], 0.f, 0.f);
+    }
+    T[(e * kRowsDiag + 4) * 64 + dl] = v;
+  }
+  return bad;
+}
+
+// Lane's first table row of the expert whose rows start `eoff` bytes into
+// the table (the ring holds that offset): one add; the expert's other rows
+// are constant offsets from it.
+__device__ __forceinline__ const float4* expert_rows(const Smem& s, int eoff, int lane) {
+  return reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s.T + lane) + eoff);
+}
+
+// This lane's entry of the wave's sum U_e, whose column starts `uoff` bytes
+// into U.
+__device__ __forceinline__ float* usum_at(float* U, int uoff, int lane) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(U + lane) + uoff);
 }
 
 // State update and readout of one token for one lane, given the per-state
 // exponents m[n] = Delta Abar[n] log2(e) (SA: one exponent m[0]) and the
-// Euler input dx = Delta x; B_t/C_t come from ring slot `slot`, position `i`.
+// Euler input dx = Delta x; bc points at the token's B_t (4 rows) and C_t
+// (4 rows) in the ring.
 template <bool TRACK, bool SA, bool ZOH>
-__device__ __forceinline__ float update_readout(const Smem& s, int slot, int i, const float* m,
-                                                float dx, float* h, float* g) {
-  const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
+__device__ __forceinline__ float update_readout(const float4* bc, const float* m, float dx,
+                                                float* h, float* g) {
   const float a0 = SA ? hw_exp2(m[0]) : 0.f;
   const float dx0 = (SA && ZOH) ? dx * zoh_phi(a0, m[0]) : dx;
   float yv = 0.f;
@@ -128,45 +212,45 @@ __device__ __forceinline__ float update_readout(const Smem& s, int slot, int i, 
 }
 
 // One token of the mixed recurrence for one lane with k == K known at compile
-// time.  Routing (experts e[j], gates gw[j]) is wave-uniform.  All of the
-// token's table reads (dt_bias/Dskip and the A rows) are issued together.
-// ACC_U: add the token's exponents m[n] to the chunk's sums ms[n] (registers).
+// time.  Routing (experts e[j], gates gw[j]) is wave-uniform; each selected
+// expert's table block is read with one address and all of the token's table
+// reads are issued together.  ACC_U: add Delta g_j to the wave's sums U_e.
 template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ float mix_token_k(const Smem& s, float* ms, const int* e,
-                                             const float* gw, int slot, int i, int lane,
+__device__ __forceinline__ float mix_token_k(const Smem& s, const int* e, const int* uo,
+                                             const float* gw, const float4* bc, int lane,
                                              float xv, float rv, float* h, float* g) {
-  float2 bd[K];
+  float4 bd[K];
   float4 ar[SA ? 1 : K][4];
-  float as[K];
-  const float* Asc = reinterpret_cast<const float*>(s.A);
+  float uold[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    bd[j] = s.BD[e[j] * 64 + lane];
+    if (ACC_U) uold[j] = *usum_at(s.U, uo[j], lane);
+    const float4* te = expert_rows(s, e[j], lane);
     if constexpr (SA) {
-      as[j] = Asc[e[j] * 64 + lane];
+      bd[j] = te[0];  // (A log2 e, dt_bias, Dskip, 0)
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ar[j][q] = s.A[(e[j] * 4 + q) * 64 + lane];
+      for (int q = 0; q < 4; ++q) ar[j][q] = te[q * 64];
+      bd[j] = te[4 * 64];  // (dt_bias, Dskip, 0, 0)
     }
   }
   // mixed dt_bias and Dskip
   float beta = 0.f, delta = 0.f;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    beta = fmaf(gw[j], bd[j].x, beta);
-    delta = fmaf(gw[j], bd[j].y, delta);
+    beta = fmaf(gw[j], SA ? bd[j].y : bd[j].x, beta);
+    delta = fmaf(gw[j], SA ? bd[j].z : bd[j].y, delta);
   }
   const float dlt = softplus_f32(rv + beta);
-  const float dl2 = dlt * kLog2e;
   float u[K];
 #pragma unroll
-  for (int j = 0; j < K; ++j) u[j] = dl2 * gw[j];
-  // mixed exponents m[n] = sum_j u_j A[e_j, d, n]
+  for (int j = 0; j < K; ++j) u[j] = dlt * gw[j];
+  // mixed exponents m[n] = sum_j u_j A[e_j, d, n] log2 e
   float m[SA ? 1 : kN];
   if constexpr (SA) {
-    m[0] = 0.f;
+    m[0] = u[0] * bd[0].x;
 #pragma unroll
-    for (int j = 0; j < K; ++j) m[0] = fmaf(u[j], as[j], m[0]);
+    for (int j = 1; j < K; ++j) m[0] = fmaf(u[j], bd[j].x, m[0]);
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -187,129 +271,126 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, float* ms, const int
         m[4 * q + 3] = fmaf(u[j], a.w, m[4 * q + 3]);
       }
   }
-  if (ACC_U)
+  const float yv = update_readout<TRACK, SA, ZOH>(bc, m, dlt * xv, h, g);
+  if (ACC_U) {
+    // U_e += u_j; a slot that repeats an earlier slot's expert adds onto
+    // that slot's new value (both were read before either store)
+    float unew[K];
 #pragma unroll
-    for (int n = 0; n < (SA ? 1 : kN); ++n) ms[n] += m[n];
-  const float yv = update_readout<TRACK, SA, ZOH>(s, slot, i, m, dlt * xv, h, g);
+    for (int j = 0; j < K; ++j) {
+      float base = uold[j];
+#pragma unroll
+      for (int i = 0; i < j; ++i) base = uo[i] == uo[j] ? unew[i] : base;
+      unew[j] = base + u[j];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) *usum_at(s.U, uo[j], lane) = unew[j];
+  }
   return fmaf(delta, xv, yv);
 }
 
-// One token of the mixed recurrence for one lane.  Routing (experts e[j],
-// gates g[j], j < k) is wave-uniform; B_t/C_t come from ring slot `slot`,
-// position `i`.  Every LDS address below depends only on (e, lane), so all of
-// a token's reads can be in flight together.
-//   K > 0: k == K known at compile time (mix_token_k); K == 0: runtime k.
-//   TRACK: also decay the carried part g (fix-up pass; with SA, g[0] is the
-//          carried part's common decay factor).
-//   ACC_U: add the token's exponents to the chunk's sums ms (chunk pass).
-//   SA: one transition per (expert, channel), shared by the 16 states (the
-//       Mamba-2 form A = a I): one exponential per token instead of 16.
-//   ZOH: zero-order-hold input term, zoh_phi(a) times the Euler term.
-template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, float* ms,
-                                           const int* e, const float* gw, int slot, int i,
-                                           int lane, float xv, float rv, float* h, float* g) {
-  if constexpr (K > 0)
-    return mix_token_k<K, TRACK, ACC_U, SA, ZOH>(s, ms, e, gw, slot, i, lane, xv, rv, h, g);
-  const int k = K > 0 ? K : p.k;
-  // mixed dt_bias and Dskip
+// The same for k known only at run time (k > 2).
+template <bool TRACK, bool ACC_U, bool SA, bool ZOH>
+__device__ __forceinline__ float mix_token_any(const Smem& s, int k, const int* e,
+                                               const int* uo, const float* gw,
+                                               const float4* bc, int lane, float xv, float rv,
+                                               float* h, float* g) {
   float beta = 0.f, delta = 0.f;
-  auto bias_slot = [&](int j) {
-    const float2 bd = s.BD[e[j] * 64 + lane];
-    beta = fmaf(gw[j], bd.x, beta);
-    delta = fmaf(gw[j], bd.y, delta);
-  };
-  if constexpr (K > 0) {
-#pragma unroll
-    for (int j = 0; j < K; ++j) bias_slot(j);
-  } else {
-    for (int j = 0; j < k; ++j) bias_slot(j);
+  for (int j = 0; j < k; ++j) {
+    const float4 bd = expert_rows(s, e[j], lane)[SA ? 0 : 4 * 64];
+    beta = fmaf(gw[j], SA ? bd.y : bd.x, beta);
+    delta = fmaf(gw[j], SA ? bd.z : bd.y, delta);
   }
   const float dlt = softplus_f32(rv + beta);
-  if constexpr (SA) {
-    // mixed exponent Delta * sum_j g_j A[e_j, d] * log2(e), one per token
-    const float dl2 = dlt * kLog2e;
-    const float* As = reinterpret_cast<const float*>(s.A);
-    float m = 0.f;
-    auto a_slot = [&](int j) {
-      const float u = dl2 * gw[j];
-      m = fmaf(u, As[e[j] * 64 + lane], m);
-    };
-    if constexpr (K > 0) {
+  float m[SA ? 1 : kN];
 #pragma unroll
-      for (int j = 0; j < K; ++j) a_slot(j);
+  for (int n = 0; n < (SA ? 1 : kN); ++n) m[n] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const float u = dlt * gw[j];
+    if (ACC_U) {
+      float* up = usum_at(s.U, uo[j], lane);
+      *up = *up + u;
+    }
+    const float4* te = expert_rows(s, e[j], lane);
+    if constexpr (SA) {
+      m[0] = fmaf(u, te[0].x, m[0]);
     } else {
-      for (int j = 0; j < k; ++j) a_slot(j);
-    }
-    if (ACC_U) ms[0] += m;
-    const float a = hw_exp2(m);
-    const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
-    const float dx = ZOH ? dlt * xv * zoh_phi(a, m) : dlt * xv;
-    float yv = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 b4 = bc[q], c4 = bc[4 + q];
-      const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, cv[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = 4 * q + r;
-        h[n] = fmaf(a, h[n], dx * bv[r]);
-        yv = fmaf(cv[r], h[n], yv);
-      }
-    }
-    if (TRACK) g[0] *= a;
-    return fmaf(delta, xv, yv);
-  }
-  // mixed exponent m[n] = Delta * sum_j g_j A[e_j, d, n] * log2(e)
-  float m[kN];
-#pragma unroll
-  for (int n = 0; n < kN; ++n) m[n] = 0.f;
-  const float dl2 = dlt * kLog2e;
-  auto a_slot = [&](int j) {
-    const float u = dl2 * gw[j];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 a = s.A[(e[j] * 4 + q) * 64 + lane];
-      if (K > 0 && j == 0) {
-        m[4 * q + 0] = u * a.x;
-        m[4 * q + 1] = u * a.y;
-        m[4 * q + 2] = u * a.z;
-        m[4 * q + 3] = u * a.w;
-      } else {
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = te[q * 64];
         m[4 * q + 0] = fmaf(u, a.x, m[4 * q + 0]);
         m[4 * q + 1] = fmaf(u, a.y, m[4 * q + 1]);
         m[4 * q + 2] = fmaf(u, a.z, m[4 * q + 2]);
         m[4 * q + 3] = fmaf(u, a.w, m[4 * q + 3]);
       }
     }
-  };
-  if constexpr (K > 0) {
-#pragma unroll
-    for (int j = 0; j < K; ++j) a_slot(j);
-  } else {
-    for (int j = 0; j < k; ++j) a_slot(j);
   }
-  if (ACC_U)
-#pragma unroll
-    for (int n = 0; n < kN; ++n) ms[n] += m[n];
-  const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
-  const float dx = dlt * xv;
-  float yv = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 b4 = bc[q], c4 = bc[4 + q];
-    const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, cv[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = 4 * q + r;
-      const float a = hw_exp2(m[n]);
-      const float inj = ZOH ? (dx * bv[r]) * zoh_phi(a, m[n]) : dx * bv[r];
-      h[n] = fmaf(a, h[n], inj);
-      yv = fmaf(cv[r], h[n], yv);
-      if (TRACK) g[n] *= a;
-    }
-  }
+  const float yv = update_readout<TRACK, SA, ZOH>(bc, m, dlt * xv, h, g);
   return fmaf(delta, xv, yv);
+}
+
+// One token from ring slot `slot`, position i (routing read from the ring).
+template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
+__device__ __forceinline__ float ring_token(const MixParams& p, const Smem& s, int slot, int i,
+                                            int lane, float xv, float rv, float* h, float* g) {
+  const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
+  if constexpr (K > 0) {
+    int ev[K], uv[K];
+    float gv[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      ev[j] = s.ring.e[(slot * kTB + i) * K + j];
+      gv[j] = s.ring.g[(slot * kTB + i) * K + j];
+      uv[j] = ACC_U ? s.ring.uo[(slot * kTB + i) * K + j] : 0;
+    }
+    return mix_token_k<K, TRACK, ACC_U, SA, ZOH>(s, ev, uv, gv, bc, lane, xv, rv, h, g);
+  } else {
+    const int k = p.k;
+    int eb[16], ub[16];
+    float gb[16];
+    for (int j = 0; j < k; ++j) {
+      eb[j] = s.ring.e[(slot * kTB + i) * k + j];
+      gb[j] = s.ring.g[(slot * kTB + i) * k + j];
+      ub[j] = ACC_U ? s.ring.uo[(slot * kTB + i) * k + j] : 0;
+    }
+    return mix_token_any<TRACK, ACC_U, SA, ZOH>(s, k, eb, ub, gb, bc, lane, xv, rv, h, g);
+  }
+}
+
+// True (on every lane) once the carried part g has decayed below fp32
+// resolution of the state on every lane of the wave.
+template <bool SA>
+__device__ __forceinline__ bool carried_part_gone(const float* h, const float* g) {
+  float mh = 0.f;
+#pragma unroll
+  for (int q = 0; q < kN; ++q) mh = fmaxf(mh, fabsf(h[q]));
+  const float thr = fmaxf(kFixupTol * mh, kTiny);
+  bool conv = true;
+  if constexpr (SA) {
+    conv = fabsf(g[0]) * g[1] <= thr;  // g[1] = max_n |h_in[n]|; NaN: not converged
+  } else {
+#pragma unroll
+    for (int q = 0; q < kN; ++q) conv &= fabsf(g[q]) <= thr;  // NaN: not converged
+  }
+  return __all(conv);
+}
+
+// Store y of two consecutive tokens (rows i, i + 1 of the block's buffer):
+// one conversion for both in bf16.
+template <typename TOut>
+__device__ __forceinline__ void store_y2(stage::rsrc_t ry, uint32_t yoff, uint32_t yrow, int i,
+                                         float y0, float y1) {
+  if constexpr (std::is_same<TOut, bf16_t>::value) {
+    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    const f2_t f = {y0, y1};
+    const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf2_t));
+    stage::buf_store(ry, yoff, (uint32_t)i * yrow, (bf16_t)(pk & 0xffffu));
+    stage::buf_store(ry, yoff, (uint32_t)(i + 1) * yrow, (bf16_t)(pk >> 16));
+  } else {
+    stage::buf_store(ry, yoff, (uint32_t)i * yrow, y0);
+    stage::buf_store(ry, yoff, (uint32_t)(i + 1) * yrow, y1);
+  }
 }
 
 // Walk tokens [t0, t1) of sequence b for one lane, staging each block of kTB
@@ -319,9 +400,9 @@ __device__ __forceinline__ float mix_token(const MixParams& p, const Smem& s, fl
 // a fixed per-lane channel offset); the prefetch of the next block is issued
 // before the current one computes and is waited on only when it is used.
 template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* ms, int b, int t0,
-                                     int t1, int d, bool active, bool full_tile, int lane,
-                                     bool truncate, float* h, float* g, int& gate_bad) {
+__device__ __forceinline__ void walk(const MixParams& p, const Smem& s, int b, int t0, int t1,
+                                     int d, bool active, bool full_tile, int lane, bool truncate,
+                                     float* h, float* g, int& gate_bad) {
   constexpr int KW = (kTB * (K > 0 ? K : 16) + 63) / 64;
   const int k = K > 0 ? K : p.k;
   const int D = p.D;
@@ -332,7 +413,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* m
   const uint32_t yoff = (uint32_t)d * (uint32_t)sizeof(TOut);
   const uint32_t xrow = (uint32_t)D * (uint32_t)sizeof(TIn);
   const uint32_t yrow = (uint32_t)D * (uint32_t)sizeof(TOut);
-  TIn xc[kTB], rc[kTB], xn[kTB], rn[kTB];
+  TIn xa[kTB], ra[kTB], xb[kTB], rb[kTB];
   stage::Stager<TIn, KW> st;
   st.init(lane);
   auto valid_at = [&](int t) { return (int)min((size_t)kTB, total - (row + t)); };
@@ -351,105 +432,105 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* m
   };
 
   st.issue(p, row + t0, valid_at(t0), k);
-  load_xr(t0, xc, rc);
-  st.commit(s.ring, 0, min(kTB, t1 - t0), k, p.E, lane, gate_bad);
+  load_xr(t0, xa, ra);
+  const int escale = expert_stride(SA), uscale = 64 * 4;
+  st.commit(s.ring, 0, min(kTB, t1 - t0), k, p.E, lane, gate_bad, escale, uscale);
 
-  int slot = 0;
-  for (int tb = t0; tb < t1; tb += kTB, slot ^= 1) {
+  int tb = t0;
+  // One whole block at tb from ring slot SL and buffers xc/rc (compile-time
+  // slot and buffers); prefetches the next block into xn/rn and the other
+  // slot.  Returns false when the walk stops here (carried part decayed).
+  auto fast_block = [&](auto SLOT, TIn* xc, TIn* rc, TIn* xn, TIn* rn) -> bool {
+    constexpr int sl = decltype(SLOT)::value;
+    const int tn = tb + kTB;
+    const bool more = tn < t1;
+    // the prefetch always runs (the last block re-reads itself): a
+    // conditional load would make the compiler keep and copy the old buffers
+    const int tl = more ? tn : tb;
+    st.issue(p, row + tl, valid_at(tl), k);
+    load_xr(tl, xn, rn);
+    wave_sync();
+    const stage::rsrc_t ry = stage::rows_rsrc<TOut>(p.y, row + tb, kTB, D);
+#pragma unroll
+    for (int i = 0; i < kTB; i += 2) {
+      const float y0 = ring_token<K, TRACK, ACC_U, SA, ZOH>(p, s, sl, i, lane, to_f32(xc[i]),
+                                                            to_f32(rc[i]), h, g);
+      const float y1 = ring_token<K, TRACK, ACC_U, SA, ZOH>(
+          p, s, sl, i + 1, lane, to_f32(xc[i + 1]), to_f32(rc[i + 1]), h, g);
+      store_y2<TOut>(ry, yoff, yrow, i, y0, y1);
+    }
+    if (TRACK && truncate && carried_part_gone<SA>(h, g)) return false;
+    if (more)
+      st.commit(s.ring, sl ^ 1, min(kTB, t1 - tn), k, p.E, lane, gate_bad, escale, uscale);
+    tb = tn;
+    return true;
+  };
+
+  int slot = 0;  // ring slot and buffer of the block at tb
+  if (full_tile && K > 0) {
+    // whole blocks in pairs: slot 0 with xa/ra, then slot 1 with xb/rb
+    const std::integral_constant<int, 0> s0;
+    const std::integral_constant<int, 1> s1;
+    while (tb + kTB <= t1) {
+      if (!fast_block(s0, xa, ra, xb, rb)) return;
+      if (tb + kTB > t1) {
+        slot = 1;
+        break;
+      }
+      if (!fast_block(s1, xb, rb, xa, ra)) return;
+    }
+    if (tb >= t1) return;
+    if (slot == 1) {
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        xa[i] = xb[i];
+        ra[i] = rb[i];
+      }
+    }
+  }
+  // Guarded blocks: the ragged tail of a full tile, or every block of a
+  // ragged tile or of a runtime k (the block at tb is in slot `slot`, xa/ra).
+  for (; tb < t1; slot ^= 1) {
     const int n = min(kTB, t1 - tb);
     const int tn = tb + kTB;
     const bool more = tn < t1;
     if (more) {
       st.issue(p, row + tn, valid_at(tn), k);
-      load_xr(tn, xn, rn);
+      load_xr(tn, xb, rb);
     }
     wave_sync();
     // stores past the block's n tokens fall outside this buffer and are dropped
     const stage::rsrc_t ry = stage::rows_rsrc<TOut>(p.y, row + tb, n, D);
-    // full blocks on full tiles run as one branch-free basic block of kTB
-    // tokens, so the scheduler can overlap a token's LDS reads with the
-    // previous token's arithmetic; the ragged tail keeps its guards
-    const bool fast = n == kTB && full_tile;
-    if constexpr (K > 0) {
-      if (fast) {
 #pragma unroll
-        for (int i = 0; i < kTB; ++i) {
-          int ev[K];
-          float gv[K];
-#pragma unroll
-          for (int j = 0; j < K; ++j) {
-            ev[j] = s.ring.e[(slot * kTB + i) * K + j];
-            gv[j] = s.ring.g[(slot * kTB + i) * K + j];
-          }
-          const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, ms, ev, gv, slot, i, lane,
-                                                      to_f32(xc[i]), to_f32(rc[i]), h, g);
-          stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kTB; ++i) {
-          if (i < n) {
-            int ev[K];
-            float gv[K];
-#pragma unroll
-            for (int j = 0; j < K; ++j) {
-              ev[j] = s.ring.e[(slot * kTB + i) * K + j];
-              gv[j] = s.ring.g[(slot * kTB + i) * K + j];
-            }
-            const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
-            const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, ms, ev, gv, slot, i, lane, xv, rv,
-                                                        h, g);
-            if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kTB; ++i) {
-        if (i < n) {
-          int eb[16];
-          float gb[16];
-          for (int j = 0; j < k; ++j) {
-            eb[j] = s.ring.e[(slot * kTB + i) * k + j];
-            gb[j] = s.ring.g[(slot * kTB + i) * k + j];
-          }
-          const float xv = active ? to_f32(xc[i]) : 0.f, rv = active ? to_f32(rc[i]) : 0.f;
-          const float yv = mix_token<K, TRACK, ACC_U, SA, ZOH>(p, s, ms, eb, gb, slot, i, lane, xv, rv, h,
-                                                      g);
-          if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
-        }
+    for (int i = 0; i < kTB; ++i) {
+      if (i < n) {
+        const float xv = active ? to_f32(xa[i]) : 0.f, rv = active ? to_f32(ra[i]) : 0.f;
+        const float yv = ring_token<K, TRACK, ACC_U, SA, ZOH>(p, s, slot, i, lane, xv, rv, h, g);
+        if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
       }
     }
-    if (TRACK && truncate) {
-      float mh = 0.f;
-#pragma unroll
-      for (int q = 0; q < kN; ++q) mh = fmaxf(mh, fabsf(h[q]));
-      const float thr = fmaxf(kFixupTol * mh, kTiny);
-      bool conv = true;
-      if constexpr (SA) {
-        conv = fabsf(g[0]) * g[1] <= thr;  // g[1] = max_n |h_in[n]|; NaN: not converged
-      } else {
-#pragma unroll
-        for (int q = 0; q < kN; ++q) conv &= fabsf(g[q]) <= thr;  // NaN: not converged
-      }
-      if (__all(conv)) break;
-    }
+    if (TRACK && truncate && carried_part_gone<SA>(h, g)) return;
     if (more) {
-      st.commit(s.ring, slot ^ 1, min(kTB, t1 - tn), k, p.E, lane, gate_bad);
+      st.commit(s.ring, slot ^ 1, min(kTB, t1 - tn), k, p.E, lane, gate_bad, escale, uscale);
 #pragma unroll
       for (int i = 0; i < kTB; ++i) {
-        xc[i] = xn[i];
-        rc[i] = rn[i];
+        xa[i] = xb[i];
+        ra[i] = rb[i];
       }
     }
+    tb = tn;
   }
 }
 
-// Pass 1 (or the only pass when CHUNKED is false).
-template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA, bool ZOH>
+// Pass 1 (or the only pass when CHUNKED is false).  EMAX >= E: columns of
+// each wave's sums U_e.
+template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA, bool ZOH,
+          int EMAX>
 __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
+  __shared__ float usum[CHUNKED ? WAVES * EMAX * 64 : 1];
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, wave, SA);
+  Smem s = smem_layout(p.E, K > 0 ? K : p.k, wave, SA);
+  if (CHUNKED) s.U = usum + wave * EMAX * 64;
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
   const int tile = bid % p.ntiles;
@@ -459,7 +540,9 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
 
-  int bad = stage::load_table(p, s.A, s.BD, d0, SA);
+  int bad = load_table(p, const_cast<float4*>(s.T), d0, SA);
+  if (CHUNKED)
+    for (int e = 0; e < p.E; ++e) s.U[e * 64 + lane] = 0.f;
   bad = __syncthreads_or(bad);
 
   const int c = cg * WAVES + wave;
@@ -475,21 +558,36 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   // every chunk writes y (provisional for chunks >= 1, recomputed by the
   // fix-up pass where the carried-in state still matters)
   int gate_bad = 0;
-  // the chunk's summed exponents (SA: ms[0] only)
-  float ms[kN];
-#pragma unroll
-  for (int n = 0; n < kN; ++n) ms[n] = 0.f;
-  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH>(p, s, ms, b, t0, t1, d, active, d0 + 64 <= p.D,
-                                              lane, false, h, nullptr, gate_bad);
+  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH>(p, s, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
+                                              false, h, nullptr, gate_bad);
 
   if (CHUNKED) {
-    // total decay of the chunk: P[n] = exp2(sum_t m_t[n]); with SA one decay
-    // per channel, written to every state row for the carry pass
+    // total decay of the chunk: P[n] = exp2(sum_e U_e A[e, d, n] log2 e); with
+    // SA one decay per channel, written to every state row for the carry pass
+    float lg[SA ? 1 : kN];
+#pragma unroll
+    for (int n = 0; n < (SA ? 1 : kN); ++n) lg[n] = 0.f;
+    for (int e = 0; e < p.E; ++e) {
+      const float u = s.U[e * 64 + lane];
+      const float4* te = s.T + e * (SA ? 64 : kRowsDiag * 64) + lane;
+      if constexpr (SA) {
+        lg[0] = fmaf(u, te[0].x, lg[0]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 a = te[q * 64];
+          lg[4 * q + 0] = fmaf(u, a.x, lg[4 * q + 0]);
+          lg[4 * q + 1] = fmaf(u, a.y, lg[4 * q + 1]);
+          lg[4 * q + 2] = fmaf(u, a.z, lg[4 * q + 2]);
+          lg[4 * q + 3] = fmaf(u, a.w, lg[4 * q + 3]);
+        }
+      }
+    }
     if (active) {
       const size_t base = (((size_t)b * p.nchunks + c) * kN) * p.D + d;
 #pragma unroll
       for (int n = 0; n < kN; ++n) {
-        p.P[base + (size_t)n * p.D] = hw_exp2(ms[SA ? 0 : n]);
+        p.P[base + (size_t)n * p.D] = hw_exp2(lg[SA ? 0 : n]);
         p.H[base + (size_t)n * p.D] = h[n];
       }
     }
@@ -516,7 +614,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const int b = bid / ncg;
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
-  stage::load_table(p, s.A, s.BD, d0, SA);
+  load_table(p, const_cast<float4*>(s.T), d0, SA);
   __syncthreads();
 
   const int c = 1 + cg * WAVES + wave;
@@ -541,11 +639,11 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const bool truncate = p.carry == SWIMBA_CARRY_FIXUP &&
                         p.flags[((size_t)b * p.nchunks + c) * p.ntiles + tile] == 0;
   int gate_bad = 0;
-  walk<TIn, TOut, K, true, false, SA, ZOH>(p, s, nullptr, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
-                                  truncate, h, g, gate_bad);
+  walk<TIn, TOut, K, true, false, SA, ZOH>(p, s, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
+                                           truncate, h, g, gate_bad);
 }
 
-template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH>
+template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH, int EMAX>
 int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   MixParams p;
   p.B = a->B;
@@ -580,8 +678,8 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   if (pl.nchunks <= 1) {
     p.nchunks = 1;
     dim3 grid((unsigned)((size_t)p.B * p.ntiles));
-    allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH>, smem3);
-    const int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH>, grid,
+    allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH, EMAX>, smem3);
+    const int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH, EMAX>, grid,
                                 dim3(WAVES * 64), smem3, st, ev, p);
     if (rc != SWIMBA_OK) return rc;
     record_skipped(ev ? ev + 2 : nullptr, st);
@@ -590,29 +688,35 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   }
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   dim3 grid1((unsigned)((size_t)p.B * ncg * p.ntiles));
-  allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH>, smem1);
-  int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH>, grid1, dim3(WAVES * 64),
-                        smem1, st, ev, p);
+  allow_dynamic_lds(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH, EMAX>, smem1);
+  int rc = launch_timed(mix_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH, EMAX>, grid1,
+                        dim3(WAVES * 64), smem1, st, ev, p);
   if (rc != SWIMBA_OK) return rc;
   rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 0, st, ev ? ev + 2 : nullptr);
   if (rc != SWIMBA_OK) return rc;
   const int ncg3 = (p.nchunks - 1 + WAVES - 1) / WAVES;
   dim3 grid3((unsigned)((size_t)p.B * ncg3 * p.ntiles));
   allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH>, smem3);
-  return launch_timed(mix_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH>, grid3, dim3(WAVES * 64), smem3, st,
-                      ev ? ev + 4 : nullptr, p);
+  return launch_timed(mix_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH>, grid3, dim3(WAVES * 64),
+                      smem3, st, ev ? ev + 4 : nullptr, p);
+}
+
+template <typename TIn, typename TOut, int WAVES, bool SA, bool ZOH, int EMAX>
+int launch_mixed_e(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
+  switch (a->k) {
+    case 1:
+      return launch_mixed_t<TIn, TOut, WAVES, 1, SA, ZOH, EMAX>(a, pl, ws, st);
+    case 2:
+      return launch_mixed_t<TIn, TOut, WAVES, 2, SA, ZOH, EMAX>(a, pl, ws, st);
+    default:
+      return launch_mixed_t<TIn, TOut, WAVES, 0, SA, ZOH, EMAX>(a, pl, ws, st);
+  }
 }
 
 template <typename TIn, typename TOut, int WAVES, bool SA, bool ZOH>
 int launch_mixed_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
-  switch (a->k) {
-    case 1:
-      return launch_mixed_t<TIn, TOut, WAVES, 1, SA, ZOH>(a, pl, ws, st);
-    case 2:
-      return launch_mixed_t<TIn, TOut, WAVES, 2, SA, ZOH>(a, pl, ws, st);
-    default:
-      return launch_mixed_t<TIn, TOut, WAVES, 0, SA, ZOH>(a, pl, ws, st);
-  }
+  if (a->E <= 8) return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 8>(a, pl, ws, st);
+  return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 16>(a, pl, ws, st);
 }
 
 template <typename TIn, typename TOut, int WAVES, bool SA>
