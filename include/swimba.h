@@ -131,7 +131,8 @@ typedef struct {
   const void* dt_raw;           /* [B, L, D]  step size before bias and softplus          */
   const void* Bm;               /* [B, L, N]  selective input vector B_t (16-byte aligned)  */
   const void* Cm;               /* [B, L, N]  selective output vector C_t (16-byte aligned) */
-  const int32_t* idx;           /* [B, L, k]  routing, 0 <= idx < E                       */
+  const int32_t* idx;           /* [B, L, k]  routing, 0 <= idx < E (values outside are
+                                   not reported: the kernels clamp them to 0 or E-1)    */
   const float* gate;            /* [B, L, k]  routing weights                             */
   const float* A;               /* [E, D, N]  per-expert diagonal transition (< 0);
                                    [E, D] with a_form SCALAR                            */
@@ -187,9 +188,11 @@ int swimba_scan_plan(const swimba_scan_args* a, int design, int* chunk, int* nch
  * "Mamba": exp(Delta A) transition, Figure 2 on-chip state).
  *   ws, ws_bytes: device workspace of at least swimba_scan_workspace_size(a,0)
  *   bytes, 256-byte aligned; its contents on entry do not matter.
- * Constraints: B, L >= 0; D >= 1; N == 16; 1 <= k <= E <= 16 (the selected
- * experts' tables are staged in LDS); chunk >= 0.  L == 0 writes h_final = h0
- * (or zeros).
+ * Constraints: B, L >= 0; D >= 1; N == 16; 1 <= k <= E <= 64; chunk >= 0;
+ * with E > 16, E * D * 64 < 2^31 (SWIMBA_EUNSUPPORTED otherwise).  Up to 16
+ * experts the expert tables are staged in LDS; with more, each token's
+ * selected expert rows are read from memory (slower per token).  L == 0
+ * writes h_final = h0 (or zeros).
  */
 int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -287,7 +290,7 @@ typedef struct {
  *   forward's disc must be EULER; ZOH returns SWIMBA_EUNSUPPORTED).  It
  *   holds every state h_t (64 bytes per token and channel) besides the
  *   chunk records.
- * Constraints: those of swimba_scan (E <= 16) with a_form DIAGONAL (SCALAR
+ * Constraints: those of swimba_scan with E <= 16 and a_form DIAGONAL (SCALAR
  * returns SWIMBA_EUNSUPPORTED).  B == 0 or L == 0 writes zero parameter gradients
  * and dh0 = dh_final (or zeros).  Every output is deterministic.
  */
@@ -303,7 +306,8 @@ typedef struct {
   const void* Bm;               /* [B, N]                                        */
   const void* Cm;               /* [B, N]                                        */
   const float* Wr;              /* [D, E]: route this token when idx == NULL     */
-  const int32_t* idx;           /* NULL, or forced routing [B, k]                */
+  const int32_t* idx;           /* NULL, or forced routing [B, k], 0 <= idx < E
+                                   (values outside are clamped to 0 or E-1)      */
   const float* gate;            /* [B, k] with idx                               */
   int32_t* idx_out;             /* NULL, or [B, k]: routing used                 */
   float* gate_out;              /* NULL, or [B, k]                               */

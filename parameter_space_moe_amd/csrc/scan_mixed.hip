@@ -64,7 +64,33 @@ __global__ __launch_bounds__(256) void mix_carry_kernel(int B, int C, int D, int
   }
 }
 
+// Contraction check of the expert tables for the scans that read expert rows
+// from memory: flags[tile] = 1 if any A[e, d, :] of the tile's 64 channels is
+// not strictly negative (or NaN).  One workgroup per tile; consecutive
+// threads read consecutive floats of each expert's block.
+__global__ __launch_bounds__(256) void a_flags_kernel(const float* __restrict__ A, int E, int D,
+                                                      int scalar_a, int32_t* __restrict__ flags) {
+  const int tile = blockIdx.x, d0 = tile * 64;
+  const int per = scalar_a ? 1 : kN;
+  const int nd = min(64, D - d0);
+  int bad = 0;
+  for (int i = threadIdx.x; i < E * nd * per; i += blockDim.x) {
+    const int e = i / (nd * per), r = i % (nd * per);
+    const float a = A[((size_t)e * D + d0) * per + r];
+    bad |= !(a < 0.f);
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) flags[tile] = bad ? 1 : 0;
+}
+
 }  // namespace mixed
+
+int launch_a_flags(const float* A, int E, int D, bool scalar_a, int32_t* flags, hipStream_t st) {
+  const int ntiles = (D + 63) / 64;
+  hipLaunchKernelGGL(mixed::a_flags_kernel, dim3((unsigned)ntiles), dim3(256), 0, st, A, E, D,
+                     scalar_a ? 1 : 0, flags);
+  return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
+}
 
 int launch_scan_ff(const swimba_scan_args*, const ScanPlan&, void*, hipStream_t);
 int launch_scan_fb(const swimba_scan_args*, const ScanPlan&, void*, hipStream_t);

@@ -19,6 +19,11 @@
 // and five conflict-free reads per token.  The waves of a workgroup are
 // consecutive chunks of the same channel tile and share that table.
 //
+// More than 16 experts do not fit that table (5 KiB per expert and tile):
+// then each selected expert's rows are read from memory per token (A is
+// L2-resident), with buffer loads at the expert's offset, and the chunk
+// decays are summed in registers.
+//
 // The walk runs pairs of 8-token blocks with the two ring slots and two x /
 // dt_raw buffers fixed in the code (no register copies between blocks); a
 // ragged tail block or a ragged tile takes a guarded path after the full
@@ -79,6 +84,16 @@ struct MixParams {
   float* P;           // [B][C][16][D] chunk decays
   float* H;           // [B][C][16][D] chunk end states, then carried-in states
   int32_t* flags;     // [B][C][ntiles] 1 = contraction not guaranteed
+  const int32_t* tflags;  // [ntiles] 1 = some A of the tile is not negative (rows
+                          // read from memory; the table path checks while staging)
+};
+
+// Expert rows read from memory per token (more experts than the LDS table
+// holds): buffers over A, dt_bias and Dskip, and the lane's offsets into a
+// row (past every buffer for lanes beyond D: those loads return 0).
+struct Rows {
+  stage::rsrc_t a, bias, dsk;
+  uint32_t voa, vob;
 };
 
 __host__ __device__ inline int table_rows(bool scalar_a) { return scalar_a ? 1 : kRowsDiag; }
@@ -215,23 +230,48 @@ __device__ __forceinline__ float update_readout(const float4* bc, const float* m
 // time.  Routing (experts e[j], gates gw[j]) is wave-uniform; each selected
 // expert's table block is read with one address and all of the token's table
 // reads are issued together.  ACC_U: add Delta g_j to the wave's sums U_e.
-template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ float mix_token_k(const Smem& s, const int* e, const int* uo,
-                                             const float* gw, const float4* bc, int lane,
-                                             float xv, float rv, float* h, float* g) {
+template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH, bool TAB>
+__device__ __forceinline__ float mix_token_k(const Smem& s, const Rows& R, float* ms,
+                                             const int* e, const int* uo, const float* gw,
+                                             const float4* bc, int lane, float xv, float rv,
+                                             float* h, float* g) {
   float4 bd[K];
   float4 ar[SA ? 1 : K][4];
   float uold[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    if (ACC_U) uold[j] = *usum_at(s.U, uo[j], lane);
-    const float4* te = expert_rows(s, e[j], lane);
-    if constexpr (SA) {
-      bd[j] = te[0];  // (A log2 e, dt_bias, Dskip, 0)
-    } else {
+    if constexpr (TAB) {
+      if (ACC_U) uold[j] = *usum_at(s.U, uo[j], lane);
+      const float4* te = expert_rows(s, e[j], lane);
+      if constexpr (SA) {
+        bd[j] = te[0];  // (A log2 e, dt_bias, Dskip, 0)
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ar[j][q] = te[q * 64];
-      bd[j] = te[4 * 64];  // (dt_bias, Dskip, 0, 0)
+        for (int q = 0; q < 4; ++q) ar[j][q] = te[q * 64];
+        bd[j] = te[4 * 64];  // (dt_bias, Dskip, 0, 0)
+      }
+    }
+  }
+  if constexpr (!TAB) {
+    // rows from memory: e[j] and uo[j] are the byte offsets of the expert's
+    // A block and of its dt_bias / Dskip entries (wave-uniform)
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const uint32_t soa = (uint32_t)uniform(e[j]), sob = (uint32_t)uniform(uo[j]);
+      const float bj = stage::buf_load<float>(R.bias, R.vob, sob);
+      const float dj = stage::buf_load<float>(R.dsk, R.vob, sob);
+      if constexpr (SA) {
+        bd[j] = make_float4(stage::buf_load<float>(R.a, R.vob, sob), bj, dj, 0.f);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const stage::v4u v =
+              __builtin_amdgcn_raw_buffer_load_b128(R.a, (int)(R.voa + q * 16), (int)soa, 0);
+          ar[j][q] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y),
+                                 __uint_as_float(v.z), __uint_as_float(v.w));
+        }
+        bd[j] = make_float4(bj, dj, 0.f, 0.f);
+      }
     }
   }
   // mixed dt_bias and Dskip
@@ -242,9 +282,11 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, const int* e, const 
     delta = fmaf(gw[j], SA ? bd[j].z : bd[j].y, delta);
   }
   const float dlt = softplus_f32(rv + beta);
+  // rows from memory hold A itself: log2 e goes into u
+  const float dls = TAB ? dlt : dlt * kLog2e;
   float u[K];
 #pragma unroll
-  for (int j = 0; j < K; ++j) u[j] = dlt * gw[j];
+  for (int j = 0; j < K; ++j) u[j] = dls * gw[j];
   // mixed exponents m[n] = sum_j u_j A[e_j, d, n] log2 e
   float m[SA ? 1 : kN];
   if constexpr (SA) {
@@ -271,8 +313,11 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, const int* e, const 
         m[4 * q + 3] = fmaf(u[j], a.w, m[4 * q + 3]);
       }
   }
+  if (ACC_U && !TAB)
+#pragma unroll
+    for (int n = 0; n < (SA ? 1 : kN); ++n) ms[n] += m[n];
   const float yv = update_readout<TRACK, SA, ZOH>(bc, m, dlt * xv, h, g);
-  if (ACC_U) {
+  if (ACC_U && TAB) {
     // U_e += u_j; a slot that repeats an earlier slot's expert adds onto
     // that slot's new value (both were read before either store)
     float unew[K];
@@ -290,49 +335,80 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, const int* e, const 
 }
 
 // The same for k known only at run time (k > 2).
-template <bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ float mix_token_any(const Smem& s, int k, const int* e,
-                                               const int* uo, const float* gw,
+template <bool TRACK, bool ACC_U, bool SA, bool ZOH, bool TAB>
+__device__ __forceinline__ float mix_token_any(const Smem& s, const Rows& R, float* ms, int k,
+                                               const int* e, const int* uo, const float* gw,
                                                const float4* bc, int lane, float xv, float rv,
                                                float* h, float* g) {
   float beta = 0.f, delta = 0.f;
   for (int j = 0; j < k; ++j) {
-    const float4 bd = expert_rows(s, e[j], lane)[SA ? 0 : 4 * 64];
-    beta = fmaf(gw[j], SA ? bd.y : bd.x, beta);
-    delta = fmaf(gw[j], SA ? bd.z : bd.y, delta);
+    float bj, dj;
+    if constexpr (TAB) {
+      const float4 bd = expert_rows(s, e[j], lane)[SA ? 0 : 4 * 64];
+      bj = SA ? bd.y : bd.x;
+      dj = SA ? bd.z : bd.y;
+    } else {
+      const uint32_t sob = (uint32_t)uniform(uo[j]);
+      bj = stage::buf_load<float>(R.bias, R.vob, sob);
+      dj = stage::buf_load<float>(R.dsk, R.vob, sob);
+    }
+    beta = fmaf(gw[j], bj, beta);
+    delta = fmaf(gw[j], dj, delta);
   }
   const float dlt = softplus_f32(rv + beta);
+  const float dls = TAB ? dlt : dlt * kLog2e;
   float m[SA ? 1 : kN];
 #pragma unroll
   for (int n = 0; n < (SA ? 1 : kN); ++n) m[n] = 0.f;
   for (int j = 0; j < k; ++j) {
-    const float u = dlt * gw[j];
-    if (ACC_U) {
+    const float u = dls * gw[j];
+    if (ACC_U && TAB) {
       float* up = usum_at(s.U, uo[j], lane);
       *up = *up + u;
     }
-    const float4* te = expert_rows(s, e[j], lane);
-    if constexpr (SA) {
-      m[0] = fmaf(u, te[0].x, m[0]);
-    } else {
+    if constexpr (TAB) {
+      const float4* te = expert_rows(s, e[j], lane);
+      if constexpr (SA) {
+        m[0] = fmaf(u, te[0].x, m[0]);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 a = te[q * 64];
-        m[4 * q + 0] = fmaf(u, a.x, m[4 * q + 0]);
-        m[4 * q + 1] = fmaf(u, a.y, m[4 * q + 1]);
-        m[4 * q + 2] = fmaf(u, a.z, m[4 * q + 2]);
-        m[4 * q + 3] = fmaf(u, a.w, m[4 * q + 3]);
+        for (int q = 0; q < 4; ++q) {
+          const float4 a = te[q * 64];
+          m[4 * q + 0] = fmaf(u, a.x, m[4 * q + 0]);
+          m[4 * q + 1] = fmaf(u, a.y, m[4 * q + 1]);
+          m[4 * q + 2] = fmaf(u, a.z, m[4 * q + 2]);
+          m[4 * q + 3] = fmaf(u, a.w, m[4 * q + 3]);
+        }
+      }
+    } else {
+      const uint32_t soa = (uint32_t)uniform(e[j]), sob = (uint32_t)uniform(uo[j]);
+      if constexpr (SA) {
+        m[0] = fmaf(u, stage::buf_load<float>(R.a, R.vob, sob), m[0]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const stage::v4u v =
+              __builtin_amdgcn_raw_buffer_load_b128(R.a, (int)(R.voa + q * 16), (int)soa, 0);
+          m[4 * q + 0] = fmaf(u, __uint_as_float(v.x), m[4 * q + 0]);
+          m[4 * q + 1] = fmaf(u, __uint_as_float(v.y), m[4 * q + 1]);
+          m[4 * q + 2] = fmaf(u, __uint_as_float(v.z), m[4 * q + 2]);
+          m[4 * q + 3] = fmaf(u, __uint_as_float(v.w), m[4 * q + 3]);
+        }
       }
     }
   }
+  if (ACC_U && !TAB)
+#pragma unroll
+    for (int n = 0; n < (SA ? 1 : kN); ++n) ms[n] += m[n];
   const float yv = update_readout<TRACK, SA, ZOH>(bc, m, dlt * xv, h, g);
   return fmaf(delta, xv, yv);
 }
 
 // One token from ring slot `slot`, position i (routing read from the ring).
-template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ float ring_token(const MixParams& p, const Smem& s, int slot, int i,
-                                            int lane, float xv, float rv, float* h, float* g) {
+template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH, bool TAB>
+__device__ __forceinline__ float ring_token(const MixParams& p, const Smem& s, const Rows& R,
+                                            float* ms, int slot, int i, int lane, float xv,
+                                            float rv, float* h, float* g) {
   const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
   if constexpr (K > 0) {
     int ev[K], uv[K];
@@ -341,9 +417,10 @@ __device__ __forceinline__ float ring_token(const MixParams& p, const Smem& s, i
     for (int j = 0; j < K; ++j) {
       ev[j] = s.ring.e[(slot * kTB + i) * K + j];
       gv[j] = s.ring.g[(slot * kTB + i) * K + j];
-      uv[j] = ACC_U ? s.ring.uo[(slot * kTB + i) * K + j] : 0;
+      uv[j] = (ACC_U || !TAB) ? s.ring.uo[(slot * kTB + i) * K + j] : 0;
     }
-    return mix_token_k<K, TRACK, ACC_U, SA, ZOH>(s, ev, uv, gv, bc, lane, xv, rv, h, g);
+    return mix_token_k<K, TRACK, ACC_U, SA, ZOH, TAB>(s, R, ms, ev, uv, gv, bc, lane, xv, rv, h,
+                                                      g);
   } else {
     const int k = p.k;
     int eb[16], ub[16];
@@ -351,9 +428,10 @@ __device__ __forceinline__ float ring_token(const MixParams& p, const Smem& s, i
     for (int j = 0; j < k; ++j) {
       eb[j] = s.ring.e[(slot * kTB + i) * k + j];
       gb[j] = s.ring.g[(slot * kTB + i) * k + j];
-      ub[j] = ACC_U ? s.ring.uo[(slot * kTB + i) * k + j] : 0;
+      ub[j] = (ACC_U || !TAB) ? s.ring.uo[(slot * kTB + i) * k + j] : 0;
     }
-    return mix_token_any<TRACK, ACC_U, SA, ZOH>(s, k, eb, ub, gb, bc, lane, xv, rv, h, g);
+    return mix_token_any<TRACK, ACC_U, SA, ZOH, TAB>(s, R, ms, k, eb, ub, gb, bc, lane, xv, rv, h,
+                                                     g);
   }
 }
 
@@ -399,10 +477,11 @@ __device__ __forceinline__ void store_y2(stage::rsrc_t ry, uint32_t yoff, uint32
 // x, dt_raw and y go through per-block buffer resources (scalar token offsets,
 // a fixed per-lane channel offset); the prefetch of the next block is issued
 // before the current one computes and is waited on only when it is used.
-template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
-__device__ __forceinline__ void walk(const MixParams& p, const Smem& s, int b, int t0, int t1,
-                                     int d, bool active, bool full_tile, int lane, bool truncate,
-                                     float* h, float* g, int& gate_bad) {
+template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA, bool ZOH,
+          bool TAB>
+__device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* ms, int b, int t0,
+                                     int t1, int d, bool active, bool full_tile, int lane,
+                                     bool truncate, float* h, float* g, int& gate_bad) {
   constexpr int KW = (kTB * (K > 0 ? K : 16) + 63) / 64;
   const int k = K > 0 ? K : p.k;
   const int D = p.D;
@@ -416,6 +495,16 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, int b, i
   TIn xa[kTB], ra[kTB], xb[kTB], rb[kTB];
   stage::Stager<TIn, KW> st;
   st.init(lane);
+  Rows R;
+  if constexpr (!TAB) {
+    const uint32_t nab = (uint32_t)p.E * (uint32_t)D * (SA ? 4u : (uint32_t)kN * 4u);
+    const uint32_t nbb = (uint32_t)p.E * (uint32_t)D * 4u;
+    R.a = stage::make_rsrc(p.A, nab);
+    R.bias = stage::make_rsrc(p.bias, nbb);
+    R.dsk = stage::make_rsrc(p.Dsk, nbb);
+    R.voa = active ? (uint32_t)d * (uint32_t)kN * 4u : stage::kOffNone;
+    R.vob = active ? (uint32_t)d * 4u : stage::kOffNone;
+  }
   auto valid_at = [&](int t) { return (int)min((size_t)kTB, total - (row + t)); };
   auto load_xr = [&](int t, TIn* xs, TIn* rs) {
     const int v = valid_at(t);
@@ -433,7 +522,10 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, int b, i
 
   st.issue(p, row + t0, valid_at(t0), k);
   load_xr(t0, xa, ra);
-  const int escale = expert_stride(SA), uscale = 64 * 4;
+  // ring offsets: table rows and sum columns, or (rows from memory) the
+  // expert's A block and its dt_bias / Dskip row
+  const int escale = TAB ? expert_stride(SA) : D * (SA ? 4 : kN * 4);
+  const int uscale = TAB ? 64 * 4 : D * 4;
   st.commit(s.ring, 0, min(kTB, t1 - t0), k, p.E, lane, gate_bad, escale, uscale);
 
   int tb = t0;
@@ -453,10 +545,10 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, int b, i
     const stage::rsrc_t ry = stage::rows_rsrc<TOut>(p.y, row + tb, kTB, D);
 #pragma unroll
     for (int i = 0; i < kTB; i += 2) {
-      const float y0 = ring_token<K, TRACK, ACC_U, SA, ZOH>(p, s, sl, i, lane, to_f32(xc[i]),
-                                                            to_f32(rc[i]), h, g);
-      const float y1 = ring_token<K, TRACK, ACC_U, SA, ZOH>(
-          p, s, sl, i + 1, lane, to_f32(xc[i + 1]), to_f32(rc[i + 1]), h, g);
+      const float y0 = ring_token<K, TRACK, ACC_U, SA, ZOH, TAB>(
+          p, s, R, ms, sl, i, lane, to_f32(xc[i]), to_f32(rc[i]), h, g);
+      const float y1 = ring_token<K, TRACK, ACC_U, SA, ZOH, TAB>(
+          p, s, R, ms, sl, i + 1, lane, to_f32(xc[i + 1]), to_f32(rc[i + 1]), h, g);
       store_y2<TOut>(ry, yoff, yrow, i, y0, y1);
     }
     if (TRACK && truncate && carried_part_gone<SA>(h, g)) return false;
@@ -467,7 +559,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, int b, i
   };
 
   int slot = 0;  // ring slot and buffer of the block at tb
-  if (full_tile && K > 0) {
+  if (full_tile && K > 0 && TAB) {
     // whole blocks in pairs: slot 0 with xa/ra, then slot 1 with xb/rb
     const std::integral_constant<int, 0> s0;
     const std::integral_constant<int, 1> s1;
@@ -489,7 +581,8 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, int b, i
     }
   }
   // Guarded blocks: the ragged tail of a full tile, or every block of a
-  // ragged tile or of a runtime k (the block at tb is in slot `slot`, xa/ra).
+  // ragged tile, of a runtime k or with expert rows read from memory (the
+  // block at tb is in slot `slot`, xa/ra).
   for (; tb < t1; slot ^= 1) {
     const int n = min(kTB, t1 - tb);
     const int tn = tb + kTB;
@@ -505,7 +598,8 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, int b, i
     for (int i = 0; i < kTB; ++i) {
       if (i < n) {
         const float xv = active ? to_f32(xa[i]) : 0.f, rv = active ? to_f32(ra[i]) : 0.f;
-        const float yv = ring_token<K, TRACK, ACC_U, SA, ZOH>(p, s, slot, i, lane, xv, rv, h, g);
+        const float yv =
+            ring_token<K, TRACK, ACC_U, SA, ZOH, TAB>(p, s, R, ms, slot, i, lane, xv, rv, h, g);
         if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
       }
     }
@@ -524,13 +618,16 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, int b, i
 
 // Pass 1 (or the only pass when CHUNKED is false).  EMAX >= E: columns of
 // each wave's sums U_e.
+// EMAX > 16: the selected experts' rows come from memory (no table; the
+// chunk decays are summed in registers).
 template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA, bool ZOH,
           int EMAX>
 __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
-  __shared__ float usum[CHUNKED ? WAVES * EMAX * 64 : 1];
+  constexpr bool TAB = EMAX <= 16;
+  __shared__ float usum[CHUNKED && TAB ? WAVES * EMAX * 64 : 1];
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  Smem s = smem_layout(p.E, K > 0 ? K : p.k, wave, SA);
-  if (CHUNKED) s.U = usum + wave * EMAX * 64;
+  Smem s = smem_layout(TAB ? p.E : 0, K > 0 ? K : p.k, wave, SA);
+  if (CHUNKED && TAB) s.U = usum + wave * EMAX * 64;
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
   const int tile = bid % p.ntiles;
@@ -540,10 +637,15 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
 
-  int bad = load_table(p, const_cast<float4*>(s.T), d0, SA);
-  if (CHUNKED)
-    for (int e = 0; e < p.E; ++e) s.U[e * 64 + lane] = 0.f;
-  bad = __syncthreads_or(bad);
+  int bad = 0;
+  if constexpr (TAB) {
+    bad = load_table(p, const_cast<float4*>(s.T), d0, SA);
+    if (CHUNKED)
+      for (int e = 0; e < p.E; ++e) s.U[e * 64 + lane] = 0.f;
+    bad = __syncthreads_or(bad);
+  } else if (CHUNKED) {
+    bad = p.tflags[tile];
+  }
 
   const int c = cg * WAVES + wave;
   if (c >= p.nchunks) return;  // no barrier below
@@ -558,16 +660,18 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   // every chunk writes y (provisional for chunks >= 1, recomputed by the
   // fix-up pass where the carried-in state still matters)
   int gate_bad = 0;
-  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH>(p, s, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
-                                              false, h, nullptr, gate_bad);
+  float lg[SA ? 1 : kN];  // the chunk's exponent sums (rows from memory)
+#pragma unroll
+  for (int n = 0; n < (SA ? 1 : kN); ++n) lg[n] = 0.f;
+  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH, TAB>(p, s, lg, b, t0, t1, d, active,
+                                                   d0 + 64 <= p.D, lane, false, h, nullptr,
+                                                   gate_bad);
 
   if (CHUNKED) {
-    // total decay of the chunk: P[n] = exp2(sum_e U_e A[e, d, n] log2 e); with
-    // SA one decay per channel, written to every state row for the carry pass
-    float lg[SA ? 1 : kN];
-#pragma unroll
-    for (int n = 0; n < (SA ? 1 : kN); ++n) lg[n] = 0.f;
-    for (int e = 0; e < p.E; ++e) {
+    // total decay of the chunk: P[n] = exp2(sum_e U_e A[e, d, n] log2 e) (table
+    // path; rows from memory: the summed exponents); with SA one decay per
+    // channel, written to every state row for the carry pass
+    for (int e = 0; e < (TAB ? p.E : 0); ++e) {
       const float u = s.U[e * 64 + lane];
       const float4* te = s.T + e * (SA ? 64 : kRowsDiag * 64) + lane;
       if constexpr (SA) {
@@ -601,10 +705,11 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
 
 // Pass 3: chunks 1.. re-run from their carried-in state until the carried part
 // has decayed away (or to the chunk's end).
-template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH>
+template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH, int EMAX>
 __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
+  constexpr bool TAB = EMAX <= 16;
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const Smem s = smem_layout(p.E, K > 0 ? K : p.k, wave, SA);
+  const Smem s = smem_layout(TAB ? p.E : 0, K > 0 ? K : p.k, wave, SA);
   const int nfix = p.nchunks - 1;
   const int ncg = (nfix + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
@@ -614,8 +719,10 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const int b = bid / ncg;
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
-  load_table(p, const_cast<float4*>(s.T), d0, SA);
-  __syncthreads();
+  if constexpr (TAB) {
+    load_table(p, const_cast<float4*>(s.T), d0, SA);
+    __syncthreads();
+  }
 
   const int c = 1 + cg * WAVES + wave;
   if (c >= p.nchunks) return;
@@ -639,8 +746,8 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const bool truncate = p.carry == SWIMBA_CARRY_FIXUP &&
                         p.flags[((size_t)b * p.nchunks + c) * p.ntiles + tile] == 0;
   int gate_bad = 0;
-  walk<TIn, TOut, K, true, false, SA, ZOH>(p, s, b, t0, t1, d, active, d0 + 64 <= p.D, lane,
-                                           truncate, h, g, gate_bad);
+  walk<TIn, TOut, K, true, false, SA, ZOH, TAB>(p, s, nullptr, b, t0, t1, d, active,
+                                                d0 + 64 <= p.D, lane, truncate, h, g, gate_bad);
 }
 
 template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH, int EMAX>
@@ -672,8 +779,17 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
   p.flags = pl.nchunks > 1 ? reinterpret_cast<int32_t*>(w + pl.off_flags) : nullptr;
 
-  const size_t smem1 = smem_bytes(p.E, p.k, WAVES, SA);
+  constexpr bool TAB = EMAX <= 16;
+  const size_t smem1 = smem_bytes(TAB ? p.E : 0, p.k, WAVES, SA);
   const size_t smem3 = smem1;
+  p.tflags = nullptr;
+  if (!TAB && pl.nchunks > 1) {
+    // contraction check of every tile's A (the table path checks while staging)
+    int32_t* tf = reinterpret_cast<int32_t*>(w + pl.off_tflags);
+    p.tflags = tf;
+    const int rc = launch_a_flags(p.A, p.E, p.D, SA, tf, st);
+    if (rc != SWIMBA_OK) return rc;
+  }
   const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
   if (pl.nchunks <= 1) {
     p.nchunks = 1;
@@ -696,8 +812,8 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   if (rc != SWIMBA_OK) return rc;
   const int ncg3 = (p.nchunks - 1 + WAVES - 1) / WAVES;
   dim3 grid3((unsigned)((size_t)p.B * ncg3 * p.ntiles));
-  allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH>, smem3);
-  return launch_timed(mix_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH>, grid3, dim3(WAVES * 64),
+  allow_dynamic_lds(mix_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH, EMAX>, smem3);
+  return launch_timed(mix_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH, EMAX>, grid3, dim3(WAVES * 64),
                       smem3, st, ev ? ev + 4 : nullptr, p);
 }
 
@@ -716,7 +832,8 @@ int launch_mixed_e(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
 template <typename TIn, typename TOut, int WAVES, bool SA, bool ZOH>
 int launch_mixed_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   if (a->E <= 8) return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 8>(a, pl, ws, st);
-  return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 16>(a, pl, ws, st);
+  if (a->E <= 16) return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 16>(a, pl, ws, st);
+  return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 64>(a, pl, ws, st);
 }
 
 template <typename TIn, typename TOut, int WAVES, bool SA>

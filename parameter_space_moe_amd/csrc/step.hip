@@ -108,10 +108,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     // are read as 16-byte vectors when E is a multiple of 4 (one cache-line
     // visit per row instead of one per expert).
     const bool vec = (p.E & 3) == 0 && (reinterpret_cast<uintptr_t>(p.Wr) & 15) == 0;
-    // Every workgroup reads all of Wr at the same time; starting each at a
-    // different channel spreads the reads over the L2 channels instead of
-    // sending all compute units to the same lines at once.
-    const int rot = (int)(((long long)blockIdx.x * 1031) % p.D);
+    // Every workgroup reads all of Wr at the same time; starting each row at
+    // a different channel spreads the reads over the L2 channels instead of
+    // sending all compute units to the same lines at once.  The rotation
+    // depends on the row only: the slices of a row add the same products in
+    // the same order, so they compute bit-identical logits and agree on the
+    // routing even at a near-tie.
+    const int rot = (int)(((long long)b * 1031) % p.D);
     for (int eb = 0; eb < p.E; eb += 8) {
       const bool two = eb + 4 < p.E;  // the block's second group of 4 exists
       float part[8];

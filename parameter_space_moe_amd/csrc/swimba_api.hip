@@ -38,9 +38,12 @@ int validate_scan(const swimba_scan_args* a, int design) {
   if (a->N != SWIMBA_STATE_N) return SWIMBA_EUNSUPPORTED;
   if (a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
   if (separate && a->E > 16) return SWIMBA_EUNSUPPORTED;
-  // the mixed and per-slot scans stage E tables of 4.5 KiB (plus per-wave
-  // sums) in LDS
-  if (!separate && a->E > 16) return SWIMBA_EUNSUPPORTED;
+  // the per-slot scan stages the E expert tables in LDS
+  if (design == 2 && a->E > 16) return SWIMBA_EUNSUPPORTED;
+  // the mixed scan with more than 16 experts reads expert rows through 32-bit
+  // buffer offsets
+  if (design == 0 && a->E > 16 && (size_t)a->E * a->D * SWIMBA_STATE_N * 4 > 0x7fffffffu)
+    return SWIMBA_EUNSUPPORTED;
   // per-slot scan: k x 16 states per lane in registers
   if (design == 2 && a->k > 4) return SWIMBA_EUNSUPPORTED;
   return SWIMBA_OK;
@@ -123,7 +126,7 @@ int auto_chunk(long long B, long long L, int ntiles, bool separate, bool small_o
 // Chunk count and the P / H (/ flags) workspace of a chunked scan whose
 // chunk pass writes `rows` state rows per (sequence, chunk, channel).
 void plan_layout(const ScanPlan& in, int B, int L, int D, int chunk, size_t rows, bool flags,
-                 ScanPlan* p) {
+                 bool tflags, ScanPlan* p) {
   *p = in;
   if (chunk > L) chunk = L;
   p->chunk = chunk;
@@ -133,8 +136,9 @@ void plan_layout(const ScanPlan& in, int B, int L, int D, int chunk, size_t rows
     p->off_P = 0;
     p->off_H = align256(arr);
     p->off_flags = p->off_H + align256(arr);
-    p->bytes = p->off_flags +
-               (flags ? align256((size_t)B * p->nchunks * p->ntiles * sizeof(int32_t)) : 0);
+    p->off_tflags = p->off_flags +
+                    (flags ? align256((size_t)B * p->nchunks * p->ntiles * sizeof(int32_t)) : 0);
+    p->bytes = p->off_tflags + (tflags ? align256((size_t)p->ntiles * sizeof(int32_t)) : 0);
   }
 }
 
@@ -154,10 +158,11 @@ int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p, int dev) {
   bool small = false;  // mixed scan with too little work for four waves per SIMD
   const int chunk =
       a->chunk > 0 ? a->chunk
-                   : auto_chunk(a->B, a->L, q.ntiles, separate, slots || a->E <= 8, &small, dev);
+                   : auto_chunk(a->B, a->L, q.ntiles, separate,
+                                slots || a->E <= 8 || a->E > 16, &small, dev);
   const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N
                                : (slots ? (size_t)a->k * SWIMBA_STATE_N : SWIMBA_STATE_N);
-  plan_layout(q, a->B, a->L, a->D, chunk, rows, true, p);
+  plan_layout(q, a->B, a->L, a->D, chunk, rows, true, !separate && !slots && a->E > 16, p);
   // chunks of one tile share the workgroup's expert table: 8 waves when there
   // are enough chunks to fill them (and the problem is not the small case)
   if (!separate && !slots && p->nchunks >= 8 && !small) p->waves = 8;
@@ -172,6 +177,8 @@ int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p, int dev) {
   if (rc != SWIMBA_OK) return rc;
   if (!dtype_ok(g->dy_dtype)) return SWIMBA_EINVAL;
   if (a->a_form != SWIMBA_A_DIAGONAL || a->disc != SWIMBA_DISC_EULER) return SWIMBA_EUNSUPPORTED;
+  // the backward's passes stage the E expert tables in LDS
+  if (a->E > 16) return SWIMBA_EUNSUPPORTED;
   *p = BwdPlan();
   p->waves = backward_lds_bytes(a->E, a->k, 8) <= 80 * 1024 ? 8 : 4;
   if (backward_lds_bytes(a->E, a->k, p->waves) > 160 * 1024 ||
@@ -234,7 +241,7 @@ int plan_streams(const swimba_stream_args* a, ScanPlan* p, int dev) {
   // no expert table in LDS: every problem may take the small-problem layout
   bool small = false;
   const int chunk = a->chunk > 0 ? a->chunk : auto_chunk(a->B, a->L, q.ntiles, false, true, &small, dev);
-  plan_layout(q, a->B, a->L, a->D, chunk, SWIMBA_STATE_N, false, p);
+  plan_layout(q, a->B, a->L, a->D, chunk, SWIMBA_STATE_N, false, false, p);
   return SWIMBA_OK;
 }
 

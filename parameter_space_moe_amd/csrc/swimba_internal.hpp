@@ -19,6 +19,7 @@ struct ScanPlan {
   int nchunks = 0;      // ceil(L / chunk); <= 1 means a single pass
   int waves = 4;        // waves per workgroup (chunks sharing one table)
   size_t off_P = 0, off_H = 0, off_flags = 0, bytes = 0;  // workspace layout
+  size_t off_tflags = 0;  // per-tile A checks (mixed scan with more than 16 experts)
 };
 
 // Plan of a backward call: the forward's chunking plus the workspace of the
@@ -76,6 +77,8 @@ int launch_streams_bb(const swimba_stream_args* a, const ScanPlan& p, void* ws, 
 // trajectory count).
 int launch_carry(int B, int C, int D, int E, const float* P, float* H, float* h_final,
                  int separate, hipStream_t st, const hipEvent_t* ev);
+// flags[tile] = 1 if any A of the tile's 64 channels is not negative.
+int launch_a_flags(const float* A, int E, int D, bool scalar_a, int32_t* flags, hipStream_t st);
 
 // Compute units of device `dev` (-1: the current device), cached per device.
 int device_cus(int dev);
