@@ -99,9 +99,11 @@ def test_route_workload(name):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D,E,k", [(100, 1, 1), (100, 3, 2), (96, 5, 5), (64, 17, 3),
                                    (72, 64, 4), (1, 8, 2), (513, 16, 16), (1030, 5, 2),
-                                   (2048, 8, 2), (1100, 33, 4), (4099, 16, 3)])
+                                   (2048, 8, 2), (1100, 33, 4), (4099, 16, 3), (96, 48, 2),
+                                   (128, 64, 20), (64, 64, 64), (200, 40, 2), (5, 23, 7)])
 def test_route_shapes(dtype, D, E, k):
-    """Ragged D (scalar staging path), E not a kernel width, the wide-E path,
+    """Ragged D (scalar staging path), E not a kernel width, the wide-E path
+    (17..64 experts: 2, 3 and 4 slices of 16, more than 16 slots, k = E),
     k = E, D = 1, a token count that is not a multiple of 64, and wide rows."""
     w, inp, t = small_case(B=3, L=45, D=D, E=E, k=k, dtype=dtype, seed=D + E)
     idx, gate = route_on_gpu(t, w)
@@ -127,6 +129,39 @@ def test_route_exact_ties_prefer_lower_expert():
         for a, b in ((1, 4), (2, 5)):
             if a in s and b in s:
                 assert s.index(a) < s.index(b)
+
+
+@pytest.mark.parametrize("E", [40, 64])
+def test_route_exact_ties_prefer_lower_expert_wide(E):
+    """Duplicated Wr columns across 16-expert slices tie exactly: the lower
+    expert comes first."""
+    w, inp, t = small_case(B=1, L=200, D=256, E=E, k=4, dtype="bf16", seed=E)
+    Wr = inp["Wr"].copy()
+    Wr[:, 33] = Wr[:, 2]
+    Wr[:, E - 1] = Wr[:, 17]
+    idx, gate = swimba.route(t["x"], torch.from_numpy(Wr).to(DEV), 4)
+    gi = idx.cpu().numpy().reshape(-1, 4)
+    for tk in range(gi.shape[0]):
+        s_ = list(gi[tk])
+        for a, b in ((2, 33), (17, E - 1)):
+            if a in s_ and b in s_:
+                assert s_.index(a) < s_.index(b)
+        assert len(set(s_)) == 4
+
+
+def test_route_wide_layer():
+    """64 experts at B = 2, L = 4096, D = 4096 (bf16): every token against the
+    oracle's router."""
+    w, inp, t = small_case(B=2, L=4096, D=4096, E=64, k=2, dtype="bf16", seed=640)
+    idx, gate = route_on_gpu(t, w)
+    gi = idx.cpu().numpy().reshape(-1, 2)
+    gg = gate.cpu().numpy().reshape(-1, 2).astype(np.float64)
+    ridx, rgate, logits, absdot = oracle.route(inp["x"].reshape(-1, w.D), inp["Wr"], 2)
+    tol = route_tolerance(absdot, w.D)
+    ties = check_route(gi, logits, tol, 2)
+    same = np.all(gi == ridx, axis=1)
+    assert np.all(np.abs(gg - rgate)[same] <= gate_bound(ridx, tol)[same])
+    assert ties <= max(2, gi.shape[0] // 200), ties
 
 
 def test_route_empty():
