@@ -287,9 +287,12 @@ typedef struct {
  * as swimba_scan).
  *   ws, ws_bytes: device workspace of at least
  *   swimba_scan_backward_workspace_size(g) bytes, 256-byte aligned (the
- *   forward's disc must be EULER; ZOH returns SWIMBA_EUNSUPPORTED).  It
- *   holds every state h_t (64 bytes per token and channel) besides the
- *   chunk records.
+ *   forward's disc must be EULER; ZOH returns SWIMBA_EUNSUPPORTED).  No
+ *   state is kept per token: the gradient pass rebuilds each 8-token block's
+ *   states from a checkpoint, so the workspace holds the per-chunk records
+ *   (decays, states, adjoints, parameter-gradient partials), the block
+ *   checkpoints (16 bytes per token and channel) and per-tile sums over
+ *   channels (about 0.5 bytes per token and channel).
  * Constraints: those of swimba_scan with E <= 16 and a_form DIAGONAL (SCALAR
  * returns SWIMBA_EUNSUPPORTED).  B == 0 or L == 0 writes zero parameter gradients
  * and dh0 = dh_final (or zeros).  Every output is deterministic.

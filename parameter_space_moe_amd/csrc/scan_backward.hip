@@ -62,9 +62,7 @@ int reverse_carry(const BwdParams& p, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
 }
 
-// ---------------------------------------------------------------- pass 6
-// dB, dC and dgate: the per-tile (dC) and per-wave (dB, dgate) channel sums
-// added in order.
+// ---------------------------------------------------------------- pass 5
 // sum_w src[w * stride] for w = 0 .. n-1, added in that order; the loads are
 // issued eight at a time so that one memory round trip serves eight terms.
 __device__ __forceinline__ float ordered_sum(const float* __restrict__ src, size_t stride, int n) {
@@ -81,24 +79,25 @@ __device__ __forceinline__ float ordered_sum(const float* __restrict__ src, size
   return s;
 }
 
-__global__ __launch_bounds__(256) void bwd_reduce_tokens_kernel(const float* __restrict__ redC,
-                                                                const float* __restrict__ redB,
+// dB, dC and dgate: the per-tile channel sums ([tile][token][R]: dB, dC,
+// then the gate terms) added in tile order.
+__global__ __launch_bounds__(256) void bwd_reduce_tokens_kernel(const float* __restrict__ red,
                                                                 int ntiles, size_t tokens, int k,
-                                                                float* __restrict__ dB,
+                                                                int R, float* __restrict__ dB,
                                                                 float* __restrict__ dC,
                                                                 float* __restrict__ dgate) {
-  const int kr = kN + k;
+  const int W = 2 * kN + k;
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < tokens * kN) dC[i] = ordered_sum(redC + i, tokens * kN, ntiles);
-  if (i < tokens * kr) {
-    const float s = ordered_sum(redB + i, tokens * kr, ntiles * 4);
-    const size_t bt = i / kr;
-    const int c = (int)(i % kr);
-    if (c < kN)
-      dB[bt * kN + c] = s;
-    else
-      dgate[bt * k + c - kN] = s;
-  }
+  if (i >= tokens * W) return;
+  const size_t bt = i / W;
+  const int col = (int)(i % W);
+  const float s = ordered_sum(red + bt * R + col, tokens * R, ntiles);
+  if (col < kN)
+    dB[bt * kN + col] = s;
+  else if (col < 2 * kN)
+    dC[bt * kN + col - kN] = s;
+  else
+    dgate[bt * k + col - 2 * kN] = s;
 }
 
 // dA, dbias and dDskip: the per-(sequence, chunk) partials added in order.
@@ -126,9 +125,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(const float* __r
 int reduce_outputs(const BwdParams& p, float* dB, float* dC, float* dgate, float* dA,
                    float* dbias, float* dDsk, hipStream_t st) {
   const size_t tokens = (size_t)p.B * p.L;
-  const size_t n1 = tokens * (kN + p.k);
+  const size_t n1 = tokens * (2 * kN + p.k);
   hipLaunchKernelGGL(bwd_reduce_tokens_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0,
-                     st, p.redC, p.redB, p.ntiles, tokens, p.k, dB, dC, dgate);
+                     st, p.red, p.ntiles, tokens, p.k, backward_red_width(p.k), dB, dC, dgate);
   if (hipGetLastError() != hipSuccess) return SWIMBA_EHIP;
   const size_t n2 = (size_t)p.E * p.D * (kN + 2);
   hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0,

@@ -186,20 +186,20 @@ int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p, int dev) {
     return SWIMBA_EUNSUPPORTED;
   p->ntiles = sp.ntiles;
   if (a->B == 0 || a->L == 0) return SWIMBA_OK;
-  // Own chunking (the forward is recomputed here): about two waves per SIMD
-  // over all chunks, a whole number of workgroups per (sequence, tile), and
-  // chunks of at least 64 tokens; a caller's chunk size is kept.
+  // Own chunking (the forward is recomputed here): about four waves per SIMD
+  // in the chunk pass (a wave per chunk), chunks of whole 8-token blocks and
+  // at least 64 tokens; a caller's chunk size is kept.
   if (a->chunk > 0) {
     p->chunk = sp.chunk;
   } else {
     const long long cus = device_cus(dev);
     const long long base = (long long)a->B * sp.ntiles;
-    long long want = (8 * cus + base - 1) / base;
-    want = (want + p->waves - 1) / p->waves * p->waves;
+    long long want = (16 * cus + base - 1) / base;
     const long long maxc = (a->L + 63) / 64;
     if (want > maxc) want = maxc;
     if (want < 1) want = 1;
-    p->chunk = (int)((a->L + want - 1) / want);
+    const long long ch = (a->L + want - 1) / want;
+    p->chunk = (int)((ch + 7) / 8 * 8);
   }
   p->nchunks = (int)(((long long)a->L + p->chunk - 1) / p->chunk);
   p->ncg = (p->nchunks + p->waves - 1) / p->waves;
@@ -214,9 +214,13 @@ int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p, int dev) {
   p->off_P = take(arr);
   p->off_H = take(arr);
   p->off_adj = take(arr);
-  p->off_hs = take(B * L * D * SWIMBA_STATE_N * sizeof(float));
-  p->off_redC = take((size_t)p->ntiles * B * L * SWIMBA_STATE_N * sizeof(float));
-  p->off_redB = take((size_t)p->ntiles * 4 * B * L * (SWIMBA_STATE_N + a->k) * sizeof(float));
+  // checkpoints before every block of 8 tokens but a chunk's first: the
+  // chunk pass's local state and its decay product since the chunk's start
+  p->nbk = (p->chunk + 7) / 8 - 1;
+  const size_t ck = B * p->nchunks * (size_t)p->nbk * SWIMBA_STATE_N * D * sizeof(float);
+  p->off_ckH = take(ck);
+  p->off_ckG = take(ck);
+  p->off_red = take((size_t)p->ntiles * B * L * backward_red_width(a->k) * sizeof(float));
   p->off_pA = take(B * p->nchunks * E * D * SWIMBA_STATE_N * sizeof(float));
   p->off_pBD = take(B * p->nchunks * E * 2 * D * sizeof(float));
   p->bytes = o;

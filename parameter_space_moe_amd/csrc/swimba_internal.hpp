@@ -26,7 +26,8 @@ struct ScanPlan {
 // backward passes (all offsets 256-byte aligned).
 struct BwdPlan {
   int ntiles = 0, chunk = 0, nchunks = 0, ncg = 0, waves = 4;
-  size_t off_P = 0, off_H = 0, off_adj = 0, off_hs = 0, off_redC = 0, off_redB = 0;
+  int nbk = 0;  // block checkpoints per chunk: one before each block but the first
+  size_t off_P = 0, off_H = 0, off_adj = 0, off_ckH = 0, off_ckG = 0, off_red = 0;
   size_t off_pA = 0, off_pBD = 0;
   size_t bytes = 0;
 };
@@ -38,15 +39,20 @@ struct BwdPlan {
 // per expert with every expert advancing at every token.
 int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p, int dev);
 int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p, int dev);
-// LDS of the backward's gradient pass (four waves): the tile's expert tables,
-// and per wave a staging ring and the dense gate vectors of its tokens.
+// Per-token channel sums of the backward's gradient pass: dB (16), dC (16)
+// and the k gate terms, padded to an even count.
+inline int backward_red_width(int k) { return 2 * SWIMBA_STATE_N + ((k + 1) & ~1); }
+// LDS of the backward's gradient pass (four waves): the tile's expert tables
+// (A, then dt_bias and Dskip), their gradient accumulators of the same
+// shapes, a 512-byte sink, one staging ring shared by the waves, and the waves'
+// per-token sums of one block.
 inline size_t backward_grad_lds_bytes(int E, int k) {
-  const size_t emax = E <= 4 ? 4 : (E <= 8 ? 8 : 16);
-  return (size_t)E * 64 * 16 * 4 + (size_t)E * 64 * 8 +
-         4 * ((size_t)2 * 8 * 32 * 4 + (size_t)2 * 2 * 8 * k * 4 + (size_t)2 * 8 * emax * 4);
+  return (size_t)E * 64 * (2 * 16 * 4 + 2 * 8) + 128 * 4 +
+         ((size_t)2 * 8 * 32 * 4 + (size_t)2 * 2 * 8 * k * 4) +
+         (size_t)4 * 8 * (2 * SWIMBA_STATE_N + 4 * k) * 4;
 }
-// LDS of the backward's chunk and state passes: expert table and one staging
-// ring per wave.
+// LDS of the backward's chunk pass: expert table and one staging ring per
+// wave.
 inline size_t backward_lds_bytes(int E, int k, int waves) {
   return (size_t)E * (4 * 64 * 16 + 64 * 8) +
          (size_t)waves * ((size_t)2 * 8 * 32 * 4 + (size_t)2 * 2 * 8 * k * 4);
