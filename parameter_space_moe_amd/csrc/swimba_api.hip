@@ -98,9 +98,11 @@ int auto_chunk(long long B, long long L, int ntiles, bool separate, bool small_o
   long long want, min_chunk = 128;
   *small = false;
   if (separate) {
-    // a workgroup per (sequence, tile, chunk) with one wave per expert: aim
-    // for four workgroups per CU (two resident, two rounds)
-    want = (4 * cus + base - 1) / base;
+    // a workgroup per (sequence, tile, chunk) with one wave per expert: one
+    // chunk when the (sequence, tile) workgroups alone give each CU two (both
+    // resident: no re-walk of later chunks), else about four workgroups per
+    // CU (two resident, two rounds)
+    want = base >= 2 * cus ? 1 : (4 * cus + base - 1) / base;
     min_chunk = 64;
   } else if (base * (L / 256) >= 16 * cus) {
     // about four resident waves per SIMD (16 per CU) from the independent

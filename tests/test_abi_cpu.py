@@ -148,6 +148,22 @@ def test_slots_rejects_and_workspace(lib):
     assert (c.value, n.value) == (512, 8)
 
 
+def test_separate_plan_single_pass_when_tiles_fill_the_gpu(lib):
+    # (sequence, tile) workgroups of one wave per expert: with two per compute
+    # unit (256 CUs when no device answers) the separate design runs each
+    # sequence in one chunk, else it chunks and re-walks later chunks
+    c, n = ctypes.c_int(), ctypes.c_int()
+    a = scan_args(B=8, L=4096, D=4096, E=8, k=2)
+    assert lib.swimba_scan_plan(ctypes.byref(a), sw.DESIGN_SEPARATE, ctypes.byref(c),
+                                ctypes.byref(n)) == sw.OK
+    assert (c.value, n.value) == (4096, 1)
+    assert lib.swimba_scan_workspace_size(ctypes.byref(a), sw.DESIGN_SEPARATE) == 0
+    a = scan_args(B=4, L=2048, D=1536, E=8, k=2)
+    assert lib.swimba_scan_plan(ctypes.byref(a), sw.DESIGN_SEPARATE, ctypes.byref(c),
+                                ctypes.byref(n)) == sw.OK
+    assert n.value > 1 and c.value % 64 == 0
+
+
 def test_all_experts_rejects_and_workspace(lib):
     # one wave per expert in a workgroup: E <= 16, as the per-expert design
     assert lib.swimba_scan_all_experts(ctypes.byref(scan_args(E=17)), None, 0, None) == \
