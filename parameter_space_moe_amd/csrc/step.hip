@@ -54,16 +54,20 @@ constexpr int kBatch = 4;
 // per thread cover rows of up to 5120 channels in one round of loads.
 constexpr int kRU = 5;
 
+// A thread's loads of one batch: its quad of states of each of the kBatch
+// channels, and x and dt_raw of the one channel whose scalar work it does
+// (lane q of a quad: the batch's q-th channel).
 template <typename TIn>
-struct ChanLoads {
-  float4 h;
+struct BatchLoads {
+  float4 h[kBatch];
   TIn x, r;
 };
 
 // K > 0: k == K known at compile time (the parameter loads of a whole batch
 // are issued together); K == 0: runtime k.  SA: A is [E][D] (K > 0 only; the
-// runtime-k path reads p.scalar_a).
-template <typename TIn, typename TOut, int K, bool SA>
+// runtime-k path reads p.scalar_a).  FUSED: the routing is computed here
+// (p.Wr), else read from p.idx / p.gate.
+template <typename TIn, typename TOut, int K, bool SA, bool FUSED>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
   __shared__ float s_part[kStepWaves][64];
   __shared__ int s_idx[64];
@@ -80,22 +84,26 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
   const int cl = tid >> 2;
 
   // state, x and dt_raw of this thread's first batch do not depend on the
-  // routing: start them before the router
-  auto issue = [&](int dc, ChanLoads<TIn>* L) {
+  // routing: they start right after the router's first loads (loads retire
+  // in issue order, so the router would otherwise wait for them)
+  const int dsafe = dbeg < p.D ? dbeg : 0;  // a valid channel for idle loads
+  auto issue = [&](int dc, BatchLoads<TIn>& L) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int d = dc + u * kStepChan + cl;
-      const int dd = d < dend ? d : dbeg;
+      const int dd = d < dend ? d : dsafe;
       // 32-bit offsets from the row's base (no 64-bit address arithmetic)
-      L[u].h = at32(St, (uint32_t)dd * 4 + q);
-      L[u].x = at32(X, (uint32_t)dd);
-      L[u].r = at32(R, (uint32_t)dd);
+      L.h[u] = at32(St, (uint32_t)dd * 4 + q);
     }
+    const int d = dc + q * kStepChan + cl;
+    const int dd = d < dend ? d : dsafe;
+    L.x = at32(X, (uint32_t)dd);
+    L.r = at32(R, (uint32_t)dd);
   };
-  ChanLoads<TIn> cur[kBatch];
-  if (dbeg < dend) issue(dbeg, cur);
+  BatchLoads<TIn> cur;
 
-  if (p.idx != nullptr) {
+  if constexpr (!FUSED) {
+    issue(dbeg, cur);
     if (tid < p.k) {
       int e = p.idx[(size_t)b * p.k + tid];
       s_idx[tid] = e < 0 ? 0 : (e >= p.E ? p.E - 1 : e);
@@ -115,60 +123,72 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     // the same order, so they compute bit-identical logits and agree on the
     // routing even at a near-tie.
     const int rot = (int)(((long long)b * 1031) % p.D);
-    for (int eb = 0; eb < p.E; eb += 8) {
+    constexpr int kRound = kRU * kStepThreads;  // channels per round of loads
+    // loads of one round: x at kRU channels and their Wr entries of experts
+    // eb .. eb + 7, from clamped (valid) addresses, masked after
+    auto round_loads = [&](int eb, int d0, float* xv, float (*wv)[8]) {
       const bool two = eb + 4 < p.E;  // the block's second group of 4 exists
+#pragma unroll
+      for (int u = 0; u < kRU; ++u) {
+        const int d = d0 + u * kStepThreads;
+        const bool ok = d < p.D;
+        const int dr = d + rot;
+        const int dd = ok ? (dr >= p.D ? dr - p.D : dr) : 0;
+        const float xr = to_f32(X[dd]);
+        xv[u] = ok ? xr : 0.f;
+        if (vec) {
+          const float4* w4 = reinterpret_cast<const float4*>(p.Wr + (size_t)dd * p.E + eb);
+          const float4 lo = load_nt(w4), hi = load_nt(w4 + (two ? 1 : 0));
+          wv[u][0] = lo.x;
+          wv[u][1] = lo.y;
+          wv[u][2] = lo.z;
+          wv[u][3] = lo.w;
+          wv[u][4] = hi.x;
+          wv[u][5] = hi.y;
+          wv[u][6] = hi.z;
+          wv[u][7] = hi.w;
+        } else {
+          const float* w = p.Wr + (size_t)dd * p.E;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wv[u][i] = load_nt(w + min(eb + i, p.E - 1));
+        }
+      }
+    };
+    auto round_fma = [&](const float* xv, const float (*wv)[8], float* part) {
+#pragma unroll
+      for (int u = 0; u < kRU; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[i] = fmaf(xv[u], wv[u][i], part[i]);
+    };
+    // the first round's loads, then the state loads of the first batch, in
+    // straight-line code: waiting for the router's data does not wait for
+    // the state
+    float xv0[kRU], wv0[kRU][8];
+    round_loads(0, tid, xv0, wv0);
+    issue(dbeg, cur);
+    for (int eb = 0; eb < p.E; eb += 8) {
       float part[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) part[i] = 0.f;
-      for (int d0 = tid; d0 < p.D; d0 += kRU * kStepThreads) {
+      if (eb == 0) round_fma(xv0, wv0, part);
+      for (int d0 = tid + (eb == 0 ? kRound : 0); d0 < p.D; d0 += kRound) {
         float xv[kRU], wv[kRU][8];
-        // unconditional loads from clamped (valid) addresses, masked after:
-        // a load under a branch would be waited on inside that branch
-        if (vec) {
-#pragma unroll
-          for (int u = 0; u < kRU; ++u) {
-            const int d = d0 + u * kStepThreads;
-            const bool ok = d < p.D;
-            const int dr = d + rot;
-            const int dd = ok ? (dr >= p.D ? dr - p.D : dr) : 0;
-            const float xr = to_f32(X[dd]);
-            xv[u] = ok ? xr : 0.f;
-            const float4* w4 = reinterpret_cast<const float4*>(p.Wr + (size_t)dd * p.E + eb);
-            const float4 lo = load_nt(w4), hi = load_nt(w4 + (two ? 1 : 0));
-            wv[u][0] = lo.x;
-            wv[u][1] = lo.y;
-            wv[u][2] = lo.z;
-            wv[u][3] = lo.w;
-            wv[u][4] = hi.x;
-            wv[u][5] = hi.y;
-            wv[u][6] = hi.z;
-            wv[u][7] = hi.w;
-          }
-        } else {
-#pragma unroll
-          for (int u = 0; u < kRU; ++u) {
-            const int d = d0 + u * kStepThreads;
-            const bool ok = d < p.D;
-            const int dr = d + rot;
-            const int dd = ok ? (dr >= p.D ? dr - p.D : dr) : 0;
-            const float xr = to_f32(X[dd]);
-            xv[u] = ok ? xr : 0.f;
-            const float* w = p.Wr + (size_t)dd * p.E;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) wv[u][i] = load_nt(w + min(eb + i, p.E - 1));
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < kRU; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) part[i] = fmaf(xv[u], wv[u][i], part[i]);
+        round_loads(eb, d0, xv, wv);
+        round_fma(xv, wv, part);
       }
+      // the eight wave sums as one exchange tree: lane l ends with the sum
+      // of partial l >> 3 (bits 5, 4, 3 select the partial, the rest is summed)
+      float u4[4], u2[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float v = part[i];
-        v = wave_sum64(v);
-        if (lane == 0 && eb + i < p.E) s_part[wave][eb + i] = v;
-      }
+      for (int i = 0; i < 4; ++i) u4[i] = xchg_add<32>(part[i], part[i + 4]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) u2[i] = xchg_add<16>(u4[i], u4[i + 2]);
+      const bool hi8 = (lane & 8) != 0;
+      float v = (hi8 ? u2[1] : u2[0]) + xor_lane<8>(hi8 ? u2[0] : u2[1], lane);
+      v += xor_lane<4>(v, lane);
+      v += xor_lane<2>(v, lane);
+      v += xor_lane<1>(v, lane);
+      if ((lane & 7) == 0 && eb + (lane >> 3) < p.E) s_part[wave][eb + (lane >> 3)] = v;
     }
     __syncthreads();
     if (wave == 0) {
@@ -234,7 +254,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     if (p.gate_out) p.gate_out[(size_t)b * p.k + tid] = s_gate[tid];
   }
 
-  // state update: thread = (channel within the iteration, quad of states)
+  // state update: thread = (channel within the iteration, quad of states).
+  // The per-channel scalars (Delta, the input and skip terms) are computed
+  // once per channel: lane q of a quad for the batch's q-th channel, then
+  // broadcast to the quad; lane q also stores that channel's y.
   const TIn* Bp = reinterpret_cast<const TIn*>(p.Bm) + (size_t)b * kN + 4 * q;
   const TIn* Cp = reinterpret_cast<const TIn*>(p.Cm) + (size_t)b * kN + 4 * q;
   float Bv[4], Cv[4];
@@ -244,147 +267,158 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepParams p) {
     Cv[i] = to_f32(Cp[i]);
   }
   TOut* Y = reinterpret_cast<TOut*>(p.y) + (size_t)b * p.D;
+  constexpr int KM = K > 0 ? K : 64;
+  const int k = K > 0 ? K : p.k;
+  int ev[K > 0 ? K : 1];
+  float gv[K > 0 ? K : 1];
+  const float* bzr[K > 0 ? K : 1];
+  const float* dkr[K > 0 ? K : 1];
+  const float* asr[K > 0 ? K : 1];
+  const float4* avr[K > 0 ? K : 1];
   if constexpr (K > 0) {
-    int ev[K];
-    float gv[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       ev[j] = uniform(s_idx[j]);
       gv[j] = uniform(s_gate[j]);
-    }
-    // the selected experts' rows (wave-uniform bases)
-    const float* bzr[K];
-    const float* dkr[K];
-    const float* asr[K];
-    const float4* avr[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
+      // the selected experts' rows (wave-uniform bases)
       bzr[j] = p.bias + (size_t)ev[j] * p.D;
       dkr[j] = p.Dsk + (size_t)ev[j] * p.D;
       asr[j] = p.A + (size_t)ev[j] * p.D;
       avr[j] = reinterpret_cast<const float4*>(p.A + (size_t)ev[j] * p.D * kN);
     }
-    for (int dc = dbeg; dc < dend; dc += kBatch * kStepChan) {
-      // the selected experts' parameters of this batch's channels (L2): all
-      // issued together and before the next batch's state loads, so that
-      // waiting for them leaves the state loads in flight
-      float4 av[kBatch][K];
-      float bz[kBatch][K], dk[kBatch][K];
+  }
+  const bool scalar_a = K > 0 ? SA : p.scalar_a != 0;
+  (void)KM;
+  for (int dc = dbeg; dc < dend; dc += kBatch * kStepChan) {
+    const int dq = dc + q * kStepChan + cl;  // this lane's scalar channel
+    const int ddq = dq < dend ? dq : dsafe;
+    // the selected experts' parameters (L2): issued together and before the
+    // next batch's state loads, so that waiting for them leaves the state
+    // loads in flight
+    float4 av[kBatch][K > 0 ? K : 1];
+    float bz[K > 0 ? K : 1], dk[K > 0 ? K : 1];
+    if constexpr (K > 0) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        bz[j] = at32(bzr[j], (uint32_t)ddq);
+        dk[j] = at32(dkr[j], (uint32_t)ddq);
+      }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int d = dc + u * kStepChan + cl;
-        const int dd = d < dend ? d : dbeg;
+        const int dd = d < dend ? d : dsafe;
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-          bz[u][j] = at32(bzr[j], (uint32_t)dd);
-          dk[u][j] = at32(dkr[j], (uint32_t)dd);
+        for (int j = 0; j < K; ++j)
           av[u][j] = SA ? make_float4(at32(asr[j], (uint32_t)dd), 0.f, 0.f, 0.f)
                         : at32(avr[j], (uint32_t)dd * 4 + q);
-        }
       }
-      // the next batch (past the end: a valid, unused reload of the first
-      // channels), issued on every iteration so every path has the same
-      // loads in flight
-      ChanLoads<TIn> nxt[kBatch];
-      issue(dc + kBatch * kStepChan, nxt);
+    }
+    // the next batch (past the end: a valid, unused reload), issued on
+    // every iteration so every path has the same loads in flight
+    BatchLoads<TIn> nxt;
+    issue(dc + kBatch * kStepChan, nxt);
+    // scalars of this lane's channel
+    float beta = 0.f, delta = 0.f;
+    if constexpr (K > 0) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int d = dc + u * kStepChan + cl;
-        const bool active = d < dend;
-        const float xv = to_f32(cur[u].x), rv = to_f32(cur[u].r);
-        float beta = 0.f, delta = 0.f;
-        float m[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < K; ++j) {
+        beta = fmaf(gv[j], bz[j], beta);
+        delta = fmaf(gv[j], dk[j], delta);
+      }
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int e = s_idx[j];
+        const float gj = s_gate[j];
+        beta = fmaf(gj, p.bias[(size_t)e * p.D + ddq], beta);
+        delta = fmaf(gj, p.Dsk[(size_t)e * p.D + ddq], delta);
+      }
+    }
+    const float xq = to_f32(cur.x);
+    const float dltq = softplus_f32(to_f32(cur.r) + beta);
+    const float dl2q = dltq * kLog2e, dxq = dltq * xq, skq = delta * xq;
+    float yq = 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int d = dc + u * kStepChan + cl;
+      const bool active = d < dend;
+      // channel u's scalars from quad lane u
+      float dl2, dx, sk;
+      if (u == 0) {
+        dl2 = dpp_mov<0x00>(dl2q), dx = dpp_mov<0x00>(dxq), sk = dpp_mov<0x00>(skq);
+      } else if (u == 1) {
+        dl2 = dpp_mov<0x55>(dl2q), dx = dpp_mov<0x55>(dxq), sk = dpp_mov<0x55>(skq);
+      } else if (u == 2) {
+        dl2 = dpp_mov<0xAA>(dl2q), dx = dpp_mov<0xAA>(dxq), sk = dpp_mov<0xAA>(skq);
+      } else {
+        dl2 = dpp_mov<0xFF>(dl2q), dx = dpp_mov<0xFF>(dxq), sk = dpp_mov<0xFF>(skq);
+      }
+      float m[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (K > 0) {
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-          beta = fmaf(gv[j], bz[u][j], beta);
-          delta = fmaf(gv[j], dk[u][j], delta);
           m[0] = fmaf(gv[j], av[u][j].x, m[0]);
           m[1] = fmaf(gv[j], av[u][j].y, m[1]);
           m[2] = fmaf(gv[j], av[u][j].z, m[2]);
           m[3] = fmaf(gv[j], av[u][j].w, m[3]);
         }
-        if (SA) m[1] = m[2] = m[3] = m[0];
-        const float dlt = softplus_f32(rv + beta);
-        const float dl2 = dlt * kLog2e, dx = dlt * xv;
-        float hv[4] = {cur[u].h.x, cur[u].h.y, cur[u].h.z, cur[u].h.w};
-        float yv = 0.f;
-        // the input term is chosen once per channel, not per state
-        if (p.zoh) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a = hw_exp2(dl2 * m[i]);
-            hv[i] = fmaf(a, hv[i], (dx * Bv[i]) * zoh_phi(a, dl2 * m[i]));
-            yv = fmaf(Cv[i], hv[i], yv);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hv[i] = fmaf(hw_exp2(dl2 * m[i]), hv[i], dx * Bv[i]);
-            yv = fmaf(Cv[i], hv[i], yv);
-          }
-        }
-        // quad sum of the readout (lanes 4c..4c+3 hold one channel)
-        yv += xor_lane<1>(yv, lane);
-        yv += xor_lane<2>(yv, lane);
-        if (active) {
-          at32(St, (uint32_t)d * 4 + q) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-          if (q == 0) at32(Y, (uint32_t)d) = from_f32<TOut>(fmaf(delta, xv, yv));
+      } else {
+        const int dd = active ? d : dsafe;
+        for (int j = 0; j < k; ++j) {
+          const int e = s_idx[j];
+          const float gj = s_gate[j];
+          const float4 a =
+              scalar_a ? make_float4(p.A[(size_t)e * p.D + dd], 0.f, 0.f, 0.f)
+                       : *reinterpret_cast<const float4*>(p.A + ((size_t)e * p.D + dd) * kN +
+                                                          4 * q);
+          m[0] = fmaf(gj, a.x, m[0]);
+          m[1] = fmaf(gj, a.y, m[1]);
+          m[2] = fmaf(gj, a.z, m[2]);
+          m[3] = fmaf(gj, a.w, m[3]);
         }
       }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) cur[u] = nxt[u];
-    }
-    return;
-  }
-  for (int dc = dbeg; dc < dend; dc += kBatch * kStepChan) {
-    ChanLoads<TIn> nxt[kBatch];
-    const int dn = dc + kBatch * kStepChan;
-    if (dn < dend) issue(dn, nxt);
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int d = dc + u * kStepChan + cl;
-      const bool active = d < dend;
-      const int dd = active ? d : dbeg;
-      const float xv = to_f32(cur[u].x), rv = to_f32(cur[u].r);
-      float beta = 0.f, delta = 0.f;
-      float m[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < p.k; ++j) {
-        const int e = s_idx[j];
-        const float gj = s_gate[j];
-        beta = fmaf(gj, p.bias[(size_t)e * p.D + dd], beta);
-        delta = fmaf(gj, p.Dsk[(size_t)e * p.D + dd], delta);
-        const float4 a =
-            p.scalar_a
-                ? make_float4(p.A[(size_t)e * p.D + dd], 0.f, 0.f, 0.f)
-                : *reinterpret_cast<const float4*>(p.A + ((size_t)e * p.D + dd) * kN + 4 * q);
-        m[0] = fmaf(gj, a.x, m[0]);
-        m[1] = fmaf(gj, a.y, m[1]);
-        m[2] = fmaf(gj, a.z, m[2]);
-        m[3] = fmaf(gj, a.w, m[3]);
-      }
-      if (p.scalar_a) m[1] = m[2] = m[3] = m[0];
-      const float dlt = softplus_f32(rv + beta);
-      const float dl2 = dlt * kLog2e, dx = dlt * xv;
-      float hv[4] = {cur[u].h.x, cur[u].h.y, cur[u].h.z, cur[u].h.w};
+      if (scalar_a) m[1] = m[2] = m[3] = m[0];
+      float hv[4] = {cur.h[u].x, cur.h[u].y, cur.h[u].z, cur.h[u].w};
       float yv = 0.f;
+      // the input term is chosen once per channel, not per state
+      if (p.zoh) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = hw_exp2(dl2 * m[i]);
-        const float inj = p.zoh ? (dx * Bv[i]) * zoh_phi(a, dl2 * m[i]) : dx * Bv[i];
-        hv[i] = fmaf(a, hv[i], inj);
-        yv = fmaf(Cv[i], hv[i], yv);
+        for (int i = 0; i < 4; ++i) {
+          const float a = hw_exp2(dl2 * m[i]);
+          hv[i] = fmaf(a, hv[i], (dx * Bv[i]) * zoh_phi(a, dl2 * m[i]));
+          yv = fmaf(Cv[i], hv[i], yv);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hv[i] = fmaf(hw_exp2(dl2 * m[i]), hv[i], dx * Bv[i]);
+          yv = fmaf(Cv[i], hv[i], yv);
+        }
       }
       // quad sum of the readout (lanes 4c..4c+3 hold one channel)
       yv += xor_lane<1>(yv, lane);
       yv += xor_lane<2>(yv, lane);
-      if (active) {
-        St[(size_t)d * 4 + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
-        if (q == 0) Y[d] = from_f32<TOut>(fmaf(delta, xv, yv));
-      }
+      if (q == u) yq = yv + sk;
+      if (active) at32(St, (uint32_t)d * 4 + q) = make_float4(hv[0], hv[1], hv[2], hv[3]);
     }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) cur[u] = nxt[u];
+    if (dq < dend) at32(Y, (uint32_t)dq) = from_f32<TOut>(yq);
+    cur = nxt;
   }
+}
+
+template <typename TIn, typename TOut, bool FUSED>
+int launch_step_k(int k, bool scalar_a, dim3 grid, dim3 block, const StepParams& p,
+                  hipStream_t s) {
+  if (k == 1 && scalar_a)
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 1, true, FUSED>), grid, block, 0, s, p);
+  else if (k == 1)
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 1, false, FUSED>), grid, block, 0, s, p);
+  else if (k == 2 && scalar_a)
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 2, true, FUSED>), grid, block, 0, s, p);
+  else if (k == 2)
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 2, false, FUSED>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((step_kernel<TIn, TOut, 0, false, FUSED>), grid, block, 0, s, p);
+  return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
 }
 
 template <typename TIn, typename TOut>
@@ -417,17 +451,8 @@ int launch_step_t(const swimba_step_args* a, hipStream_t s) {
   p.state = a->state;
   p.y = a->y;
   const dim3 grid((unsigned)((size_t)a->B * slices)), block(kStepThreads);
-  if (a->k == 1 && p.scalar_a)
-    hipLaunchKernelGGL((step_kernel<TIn, TOut, 1, true>), grid, block, 0, s, p);
-  else if (a->k == 1)
-    hipLaunchKernelGGL((step_kernel<TIn, TOut, 1, false>), grid, block, 0, s, p);
-  else if (a->k == 2 && p.scalar_a)
-    hipLaunchKernelGGL((step_kernel<TIn, TOut, 2, true>), grid, block, 0, s, p);
-  else if (a->k == 2)
-    hipLaunchKernelGGL((step_kernel<TIn, TOut, 2, false>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((step_kernel<TIn, TOut, 0, false>), grid, block, 0, s, p);
-  return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
+  if (a->idx != nullptr) return launch_step_k<TIn, TOut, false>(a->k, p.scalar_a, grid, block, p, s);
+  return launch_step_k<TIn, TOut, true>(a->k, p.scalar_a, grid, block, p, s);
 }
 
 }  // namespace
