@@ -49,7 +49,9 @@ __device__ __forceinline__ void load4(const TIn* row, int d, int D, bool ok, Raw
   }
 }
 
-template <typename TIn, bool VEC>
+// MASK: the step may run past D (its last step); otherwise every lane's four
+// channels exist and no select is needed.
+template <typename TIn, bool VEC, bool MASK = true>
 __device__ __forceinline__ void cvt4(const Raw4<TIn, VEC>& r, int d, int D, bool ok, float* v) {
   if (VEC) {
     if constexpr (sizeof(TIn) == 2) {
@@ -63,8 +65,10 @@ __device__ __forceinline__ void cvt4(const Raw4<TIn, VEC>& r, int d, int D, bool
       v[2] = r.v.z;
       v[3] = r.v.w;
     }
+    if constexpr (MASK) {
 #pragma unroll
-    for (int c = 0; c < kCPL; ++c) v[c] = ok ? v[c] : 0.f;
+      for (int c = 0; c < kCPL; ++c) v[c] = ok ? v[c] : 0.f;
+    }
   } else {
 #pragma unroll
     for (int c = 0; c < kCPL; ++c) v[c] = (ok && d + c < D) ? to_f32(r.s[c]) : 0.f;
@@ -73,13 +77,17 @@ __device__ __forceinline__ void cvt4(const Raw4<TIn, VEC>& r, int d, int D, bool
 
 // Wr rows of one 256-channel step in LDS, shared by the workgroup's four
 // waves (each owns different tokens): element (channel 4l + c, expert 4qe..)
-// sits at float4 index (c * EC/4 + qe) * 64 + l, so lane l's reads of its four
-// rows are contiguous across the wave (no bank conflicts).
+// sits at float4 index (c * EC/4 + qe) * kRow + l, so lane l's reads of its
+// four rows are contiguous across the wave.  Rows are padded to kRow = 65
+// float4s: the staging stores, where consecutive lanes write consecutive
+// rows, then fall on different banks.
+constexpr int kRow = 65;
 template <int EC>
 struct WStage {
   static_assert(EC >= 4 && EC % 4 == 0, "experts are staged as float4s");
   static constexpr int kVecs = 64 * kCPL * EC / 4;                  // float4s per step
   static constexpr int kPerThread = (kVecs + kRouteThreads - 1) / kRouteThreads;
+  static constexpr int kSlots = kCPL * EC / 4 * kRow;               // LDS float4s per step
   float4 v[kPerThread];
 };
 
@@ -113,7 +121,7 @@ __device__ __forceinline__ void wstage_store(float4* buf, int tid, const WStage<
     if (i < WStage<EC>::kVecs) {
       const int ch = i / (EC / 4), qe = i % (EC / 4);
       const int l = ch / kCPL, c = ch % kCPL;
-      buf[(c * (EC / 4) + qe) * 64 + l] = st.v[j];
+      buf[(c * (EC / 4) + qe) * kRow + l] = st.v[j];
     }
   }
 }
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
     for (int r = 0; r < R; ++r) load4<TIn, VEC>(rows[r], d, D, d < D, xn[r]);
   }
   if constexpr (WLDS) {
-    __shared__ float4 wbuf[2][WStage<EC>::kVecs];
+    __shared__ float4 wbuf[2][WStage<EC>::kSlots];
     const int tid = threadIdx.x;
     WStage<EC> st;
     wstage_load<EC, EXACT>(Wr, D, E, step_base(0), tid, st);
@@ -177,8 +185,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
       const bool ok = d < D;
       const bool more = i + 1 < nsteps;
       float xv[R][kCPL];
+      if (step_base(i) + kStep <= D) {  // a whole step (uniform): no masking
 #pragma unroll
-      for (int r = 0; r < R; ++r) cvt4<TIn, VEC>(xn[r], d, D, ok, xv[r]);
+        for (int r = 0; r < R; ++r) cvt4<TIn, VEC, false>(xn[r], d, D, ok, xv[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) cvt4<TIn, VEC, true>(xn[r], d, D, ok, xv[r]);
+      }
       if (more) {
         // the stage first: waiting for it below leaves the x loads in flight
         const int dcn = step_base(i + 1), dn = dcn + lane * kCPL;
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TIn* __restr
         float w[EC];
 #pragma unroll
         for (int qe = 0; qe < EC / 4; ++qe) {
-          const float4 v = wbuf[buf][(c * (EC / 4) + qe) * 64 + lane];
+          const float4 v = wbuf[buf][(c * (EC / 4) + qe) * kRow + lane];
           w[4 * qe + 0] = v.x;
           w[4 * qe + 1] = v.y;
           w[4 * qe + 2] = v.z;

@@ -28,6 +28,7 @@ constexpr int kWideR = 4;    // tokens per wave
 constexpr int kWideTG = 2;   // token groups per workgroup
 constexpr int kWideEG = 2;   // 16-expert slices per pass
 constexpr int kWidePasses = 2;  // passes over the channels (32 experts each)
+constexpr int kSlice = 16 * kRow;  // LDS float4s of one 16-expert slice of a step
 
 struct WideStage {
   static constexpr int kThreads = 64 * kWideTG * kWideEG;
@@ -38,7 +39,8 @@ struct WideStage {
 
 // Wr rows of the step at channel dc for the pass's experts eb..eb+31:
 // element (channel 4l + c, expert eb + 16 g + 4 qe ..) sits at float4 index
-// g * 1024 + (c * 4 + qe) * 64 + l, so a wave's reads of its slice are
+// g * kSlice + (c * 4 + qe) * kRow + l (rows padded to kRow float4s, so the
+// staging stores fall on different banks), so a wave's reads of its slice are
 // lane-contiguous.  Experts past E and channels past D read as 0.
 // VEC4: E is a multiple of 4 and Wr 16-byte aligned (one 16-byte load per
 // four experts).
@@ -72,7 +74,7 @@ __device__ __forceinline__ void wide_stage_store(float4* buf, int tid, const Wid
     const int i = tid + WideStage::kThreads * j;
     const int g = i >> 10, r = i & 1023, ch = r >> 2, qe = r & 3;
     const int l = ch >> 2, c = ch & 3;
-    buf[g * 1024 + (c * 4 + qe) * 64 + l] = st.v[j];
+    buf[g * kSlice + (c * 4 + qe) * kRow + l] = st.v[j];
   }
 }
 
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(64 * kWideTG * kWideEG) void route_wide_kernel(
     int32_t* __restrict__ idx, float* __restrict__ gate) {
   constexpr int R = kWideR, EC = kWideEC, TG = kWideTG, EG = kWideEG;
   constexpr int EMAX = kWidePasses * EG * 16;
-  __shared__ float4 wbuf[2][EG * 1024];
+  __shared__ float4 wbuf[2][EG * kSlice];
   __shared__ float s_logit[TG][R][EMAX];
   __shared__ int s_sel_e[TG][R][EMAX];
   __shared__ float s_sel_v[TG][R][EMAX];
@@ -127,7 +129,12 @@ __global__ __launch_bounds__(64 * kWideTG * kWideEG) void route_wide_kernel(
       const bool more = i + 1 < nsteps;
       float xv[R][kCPL];
 #pragma unroll
-      for (int j = 0; j < R; ++j) cvt4<TIn, VEC>(xn[j], d, D, ok, xv[j]);
+      for (int j = 0; j < R; ++j) {
+        if (step_base(i) + kStep <= D)  // a whole step (uniform): no masking
+          cvt4<TIn, VEC, false>(xn[j], d, D, ok, xv[j]);
+        else
+          cvt4<TIn, VEC, true>(xn[j], d, D, ok, xv[j]);
+      }
       if (more) {
         // the stage first: waiting for it below leaves the x loads in flight
         const int dcn = step_base(i + 1), dn = dcn + lane * kCPL;
@@ -135,13 +142,13 @@ __global__ __launch_bounds__(64 * kWideTG * kWideEG) void route_wide_kernel(
 #pragma unroll
         for (int j = 0; j < R; ++j) load4<TIn, VEC>(rows[j], dn, D, dn < D, xn[j]);
       }
-      const float4* wb = wbuf[buf] + g * 1024;
+      const float4* wb = wbuf[buf] + g * kSlice;
 #pragma unroll
       for (int c = 0; c < kCPL; ++c) {
         float w[EC];
 #pragma unroll
         for (int qe = 0; qe < EC / 4; ++qe) {
-          const float4 v = wb[(c * (EC / 4) + qe) * 64 + lane];
+          const float4 v = wb[(c * (EC / 4) + qe) * kRow + lane];
           w[4 * qe + 0] = v.x;
           w[4 * qe + 1] = v.y;
           w[4 * qe + 2] = v.z;
