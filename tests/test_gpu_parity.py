@@ -536,3 +536,44 @@ def test_prepared_step_matches_step():
                             P["Dskip"], st2, Wr=P["Wr"], k=w.k, y=y2)()
         assert torch.equal(y1, y2)
     assert torch.equal(st1, st2)
+
+
+@pytest.mark.parametrize("E", [4, 20])
+def test_out_of_range_expert_ids_are_clamped(E):
+    """Expert ids below 0 or at E and above in a caller's routing are read as
+    0 and E - 1 (include/swimba.h): the scans (LDS-table and rows-from-memory
+    paths), the separate design (E <= 16) and the decode step give the same
+    bits as with the clamped ids, and the mixed scan matches the oracle fed
+    the clamped ids."""
+    w, inp, t = small_case(B=2, L=200, D=96, E=E, k=2, seed=E + 3)
+    rng = np.random.default_rng(E)
+    bad = rng.integers(-3, E + 4, size=(2, 200, 2)).astype(np.int32)
+    bad[0, :4] = [[-1, E], [E + 3, -3], [0, E - 1], [-2, 2]]
+    good = np.clip(bad, 0, E - 1).astype(np.int32)
+    gate = torch.from_numpy(rng.uniform(0.1, 0.9, size=(2, 200, 2)).astype(np.float32)).to(DEV)
+    ib, ig = torch.from_numpy(bad).to(DEV), torch.from_numpy(good).to(DEV)
+    args = lambda idx: (t["x"], t["dt_raw"], t["Bm"], t["Cm"], idx, gate, t["A"], t["dt_bias"],
+                        t["Dskip"])
+    for chunk in (0, 64):
+        yb, hb = swimba.scan(*args(ib), chunk=chunk)
+        yg, hg = swimba.scan(*args(ig), chunk=chunk)
+        assert torch.equal(yb, yg) and torch.equal(hb, hg), chunk
+    ry, rh = oracle.scan(inp["x"], inp["dt_raw"], inp["Bm"], inp["Cm"], good, host(gate),
+                         inp["A"], inp["dt_bias"], inp["Dskip"])
+    assert rel_err(host(yb), ry) < TOL_F32 and rel_err(host(hb), rh) < TOL_F32
+    if E <= 16:
+        yb, hb = swimba.scan_separate(*args(ib), chunk=64)
+        yg, hg = swimba.scan_separate(*args(ig), chunk=64)
+        assert torch.equal(yb, yg) and torch.equal(hb, hg)
+    # decode step with the routing given
+    st_b = torch.zeros((2, 96, 16), dtype=torch.float32, device=DEV)
+    st_g = torch.zeros_like(st_b)
+    for s in range(3):
+        xs, rs = t["x"][:, s].contiguous(), t["dt_raw"][:, s].contiguous()
+        bs, cs = t["Bm"][:, s].contiguous(), t["Cm"][:, s].contiguous()
+        gs = gate[:, s].contiguous()
+        y1 = swimba.step(xs, rs, bs, cs, t["A"], t["dt_bias"], t["Dskip"], st_b,
+                         idx=ib[:, s].contiguous(), gate=gs)
+        y2 = swimba.step(xs, rs, bs, cs, t["A"], t["dt_bias"], t["Dskip"], st_g,
+                         idx=ig[:, s].contiguous(), gate=gs)
+        assert torch.equal(y1, y2) and torch.equal(st_b, st_g), s
