@@ -870,11 +870,10 @@ int launch_bwd_w(const swimba_scan_grad_args* g, const BwdPlan& pl, void* ws, hi
   }
 }
 
-// Eight chunks (waves) share a workgroup's expert table in the chunk pass
-// when the LDS allows it, four otherwise.
+// Four chunks (waves) share a workgroup's expert table in the chunk pass.
 template <typename TIn, typename TDy>
 int launch_bwd_k(const swimba_scan_grad_args* g, const BwdPlan& pl, void* ws, hipStream_t st) {
-  if (pl.waves == 8) return launch_bwd_w<TIn, TDy, 8>(g, pl, ws, st);
+  (void)pl.waves;
   return launch_bwd_w<TIn, TDy, 4>(g, pl, ws, st);
 }
 

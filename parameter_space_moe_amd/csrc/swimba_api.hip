@@ -182,7 +182,10 @@ int plan_backward(const swimba_scan_grad_args* g, BwdPlan* p, int dev) {
   // the backward's passes stage the E expert tables in LDS
   if (a->E > 16) return SWIMBA_EUNSUPPORTED;
   *p = BwdPlan();
-  p->waves = backward_lds_bytes(a->E, a->k, 8) <= 80 * 1024 ? 8 : 4;
+  // four chunks (waves) per chunk-pass workgroup: at the small layers that
+  // gives whole rounds of workgroups per CU (eight left half of the CUs with
+  // one workgroup and half with two)
+  p->waves = 4;
   if (backward_lds_bytes(a->E, a->k, p->waves) > 160 * 1024 ||
       backward_grad_lds_bytes(a->E, a->k) > 160 * 1024)
     return SWIMBA_EUNSUPPORTED;
