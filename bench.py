@@ -429,11 +429,16 @@ def ratios_at(lay, swimba, dev, reps, flush=None):
     ms_mixed = time_events(lay.scan, reps, flush=flush)
     res["mixed_scan"] = {"ms": round(ms_mixed, 4), "G_tc_per_s": round(w.tc / ms_mixed / 1e6, 3)}
     hfs = torch.empty((w.B, w.E, w.D, N_STATE), dtype=torch.float32, device=dev)
+    # the separate design at its own chunking (chunks are an implementation
+    # detail of each design: its fix-up stops after a number of selections
+    # per expert, so it takes a few long chunks)
     sep = swimba.PreparedScan(True, lay.x, lay.dtr, lay.Bm, lay.Cm, lay.idx, lay.gate, lay.A,
-                              lay.bias, lay.Dsk, y=lay.y, h_final=hfs, chunk=w.chunk)
+                              lay.bias, lay.Dsk, y=lay.y, h_final=hfs, chunk=0)
     ms_sep = time_events(sep, reps, flush=flush)
+    sc, sn = swimba.scan_plan(lay.x, lay.A, lay.idx, separate=True)
     res["separate_scan"] = {"ms": round(ms_sep, 4), "G_tc_per_s": round(w.tc / ms_sep / 1e6, 3),
                             "separate_over_mixed": round(ms_sep / ms_mixed, 3),
+                            "chunk": sc, "chunks": sn,
                             "workspace_MB": round(sep.workspace.numel() / 1e6, 1)}
     del sep, hfs
     idx1 = torch.zeros((w.B, w.L, 1), dtype=torch.int32, device=dev)

@@ -22,11 +22,21 @@
 // that is E updates per token.
 //
 // Chunks are joined exactly: pass 1 runs every chunk from zero (chunk 0 from
-// h0) and records each expert's end state and decay P_e[n] = exp2(S_e A'[e,n]),
-// with S_e the Delta summed over the chunk's selections of e (ALL: over all
-// its tokens) and A' = A log2 e;
+// h0), writes provisional y and records each expert's end state and decay
+// P_e[n] = exp2(S_e A'[e,n]), with S_e the Delta summed over the chunk's
+// selections of e (ALL: over all its tokens) and A' = A log2 e;
 // pass 2 carries the states across chunks (shared with the mixed scan); pass 3
-// re-runs chunks 1.. from their carried-in states.
+// re-runs chunks 1.. from their carried-in states h_in.  An expert's carried
+// part after its selections so far is h_in[n] exp2(S_e A'[e,n]) -- its A is
+// fixed, only Delta varies -- so a lane bounds it by
+// max_n |h_in[n]| * exp2(S_e max_n A'[e,n]) without tracking it per state.
+// With every A < 0 the carried part only shrinks; once it is below 2^-24 of
+// the state on every lane of every expert's wave, the rest of the chunk keeps
+// the provisional y (equal to fp32 resolution of the state) and the workgroup
+// stops.  A tile with some A >= 0 (or NaN), or a caller asking for the full
+// re-walk, re-runs the whole chunk.  The decay is set by how often an expert
+// is selected, not by the token count, so the planner gives this design long
+// chunks.
 #pragma once
 #include "scan_common.hpp"
 #include "swimba_device.hpp"
@@ -52,7 +62,11 @@ struct SepParams {
   float* h_final;    // [B][E][D][16]
   float* P;          // [B][C][E*16][D]
   float* H;          // [B][C][E*16][D]
+  int trunc;         // fix-up stops once every carried part has decayed
 };
+
+constexpr float kFixupTol = 5.9604645e-08f;  // 2^-24
+constexpr float kTiny = 1e-30f;
 
 enum { kPassFirst = 0, kPassFixup = 1, kPassSingle = 2 };
 
@@ -235,6 +249,9 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   const size_t row = (size_t)b * p.L;
   const int rows = p.E * kN;
 
+  // fix-up: wave e still carries a part of h_in that is above fp32
+  // resolution of its state (written after the walk, read after the barrier)
+  __shared__ int s_busy[16];
   float Ae[kN], h[kN];
   if (SA) {
     Ae[0] = p.A[(size_t)ex * p.D + dd] * kLog2e;
@@ -256,8 +273,20 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
     h[n] = v;
   }
   float S = 0.f;
-  // pass 1 needs no output for chunks >= 1 (pass 3 recomputes them)
-  const bool readout = PASS != kPassFirst || c == 0;
+  // The fix-up's bound on the carried part: max_n |h_in[n]| and the slowest
+  // decay max_n A'[n] (no stop unless it is < 0 on every lane of every wave).
+  float hin_max = 0.f, a_max = SA ? Ae[0] : -INFINITY;
+  if (PASS == kPassFixup) {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      hin_max = fmaxf(hin_max, fabsf(h[n]));
+      if (!SA) a_max = fmaxf(a_max, Ae[n]);
+    }
+  }
+  const bool trunc = PASS == kPassFixup && p.trunc != 0;
+  // pass 1 writes provisional y for every chunk when the fix-up may stop
+  // early; otherwise chunks >= 1 need none (pass 3 recomputes them)
+  const bool readout = PASS != kPassFirst || c == 0 || p.trunc != 0;
   TOut* Y = reinterpret_cast<TOut*>(p.y);
 
   for (int ts = t0; ts < t1; ts += R) {
@@ -268,6 +297,17 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
       walk_round<TIn, K, true, SA, ZOH, ALL>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
     else
       walk_round<TIn, K, false, SA, ZOH, ALL>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
+    if (trunc) {
+      // this lane's carried part is at most hin_max * exp2(S a_max); NaN or
+      // a non-negative A keep the lane busy
+      float mh = 0.f;
+#pragma unroll
+      for (int q = 0; q < kN; ++q) mh = fmaxf(mh, fabsf(h[q]));
+      const bool gone = !active || (a_max < 0.f && hin_max * hw_exp2(S * a_max) <=
+                                                       fmaxf(kFixupTol * mh, kTiny));
+      const bool busy = __ballot(!gone) != 0;
+      if (lane == 0) s_busy[ex] = busy ? 1 : 0;
+    }
     __syncthreads();
     // every (token, slot) output was written by its expert's wave; add them in
     // slot order.  The next round's staging touches no output buffer, and its
@@ -281,6 +321,13 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
           Y[(row + ts + i) * p.D + d0 + cl] = from_f32<TOut>(v);
         }
       }
+    }
+    if (trunc) {
+      // every thread reads the same flags after the same barrier: the exit is
+      // uniform over the workgroup
+      int busy = 0;
+      for (int e = 0; e < p.E; ++e) busy |= s_busy[e];
+      if (busy == 0) break;
     }
   }
 
@@ -322,6 +369,7 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
   p.h0 = a->h0;
   p.y = a->y;
   p.h_final = a->h_final;
+  p.trunc = a->carry != SWIMBA_CARRY_REWALK;
   char* w = static_cast<char*>(ws);
   p.P = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_P) : nullptr;
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;

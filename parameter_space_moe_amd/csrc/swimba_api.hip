@@ -91,19 +91,24 @@ namespace {
 // lane-per-channel scan over B * ntiles independent recurrences of length L.
 // `small_ok`: the kernel may run the small-problem layout (two 4-wave
 // workgroups per CU); *small tells whether it was chosen.
-int auto_chunk(long long B, long long L, int ntiles, bool separate, bool small_ok, bool* small,
-               int dev) {
+int auto_chunk(long long B, long long L, int ntiles, int E, bool separate, bool small_ok,
+               bool* small, int dev) {
   const long long cus = device_cus(dev);
   const long long base = B * ntiles;
   long long want, min_chunk = 128;
   *small = false;
   if (separate) {
-    // a workgroup per (sequence, tile, chunk) with one wave per expert: one
-    // chunk when the (sequence, tile) workgroups alone give each CU two (both
-    // resident: no re-walk of later chunks), else about four workgroups per
-    // CU (two resident, two rounds)
-    want = base >= 2 * cus ? 1 : (4 * cus + base - 1) / base;
-    min_chunk = 64;
+    // A workgroup per (sequence, tile, chunk) with one wave per expert.  A CU
+    // holds about 20 such waves (five per SIMD at the passes' register use)
+    // and the LDS of two workgroups.  One chunk when the (sequence, tile)
+    // workgroups fill those slots; else as many chunks as fill them once.
+    // The fix-up stops once every carried state has decayed, which takes a
+    // number of selections per expert rather than of tokens, so long chunks
+    // keep it a small part of the work.
+    const long long per_cu = E > 10 ? 1 : 2;
+    const long long slots = cus * per_cu;
+    want = base >= slots ? 1 : slots / base;
+    min_chunk = 256;
   } else if (base * (L / 256) >= 16 * cus) {
     // about four resident waves per SIMD (16 per CU) from the independent
     // (b, tile) recurrences, in chunks no shorter than a few fix-up horizons
@@ -160,7 +165,7 @@ int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p, int dev) {
   bool small = false;  // mixed scan with too little work for four waves per SIMD
   const int chunk =
       a->chunk > 0 ? a->chunk
-                   : auto_chunk(a->B, a->L, q.ntiles, separate,
+                   : auto_chunk(a->B, a->L, q.ntiles, a->E, separate,
                                 slots || a->E <= 8 || a->E > 16, &small, dev);
   const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N
                                : (slots ? (size_t)a->k * SWIMBA_STATE_N : SWIMBA_STATE_N);
@@ -249,7 +254,8 @@ int plan_streams(const swimba_stream_args* a, ScanPlan* p, int dev) {
   }
   // no expert table in LDS: every problem may take the small-problem layout
   bool small = false;
-  const int chunk = a->chunk > 0 ? a->chunk : auto_chunk(a->B, a->L, q.ntiles, false, true, &small, dev);
+  const int chunk =
+      a->chunk > 0 ? a->chunk : auto_chunk(a->B, a->L, q.ntiles, 1, false, true, &small, dev);
   plan_layout(q, a->B, a->L, a->D, chunk, SWIMBA_STATE_N, false, false, p);
   return SWIMBA_OK;
 }

@@ -149,9 +149,10 @@ def test_slots_rejects_and_workspace(lib):
 
 
 def test_separate_plan_single_pass_when_tiles_fill_the_gpu(lib):
-    # (sequence, tile) workgroups of one wave per expert: with two per compute
-    # unit (256 CUs when no device answers) the separate design runs each
-    # sequence in one chunk, else it chunks and re-walks later chunks
+    # (sequence, tile) workgroups of one wave per expert: two per compute unit
+    # up to 10 experts, one beyond (256 CUs when no device answers); the
+    # separate design runs each sequence in one chunk when they fill those
+    # slots, else in as many long chunks as fill them once
     c, n = ctypes.c_int(), ctypes.c_int()
     a = scan_args(B=8, L=4096, D=4096, E=8, k=2)
     assert lib.swimba_scan_plan(ctypes.byref(a), sw.DESIGN_SEPARATE, ctypes.byref(c),
@@ -162,6 +163,11 @@ def test_separate_plan_single_pass_when_tiles_fill_the_gpu(lib):
     assert lib.swimba_scan_plan(ctypes.byref(a), sw.DESIGN_SEPARATE, ctypes.byref(c),
                                 ctypes.byref(n)) == sw.OK
     assert n.value > 1 and c.value % 64 == 0
+    assert (c.value, n.value) == (448, 5)  # 96 workgroups per chunk, 512 slots
+    a = scan_args(B=1, L=65536, D=2560, E=16, k=2)
+    assert lib.swimba_scan_plan(ctypes.byref(a), sw.DESIGN_SEPARATE, ctypes.byref(c),
+                                ctypes.byref(n)) == sw.OK
+    assert (c.value, n.value) == (10944, 6)  # 40 workgroups per chunk, 256 slots
 
 
 def test_all_experts_rejects_and_workspace(lib):

@@ -401,6 +401,71 @@ def test_separate_workload_sampled():
     assert rel_err(host(hf)[:, :, dsel], rh) < TOL_BF16
 
 
+def test_separate_long_context_sampled():
+    """The long-context workload in the separate design at the library's own
+    chunking (the launch the benchmark times: a few long chunks whose fix-up
+    stops once every expert's carried state has decayed), on sampled
+    channels."""
+    w, inp, t = workload("long_context")
+    idx, gate = route_on_gpu(t, w)
+    chunk, nchunks = swimba.scan_plan(t["x"], t["A"], idx, separate=swimba.DESIGN_SEPARATE)
+    assert nchunks > 1
+    dsel = np.sort(np.random.default_rng(4).choice(w.D, 12, replace=False))
+    ry, rh = oracle_scan(inp, idx, gate, dsel=dsel, separate=True)
+    y, hf = swimba.scan_separate(*scan_args(t, idx, gate))
+    assert_faithful_bf16(y[:, :, torch.from_numpy(dsel).to(DEV)], ry, "separate y")
+    assert rel_err(host(hf)[:, :, dsel], rh) < TOL_BF16
+
+
+@pytest.mark.parametrize("E,k", [(4, 2), (16, 2), (8, 1)])
+def test_separate_fixup_stops_and_matches_rewalk(E, k):
+    """Chunks much longer than the decay horizon: the fix-up stops early, and
+    its y equals the full re-walk's to fp32 resolution; both match the
+    oracle, with h0."""
+    w, inp, t = small_case(B=2, L=3000, D=136, E=E, k=k, dtype="f32", seed=70 + E)
+    rng = np.random.default_rng(11)
+    H0 = rng.standard_normal((2, E, 136, 16)).astype(np.float32)
+    h0 = torch.from_numpy(H0).to(DEV)
+    idx, gate = route_on_gpu(t, w)
+    ya, ha = swimba.scan_separate(*scan_args(t, idx, gate), h0=h0, chunk=1024)
+    yr, hr = swimba.scan_separate(*scan_args(t, idx, gate), h0=h0, chunk=1024, carry="rewalk")
+    ry, rh = oracle_scan(inp, idx, gate, h0=H0, separate=True)
+    assert rel_err(host(ya), ry) < TOL_F32 and rel_err(host(ha), rh) < TOL_F32
+    assert rel_err(host(yr), ry) < TOL_F32 and rel_err(host(hr), rh) < TOL_F32
+    assert rel_err(host(ya), host(yr)) < 1e-5
+    assert torch.equal(ha, hr)  # final states come from the carry pass in both
+
+
+def test_separate_idle_expert_keeps_fixup_running():
+    """One expert is selected in the first chunk only, so its carried state
+    never decays in later chunks: the fix-up must walk them to the end (it
+    cannot stop), and still match the oracle."""
+    w, inp, t = small_case(B=1, L=2048, D=64, E=4, k=1, dtype="f32", seed=73)
+    idx = np.zeros((1, 2048, 1), dtype=np.int32)
+    idx[0, :300, 0] = np.arange(300) % 4          # every expert early on
+    idx[0, 300:, 0] = 1 + np.arange(1748) % 2     # then experts 1 and 2 only
+    idx[0, 1900:, 0] = 3                          # expert 3 comes back late
+    gate = np.ones((1, 2048, 1), dtype=np.float32)
+    y, hf = swimba.scan_separate(*scan_args(t, torch.from_numpy(idx).to(DEV),
+                                            torch.from_numpy(gate).to(DEV)), chunk=512)
+    ry, rh = oracle_scan(inp, idx, gate, separate=True)
+    assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
+
+
+def test_separate_noncontractive_falls_back_to_rewalk():
+    """Some A > 0: the separate design's fix-up may not stop early; it
+    re-walks whole chunks and still matches the oracle."""
+    w, inp, t = small_case(B=1, L=1500, D=64, E=4, k=2, dtype="f32", seed=75)
+    A = inp["A"].copy()
+    A[1, :, 5] = 0.01
+    inp["A"] = A
+    t["A"] = torch.from_numpy(A).to(DEV)
+    idx, gate = route_on_gpu(t, w)
+    y, hf = swimba.scan_separate(*scan_args(t, idx, gate), chunk=512)
+    ry, rh = oracle_scan(inp, idx, gate, separate=True)
+    assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
+
+
 def test_separate_constant_top1_equals_mixed():
     w, inp, t = small_case(B=1, L=400, D=64, E=4, k=1, dtype="f32", seed=61)
     idx = torch.full((1, 400, 1), 2, dtype=torch.int32, device=DEV)
