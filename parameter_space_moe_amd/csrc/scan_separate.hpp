@@ -75,9 +75,15 @@ __host__ __device__ constexpr int round_tokens(int k) {
   return k <= 2 ? 64 : (k <= 4 ? 32 : (k <= 8 ? 16 : 8));
 }
 
+// The prefetched layout (PF below) stages 128 bf16 or 64 fp32 tokens per round.
 template <typename TIn>
-__host__ __device__ constexpr size_t sep_smem_bytes(int k) {
-  return (size_t)round_tokens(k) *
+__host__ __device__ constexpr int round_tokens(int k, bool pf) {
+  return pf ? (sizeof(TIn) == 2 ? 128 : 64) : round_tokens(k);
+}
+
+template <typename TIn>
+__host__ __device__ constexpr size_t sep_smem_bytes(int k, bool pf) {
+  return (size_t)round_tokens<TIn>(k, pf) *
          (32 * 4 + (size_t)k * 64 * 4 + 2 * (size_t)k * 4 + 2 * 64 * sizeof(TIn));
 }
 
@@ -92,9 +98,8 @@ struct SepSmem {
 };
 
 template <typename TIn>
-__device__ __forceinline__ SepSmem<TIn> sep_layout(int k) {
+__device__ __forceinline__ SepSmem<TIn> sep_layout(int k, int R) {
   extern __shared__ float4 smem_raw[];
-  const int R = round_tokens(k);
   char* p = reinterpret_cast<char*>(smem_raw);
   SepSmem<TIn> s;
   s.bc = reinterpret_cast<float*>(p);
@@ -109,6 +114,19 @@ __device__ __forceinline__ SepSmem<TIn> sep_layout(int k) {
   p += (size_t)R * 64 * sizeof(TIn);
   s.rs = reinterpret_cast<TIn*>(p);
   return s;
+}
+
+// The stage seen from token `i0` of the round on.
+template <typename TIn>
+__device__ __forceinline__ SepSmem<TIn> stage_from(const SepSmem<TIn>& s, int i0, int k) {
+  SepSmem<TIn> t;
+  t.bc = s.bc + i0 * 32;
+  t.yb = s.yb + i0 * k * 64;
+  t.e = s.e + i0 * k;
+  t.g = s.g + i0 * k;
+  t.xs = s.xs + i0 * 64;
+  t.rs = s.rs + i0 * 64;
+  return t;
 }
 
 // Stage tokens [ts, ts + n) of sequence row `row` for the tile at d0 (all
@@ -141,6 +159,109 @@ __device__ __forceinline__ void stage_round(const SepParams& p, const SepSmem<TI
     const TIn xv = X[o], rv = Rr[o];
     s.xs[q] = ok ? xv : TIn(0);
     s.rs[q] = ok ? rv : TIn(0);
+  }
+}
+
+// Register prefetch of one staged round, for workgroups of at least 11 waves
+// (11 or more experts: one such workgroup per CU, so no other workgroup's
+// work hides the wait for a round's loads), k <= 2, D a multiple of 16 bytes'
+// worth of channels and x, dt_raw 16-byte aligned.  The loads of round r + 1
+// are issued as 16-byte packets before the walk of round r and stored to LDS
+// after it.  A round is 128 bf16 or 64 fp32 tokens: x and dt_raw are
+// 2 x 128 x 8 (or 2 x 64 x 16) = 2048 packets, B_t and C_t 512, so with at
+// least 704 threads a thread holds three plus one packets and one routing
+// entry.
+template <typename TIn>
+struct RoundRegs {
+  static constexpr int kEpp = 16 / (int)sizeof(TIn);   // elements per packet
+  static constexpr int kR = sizeof(TIn) == 2 ? 128 : 64;  // tokens per round
+  static constexpr int kPpr = 64 / kEpp;                // packets per tile row
+  static constexpr int kPpt = kN / kEpp;                // packets per B_t (C_t)
+  static constexpr int kX = 3;
+  uint4 xr[kX], bc;
+  int32_t e;
+  float g;
+};
+
+template <typename TIn>
+__device__ __forceinline__ void fetch_round(const SepParams& p, RoundRegs<TIn>& f, size_t row,
+                                            int ts, int n, int k, int d0) {
+  using RR = RoundRegs<TIn>;
+  const int nthr = blockDim.x, tid = threadIdx.x;
+  const int width = min(64, p.D - d0);
+#pragma unroll
+  for (int u = 0; u < RR::kX; ++u) {
+    const int q = tid + u * nthr;
+    const int which = q >= RR::kR * RR::kPpr, r = which ? q - RR::kR * RR::kPpr : q;
+    const int i = r / RR::kPpr, c = (r % RR::kPpr) * RR::kEpp;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (q < 2 * RR::kR * RR::kPpr && i < n && c < width) {
+      const TIn* src = reinterpret_cast<const TIn*>(which ? p.dt : p.x) +
+                       (row + ts + i) * p.D + d0 + c;
+      v = *reinterpret_cast<const uint4*>(src);
+    }
+    f.xr[u] = v;
+  }
+  {
+    const int q = tid;
+    const int which = q >= RR::kR * RR::kPpt, r = which ? q - RR::kR * RR::kPpt : q;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (q < 2 * RR::kR * RR::kPpt && r / RR::kPpt < n) {
+      const TIn* src = reinterpret_cast<const TIn*>(which ? p.Cm : p.Bm) + (row + ts) * kN +
+                       r * RR::kEpp;
+      v = *reinterpret_cast<const uint4*>(src);
+    }
+    f.bc = v;
+  }
+  f.e = 0;
+  f.g = 0.f;
+  if (tid < n * k) {
+    f.e = p.idx[(row + ts) * k + tid];
+    f.g = p.gate[(row + ts) * k + tid];
+  }
+}
+
+// Store a fetched round into the LDS stage (the layout stage_round writes).
+template <typename TIn>
+__device__ __forceinline__ void commit_round(const SepParams& p, const SepSmem<TIn>& s,
+                                             const RoundRegs<TIn>& f, int n, int k) {
+  using RR = RoundRegs<TIn>;
+  const int nthr = blockDim.x, tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < RR::kX; ++u) {
+    const int q = tid + u * nthr;
+    const int which = q >= RR::kR * RR::kPpr, r = which ? q - RR::kR * RR::kPpr : q;
+    const int i = r / RR::kPpr, c = (r % RR::kPpr) * RR::kEpp;
+    if (q < 2 * RR::kR * RR::kPpr && i < n)
+      *reinterpret_cast<uint4*>((which ? s.rs : s.xs) + i * 64 + c) = f.xr[u];
+  }
+  {
+    const int q = tid;
+    const int which = q >= RR::kR * RR::kPpt, r = which ? q - RR::kR * RR::kPpt : q;
+    const int i = r / RR::kPpt, part = r % RR::kPpt;
+    if (q < 2 * RR::kR * RR::kPpt && i < n) {
+      float* dst = s.bc + i * 32 + which * kN + part * RR::kEpp;
+      if constexpr (sizeof(TIn) == 2) {
+        const uint32_t w[4] = {f.bc.x, f.bc.y, f.bc.z, f.bc.w};
+        float4 lo, hi;
+        lo.x = __uint_as_float(w[0] << 16);
+        lo.y = __uint_as_float(w[0] & 0xffff0000u);
+        lo.z = __uint_as_float(w[1] << 16);
+        lo.w = __uint_as_float(w[1] & 0xffff0000u);
+        hi.x = __uint_as_float(w[2] << 16);
+        hi.y = __uint_as_float(w[2] & 0xffff0000u);
+        hi.z = __uint_as_float(w[3] << 16);
+        hi.w = __uint_as_float(w[3] & 0xffff0000u);
+        reinterpret_cast<float4*>(dst)[0] = lo;
+        reinterpret_cast<float4*>(dst)[1] = hi;
+      } else {
+        *reinterpret_cast<uint4*>(dst) = f.bc;
+      }
+    }
+  }
+  if (tid < n * k) {
+    s.e[tid] = f.e < 0 ? 0 : (f.e >= p.E ? p.E - 1 : f.e);
+    s.g[tid] = f.g;
   }
 }
 
@@ -226,13 +347,15 @@ __device__ __forceinline__ void walk_round(const SepSmem<TIn>& s, int n, int k, 
   }
 }
 
-template <typename TIn, typename TOut, int PASS, int K, bool SA, bool ZOH, bool ALL>
+// PF: rounds are prefetched in registers (RoundRegs; 11 or more experts,
+// k <= 2).
+template <typename TIn, typename TOut, int PASS, int K, bool SA, bool ZOH, bool ALL, bool PF>
 __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   const int k = K > 0 ? K : p.k;
-  const int R = round_tokens(k);
+  const int R = round_tokens<TIn>(k, PF);
   const int tid = threadIdx.x, lane = tid & 63, nthr = blockDim.x;
   const int ex = uniform((int)(threadIdx.x >> 6));  // this wave's expert
-  const SepSmem<TIn> s = sep_layout<TIn>(k);
+  const SepSmem<TIn> s = sep_layout<TIn>(k, R);
 
   const int first = PASS == kPassFixup ? 1 : 0;
   const int nwork = PASS == kPassSingle ? 1 : p.nchunks - first;
@@ -289,14 +412,26 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   const bool readout = PASS != kPassFirst || c == 0 || p.trunc != 0;
   TOut* Y = reinterpret_cast<TOut*>(p.y);
 
+  RoundRegs<TIn> f;
+  if (PF) fetch_round<TIn>(p, f, row, t0, min(R, t1 - t0), k, d0);
   for (int ts = t0; ts < t1; ts += R) {
     const int n = min(R, t1 - ts);
-    stage_round<TIn>(p, s, row, ts, n, k, d0);
-    __syncthreads();
-    if (readout)
-      walk_round<TIn, K, true, SA, ZOH, ALL>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
+    if (PF)
+      commit_round<TIn>(p, s, f, n, k);
     else
-      walk_round<TIn, K, false, SA, ZOH, ALL>(s, n, k, ex, lane, h, S, Ae, bias, dsk);
+      stage_round<TIn>(p, s, row, ts, n, k, d0);
+    __syncthreads();
+    // the next round's loads land while this one is walked
+    if (PF && ts + R < t1) fetch_round<TIn>(p, f, row, ts + R, min(R, t1 - ts - R), k, d0);
+    // walked 64 tokens at a time (one lane per token in the selection ballots)
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const SepSmem<TIn> sw = stage_from(s, i0, k);
+      const int nw = min(64, n - i0);
+      if (readout)
+        walk_round<TIn, K, true, SA, ZOH, ALL>(sw, nw, k, ex, lane, h, S, Ae, bias, dsk);
+      else
+        walk_round<TIn, K, false, SA, ZOH, ALL>(sw, nw, k, ex, lane, h, S, Ae, bias, dsk);
+    }
     if (trunc) {
       // this lane's carried part is at most hin_max * exp2(S a_max); NaN or
       // a non-negative A keep the lane busy
@@ -346,7 +481,7 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   }
 }
 
-template <typename TIn, typename TOut, int K, bool SA, bool ZOH, bool ALL>
+template <typename TIn, typename TOut, int K, bool SA, bool ZOH, bool ALL, bool PF>
 int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   SepParams p;
   p.B = a->B;
@@ -373,40 +508,48 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
   char* w = static_cast<char*>(ws);
   p.P = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_P) : nullptr;
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
-  const size_t smem = sep_smem_bytes<TIn>(p.k);
+  const size_t smem = sep_smem_bytes<TIn>(p.k, PF);
   const dim3 block((unsigned)(p.E * 64));
   const size_t tiles = (size_t)p.B * p.ntiles;
   const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL, PF>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL, PF>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL, PF>, smem);
   if (pl.nchunks <= 1) {
-    const int rc = launch_timed(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL>, dim3((unsigned)tiles),
+    const int rc = launch_timed(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL, PF>, dim3((unsigned)tiles),
                                 block, smem, st, ev, p);
     if (rc != SWIMBA_OK) return rc;
     record_skipped(ev ? ev + 2 : nullptr, st);
     record_skipped(ev ? ev + 4 : nullptr, st);
     return SWIMBA_OK;
   }
-  int rc = launch_timed(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL>,
+  int rc = launch_timed(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL, PF>,
                         dim3((unsigned)(tiles * p.nchunks)), block, smem, st, ev, p);
   if (rc != SWIMBA_OK) return rc;
   rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 1, st, ev ? ev + 2 : nullptr);
   if (rc != SWIMBA_OK) return rc;
-  return launch_timed(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL>,
+  return launch_timed(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL, PF>,
                       dim3((unsigned)(tiles * (p.nchunks - 1))), block, smem, st,
                       ev ? ev + 4 : nullptr, p);
 }
 
 template <typename TIn, typename TOut, bool SA, bool ZOH, bool ALL>
 int launch_sep_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
+  // register prefetch where one workgroup fills a CU (RoundRegs' bounds:
+  // whole 16-byte packets of x and dt_raw)
+  const int epp = 16 / (int)sizeof(TIn);
+  const bool pf = !ALL && a->E >= 11 && a->D % epp == 0 &&
+                  (reinterpret_cast<uintptr_t>(a->x) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(a->dt_raw) & 15) == 0;
   switch (a->k) {
     case 1:
-      return launch_sep_t<TIn, TOut, 1, SA, ZOH, ALL>(a, pl, ws, st);
+      return pf ? launch_sep_t<TIn, TOut, 1, SA, ZOH, ALL, !ALL>(a, pl, ws, st)
+                : launch_sep_t<TIn, TOut, 1, SA, ZOH, ALL, false>(a, pl, ws, st);
     case 2:
-      return launch_sep_t<TIn, TOut, 2, SA, ZOH, ALL>(a, pl, ws, st);
+      return pf ? launch_sep_t<TIn, TOut, 2, SA, ZOH, ALL, !ALL>(a, pl, ws, st)
+                : launch_sep_t<TIn, TOut, 2, SA, ZOH, ALL, false>(a, pl, ws, st);
     default:
-      return launch_sep_t<TIn, TOut, 0, SA, ZOH, ALL>(a, pl, ws, st);
+      return launch_sep_t<TIn, TOut, 0, SA, ZOH, ALL, false>(a, pl, ws, st);
   }
 }
 

@@ -417,7 +417,24 @@ def test_separate_long_context_sampled():
     assert rel_err(host(hf)[:, :, dsel], rh) < TOL_BF16
 
 
-@pytest.mark.parametrize("E,k", [(4, 2), (16, 2), (8, 1)])
+@pytest.mark.parametrize("D", [100, 72])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_separate_many_experts_ragged_channels(D, dtype):
+    """16 experts (a workgroup fills a CU; rounds are prefetched in 16-byte
+    packets when D allows it, element by element otherwise) with a ragged
+    last tile, several chunks and h0."""
+    w, inp, t = small_case(B=2, L=700, D=D, E=16, k=2, dtype=dtype, seed=D)
+    rng = np.random.default_rng(D)
+    H0 = rng.standard_normal((2, 16, D, 16)).astype(np.float32)
+    idx, gate = route_on_gpu(t, w)
+    y, hf = swimba.scan_separate(*scan_args(t, idx, gate), h0=torch.from_numpy(H0).to(DEV),
+                                 chunk=192, y_dtype=torch.float32)
+    ry, rh = oracle_scan(inp, idx, gate, h0=H0, separate=True)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    assert rel_err(host(y), ry) < tol and rel_err(host(hf), rh) < tol
+
+
+@pytest.mark.parametrize("E,k", [(4, 2), (16, 2), (8, 1), (12, 1)])
 def test_separate_fixup_stops_and_matches_rewalk(E, k):
     """Chunks much longer than the decay horizon: the fix-up stops early, and
     its y equals the full re-walk's to fp32 resolution; both match the
