@@ -6,8 +6,11 @@ namespace swimba {
 namespace mixed {
 
 // Pass 2: carried-in state of every chunk, sequential over chunks.  One thread
-// per (b, n, d); loads of the next chunks are issued ahead of the dependent chain.
-__global__ __launch_bounds__(256) void mix_carry_kernel(int B, int C, int D, int E,
+// per (b, n, d); loads of the next chunks are issued ahead of the dependent
+// chain.  There are few threads (16 D per sequence), so workgroups are one
+// wave each and spread over every compute unit.
+constexpr int kCarryThreads = 64;
+__global__ __launch_bounds__(kCarryThreads) void mix_carry_kernel(int B, int C, int D, int E,
                                                         const float* __restrict__ P,
                                                         float* __restrict__ H,
                                                         float* __restrict__ h_final,
@@ -24,10 +27,10 @@ __global__ __launch_bounds__(256) void mix_carry_kernel(int B, int C, int D, int
   const size_t stride = (size_t)rows * D;
   const size_t base = (size_t)b * C * stride + (size_t)r * D + d;
   float h = H[base];  // chunk 0 started from h0: its end state is exact
-  // chunks 1 .. C-1 in batches of 8; each batch's loads are issued a batch
+  // chunks 1 .. C-1 in batches of 16; each batch's loads are issued a batch
   // ahead, before the current batch's stores, so the chain waits for memory
   // once per batch.  Loads past chunk C-1 read chunk C-1 again (unused).
-  constexpr int U8 = 8;
+  constexpr int U8 = 16;
   float he[U8], pc[U8];
   auto load_batch = [&](int c0, float* hb, float* pb) {
 #pragma unroll
@@ -110,7 +113,8 @@ int launch_carry(int B, int C, int D, int E, const float* P, float* H, float* h_
                  int separate, hipStream_t st, const hipEvent_t* ev) {
   const size_t rows = separate ? (size_t)E * kN : kN;
   const size_t total = (size_t)B * rows * D;
-  return launch_timed(mixed::mix_carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+  constexpr unsigned nt = mixed::kCarryThreads;
+  return launch_timed(mixed::mix_carry_kernel, dim3((unsigned)((total + nt - 1) / nt)), dim3(nt),
                       0, st, ev, B, C, D, E, P, H, h_final, separate);
 }
 
