@@ -509,7 +509,8 @@ def modes(args, lay, swimba, workloads, dev):
 def expert_sweep(swimba, dev, reps):
     """Router + mixed scan at the Mamba-1.4B-like layer shape (B=8, L=4096,
     D=4096, top-2) for E = 2 .. 64 experts: the active experts, not the
-    total, set the cost ("Fondements Théoriques", Theorem 2).  Inputs are
+    total, set the cost ("Fondements Théoriques", Theorem 2); beside it the
+    mixed scan alone and the separate design on the same routing.  Inputs are
     seeded normal draws made on the GPU; an expert count the scans do not
     take is reported as such."""
     import torch
@@ -548,10 +549,19 @@ def expert_sweep(swimba, dev, reps):
 
         ms = time_events(step, reps)
         ms_route = time_events(route, reps)
+        ms_scan = time_events(scan, reps)
+        # the separate design on the same routing (its own chunking)
+        hfs = torch.empty((B, E, D, N_STATE), dtype=torch.float32, device=dev)
+        sep = swimba.PreparedScan(True, x, dtr, Bm, Cm, idx, gate, A, bias, Dsk, y=y,
+                                  h_final=hfs)
+        ms_sep = time_events(sep, reps)
+        del sep, hfs
         base = base or ms
         out["E%d" % E] = {"ms": round(ms, 4), "route_ms": round(ms_route, 4),
                           "G_tc_per_s": round(B * L * D / ms / 1e6, 3),
-                          "over_E2": round(ms / base, 3)}
+                          "over_E2": round(ms / base, 3),
+                          "scan_ms": round(ms_scan, 4), "separate_ms": round(ms_sep, 4),
+                          "separate_over_mixed": round(ms_sep / ms_scan, 3)}
     return out
 
 

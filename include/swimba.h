@@ -224,8 +224,14 @@ int swimba_scan_noalloc(const swimba_scan_args* a, hipStream_t stream);
  * swimba_scan_separate -- the separate design ([SW] "MoE of separate SSMs"):
  * one state per expert (h0/h_final [B, E, D, N]); each selected expert
  * advances with its own parameters; y = sum_j g_j y_j.  An expert listed
- * twice for one token advances twice.  Same constraints as swimba_scan, plus
- * E <= 16.
+ * twice for one token advances twice.  Same constraints as swimba_scan.  Up
+ * to 16 experts one wave keeps one expert's states and row in registers;
+ * with more, each wave keeps the states of two (E <= 32) or four experts and
+ * reloads their rows once per staged round (slower per token).  Chunks are
+ * joined by a fix-up that stops once every expert's carried state has
+ * decayed below fp32 resolution of its state (A < 0; SWIMBA_CARRY_REWALK or
+ * a non-negative A re-walk whole chunks); the library's chunking gives this
+ * design a few long chunks.
  */
 int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
                          hipStream_t stream);

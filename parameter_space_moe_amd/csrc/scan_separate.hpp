@@ -349,12 +349,41 @@ __device__ __forceinline__ void walk_round(const SepSmem<TIn>& s, int n, int k, 
 
 // PF: rounds are prefetched in registers (RoundRegs; 11 or more experts,
 // k <= 2).
-template <typename TIn, typename TOut, int PASS, int K, bool SA, bool ZOH, bool ALL, bool PF>
+// Expert ex's transition row (pre-scaled by log2 e), dt_bias and Dskip at
+// channel dd.
+template <bool SA>
+__device__ __forceinline__ void load_expert(const SepParams& p, int ex, int dd, float* Ae,
+                                            float& bias, float& dsk) {
+  if (SA) {
+    Ae[0] = p.A[(size_t)ex * p.D + dd] * kLog2e;
+  } else {
+    const float4* Ap = reinterpret_cast<const float4*>(p.A + ((size_t)ex * p.D + dd) * kN);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = Ap[q];
+      Ae[4 * q + 0] = v.x * kLog2e;
+      Ae[4 * q + 1] = v.y * kLog2e;
+      Ae[4 * q + 2] = v.z * kLog2e;
+      Ae[4 * q + 3] = v.w * kLog2e;
+    }
+  }
+  bias = p.bias[(size_t)ex * p.D + dd];
+  dsk = p.Dsk[(size_t)ex * p.D + dd];
+}
+
+// PF: rounds are prefetched in registers (RoundRegs; 11 or more experts,
+// k <= 2).  EPW: experts per wave.  With EPW == 1 (E <= 16) wave e owns
+// expert e and keeps its row in registers for the whole chunk.  With more
+// experts the workgroup has 16 waves and wave w owns experts w, w + 16, ...;
+// it keeps all their states in registers and reloads each expert's row (L2)
+// once per staged round, before walking that expert's selections.
+template <typename TIn, typename TOut, int PASS, int K, bool SA, bool ZOH, bool ALL, bool PF,
+          int EPW>
 __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   const int k = K > 0 ? K : p.k;
   const int R = round_tokens<TIn>(k, PF);
   const int tid = threadIdx.x, lane = tid & 63, nthr = blockDim.x;
-  const int ex = uniform((int)(threadIdx.x >> 6));  // this wave's expert
+  const int wave = uniform((int)(threadIdx.x >> 6));  // experts wave, wave + 16, ...
   const SepSmem<TIn> s = sep_layout<TIn>(k, R);
 
   const int first = PASS == kPassFixup ? 1 : 0;
@@ -372,39 +401,43 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   const size_t row = (size_t)b * p.L;
   const int rows = p.E * kN;
 
-  // fix-up: wave e still carries a part of h_in that is above fp32
-  // resolution of its state (written after the walk, read after the barrier)
+  // fix-up: wave w still carries a part of h_in that is above fp32
+  // resolution of one of its experts' states (written after the walk, read
+  // after the barrier)
   __shared__ int s_busy[16];
-  float Ae[kN], h[kN];
-  if (SA) {
-    Ae[0] = p.A[(size_t)ex * p.D + dd] * kLog2e;
-  } else {
-    const float* Ap = p.A + ((size_t)ex * p.D + dd) * kN;
+  float Ae[kN], bias = 0.f, dsk = 0.f;
+  float h[EPW][kN], S[EPW], hin_max[EPW], a_max[EPW];
 #pragma unroll
-    for (int n = 0; n < kN; ++n) Ae[n] = Ap[n] * kLog2e;
-  }
-  const float bias = p.bias[(size_t)ex * p.D + dd], dsk = p.Dsk[(size_t)ex * p.D + dd];
-#pragma unroll
-  for (int n = 0; n < kN; ++n) {
-    float v = 0.f;
-    if (active) {
-      if (PASS == kPassFixup)
-        v = p.H[(((size_t)b * p.nchunks + c) * rows + ex * kN + n) * p.D + d];
-      else if (c == 0 && p.h0 != nullptr)
-        v = p.h0[(((size_t)b * p.E + ex) * p.D + d) * kN + n];
-    }
-    h[n] = v;
-  }
-  float S = 0.f;
-  // The fix-up's bound on the carried part: max_n |h_in[n]| and the slowest
-  // decay max_n A'[n] (no stop unless it is < 0 on every lane of every wave).
-  float hin_max = 0.f, a_max = SA ? Ae[0] : -INFINITY;
-  if (PASS == kPassFixup) {
+  for (int i = 0; i < EPW; ++i) {
+    const int ex = wave + 16 * i;
+    const bool own = ex < p.E;
+    const int exs = own ? ex : 0;
+    if (EPW == 1 || own) load_expert<SA>(p, exs, dd, Ae, bias, dsk);
 #pragma unroll
     for (int n = 0; n < kN; ++n) {
-      hin_max = fmaxf(hin_max, fabsf(h[n]));
-      if (!SA) a_max = fmaxf(a_max, Ae[n]);
+      float v = 0.f;
+      if (active && own) {
+        if (PASS == kPassFixup)
+          v = p.H[(((size_t)b * p.nchunks + c) * rows + exs * kN + n) * p.D + d];
+        else if (c == 0 && p.h0 != nullptr)
+          v = p.h0[(((size_t)b * p.E + exs) * p.D + d) * kN + n];
+      }
+      h[i][n] = v;
     }
+    S[i] = 0.f;
+    // The fix-up's bound on the carried part: max_n |h_in[n]| and the
+    // slowest decay max_n A'[n] (no stop unless it is < 0 on every lane of
+    // every wave).
+    hin_max[i] = 0.f;
+    a_max[i] = SA ? Ae[0] : -INFINITY;
+    if (PASS == kPassFixup) {
+#pragma unroll
+      for (int n = 0; n < kN; ++n) {
+        hin_max[i] = fmaxf(hin_max[i], fabsf(h[i][n]));
+        if (!SA) a_max[i] = fmaxf(a_max[i], Ae[n]);
+      }
+    }
+    if (!own) a_max[i] = -1.f;  // no expert: nothing is carried
   }
   const bool trunc = PASS == kPassFixup && p.trunc != 0;
   // pass 1 writes provisional y for every chunk when the fix-up may stop
@@ -423,25 +456,38 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
     __syncthreads();
     // the next round's loads land while this one is walked
     if (PF && ts + R < t1) fetch_round<TIn>(p, f, row, ts + R, min(R, t1 - ts - R), k, d0);
-    // walked 64 tokens at a time (one lane per token in the selection ballots)
-    for (int i0 = 0; i0 < n; i0 += 64) {
-      const SepSmem<TIn> sw = stage_from(s, i0, k);
-      const int nw = min(64, n - i0);
-      if (readout)
-        walk_round<TIn, K, true, SA, ZOH, ALL>(sw, nw, k, ex, lane, h, S, Ae, bias, dsk);
-      else
-        walk_round<TIn, K, false, SA, ZOH, ALL>(sw, nw, k, ex, lane, h, S, Ae, bias, dsk);
+#pragma unroll
+    for (int i = 0; i < EPW; ++i) {
+      const int ex = wave + 16 * i;
+      if (EPW > 1) {
+        if (ex >= p.E) break;  // wave-uniform
+        load_expert<SA>(p, ex, dd, Ae, bias, dsk);
+      }
+      // walked 64 tokens at a time (one lane per token in the selection ballots)
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        const SepSmem<TIn> sw = stage_from(s, i0, k);
+        const int nw = min(64, n - i0);
+        if (readout)
+          walk_round<TIn, K, true, SA, ZOH, ALL>(sw, nw, k, ex, lane, h[i], S[i], Ae, bias, dsk);
+        else
+          walk_round<TIn, K, false, SA, ZOH, ALL>(sw, nw, k, ex, lane, h[i], S[i], Ae, bias,
+                                                  dsk);
+      }
     }
     if (trunc) {
-      // this lane's carried part is at most hin_max * exp2(S a_max); NaN or
-      // a non-negative A keep the lane busy
-      float mh = 0.f;
+      // this lane's carried part of expert i is at most
+      // hin_max * exp2(S a_max); NaN or a non-negative A keep the lane busy
+      bool gone = true;
 #pragma unroll
-      for (int q = 0; q < kN; ++q) mh = fmaxf(mh, fabsf(h[q]));
-      const bool gone = !active || (a_max < 0.f && hin_max * hw_exp2(S * a_max) <=
-                                                       fmaxf(kFixupTol * mh, kTiny));
-      const bool busy = __ballot(!gone) != 0;
-      if (lane == 0) s_busy[ex] = busy ? 1 : 0;
+      for (int i = 0; i < EPW; ++i) {
+        float mh = 0.f;
+#pragma unroll
+        for (int q = 0; q < kN; ++q) mh = fmaxf(mh, fabsf(h[i][q]));
+        gone &= a_max[i] < 0.f &&
+                hin_max[i] * hw_exp2(S[i] * a_max[i]) <= fmaxf(kFixupTol * mh, kTiny);
+      }
+      const bool busy = __ballot(active && !gone) != 0;
+      if (lane == 0) s_busy[wave] = busy ? 1 : 0;
     }
     __syncthreads();
     // every (token, slot) output was written by its expert's wave; add them in
@@ -461,27 +507,34 @@ __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
       // every thread reads the same flags after the same barrier: the exit is
       // uniform over the workgroup
       int busy = 0;
-      for (int e = 0; e < p.E; ++e) busy |= s_busy[e];
+      for (int w = 0; w < nthr / 64; ++w) busy |= s_busy[w];
       if (busy == 0) break;
     }
   }
 
-  if (PASS == kPassFirst) {
-    if (active) {
-      const size_t base = ((size_t)b * p.nchunks + c) * rows + ex * kN;
 #pragma unroll
-      for (int n = 0; n < kN; ++n) {
-        p.P[(base + n) * p.D + d] = hw_exp2(S * Ae[SA ? 0 : n]);
-        p.H[(base + n) * p.D + d] = h[n];
+  for (int i = 0; i < EPW; ++i) {
+    const int ex = wave + 16 * i;
+    if (EPW > 1 && ex >= p.E) break;
+    if (PASS == kPassFirst) {
+      if (EPW > 1) load_expert<SA>(p, ex, dd, Ae, bias, dsk);
+      if (active) {
+        const size_t base = ((size_t)b * p.nchunks + c) * rows + ex * kN;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+          p.P[(base + n) * p.D + d] = hw_exp2(S[i] * Ae[SA ? 0 : n]);
+          p.H[(base + n) * p.D + d] = h[i][n];
+        }
       }
-    }
-  } else if (PASS == kPassSingle && p.h_final != nullptr && active) {
+    } else if (PASS == kPassSingle && p.h_final != nullptr && active) {
 #pragma unroll
-    for (int n = 0; n < kN; ++n) p.h_final[(((size_t)b * p.E + ex) * p.D + d) * kN + n] = h[n];
+      for (int n = 0; n < kN; ++n)
+        p.h_final[(((size_t)b * p.E + ex) * p.D + d) * kN + n] = h[i][n];
+    }
   }
 }
 
-template <typename TIn, typename TOut, int K, bool SA, bool ZOH, bool ALL, bool PF>
+template <typename TIn, typename TOut, int K, bool SA, bool ZOH, bool ALL, bool PF, int EPW>
 int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   SepParams p;
   p.B = a->B;
@@ -509,47 +562,62 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
   p.P = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_P) : nullptr;
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
   const size_t smem = sep_smem_bytes<TIn>(p.k, PF);
-  const dim3 block((unsigned)(p.E * 64));
+  const dim3 block((unsigned)(min(p.E, 16) * 64));
   const size_t tiles = (size_t)p.B * p.ntiles;
   const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL, PF>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL, PF>, smem);
-  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL, PF>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL, PF, EPW>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL, PF, EPW>, smem);
+  allow_dynamic_lds(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL, PF, EPW>, smem);
   if (pl.nchunks <= 1) {
-    const int rc = launch_timed(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL, PF>, dim3((unsigned)tiles),
+    const int rc = launch_timed(sep_kernel<TIn, TOut, kPassSingle, K, SA, ZOH, ALL, PF, EPW>, dim3((unsigned)tiles),
                                 block, smem, st, ev, p);
     if (rc != SWIMBA_OK) return rc;
     record_skipped(ev ? ev + 2 : nullptr, st);
     record_skipped(ev ? ev + 4 : nullptr, st);
     return SWIMBA_OK;
   }
-  int rc = launch_timed(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL, PF>,
+  int rc = launch_timed(sep_kernel<TIn, TOut, kPassFirst, K, SA, ZOH, ALL, PF, EPW>,
                         dim3((unsigned)(tiles * p.nchunks)), block, smem, st, ev, p);
   if (rc != SWIMBA_OK) return rc;
   rc = launch_carry(p.B, p.nchunks, p.D, p.E, p.P, p.H, p.h_final, 1, st, ev ? ev + 2 : nullptr);
   if (rc != SWIMBA_OK) return rc;
-  return launch_timed(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL, PF>,
+  return launch_timed(sep_kernel<TIn, TOut, kPassFixup, K, SA, ZOH, ALL, PF, EPW>,
                       dim3((unsigned)(tiles * (p.nchunks - 1))), block, smem, st,
                       ev ? ev + 4 : nullptr, p);
 }
 
+// Register prefetch where one workgroup fills a CU (RoundRegs' bounds:
+// at least 11 waves, whole 16-byte packets of x and dt_raw).
+template <typename TIn>
+bool use_prefetch(const swimba_scan_args* a, bool all) {
+  const int epp = 16 / (int)sizeof(TIn);
+  return !all && a->E >= 11 && a->D % epp == 0 &&
+         (reinterpret_cast<uintptr_t>(a->x) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(a->dt_raw) & 15) == 0;
+}
+
+// More than 16 experts: EPW experts per wave (their states take the
+// registers the round prefetch would use), k = 2 specialised.
+template <typename TIn, typename TOut, bool SA, bool ZOH, bool ALL, int EPW>
+int launch_sep_wide(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
+  if (a->k == 2) return launch_sep_t<TIn, TOut, 2, SA, ZOH, ALL, false, EPW>(a, pl, ws, st);
+  return launch_sep_t<TIn, TOut, 0, SA, ZOH, ALL, false, EPW>(a, pl, ws, st);
+}
+
 template <typename TIn, typename TOut, bool SA, bool ZOH, bool ALL>
 int launch_sep_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
-  // register prefetch where one workgroup fills a CU (RoundRegs' bounds:
-  // whole 16-byte packets of x and dt_raw)
-  const int epp = 16 / (int)sizeof(TIn);
-  const bool pf = !ALL && a->E >= 11 && a->D % epp == 0 &&
-                  (reinterpret_cast<uintptr_t>(a->x) & 15) == 0 &&
-                  (reinterpret_cast<uintptr_t>(a->dt_raw) & 15) == 0;
+  if (a->E > 32) return launch_sep_wide<TIn, TOut, SA, ZOH, ALL, 4>(a, pl, ws, st);
+  if (a->E > 16) return launch_sep_wide<TIn, TOut, SA, ZOH, ALL, 2>(a, pl, ws, st);
+  const bool pf = use_prefetch<TIn>(a, ALL);
   switch (a->k) {
     case 1:
-      return pf ? launch_sep_t<TIn, TOut, 1, SA, ZOH, ALL, !ALL>(a, pl, ws, st)
-                : launch_sep_t<TIn, TOut, 1, SA, ZOH, ALL, false>(a, pl, ws, st);
+      return pf ? launch_sep_t<TIn, TOut, 1, SA, ZOH, ALL, !ALL, 1>(a, pl, ws, st)
+                : launch_sep_t<TIn, TOut, 1, SA, ZOH, ALL, false, 1>(a, pl, ws, st);
     case 2:
-      return pf ? launch_sep_t<TIn, TOut, 2, SA, ZOH, ALL, !ALL>(a, pl, ws, st)
-                : launch_sep_t<TIn, TOut, 2, SA, ZOH, ALL, false>(a, pl, ws, st);
+      return pf ? launch_sep_t<TIn, TOut, 2, SA, ZOH, ALL, !ALL, 1>(a, pl, ws, st)
+                : launch_sep_t<TIn, TOut, 2, SA, ZOH, ALL, false, 1>(a, pl, ws, st);
     default:
-      return launch_sep_t<TIn, TOut, 0, SA, ZOH, ALL, false>(a, pl, ws, st);
+      return launch_sep_t<TIn, TOut, 0, SA, ZOH, ALL, false, 1>(a, pl, ws, st);
   }
 }
 

@@ -37,7 +37,6 @@ int validate_scan(const swimba_scan_args* a, int design) {
   if (a->disc != SWIMBA_DISC_EULER && a->disc != SWIMBA_DISC_ZOH) return SWIMBA_EINVAL;
   if (a->N != SWIMBA_STATE_N) return SWIMBA_EUNSUPPORTED;
   if (a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
-  if (separate && a->E > 16) return SWIMBA_EUNSUPPORTED;
   // the per-slot scan stages the E expert tables in LDS
   if (design == 2 && a->E > 16) return SWIMBA_EUNSUPPORTED;
   // the mixed scan with more than 16 experts reads expert rows through 32-bit

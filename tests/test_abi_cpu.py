@@ -109,8 +109,16 @@ def test_scan_rejects(lib, field, value, status):
     assert lib.swimba_scan(ctypes.byref(a), None, 0, None) == status
 
 
-def test_separate_rejects_many_experts(lib):
-    a = scan_args(E=17)
+def test_separate_designs_take_up_to_64_experts(lib):
+    # one wave per expert up to 16, then 16 waves of 2 or 4 experts each;
+    # valid: the call gets as far as the (missing) workspace
+    for E in (17, 32, 33, 64):
+        for design, fn in ((sw.DESIGN_SEPARATE, lib.swimba_scan_separate),
+                           (sw.DESIGN_ALL_EXPERTS, lib.swimba_scan_all_experts)):
+            a = scan_args(E=E)
+            assert sw.workspace_size(a, design) > 0
+            assert fn(ctypes.byref(a), None, 0, None) == sw.EWORKSPACE
+    a = scan_args(E=65, k=2)
     assert lib.swimba_scan_separate(ctypes.byref(a), None, 0, None) == sw.EUNSUPPORTED
 
 
@@ -171,8 +179,8 @@ def test_separate_plan_single_pass_when_tiles_fill_the_gpu(lib):
 
 
 def test_all_experts_rejects_and_workspace(lib):
-    # one wave per expert in a workgroup: E <= 16, as the per-expert design
-    assert lib.swimba_scan_all_experts(ctypes.byref(scan_args(E=17)), None, 0, None) == \
+    # up to 64 experts, as the per-expert design
+    assert lib.swimba_scan_all_experts(ctypes.byref(scan_args(E=65)), None, 0, None) == \
         sw.EUNSUPPORTED
     assert lib.swimba_scan_all_experts(ctypes.byref(scan_args(x=None)), None, 0, None) == \
         sw.EINVAL

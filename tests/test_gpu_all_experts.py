@@ -182,3 +182,14 @@ def test_all_experts_sixteen_experts_runtime_k():
     y, hf = swimba.scan_all_experts(*args(t, idx, gate), h0=t["h0"], chunk=64, zoh=True)
     ry, rh = ref(inp, idx, gate, h0=inp["h0"], zoh=True)
     assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
+
+
+@pytest.mark.parametrize("E,chunk", [(24, 0), (40, 128)])
+def test_all_experts_many_experts(E, chunk):
+    """More than 16 experts: 16 waves of two or four experts each, every
+    expert advancing at every token."""
+    w, inp, t = case(B=1, L=260, D=72, E=E, k=2, seed=E, h0=True)
+    idx, gate = swimba.route(t["x"], t["Wr"], 2)
+    y, hf = swimba.scan_all_experts(*args(t, idx, gate), h0=t["h0"], chunk=chunk)
+    ry, rh = ref(inp, idx, gate, h0=inp["h0"])
+    assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32

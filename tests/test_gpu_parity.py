@@ -483,6 +483,37 @@ def test_separate_noncontractive_falls_back_to_rewalk():
     assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
 
 
+@pytest.mark.parametrize("E,k,dtype", [(17, 2, "bf16"), (32, 2, "bf16"), (33, 3, "f32"),
+                                       (64, 2, "bf16"), (64, 1, "f32")])
+@pytest.mark.parametrize("chunk", [0, 160])
+def test_separate_many_experts(E, k, dtype, chunk):
+    """17..64 experts: 16 waves of two or four experts each (rows reloaded per
+    staged round), chunked and not, with h0 and a ragged last tile."""
+    w, inp, t = small_case(B=2, L=520, D=136, E=E, k=k, dtype=dtype, seed=E + 3 * k)
+    rng = np.random.default_rng(E)
+    H0 = rng.standard_normal((2, E, 136, 16)).astype(np.float32)
+    idx, gate = route_on_gpu(t, w)
+    y, hf = swimba.scan_separate(*scan_args(t, idx, gate), h0=torch.from_numpy(H0).to(DEV),
+                                 chunk=chunk, y_dtype=torch.float32)
+    ry, rh = oracle_scan(inp, idx, gate, h0=H0, separate=True)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    assert rel_err(host(y), ry) < tol and rel_err(host(hf), rh) < tol
+
+
+def test_separate_64_experts_layer_sampled():
+    """64 experts at the 1.4B-like layer shape (B = 8, L = 4096, D = 4096,
+    top-2, bf16) in the library's own launch, on sampled channels."""
+    w = workloads.Workload("wide", B=8, L=4096, D=4096, N=16, E=64, k=2, dtype="bf16", seed=9)
+    inp = workloads.generate(w)
+    t = dev_tensors(inp, "bf16", DEV)
+    idx, gate = route_on_gpu(t, w)
+    dsel = np.sort(np.random.default_rng(5).choice(w.D, 8, replace=False))
+    ry, rh = oracle_scan(inp, idx, gate, dsel=dsel, separate=True)
+    y, hf = swimba.scan_separate(*scan_args(t, idx, gate))
+    assert_faithful_bf16(y[:, :, torch.from_numpy(dsel).to(DEV)], ry, "separate y")
+    assert rel_err(host(hf)[:, :, dsel], rh) < TOL_BF16
+
+
 def test_separate_constant_top1_equals_mixed():
     w, inp, t = small_case(B=1, L=400, D=64, E=4, k=1, dtype="f32", seed=61)
     idx = torch.full((1, 400, 1), 2, dtype=torch.int32, device=DEV)
