@@ -75,15 +75,18 @@ __host__ __device__ constexpr int round_tokens(int k) {
   return k <= 2 ? 64 : (k <= 4 ? 32 : (k <= 8 ? 16 : 8));
 }
 
-// The prefetched layout (PF below) stages 128 bf16 or 64 fp32 tokens per round.
+// The prefetched layout (PF below) stages 128 bf16 or 64 fp32 tokens per
+// round.  With at most 4 experts (workgroups of at most 4 waves) rounds of 16
+// tokens keep the LDS of a workgroup small, so that enough of them share a CU
+// to give each SIMD several waves.
 template <typename TIn>
-__host__ __device__ constexpr int round_tokens(int k, bool pf) {
-  return pf ? (sizeof(TIn) == 2 ? 128 : 64) : round_tokens(k);
+__host__ __device__ constexpr int round_tokens(int k, int E, bool pf) {
+  return pf ? (sizeof(TIn) == 2 ? 128 : 64) : (E <= 4 ? 16 : round_tokens(k));
 }
 
 template <typename TIn>
-__host__ __device__ constexpr size_t sep_smem_bytes(int k, bool pf) {
-  return (size_t)round_tokens<TIn>(k, pf) *
+__host__ __device__ constexpr size_t sep_smem_bytes(int k, int E, bool pf) {
+  return (size_t)round_tokens<TIn>(k, E, pf) *
          (32 * 4 + (size_t)k * 64 * 4 + 2 * (size_t)k * 4 + 2 * 64 * sizeof(TIn));
 }
 
@@ -381,7 +384,7 @@ template <typename TIn, typename TOut, int PASS, int K, bool SA, bool ZOH, bool 
           int EPW>
 __global__ __launch_bounds__(1024) void sep_kernel(SepParams p) {
   const int k = K > 0 ? K : p.k;
-  const int R = round_tokens<TIn>(k, PF);
+  const int R = round_tokens<TIn>(k, p.E, PF);
   const int tid = threadIdx.x, lane = tid & 63, nthr = blockDim.x;
   const int wave = uniform((int)(threadIdx.x >> 6));  // experts wave, wave + 16, ...
   const SepSmem<TIn> s = sep_layout<TIn>(k, R);
@@ -561,7 +564,7 @@ int launch_sep_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStr
   char* w = static_cast<char*>(ws);
   p.P = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_P) : nullptr;
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
-  const size_t smem = sep_smem_bytes<TIn>(p.k, PF);
+  const size_t smem = sep_smem_bytes<TIn>(p.k, p.E, PF);
   const dim3 block((unsigned)(min(p.E, 16) * 64));
   const size_t tiles = (size_t)p.B * p.ntiles;
   const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)

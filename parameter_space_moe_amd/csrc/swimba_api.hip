@@ -97,14 +97,15 @@ int auto_chunk(long long B, long long L, int ntiles, int E, bool separate, bool 
   long long want, min_chunk = 128;
   *small = false;
   if (separate) {
-    // A workgroup per (sequence, tile, chunk) with one wave per expert.  A CU
-    // holds about 20 such waves (five per SIMD at the passes' register use)
-    // and the LDS of two workgroups.  One chunk when the (sequence, tile)
-    // workgroups fill those slots; else as many chunks as fill them once.
-    // The fix-up stops once every carried state has decayed, which takes a
-    // number of selections per expert rather than of tokens, so long chunks
-    // keep it a small part of the work.
-    const long long per_cu = E > 10 ? 1 : 2;
+    // A workgroup per (sequence, tile, chunk) with one wave per expert (16
+    // waves beyond 16 experts).  A CU holds about 20 such waves (five per
+    // SIMD at the passes' register use) and the LDS of two workgroups, or of
+    // ten with at most 4 experts (16-token rounds).  One chunk when the
+    // (sequence, tile) workgroups fill those slots; else as many chunks as
+    // fill them once.  The fix-up stops once every carried state has
+    // decayed, which takes a number of selections per expert rather than of
+    // tokens, so long chunks keep it a small part of the work.
+    const long long per_cu = E <= 4 ? (20 / E < 10 ? 20 / E : 10) : (E > 10 ? 1 : 2);
     const long long slots = cus * per_cu;
     want = base >= slots ? 1 : slots / base;
     min_chunk = 256;

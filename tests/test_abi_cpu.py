@@ -157,8 +157,9 @@ def test_slots_rejects_and_workspace(lib):
 
 
 def test_separate_plan_single_pass_when_tiles_fill_the_gpu(lib):
-    # (sequence, tile) workgroups of one wave per expert: two per compute unit
-    # up to 10 experts, one beyond (256 CUs when no device answers); the
+    # (sequence, tile) workgroups of one wave per expert: 20 / E per compute
+    # unit up to 4 experts (at most ten), two up to 10 experts, one beyond
+    # (256 CUs when no device answers); the
     # separate design runs each sequence in one chunk when they fill those
     # slots, else in as many long chunks as fill them once
     c, n = ctypes.c_int(), ctypes.c_int()
@@ -176,6 +177,11 @@ def test_separate_plan_single_pass_when_tiles_fill_the_gpu(lib):
     assert lib.swimba_scan_plan(ctypes.byref(a), sw.DESIGN_SEPARATE, ctypes.byref(c),
                                 ctypes.byref(n)) == sw.OK
     assert (c.value, n.value) == (10944, 6)  # 40 workgroups per chunk, 256 slots
+    # two experts: 16-token rounds, ten 2-wave workgroups per CU
+    a = scan_args(B=8, L=4096, D=4096, E=2, k=2)
+    assert lib.swimba_scan_plan(ctypes.byref(a), sw.DESIGN_SEPARATE, ctypes.byref(c),
+                                ctypes.byref(n)) == sw.OK
+    assert (c.value, n.value) == (832, 5)  # 512 workgroups per chunk, 2560 slots
 
 
 def test_all_experts_rejects_and_workspace(lib):
