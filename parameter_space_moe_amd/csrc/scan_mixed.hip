@@ -69,29 +69,65 @@ __global__ __launch_bounds__(kCarryThreads) void mix_carry_kernel(int B, int C, 
 
 // Contraction check of the expert tables for the scans that read expert rows
 // from memory: flags[tile] = 1 if any A[e, d, :] of the tile's 64 channels is
-// not strictly negative (or NaN).  One workgroup per tile; consecutive
-// threads read consecutive floats of each expert's block.
-__global__ __launch_bounds__(256) void a_flags_kernel(const float* __restrict__ A, int E, int D,
-                                                      int scalar_a, int32_t* __restrict__ flags) {
+// not strictly negative (or NaN).  One workgroup of 1024 threads per tile;
+// each thread issues all its loads (at most 16: E <= 64 experts x 64
+// channels x 16 states = 16384 floats as 16-byte vectors, or 4096 scalars)
+// before testing any, from clamped (valid) indices.  VEC: A is 16-byte
+// aligned (diagonal A only).
+constexpr int kFlagThreads = 1024;
+template <bool VEC>
+__global__ __launch_bounds__(kFlagThreads) void a_flags_kernel(const float* __restrict__ A, int E,
+                                                                int D, int scalar_a,
+                                                                int32_t* __restrict__ flags) {
   const int tile = blockIdx.x, d0 = tile * 64;
-  const int per = scalar_a ? 1 : kN;
   const int nd = min(64, D - d0);
+  const int tid = threadIdx.x;
   int bad = 0;
-  for (int i = threadIdx.x; i < E * nd * per; i += blockDim.x) {
-    const int e = i / (nd * per), r = i % (nd * per);
-    const float a = A[((size_t)e * D + d0) * per + r];
-    bad |= !(a < 0.f);
+  if (VEC && !scalar_a) {
+    // expert e's rows of the tile: nd * 16 contiguous floats = nd * 4 vectors
+    const int r4 = nd * 4, total = E * r4;
+    float4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int i = min(tid + j * kFlagThreads, total - 1);
+      const int e = i / r4, r = i % r4;
+      v[j] = reinterpret_cast<const float4*>(A + ((size_t)e * D + d0) * kN)[r];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      bad |= !(v[j].x < 0.f) | !(v[j].y < 0.f) | !(v[j].z < 0.f) | !(v[j].w < 0.f);
+  } else {
+    // one float per (expert, channel) (scalar A) or per (expert, channel,
+    // state): E * nd * per values, read 16 per thread per round
+    const int per = scalar_a ? 1 : kN;
+    const int total = E * nd * per;
+    for (int base = 0; base < total; base += 16 * kFlagThreads) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int i = min(base + tid + j * kFlagThreads, total - 1);
+        const int e = i / (nd * per), r = i % (nd * per);
+        v[j] = A[((size_t)e * D + d0) * per + r];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) bad |= !(v[j] < 0.f);
+    }
   }
   bad = __syncthreads_or(bad);
-  if (threadIdx.x == 0) flags[tile] = bad ? 1 : 0;
+  if (tid == 0) flags[tile] = bad ? 1 : 0;
 }
 
 }  // namespace mixed
 
 int launch_a_flags(const float* A, int E, int D, bool scalar_a, int32_t* flags, hipStream_t st) {
   const int ntiles = (D + 63) / 64;
-  hipLaunchKernelGGL(mixed::a_flags_kernel, dim3((unsigned)ntiles), dim3(256), 0, st, A, E, D,
-                     scalar_a ? 1 : 0, flags);
+  const bool vec = !scalar_a && (reinterpret_cast<uintptr_t>(A) & 15) == 0 && E <= 64;
+  if (vec)
+    hipLaunchKernelGGL(mixed::a_flags_kernel<true>, dim3((unsigned)ntiles),
+                       dim3(mixed::kFlagThreads), 0, st, A, E, D, 0, flags);
+  else
+    hipLaunchKernelGGL(mixed::a_flags_kernel<false>, dim3((unsigned)ntiles),
+                       dim3(mixed::kFlagThreads), 0, st, A, E, D, scalar_a ? 1 : 0, flags);
   return hipGetLastError() == hipSuccess ? SWIMBA_OK : SWIMBA_EHIP;
 }
 

@@ -105,6 +105,31 @@ def test_many_experts_noncontractive_falls_back():
     assert rel_err(host(y), ry) < TOL_F32 and rel_err(host(hf), rh) < TOL_F32
 
 
+@pytest.mark.parametrize("scalar_a", [False, True])
+@pytest.mark.parametrize("E", [33, 64])
+def test_many_experts_nonnegative_A_flags_its_tile(E, scalar_a):
+    """One non-negative A entry (of an expert the routing never picks) in the
+    third 64-channel tile: the per-tile check must flag that tile, whose
+    chunks are then re-walked whole -- bit for bit the same y as an explicit
+    full re-walk -- while every tile still matches the oracle."""
+    w, inp, t = case(B=1, L=700, D=200, E=E, k=2, dtype="f32", seed=E + 60, scalar_a=scalar_a)
+    A = inp["A"].copy()
+    if scalar_a:
+        A[E - 1, 150] = 0.0
+    else:
+        A[E - 1, 150, 7] = 0.0
+    inp["A"] = A
+    t["A"] = torch.from_numpy(A).to(DEV)
+    idx, gate = swimba.route(t["x"], t["Wr"], 2)
+    idx = torch.where(idx == E - 1, torch.zeros_like(idx), idx)  # never expert E - 1
+    ya, ha = swimba.scan(*args(t, idx, gate), chunk=96)
+    yr, hr = swimba.scan(*args(t, idx, gate), chunk=96, carry="rewalk")
+    assert torch.equal(ya[:, :, 128:192], yr[:, :, 128:192])
+    assert torch.equal(ha, hr)
+    ry, rh = ref(inp, idx, gate)
+    assert rel_err(host(ya), ry) < TOL_F32 and rel_err(host(ha), rh) < TOL_F32
+
+
 def test_many_experts_layer_sampled():
     """B = 2, L = 4096, D = 2048, E = 64, top-2, bf16 in the library's own
     chunking; 24 sampled channels against the oracle."""
