@@ -96,9 +96,21 @@ struct Rows {
   uint32_t voa, vob;
 };
 
-__host__ __device__ inline int table_rows(bool scalar_a) { return scalar_a ? 1 : kRowsDiag; }
-__host__ __device__ inline size_t table_bytes(int E, bool scalar_a) {
-  return (size_t)E * table_rows(scalar_a) * 64 * 16;
+// Table modes of the mixed passes (TM): 0 = expert rows read from memory
+// per token (more than 32 experts, or more than 16 with a scalar A); 1 =
+// every expert's rows in an LDS table (E <= 16); 2 = only the A rows in the
+// table (17 <= E <= 32, diagonal A: 4 KB per expert), dt_bias and Dskip read
+// from memory per token.
+__host__ __device__ constexpr int table_mode(int emax, bool scalar_a) {
+  return emax <= 16 ? 1 : ((emax <= 32 && !scalar_a) ? 2 : 0);
+}
+// LDS a workgroup of table mode 2 may use (the CU's 160 KiB)
+constexpr size_t kTabModeLds = (size_t)160 << 10;
+__host__ __device__ inline int table_rows(bool scalar_a, int tm = 1) {
+  return scalar_a ? 1 : (tm == 2 ? 4 : kRowsDiag);
+}
+__host__ __device__ inline size_t table_bytes(int E, bool scalar_a, int tm = 1) {
+  return (size_t)E * table_rows(scalar_a, tm) * 64 * 16;
 }
 // A wave's ring: the shared staging layout plus, per (token, slot), the byte
 // offset of the selected expert's U column.
@@ -106,8 +118,8 @@ __host__ __device__ inline size_t ring_bytes_u(int k) {
   return ring_bytes(k) + (size_t)2 * kTB * k * 4;
 }
 // byte stride of one expert's rows in the table
-__host__ __device__ inline int expert_stride(bool scalar_a) {
-  return table_rows(scalar_a) * 64 * 16;
+__host__ __device__ inline int expert_stride(bool scalar_a, int tm = 1) {
+  return table_rows(scalar_a, tm) * 64 * 16;
 }
 
 // LDS: the workgroup's expert table, then per wave a staging ring (dynamic
@@ -120,12 +132,12 @@ struct Smem {
   Ring ring;        // this wave's ring
 };
 
-__device__ __forceinline__ Smem smem_layout(int E, int k, int wave, bool scalar_a) {
+__device__ __forceinline__ Smem smem_layout(int E, int k, int wave, bool scalar_a, int tm = 1) {
   extern __shared__ float4 smem_raw[];
   Smem s;
   char* p = reinterpret_cast<char*>(smem_raw);
   s.T = reinterpret_cast<const float4*>(p);
-  p += table_bytes(E, scalar_a);
+  p += table_bytes(E, scalar_a, tm);
   p += ring_bytes_u(k) * wave;
   s.ring.bc = reinterpret_cast<float*>(p);
   s.ring.e = reinterpret_cast<int32_t*>(p + 2 * kTB * 32 * 4);
@@ -136,14 +148,15 @@ __device__ __forceinline__ Smem smem_layout(int E, int k, int wave, bool scalar_
 }
 
 // dynamic LDS of the chunk and fix-up passes
-__host__ inline size_t smem_bytes(int E, int k, int waves, bool scalar_a) {
-  return table_bytes(E, scalar_a) + ring_bytes_u(k) * waves;
+__host__ inline size_t smem_bytes(int E, int k, int waves, bool scalar_a, int tm = 1) {
+  return table_bytes(E, scalar_a, tm) + ring_bytes_u(k) * waves;
 }
 
 // Stage the tile's expert parameters (A scaled by log2 e); returns 1 if any A
 // in the tile is not strictly negative (including NaN).  Lanes past D get
 // zeros.
-__device__ __forceinline__ int load_table(const MixParams& p, float4* T, int d0, bool scalar_a) {
+__device__ __forceinline__ int load_table(const MixParams& p, float4* T, int d0, bool scalar_a,
+                                          int tm = 1) {
   int bad = 0;
   const int nthr = blockDim.x;
   if (scalar_a) {
@@ -171,8 +184,9 @@ __device__ __forceinline__ int load_table(const MixParams& p, float4* T, int d0,
       bad |= !(a0 < 0.f) | !(a1 < 0.f) | !(a2 < 0.f) | !(a3 < 0.f);
       v = make_float4(a0 * kLog2e, a1 * kLog2e, a2 * kLog2e, a3 * kLog2e);
     }
-    T[(e * kRowsDiag + q) * 64 + dl] = v;
+    T[(e * (tm == 2 ? 4 : kRowsDiag) + q) * 64 + dl] = v;
   }
+  if (tm == 2) return bad;  // A rows only
   for (int i = threadIdx.x; i < p.E * 64; i += nthr) {
     const int e = i >> 6, dl = i & 63, d = d0 + dl;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -230,7 +244,7 @@ __device__ __forceinline__ float update_readout(const float4* bc, const float* m
 // time.  Routing (experts e[j], gates gw[j]) is wave-uniform; each selected
 // expert's table block is read with one address and all of the token's table
 // reads are issued together.  ACC_U: add Delta g_j to the wave's sums U_e.
-template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH, bool TAB>
+template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH, int TM>
 __device__ __forceinline__ float mix_token_k(const Smem& s, const Rows& R, float* ms,
                                              const int* e, const int* uo, const float* gw,
                                              const float4* bc, int lane, float xv, float rv,
@@ -240,27 +254,29 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, const Rows& R, float
   float uold[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    if constexpr (TAB) {
-      if (ACC_U) uold[j] = *usum_at(s.U, uo[j], lane);
+    if constexpr (TM >= 1) {
+      if (ACC_U && TM == 1) uold[j] = *usum_at(s.U, uo[j], lane);
       const float4* te = expert_rows(s, e[j], lane);
       if constexpr (SA) {
         bd[j] = te[0];  // (A log2 e, dt_bias, Dskip, 0)
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) ar[j][q] = te[q * 64];
-        bd[j] = te[4 * 64];  // (dt_bias, Dskip, 0, 0)
+        if (TM == 1) bd[j] = te[4 * 64];  // (dt_bias, Dskip, 0, 0)
       }
     }
   }
-  if constexpr (!TAB) {
+  if constexpr (TM != 1) {
     // rows from memory: e[j] and uo[j] are the byte offsets of the expert's
-    // A block and of its dt_bias / Dskip entries (wave-uniform)
+    // A block (TM 0) and of its dt_bias / Dskip entries (wave-uniform)
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const uint32_t soa = (uint32_t)uniform(e[j]), sob = (uint32_t)uniform(uo[j]);
       const float bj = stage::buf_load<float>(R.bias, R.vob, sob);
       const float dj = stage::buf_load<float>(R.dsk, R.vob, sob);
-      if constexpr (SA) {
+      if constexpr (TM == 2) {
+        bd[j] = make_float4(bj, dj, 0.f, 0.f);
+      } else if constexpr (SA) {
         bd[j] = make_float4(stage::buf_load<float>(R.a, R.vob, sob), bj, dj, 0.f);
       } else {
 #pragma unroll
@@ -283,7 +299,7 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, const Rows& R, float
   }
   const float dlt = softplus_f32(rv + beta);
   // rows from memory hold A itself: log2 e goes into u
-  const float dls = TAB ? dlt : dlt * kLog2e;
+  const float dls = TM >= 1 ? dlt : dlt * kLog2e;
   float u[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) u[j] = dls * gw[j];
@@ -313,11 +329,11 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, const Rows& R, float
         m[4 * q + 3] = fmaf(u[j], a.w, m[4 * q + 3]);
       }
   }
-  if (ACC_U && !TAB)
+  if (ACC_U && TM != 1)
 #pragma unroll
     for (int n = 0; n < (SA ? 1 : kN); ++n) ms[n] += m[n];
   const float yv = update_readout<TRACK, SA, ZOH>(bc, m, dlt * xv, h, g);
-  if (ACC_U && TAB) {
+  if (ACC_U && TM == 1) {
     // U_e += u_j; a slot that repeats an earlier slot's expert adds onto
     // that slot's new value (both were read before either store)
     float unew[K];
@@ -335,7 +351,7 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, const Rows& R, float
 }
 
 // The same for k known only at run time (k > 2).
-template <bool TRACK, bool ACC_U, bool SA, bool ZOH, bool TAB>
+template <bool TRACK, bool ACC_U, bool SA, bool ZOH, int TM>
 __device__ __forceinline__ float mix_token_any(const Smem& s, const Rows& R, float* ms, int k,
                                                const int* e, const int* uo, const float* gw,
                                                const float4* bc, int lane, float xv, float rv,
@@ -343,7 +359,7 @@ __device__ __forceinline__ float mix_token_any(const Smem& s, const Rows& R, flo
   float beta = 0.f, delta = 0.f;
   for (int j = 0; j < k; ++j) {
     float bj, dj;
-    if constexpr (TAB) {
+    if constexpr (TM == 1) {
       const float4 bd = expert_rows(s, e[j], lane)[SA ? 0 : 4 * 64];
       bj = SA ? bd.y : bd.x;
       dj = SA ? bd.z : bd.y;
@@ -356,17 +372,17 @@ __device__ __forceinline__ float mix_token_any(const Smem& s, const Rows& R, flo
     delta = fmaf(gw[j], dj, delta);
   }
   const float dlt = softplus_f32(rv + beta);
-  const float dls = TAB ? dlt : dlt * kLog2e;
+  const float dls = TM >= 1 ? dlt : dlt * kLog2e;
   float m[SA ? 1 : kN];
 #pragma unroll
   for (int n = 0; n < (SA ? 1 : kN); ++n) m[n] = 0.f;
   for (int j = 0; j < k; ++j) {
     const float u = dls * gw[j];
-    if (ACC_U && TAB) {
+    if (ACC_U && TM == 1) {
       float* up = usum_at(s.U, uo[j], lane);
       *up = *up + u;
     }
-    if constexpr (TAB) {
+    if constexpr (TM >= 1) {
       const float4* te = expert_rows(s, e[j], lane);
       if constexpr (SA) {
         m[0] = fmaf(u, te[0].x, m[0]);
@@ -397,7 +413,7 @@ __device__ __forceinline__ float mix_token_any(const Smem& s, const Rows& R, flo
       }
     }
   }
-  if (ACC_U && !TAB)
+  if (ACC_U && TM != 1)
 #pragma unroll
     for (int n = 0; n < (SA ? 1 : kN); ++n) ms[n] += m[n];
   const float yv = update_readout<TRACK, SA, ZOH>(bc, m, dlt * xv, h, g);
@@ -405,7 +421,7 @@ __device__ __forceinline__ float mix_token_any(const Smem& s, const Rows& R, flo
 }
 
 // One token from ring slot `slot`, position i (routing read from the ring).
-template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH, bool TAB>
+template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH, int TM>
 __device__ __forceinline__ float ring_token(const MixParams& p, const Smem& s, const Rows& R,
                                             float* ms, int slot, int i, int lane, float xv,
                                             float rv, float* h, float* g) {
@@ -417,9 +433,9 @@ __device__ __forceinline__ float ring_token(const MixParams& p, const Smem& s, c
     for (int j = 0; j < K; ++j) {
       ev[j] = s.ring.e[(slot * kTB + i) * K + j];
       gv[j] = s.ring.g[(slot * kTB + i) * K + j];
-      uv[j] = (ACC_U || !TAB) ? s.ring.uo[(slot * kTB + i) * K + j] : 0;
+      uv[j] = (ACC_U || TM != 1) ? s.ring.uo[(slot * kTB + i) * K + j] : 0;
     }
-    return mix_token_k<K, TRACK, ACC_U, SA, ZOH, TAB>(s, R, ms, ev, uv, gv, bc, lane, xv, rv, h,
+    return mix_token_k<K, TRACK, ACC_U, SA, ZOH, TM>(s, R, ms, ev, uv, gv, bc, lane, xv, rv, h,
                                                       g);
   } else {
     const int k = p.k;
@@ -428,9 +444,9 @@ __device__ __forceinline__ float ring_token(const MixParams& p, const Smem& s, c
     for (int j = 0; j < k; ++j) {
       eb[j] = s.ring.e[(slot * kTB + i) * k + j];
       gb[j] = s.ring.g[(slot * kTB + i) * k + j];
-      ub[j] = (ACC_U || !TAB) ? s.ring.uo[(slot * kTB + i) * k + j] : 0;
+      ub[j] = (ACC_U || TM != 1) ? s.ring.uo[(slot * kTB + i) * k + j] : 0;
     }
-    return mix_token_any<TRACK, ACC_U, SA, ZOH, TAB>(s, R, ms, k, eb, ub, gb, bc, lane, xv, rv, h,
+    return mix_token_any<TRACK, ACC_U, SA, ZOH, TM>(s, R, ms, k, eb, ub, gb, bc, lane, xv, rv, h,
                                                      g);
   }
 }
@@ -478,7 +494,7 @@ __device__ __forceinline__ void store_y2(stage::rsrc_t ry, uint32_t yoff, uint32
 // a fixed per-lane channel offset); the prefetch of the next block is issued
 // before the current one computes and is waited on only when it is used.
 template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA, bool ZOH,
-          bool TAB>
+          int TM>
 __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* ms, int b, int t0,
                                      int t1, int d, bool active, bool full_tile, int lane,
                                      bool truncate, float* h, float* g, int& gate_bad) {
@@ -496,7 +512,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* m
   stage::Stager<TIn, KW> st;
   st.init(lane);
   Rows R;
-  if constexpr (!TAB) {
+  if constexpr (TM != 1) {
     const uint32_t nab = (uint32_t)p.E * (uint32_t)D * (SA ? 4u : (uint32_t)kN * 4u);
     const uint32_t nbb = (uint32_t)p.E * (uint32_t)D * 4u;
     R.a = stage::make_rsrc(p.A, nab);
@@ -524,8 +540,8 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* m
   load_xr(t0, xa, ra);
   // ring offsets: table rows and sum columns, or (rows from memory) the
   // expert's A block and its dt_bias / Dskip row
-  const int escale = TAB ? expert_stride(SA) : D * (SA ? 4 : kN * 4);
-  const int uscale = TAB ? 64 * 4 : D * 4;
+  const int escale = TM >= 1 ? expert_stride(SA, TM) : D * (SA ? 4 : kN * 4);
+  const int uscale = TM == 1 ? 64 * 4 : D * 4;
   st.commit(s.ring, 0, min(kTB, t1 - t0), k, p.E, lane, gate_bad, escale, uscale);
 
   int tb = t0;
@@ -545,9 +561,9 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* m
     const stage::rsrc_t ry = stage::rows_rsrc<TOut>(p.y, row + tb, kTB, D);
 #pragma unroll
     for (int i = 0; i < kTB; i += 2) {
-      const float y0 = ring_token<K, TRACK, ACC_U, SA, ZOH, TAB>(
+      const float y0 = ring_token<K, TRACK, ACC_U, SA, ZOH, TM>(
           p, s, R, ms, sl, i, lane, to_f32(xc[i]), to_f32(rc[i]), h, g);
-      const float y1 = ring_token<K, TRACK, ACC_U, SA, ZOH, TAB>(
+      const float y1 = ring_token<K, TRACK, ACC_U, SA, ZOH, TM>(
           p, s, R, ms, sl, i + 1, lane, to_f32(xc[i + 1]), to_f32(rc[i + 1]), h, g);
       store_y2<TOut>(ry, yoff, yrow, i, y0, y1);
     }
@@ -559,7 +575,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* m
   };
 
   int slot = 0;  // ring slot and buffer of the block at tb
-  if (full_tile && K > 0 && TAB) {
+  if (full_tile && K > 0 && TM == 1) {
     // whole blocks in pairs: slot 0 with xa/ra, then slot 1 with xb/rb
     const std::integral_constant<int, 0> s0;
     const std::integral_constant<int, 1> s1;
@@ -599,7 +615,7 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* m
       if (i < n) {
         const float xv = active ? to_f32(xa[i]) : 0.f, rv = active ? to_f32(ra[i]) : 0.f;
         const float yv =
-            ring_token<K, TRACK, ACC_U, SA, ZOH, TAB>(p, s, R, ms, slot, i, lane, xv, rv, h, g);
+            ring_token<K, TRACK, ACC_U, SA, ZOH, TM>(p, s, R, ms, slot, i, lane, xv, rv, h, g);
         if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
       }
     }
@@ -623,11 +639,12 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* m
 template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA, bool ZOH,
           int EMAX>
 __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
-  constexpr bool TAB = EMAX <= 16;
-  __shared__ float usum[CHUNKED && TAB ? WAVES * EMAX * 64 : 1];
+  constexpr int TM = table_mode(EMAX, SA);
+  constexpr bool TAB = TM >= 1;  // a table in LDS
+  __shared__ float usum[CHUNKED && TM == 1 ? WAVES * EMAX * 64 : 1];
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  Smem s = smem_layout(TAB ? p.E : 0, K > 0 ? K : p.k, wave, SA);
-  if (CHUNKED && TAB) s.U = usum + wave * EMAX * 64;
+  Smem s = smem_layout(TAB ? p.E : 0, K > 0 ? K : p.k, wave, SA, TM);
+  if (CHUNKED && TM == 1) s.U = usum + wave * EMAX * 64;
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
   const int tile = bid % p.ntiles;
@@ -639,8 +656,8 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
 
   int bad = 0;
   if constexpr (TAB) {
-    bad = load_table(p, const_cast<float4*>(s.T), d0, SA);
-    if (CHUNKED)
+    bad = load_table(p, const_cast<float4*>(s.T), d0, SA, TM);
+    if (CHUNKED && TM == 1)
       for (int e = 0; e < p.E; ++e) s.U[e * 64 + lane] = 0.f;
     bad = __syncthreads_or(bad);
   } else if (CHUNKED) {
@@ -660,10 +677,10 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
   // every chunk writes y (provisional for chunks >= 1, recomputed by the
   // fix-up pass where the carried-in state still matters)
   int gate_bad = 0;
-  float lg[SA ? 1 : kN];  // the chunk's exponent sums (rows from memory)
+  float lg[SA ? 1 : kN];  // the chunk's exponent sums (table mode 1: from U)
 #pragma unroll
   for (int n = 0; n < (SA ? 1 : kN); ++n) lg[n] = 0.f;
-  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH, TAB>(p, s, lg, b, t0, t1, d, active,
+  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH, TM>(p, s, lg, b, t0, t1, d, active,
                                                    d0 + 64 <= p.D, lane, false, h, nullptr,
                                                    gate_bad);
 
@@ -671,7 +688,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
     // total decay of the chunk: P[n] = exp2(sum_e U_e A[e, d, n] log2 e) (table
     // path; rows from memory: the summed exponents); with SA one decay per
     // channel, written to every state row for the carry pass
-    for (int e = 0; e < (TAB ? p.E : 0); ++e) {
+    for (int e = 0; e < (TM == 1 ? p.E : 0); ++e) {
       const float u = s.U[e * 64 + lane];
       const float4* te = s.T + e * (SA ? 64 : kRowsDiag * 64) + lane;
       if constexpr (SA) {
@@ -707,9 +724,10 @@ __global__ __launch_bounds__(WAVES * 64) void mix_chunk_kernel(MixParams p) {
 // has decayed away (or to the chunk's end).
 template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH, int EMAX>
 __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
-  constexpr bool TAB = EMAX <= 16;
+  constexpr int TM = table_mode(EMAX, SA);
+  constexpr bool TAB = TM >= 1;  // a table in LDS
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const Smem s = smem_layout(TAB ? p.E : 0, K > 0 ? K : p.k, wave, SA);
+  const Smem s = smem_layout(TAB ? p.E : 0, K > 0 ? K : p.k, wave, SA, TM);
   const int nfix = p.nchunks - 1;
   const int ncg = (nfix + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
@@ -720,7 +738,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
   if constexpr (TAB) {
-    load_table(p, const_cast<float4*>(s.T), d0, SA);
+    load_table(p, const_cast<float4*>(s.T), d0, SA, TM);
     __syncthreads();
   }
 
@@ -746,7 +764,7 @@ __global__ __launch_bounds__(WAVES * 64) void mix_fixup_kernel(MixParams p) {
   const bool truncate = p.carry == SWIMBA_CARRY_FIXUP &&
                         p.flags[((size_t)b * p.nchunks + c) * p.ntiles + tile] == 0;
   int gate_bad = 0;
-  walk<TIn, TOut, K, true, false, SA, ZOH, TAB>(p, s, nullptr, b, t0, t1, d, active,
+  walk<TIn, TOut, K, true, false, SA, ZOH, TM>(p, s, nullptr, b, t0, t1, d, active,
                                                 d0 + 64 <= p.D, lane, truncate, h, g, gate_bad);
 }
 
@@ -779,8 +797,9 @@ int launch_mixed_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
   p.flags = pl.nchunks > 1 ? reinterpret_cast<int32_t*>(w + pl.off_flags) : nullptr;
 
-  constexpr bool TAB = EMAX <= 16;
-  const size_t smem1 = smem_bytes(TAB ? p.E : 0, p.k, WAVES, SA);
+  constexpr int TM = table_mode(EMAX, SA);
+  constexpr bool TAB = TM >= 1;
+  const size_t smem1 = smem_bytes(TAB ? p.E : 0, p.k, WAVES, SA, TM);
   const size_t smem3 = smem1;
   p.tflags = nullptr;
   if (!TAB && pl.nchunks > 1) {
@@ -833,6 +852,12 @@ template <typename TIn, typename TOut, int WAVES, bool SA, bool ZOH>
 int launch_mixed_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   if (a->E <= 8) return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 8>(a, pl, ws, st);
   if (a->E <= 16) return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 16>(a, pl, ws, st);
+  // 17..32 experts with a diagonal A: the A rows in LDS (table mode 2), with
+  // eight waves (two per SIMD) whose rings fit beside the table
+  if constexpr (WAVES == 8 && !SA) {
+    if (a->E <= 32 && smem_bytes(a->E, a->k, 8, false, 2) <= kTabModeLds)
+      return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 32>(a, pl, ws, st);
+  }
   return launch_mixed_e<TIn, TOut, WAVES, SA, ZOH, 64>(a, pl, ws, st);
 }
 
