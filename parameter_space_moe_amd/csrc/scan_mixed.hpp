@@ -244,11 +244,13 @@ __device__ __forceinline__ float update_readout(const float4* bc, const float* m
 // time.  Routing (experts e[j], gates gw[j]) is wave-uniform; each selected
 // expert's table block is read with one address and all of the token's table
 // reads are issued together.  ACC_U: add Delta g_j to the wave's sums U_e.
-template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH, int TM>
+// PBD (rows from memory): the experts' (dt_bias, Dskip) were loaded ahead
+// into pbd.
+template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH, int TM, bool PBD = false>
 __device__ __forceinline__ float mix_token_k(const Smem& s, const Rows& R, float* ms,
                                              const int* e, const int* uo, const float* gw,
                                              const float4* bc, int lane, float xv, float rv,
-                                             float* h, float* g) {
+                                             float* h, float* g, const float2* pbd = nullptr) {
   float4 bd[K];
   float4 ar[SA ? 1 : K][4];
   float uold[K];
@@ -272,8 +274,8 @@ __device__ __forceinline__ float mix_token_k(const Smem& s, const Rows& R, float
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const uint32_t soa = (uint32_t)uniform(e[j]), sob = (uint32_t)uniform(uo[j]);
-      const float bj = stage::buf_load<float>(R.bias, R.vob, sob);
-      const float dj = stage::buf_load<float>(R.dsk, R.vob, sob);
+      const float bj = PBD ? pbd[j].x : stage::buf_load<float>(R.bias, R.vob, sob);
+      const float dj = PBD ? pbd[j].y : stage::buf_load<float>(R.dsk, R.vob, sob);
       if constexpr (TM == 2) {
         bd[j] = make_float4(bj, dj, 0.f, 0.f);
       } else if constexpr (SA) {
@@ -610,13 +612,50 @@ __device__ __forceinline__ void walk(const MixParams& p, const Smem& s, float* m
     wave_sync();
     // stores past the block's n tokens fall outside this buffer and are dropped
     const stage::rsrc_t ry = stage::rows_rsrc<TOut>(p.y, row + tb, n, D);
+    if constexpr (TM != 1 && K > 0) {
+      // dt_bias and Dskip (memory) of token i + 1's experts load while token
+      // i computes: Delta, and so every state update, waits on them (the last
+      // token reloads its own, unused)
+      auto ring_bd = [&](int i, float2* bdv) {
 #pragma unroll
-    for (int i = 0; i < kTB; ++i) {
-      if (i < n) {
-        const float xv = active ? to_f32(xa[i]) : 0.f, rv = active ? to_f32(ra[i]) : 0.f;
-        const float yv =
-            ring_token<K, TRACK, ACC_U, SA, ZOH, TM>(p, s, R, ms, slot, i, lane, xv, rv, h, g);
-        if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
+        for (int j = 0; j < K; ++j) {
+          const uint32_t sob = (uint32_t)uniform(s.ring.uo[(slot * kTB + i) * K + j]);
+          bdv[j] = make_float2(stage::buf_load<float>(R.bias, R.vob, sob),
+                               stage::buf_load<float>(R.dsk, R.vob, sob));
+        }
+      };
+      float2 cur[K], nxt[K];
+      ring_bd(0, cur);
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        if (i < n) {
+          ring_bd(min(i + 1, n - 1), nxt);
+          const float xv = active ? to_f32(xa[i]) : 0.f, rv = active ? to_f32(ra[i]) : 0.f;
+          const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
+          int ev[K], uv[K];
+          float gv[K];
+#pragma unroll
+          for (int j = 0; j < K; ++j) {
+            ev[j] = s.ring.e[(slot * kTB + i) * K + j];
+            uv[j] = s.ring.uo[(slot * kTB + i) * K + j];
+            gv[j] = s.ring.g[(slot * kTB + i) * K + j];
+          }
+          const float yv = mix_token_k<K, TRACK, ACC_U, SA, ZOH, TM, true>(
+              s, R, ms, ev, uv, gv, bc, lane, xv, rv, h, g, cur);
+          if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
+#pragma unroll
+          for (int j = 0; j < K; ++j) cur[j] = nxt[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTB; ++i) {
+        if (i < n) {
+          const float xv = active ? to_f32(xa[i]) : 0.f, rv = active ? to_f32(ra[i]) : 0.f;
+          const float yv = ring_token<K, TRACK, ACC_U, SA, ZOH, TM>(p, s, R, ms, slot, i, lane,
+                                                                    xv, rv, h, g);
+          if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
+        }
       }
     }
     if (TRACK && truncate && carried_part_gone<SA>(h, g)) return;
