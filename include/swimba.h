@@ -190,9 +190,10 @@ int swimba_scan_plan(const swimba_scan_args* a, int design, int* chunk, int* nch
  *   bytes, 256-byte aligned; its contents on entry do not matter.
  * Constraints: B, L >= 0; D >= 1; N == 16; 1 <= k <= E <= 64; chunk >= 0;
  * with E > 16, E * D * 64 < 2^31 (SWIMBA_EUNSUPPORTED otherwise).  Up to 16
- * experts the expert tables are staged in LDS; with more, each token's
- * selected expert rows are read from memory (slower per token).  L == 0
- * writes h_final = h0 (or zeros).
+ * experts the expert tables are staged in LDS; from 17 to 32 experts with a
+ * diagonal A only the A rows are (dt_bias and Dskip are read from memory per
+ * token); beyond, each token's selected expert rows are read from memory
+ * (slower per token).  L == 0 writes h_final = h0 (or zeros).
  */
 int swimba_scan(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 
