@@ -57,10 +57,11 @@ def test_many_experts_bf16_ragged(E, chunk):
     assert torch.equal(hb, hf)
 
 
-@pytest.mark.parametrize("E,k", [(64, 1), (64, 3), (40, 5)])
+@pytest.mark.parametrize("E,k", [(64, 1), (64, 3), (40, 5), (32, 1), (24, 3), (32, 4)])
 @pytest.mark.parametrize("carry", ["fixup", "rewalk"])
 def test_many_experts_k(E, k, carry):
-    """top-1 and runtime k (3, 5) with fp32 streams, both chunk joins."""
+    """top-1 and runtime k (3, 4, 5) with fp32 streams, both chunk joins;
+    up to 32 experts the A rows come from LDS, beyond from memory."""
     w, inp, t = case(B=2, L=300, D=130, E=E, k=k, dtype="f32", seed=E * 7 + k)
     idx, gate = swimba.route(t["x"], t["Wr"], k)
     ry, rh = ref(inp, idx, gate)
@@ -106,10 +107,11 @@ def test_many_experts_noncontractive_falls_back():
 
 
 @pytest.mark.parametrize("scalar_a", [False, True])
-@pytest.mark.parametrize("E", [33, 64])
+@pytest.mark.parametrize("E", [24, 33, 64])
 def test_many_experts_nonnegative_A_flags_its_tile(E, scalar_a):
     """One non-negative A entry (of an expert the routing never picks) in the
-    third 64-channel tile: the per-tile check must flag that tile, whose
+    third 64-channel tile: the per-tile check (while staging the A rows in
+    LDS up to 32 experts, a pre-pass beyond) must flag that tile, whose
     chunks are then re-walked whole -- bit for bit the same y as an explicit
     full re-walk -- while every tile still matches the oracle."""
     w, inp, t = case(B=1, L=700, D=200, E=E, k=2, dtype="f32", seed=E + 60, scalar_a=scalar_a)
