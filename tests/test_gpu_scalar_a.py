@@ -112,11 +112,13 @@ def test_scalar_a_noncontractive_fallback():
 
 
 @pytest.mark.parametrize("chunk", [0, 64])
-@pytest.mark.parametrize("k", [1, 2, 3])
-def test_scalar_a_separate(chunk, k):
-    w, inp, t = case(B=2, L=300, D=100, E=4, k=k, seed=30 + k)
+@pytest.mark.parametrize("E,k", [(4, 1), (4, 2), (4, 3), (16, 2), (24, 2), (40, 3)])
+def test_scalar_a_separate(chunk, E, k):
+    """4 experts (one per wave), 16 (prefetched rounds), 24 and 40 (two and
+    four experts per wave)."""
+    w, inp, t = case(B=2, L=300, D=100, E=E, k=k, seed=30 + k + E)
     idx, gate = swimba.route(t["x"], t["Wr"], k)
-    h0 = np.random.default_rng(9).standard_normal((2, 4, 100, 16)).astype(np.float32)
+    h0 = np.random.default_rng(9).standard_normal((2, E, 100, 16)).astype(np.float32)
     y, hf = swimba.scan_separate(*args(t, idx, gate), h0=torch.from_numpy(h0).to(DEV),
                                  chunk=chunk)
     ry, rh = ref(inp, idx, gate, h0=h0, separate=True)

@@ -70,8 +70,9 @@ def test_zoh_bf16_ragged(ydt):
 
 @pytest.mark.parametrize("scalar", [False, True])
 @pytest.mark.parametrize("chunk", [0, 64])
-def test_zoh_separate(scalar, chunk):
-    w, inp, t = case(B=2, L=300, D=100, E=4, k=2, seed=46, scalar=scalar)
+@pytest.mark.parametrize("E", [4, 16, 24, 40])
+def test_zoh_separate(scalar, chunk, E):
+    w, inp, t = case(B=2, L=300, D=100, E=E, k=2, seed=46 + E, scalar=scalar)
     idx, gate = swimba.route(t["x"], t["Wr"], 2)
     y, hf = swimba.scan_separate(*args(t, idx, gate), chunk=chunk, zoh=True)
     ry, rh = ref(inp, idx, gate, separate=True)
