@@ -41,7 +41,17 @@ def label(c):
     return "%(seed)d-%(design)s-B%(B)dL%(L)dD%(D)dE%(E)dk%(k)d-%(dtype)s" % c
 
 
-CASES = [draw(s) for s in range(NCASES)]
+def draw_wide(seed):
+    """17..64 experts for the designs that take them (mixed and separate)."""
+    c = draw(seed)
+    rng = np.random.default_rng(5000 + seed)
+    c["design"] = ("mixed", "separate")[seed % 2]
+    c["E"] = int(rng.integers(17, 65))
+    c["k"] = int(rng.integers(1, 4))
+    return c
+
+
+CASES = [draw(s) for s in range(NCASES)] + [draw_wide(NCASES + s) for s in range(16)]
 
 
 @pytest.mark.parametrize("c", CASES, ids=[label(c) for c in CASES])
