@@ -247,7 +247,9 @@ int swimba_scan_separate(const swimba_scan_args* a, void* ws, size_t ws_bytes,
  * enter a state.  Where every slot keeps one expert for the whole sequence
  * this equals swimba_scan_separate.  Workspace: swimba_scan_workspace_size
  * with SWIMBA_DESIGN_SLOTS.  Same constraints as swimba_scan, plus k <= 4
- * (the k x N states of a channel are held in registers).
+ * (the k x N states of a channel are held in registers); with more than 16
+ * experts the rows are read from memory every token and k <= 2
+ * (SWIMBA_EUNSUPPORTED otherwise).
  */
 int swimba_scan_slots(const swimba_scan_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -15,6 +15,10 @@
 // row each token.  The gates never enter a state, so the transitions are
 // contractive whenever A < 0, whatever the gates.
 //
+// More than 16 experts (MEM, k <= 2): no table; each slot reads its expert's
+// A row, dt_bias and Dskip from memory (L2) every token, the chunk decays are
+// summed per slot in registers, and a pre-pass checks every tile's A.
+//
 // Chunks are joined in the mixed scan's three passes, per slot: the chunk
 // pass runs every chunk from zero and records each slot's end state and total
 // decay P_j[n] = exp2(sum_e U_je A[e,n] log2 e) (U_je: Delta summed over the
@@ -56,6 +60,7 @@ struct SlotParams {
   float* P;           // [B][C][k*16][D] chunk decays
   float* H;           // [B][C][k*16][D] chunk end states, then carried-in states
   int32_t* flags;     // [B][C][ntiles] 1 = some A of the tile is not negative
+  const int32_t* tflags;  // [ntiles] the same per tile (MEM: from the pre-pass)
 };
 
 // LDS: the tile's expert table, per-wave decay sums per (slot, expert) and
@@ -103,10 +108,14 @@ __host__ inline size_t smem_bytes(int E, int k, bool with_u, int waves, bool sca
 //   TRACK: also decay the carried parts g (fix-up pass; with SA, g[j][0] is
 //          slot j's common decay factor and g[j][1] holds max |h_in|).
 //   ACC_U: accumulate Delta log2(e) per (slot, expert) (chunk pass).
-template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
+//   MEM:   rows from memory at channel dd (p), sums of the exponents in lg
+//          instead of U.
+template <int K, bool TRACK, bool ACC_U, bool SA, bool ZOH, bool MEM = false>
 __device__ __forceinline__ float slot_token(const Smem& s, float* U, int E, const int* e,
                                             const float* gw, int slot, int i, int lane, float xv,
-                                            float rv, float (*h)[kN], float (*g)[kN]) {
+                                            float rv, float (*h)[kN], float (*g)[kN],
+                                            const SlotParams* p = nullptr, int dd = 0,
+                                            float (*lg)[kN] = nullptr) {
   const float4* bc = reinterpret_cast<const float4*>(s.ring.bc + (slot * kTB + i) * 32);
   float bv[kN], cv[kN];
 #pragma unroll
@@ -127,8 +136,13 @@ __device__ __forceinline__ float slot_token(const Smem& s, float* U, int E, cons
   float uo[K], du[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    bdv[j] = s.BD[e[j] * 64 + lane];
-    if (ACC_U) uo[j] = U[(j * E + e[j]) * 64 + lane];
+    if constexpr (MEM) {
+      const size_t o = (size_t)e[j] * p->D + dd;
+      bdv[j] = make_float2(p->bias[o], p->Dsk[o]);
+    } else {
+      bdv[j] = s.BD[e[j] * 64 + lane];
+      if (ACC_U) uo[j] = U[(j * E + e[j]) * 64 + lane];
+    }
   }
   float y = 0.f;
 #pragma unroll
@@ -140,7 +154,10 @@ __device__ __forceinline__ float slot_token(const Smem& s, float* U, int E, cons
     const float dx = dlt * xv;
     float yj = 0.f;
     if constexpr (SA) {
-      const float m = dl2 * reinterpret_cast<const float*>(s.A)[e[j] * 64 + lane];
+      const float av = MEM ? p->A[(size_t)e[j] * p->D + dd]
+                           : reinterpret_cast<const float*>(s.A)[e[j] * 64 + lane];
+      const float m = dl2 * av;
+      if (MEM && ACC_U) lg[j][0] += m;
       const float a = hw_exp2(m);
       const float dxz = ZOH ? dx * zoh_phi(a, m) : dx;
 #pragma unroll
@@ -152,12 +169,15 @@ __device__ __forceinline__ float slot_token(const Smem& s, float* U, int E, cons
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 a4 = s.A[(e[j] * 4 + q) * 64 + lane];
+        const float4 a4 =
+            MEM ? reinterpret_cast<const float4*>(p->A + ((size_t)e[j] * p->D + dd) * kN)[q]
+                : s.A[(e[j] * 4 + q) * 64 + lane];
         const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int n = 4 * q + r;
           const float m = dl2 * av[r];
+          if (MEM && ACC_U) lg[j][n] += m;
           const float a = hw_exp2(m);
           const float inj = ZOH ? (dx * bv[n]) * zoh_phi(a, m) : dx * bv[n];
           h[j][n] = fmaf(a, h[j][n], inj);
@@ -170,7 +190,7 @@ __device__ __forceinline__ float slot_token(const Smem& s, float* U, int E, cons
   }
   // each lane owns its column of U, and (slot, expert) rows differ between
   // slots, so a plain read-modify-write accumulates correctly
-  if (ACC_U)
+  if (ACC_U && !MEM)
 #pragma unroll
     for (int j = 0; j < K; ++j) U[(j * E + e[j]) * 64 + lane] = uo[j] + du[j];
   return y;
@@ -179,10 +199,12 @@ __device__ __forceinline__ float slot_token(const Smem& s, float* U, int E, cons
 // Walk tokens [t0, t1) of sequence b for one lane, staging each block of kTB
 // tokens one block ahead (as the mixed scan's walk).  With TRACK and
 // `truncate`, stops once every slot's carried part has decayed on every lane.
-template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA, bool ZOH>
+template <typename TIn, typename TOut, int K, bool TRACK, bool ACC_U, bool SA, bool ZOH,
+          bool MEM>
 __device__ __forceinline__ void walk(const SlotParams& p, const Smem& s, float* U, int b, int t0,
                                      int t1, int d, bool active, int lane, bool truncate,
-                                     float (*h)[kN], float (*g)[kN]) {
+                                     float (*h)[kN], float (*g)[kN], float (*lg)[kN]) {
+  const int dd = active ? d : p.D - 1;  // MEM: a valid channel for idle lanes
   constexpr int KW = (kTB * K + 63) / 64;
   const int D = p.D;
   const size_t row = (size_t)b * p.L;
@@ -236,8 +258,8 @@ __device__ __forceinline__ void walk(const SlotParams& p, const Smem& s, float* 
           ev[j] = s.ring.e[(slot * kTB + i) * K + j];
           gv[j] = s.ring.g[(slot * kTB + i) * K + j];
         }
-        const float yv = slot_token<K, TRACK, ACC_U, SA, ZOH>(
-            s, U, p.E, ev, gv, slot, i, lane, to_f32(xc[i]), to_f32(rc[i]), h, g);
+        const float yv = slot_token<K, TRACK, ACC_U, SA, ZOH, MEM>(
+            s, U, p.E, ev, gv, slot, i, lane, to_f32(xc[i]), to_f32(rc[i]), h, g, &p, dd, lg);
         if (active) stage::buf_store(ry, yoff, (uint32_t)i * yrow, from_f32<TOut>(yv));
       }
     }
@@ -270,10 +292,11 @@ __device__ __forceinline__ void walk(const SlotParams& p, const Smem& s, float* 
 }
 
 // Pass 1 (or the only pass when CHUNKED is false).
-template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA, bool ZOH>
+template <typename TIn, typename TOut, int WAVES, int K, bool CHUNKED, bool SA, bool ZOH,
+          bool MEM>
 __global__ __launch_bounds__(WAVES * 64) void slot_chunk_kernel(SlotParams p) {
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const Smem s = smem_layout(p.E, K, CHUNKED, WAVES, wave, SA);
+  const Smem s = smem_layout(MEM ? 0 : p.E, K, CHUNKED && !MEM, WAVES, wave, SA);
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
   const int tile = bid % p.ntiles;
@@ -283,11 +306,17 @@ __global__ __launch_bounds__(WAVES * 64) void slot_chunk_kernel(SlotParams p) {
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
 
-  int bad = stage::load_table(p, s.A, s.BD, d0, SA);
-  float* U = s.U + (size_t)wave * K * p.E * 64;
-  if (CHUNKED)
-    for (int q = 0; q < K * p.E; ++q) U[q * 64 + lane] = 0.f;
-  bad = __syncthreads_or(bad);
+  int bad = 0;
+  float* U = nullptr;
+  if constexpr (!MEM) {
+    bad = stage::load_table(p, s.A, s.BD, d0, SA);
+    U = s.U + (size_t)wave * K * p.E * 64;
+    if (CHUNKED)
+      for (int q = 0; q < K * p.E; ++q) U[q * 64 + lane] = 0.f;
+    bad = __syncthreads_or(bad);
+  } else if (CHUNKED) {
+    bad = p.tflags[tile];
+  }
 
   const int c = cg * WAVES + wave;
   if (c >= p.nchunks) return;  // no barrier below
@@ -303,8 +332,15 @@ __global__ __launch_bounds__(WAVES * 64) void slot_chunk_kernel(SlotParams p) {
                     ? p.h0[(((size_t)b * K + j) * p.D + d) * kN + n]
                     : 0.f;
 
-  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH>(p, s, U, b, t0, t1, d, active, lane, false, h,
-                                              nullptr);
+  // MEM: each slot's exponent sums over the chunk (the table path keeps
+  // per-expert sums U in LDS instead)
+  float lg[K][kN];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int n = 0; n < kN; ++n) lg[j][n] = 0.f;
+  walk<TIn, TOut, K, false, CHUNKED, SA, ZOH, MEM>(p, s, U, b, t0, t1, d, active, lane, false, h,
+                                                   nullptr, lg);
 
   if (CHUNKED) {
     const size_t rows = (size_t)K * kN;
@@ -314,8 +350,8 @@ __global__ __launch_bounds__(WAVES * 64) void slot_chunk_kernel(SlotParams p) {
       // slot j's total decay over the chunk: exp2(sum_e U_je A[e, d, n] log2 e)
       float m[kN];
 #pragma unroll
-      for (int n = 0; n < kN; ++n) m[n] = 0.f;
-      for (int e = 0; e < p.E; ++e) {
+      for (int n = 0; n < kN; ++n) m[n] = MEM ? lg[j][n] : 0.f;
+      for (int e = 0; e < (MEM ? 0 : p.E); ++e) {
         const float u = U[(j * p.E + e) * 64 + lane];
         if (SA) {
           m[0] = fmaf(u, reinterpret_cast<const float*>(s.A)[e * 64 + lane], m[0]);
@@ -351,10 +387,10 @@ __global__ __launch_bounds__(WAVES * 64) void slot_chunk_kernel(SlotParams p) {
 
 // Pass 3: chunks 1.. re-run from their carried-in states until every slot's
 // carried part has decayed away (or to the chunk's end).
-template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH>
+template <typename TIn, typename TOut, int WAVES, int K, bool SA, bool ZOH, bool MEM>
 __global__ __launch_bounds__(WAVES * 64) void slot_fixup_kernel(SlotParams p) {
   const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const Smem s = smem_layout(p.E, K, false, WAVES, wave, SA);
+  const Smem s = smem_layout(MEM ? 0 : p.E, K, false, WAVES, wave, SA);
   const int nfix = p.nchunks - 1;
   const int ncg = (nfix + WAVES - 1) / WAVES;
   int bid = blockIdx.x;
@@ -364,8 +400,10 @@ __global__ __launch_bounds__(WAVES * 64) void slot_fixup_kernel(SlotParams p) {
   const int b = bid / ncg;
   const int d0 = tile * 64, d = d0 + lane;
   const bool active = d < p.D;
-  stage::load_table(p, s.A, s.BD, d0, SA);
-  __syncthreads();
+  if constexpr (!MEM) {
+    stage::load_table(p, s.A, s.BD, d0, SA);
+    __syncthreads();
+  }
 
   const int c = 1 + cg * WAVES + wave;
   if (c >= p.nchunks) return;
@@ -390,11 +428,11 @@ __global__ __launch_bounds__(WAVES * 64) void slot_fixup_kernel(SlotParams p) {
   }
   const bool truncate = p.carry == SWIMBA_CARRY_FIXUP &&
                         p.flags[((size_t)b * p.nchunks + c) * p.ntiles + tile] == 0;
-  walk<TIn, TOut, K, true, false, SA, ZOH>(p, s, nullptr, b, t0, t1, d, active, lane, truncate,
-                                           h, g);
+  walk<TIn, TOut, K, true, false, SA, ZOH, MEM>(p, s, nullptr, b, t0, t1, d, active, lane,
+                                                truncate, h, g, nullptr);
 }
 
-template <typename TIn, typename TOut, int K, bool SA, bool ZOH>
+template <typename TIn, typename TOut, int K, bool SA, bool ZOH, bool MEM>
 int launch_slots_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
   constexpr int WAVES = 4;
   SlotParams p;
@@ -424,14 +462,22 @@ int launch_slots_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   p.H = pl.nchunks > 1 ? reinterpret_cast<float*>(w + pl.off_H) : nullptr;
   p.flags = pl.nchunks > 1 ? reinterpret_cast<int32_t*>(w + pl.off_flags) : nullptr;
 
-  const size_t smem1 = smem_bytes(p.E, K, true, WAVES, SA);
-  const size_t smem3 = smem_bytes(p.E, K, false, WAVES, SA);
+  const size_t smem1 = MEM ? smem_bytes(0, K, false, WAVES, SA) : smem_bytes(p.E, K, true, WAVES, SA);
+  const size_t smem3 = smem_bytes(MEM ? 0 : p.E, K, false, WAVES, SA);
+  p.tflags = nullptr;
+  if (MEM && pl.nchunks > 1) {
+    // contraction check of every tile's A (the table path checks while staging)
+    int32_t* tf = reinterpret_cast<int32_t*>(w + pl.off_tflags);
+    p.tflags = tf;
+    const int rc = launch_a_flags(p.A, p.E, p.D, SA, tf, st);
+    if (rc != SWIMBA_OK) return rc;
+  }
   const hipEvent_t* ev = a->phase_events;  // (start, end) x (chunk, carry, fix-up)
   if (pl.nchunks <= 1) {
     p.nchunks = 1;
     const dim3 grid((unsigned)((size_t)p.B * p.ntiles));
-    allow_dynamic_lds(slot_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH>, smem3);
-    const int rc = launch_timed(slot_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH>, grid,
+    allow_dynamic_lds(slot_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH, MEM>, smem3);
+    const int rc = launch_timed(slot_chunk_kernel<TIn, TOut, WAVES, K, false, SA, ZOH, MEM>, grid,
                                 dim3(WAVES * 64), smem3, st, ev, p);
     if (rc != SWIMBA_OK) return rc;
     record_skipped(ev ? ev + 2 : nullptr, st);
@@ -440,8 +486,8 @@ int launch_slots_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   }
   const int ncg = (p.nchunks + WAVES - 1) / WAVES;
   const dim3 grid1((unsigned)((size_t)p.B * ncg * p.ntiles));
-  allow_dynamic_lds(slot_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH>, smem1);
-  int rc = launch_timed(slot_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH>, grid1,
+  allow_dynamic_lds(slot_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH, MEM>, smem1);
+  int rc = launch_timed(slot_chunk_kernel<TIn, TOut, WAVES, K, true, SA, ZOH, MEM>, grid1,
                         dim3(WAVES * 64), smem1, st, ev, p);
   if (rc != SWIMBA_OK) return rc;
   // the carry pass treats the k slots as k trajectories of 16 state rows
@@ -449,22 +495,28 @@ int launch_slots_t(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipS
   if (rc != SWIMBA_OK) return rc;
   const int ncg3 = (p.nchunks - 1 + WAVES - 1) / WAVES;
   const dim3 grid3((unsigned)((size_t)p.B * ncg3 * p.ntiles));
-  allow_dynamic_lds(slot_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH>, smem3);
-  return launch_timed(slot_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH>, grid3, dim3(WAVES * 64),
+  allow_dynamic_lds(slot_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH, MEM>, smem3);
+  return launch_timed(slot_fixup_kernel<TIn, TOut, WAVES, K, SA, ZOH, MEM>, grid3, dim3(WAVES * 64),
                       smem3, st, ev ? ev + 4 : nullptr, p);
 }
 
 template <typename TIn, typename TOut, bool SA, bool ZOH>
 int launch_slots_k(const swimba_scan_args* a, const ScanPlan& pl, void* ws, hipStream_t st) {
+  if (a->E > 16) {
+    // rows from memory: k <= 2 (the slots' states and exponent sums in VGPRs)
+    if (a->k == 1) return launch_slots_t<TIn, TOut, 1, SA, ZOH, true>(a, pl, ws, st);
+    if (a->k == 2) return launch_slots_t<TIn, TOut, 2, SA, ZOH, true>(a, pl, ws, st);
+    return SWIMBA_EUNSUPPORTED;
+  }
   switch (a->k) {
     case 1:
-      return launch_slots_t<TIn, TOut, 1, SA, ZOH>(a, pl, ws, st);
+      return launch_slots_t<TIn, TOut, 1, SA, ZOH, false>(a, pl, ws, st);
     case 2:
-      return launch_slots_t<TIn, TOut, 2, SA, ZOH>(a, pl, ws, st);
+      return launch_slots_t<TIn, TOut, 2, SA, ZOH, false>(a, pl, ws, st);
     case 3:
-      return launch_slots_t<TIn, TOut, 3, SA, ZOH>(a, pl, ws, st);
+      return launch_slots_t<TIn, TOut, 3, SA, ZOH, false>(a, pl, ws, st);
     case 4:
-      return launch_slots_t<TIn, TOut, 4, SA, ZOH>(a, pl, ws, st);
+      return launch_slots_t<TIn, TOut, 4, SA, ZOH, false>(a, pl, ws, st);
     default:
       return SWIMBA_EUNSUPPORTED;
   }

@@ -37,8 +37,9 @@ int validate_scan(const swimba_scan_args* a, int design) {
   if (a->disc != SWIMBA_DISC_EULER && a->disc != SWIMBA_DISC_ZOH) return SWIMBA_EINVAL;
   if (a->N != SWIMBA_STATE_N) return SWIMBA_EUNSUPPORTED;
   if (a->E > SWIMBA_MAX_EXPERTS) return SWIMBA_EUNSUPPORTED;
-  // the per-slot scan stages the E expert tables in LDS
-  if (design == 2 && a->E > 16) return SWIMBA_EUNSUPPORTED;
+  // the per-slot scan stages up to 16 expert tables in LDS; beyond, it reads
+  // the rows from memory with k <= 2
+  if (design == 2 && a->E > 16 && a->k > 2) return SWIMBA_EUNSUPPORTED;
   // the mixed scan with more than 16 experts reads expert rows through 32-bit
   // buffer offsets
   if (design == 0 && a->E > 16 && (size_t)a->E * a->D * SWIMBA_STATE_N * 4 > 0x7fffffffu)
@@ -169,7 +170,7 @@ int plan_scan(const swimba_scan_args* a, int design, ScanPlan* p, int dev) {
                                 slots || a->E <= 8 || a->E > 16, &small, dev);
   const size_t rows = separate ? (size_t)a->E * SWIMBA_STATE_N
                                : (slots ? (size_t)a->k * SWIMBA_STATE_N : SWIMBA_STATE_N);
-  plan_layout(q, a->B, a->L, a->D, chunk, rows, true, !separate && !slots && a->E > 16, p);
+  plan_layout(q, a->B, a->L, a->D, chunk, rows, true, !separate && a->E > 16, p);
   // chunks of one tile share the workgroup's expert table: 8 waves when there
   // are enough chunks to fill them (and the problem is not the small case)
   if (!separate && !slots && p->nchunks >= 8 && !small) p->waves = 8;

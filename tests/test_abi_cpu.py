@@ -137,8 +137,18 @@ def test_slots_rejects_and_workspace(lib):
     # k slot states per lane live in registers: k <= 4
     a = scan_args(E=8, k=5)
     assert lib.swimba_scan_slots(ctypes.byref(a), None, 0, None) == sw.EUNSUPPORTED
-    assert lib.swimba_scan_slots(ctypes.byref(scan_args(E=17)), None, 0, None) == \
+    # more than 16 experts: rows from memory, k <= 2 (and a per-tile A check
+    # in the workspace)
+    assert lib.swimba_scan_slots(ctypes.byref(scan_args(E=17, k=3)), None, 0, None) == \
         sw.EUNSUPPORTED
+    for E in (17, 64):
+        a = scan_args(E=E, k=2)
+        assert lib.swimba_scan_slots(ctypes.byref(a), None, 0, None) == sw.EWORKSPACE
+    a = scan_args(B=2, L=4096, D=256, E=24, k=2, chunk=512)
+    arr = 2 * 8 * 2 * 16 * 256 * 4
+    flags = 2 * 8 * 4 * 4
+    assert lib.swimba_scan_workspace_size(ctypes.byref(a), sw.DESIGN_SLOTS) == \
+        2 * arr + flags + 256
     assert lib.swimba_scan_slots(ctypes.byref(scan_args(x=None)), None, 0, None) == sw.EINVAL
     # workspace: k x 16 state rows per (sequence, chunk, channel), plus flags
     a = scan_args(B=2, L=4096, D=256, E=8, k=3, chunk=512)

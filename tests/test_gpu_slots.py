@@ -165,3 +165,38 @@ def test_slots_degenerate():
         ry, rh = ref(inp, idx, gate, h0=inp["h0"])
         assert rel_err(host(y), ry) < TOL_F32, (B, L, D, k)
         assert rel_err(host(hf), rh) < TOL_F32, (B, L, D, k)
+
+
+@pytest.mark.parametrize("scalar,zoh", [(False, False), (True, False), (False, True)])
+@pytest.mark.parametrize("chunk", [0, 96])
+@pytest.mark.parametrize("E,k,dtype", [(24, 2, "f32"), (64, 1, "f32"), (40, 2, "bf16")])
+def test_slots_many_experts(E, k, dtype, chunk, scalar, zoh):
+    """More than 16 experts: each slot reads its expert's rows from memory
+    every token (k <= 2), with h0 and a ragged last tile."""
+    w, inp, t = case(B=2, L=420, D=136, E=E, k=k, dtype=dtype, seed=E + k, h0=True,
+                     scalar=scalar)
+    idx, gate = swimba.route(t["x"], t["Wr"], k)
+    y, hf = swimba.scan_slots(*args(t, idx, gate), h0=t["h0"], chunk=chunk, zoh=zoh,
+                              y_dtype=torch.float32)
+    ry, rh = ref(inp, idx, gate, h0=inp["h0"], zoh=zoh)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert rel_err(host(y), ry) < tol and rel_err(host(hf), rh) < tol
+
+
+def test_slots_many_experts_nonnegative_A_flags_its_tile():
+    """A non-negative A entry of an expert no slot uses, in the second tile:
+    the per-tile check flags it, so that tile's chunks are re-walked whole
+    (bit for bit the explicit full re-walk), and all of it matches the
+    oracle."""
+    w, inp, t = case(B=1, L=600, D=130, E=20, k=2, seed=77)
+    A = inp["A"].copy()
+    A[19, 100, 2] = 0.0
+    inp["A"] = A
+    t["A"] = torch.from_numpy(A).to(DEV)
+    idx, gate = swimba.route(t["x"], t["Wr"], 2)
+    idx = torch.where(idx == 19, torch.zeros_like(idx), idx)
+    ya, ha = swimba.scan_slots(*args(t, idx, gate), chunk=64)
+    yr, hr = swimba.scan_slots(*args(t, idx, gate), chunk=64, carry="rewalk")
+    assert torch.equal(ya[:, :, 64:128], yr[:, :, 64:128]) and torch.equal(ha, hr)
+    ry, rh = ref(inp, idx, gate)
+    assert rel_err(host(ya), ry) < TOL_F32 and rel_err(host(ha), rh) < TOL_F32
