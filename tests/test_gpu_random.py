@@ -42,16 +42,16 @@ def label(c):
 
 
 def draw_wide(seed):
-    """17..64 experts for the designs that take them (mixed and separate)."""
+    """17..64 experts (the per-slot design with k <= 2 there)."""
     c = draw(seed)
     rng = np.random.default_rng(5000 + seed)
-    c["design"] = ("mixed", "separate")[seed % 2]
+    c["design"] = ("mixed", "separate", "slots")[seed % 3]
     c["E"] = int(rng.integers(17, 65))
-    c["k"] = int(rng.integers(1, 4))
+    c["k"] = int(rng.integers(1, 3 if c["design"] == "slots" else 4))
     return c
 
 
-CASES = [draw(s) for s in range(NCASES)] + [draw_wide(NCASES + s) for s in range(16)]
+CASES = [draw(s) for s in range(NCASES)] + [draw_wide(NCASES + s) for s in range(18)]
 
 
 @pytest.mark.parametrize("c", CASES, ids=[label(c) for c in CASES])
