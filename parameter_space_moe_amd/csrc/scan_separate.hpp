@@ -14,7 +14,12 @@
 // selected its expert, writing the gate-weighted output of every (token, slot)
 // it owns into an LDS buffer; after a barrier the workgroup adds each token's
 // k slot outputs in slot order and stores y.  Each selection is done once, so
-// the work is k updates per token.
+// the work is k updates per token.  Rounds are 64 tokens (fewer for k > 2);
+// with 11 or more experts (one workgroup fills a CU) the next round is
+// prefetched in registers and rounds of bf16 tokens are 128 long; with at
+// most 4 experts they are 16 long, so that several small workgroups share a
+// CU.  Past 16 experts the workgroup keeps 16 waves and wave w owns experts
+// w, w + 16, ... (two or four), reloading each one's row once per round.
 //
 // ALL (the third reading of separate trajectories): every expert's wave
 // advances its state at every token, whether or not the token selected the
