@@ -434,6 +434,27 @@ def test_separate_many_experts_ragged_channels(D, dtype):
     assert rel_err(host(y), ry) < tol and rel_err(host(hf), rh) < tol
 
 
+def test_separate_unaligned_streams():
+    """x and dt_raw at a 2-byte offset (views into larger buffers): the
+    16-expert workgroups stage rounds element by element instead of in
+    16-byte packets, with the same results as aligned copies."""
+    w, inp, t = small_case(B=1, L=400, D=128, E=16, k=2, dtype="bf16", seed=88)
+    idx, gate = route_on_gpu(t, w)
+    def shifted(a):
+        flat = torch.empty(a.numel() + 1, dtype=a.dtype, device=DEV)
+        v = flat[1:].view(a.shape)
+        v.copy_(a)
+        assert v.data_ptr() % 16 != 0
+        return v
+    ta = dict(t)
+    ta["x"], ta["dt_raw"] = shifted(t["x"]), shifted(t["dt_raw"])
+    y0, h0 = swimba.scan_separate(*scan_args(t, idx, gate), chunk=128, y_dtype=torch.float32)
+    y1, h1 = swimba.scan_separate(*scan_args(ta, idx, gate), chunk=128, y_dtype=torch.float32)
+    assert torch.equal(y0, y1) and torch.equal(h0, h1)
+    ry, rh = oracle_scan(inp, idx, gate, separate=True)
+    assert rel_err(host(y1), ry) < TOL_BF16 and rel_err(host(h1), rh) < TOL_BF16
+
+
 @pytest.mark.parametrize("E,k", [(4, 2), (16, 2), (8, 1), (12, 1)])
 def test_separate_fixup_stops_and_matches_rewalk(E, k):
     """Chunks much longer than the decay horizon: the fix-up stops early, and
