@@ -295,6 +295,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--designs-only", action="store_true",
+                    help="time only the mixed, separate and dense scans at the "
+                         "workload's shape (for profiler runs of their kernels)")
     ap.add_argument("--no-modes", action="store_true",
                     help="time only the step (for profiler runs)")
     args = ap.parse_args()
@@ -318,6 +321,13 @@ def main():
         return
     print("bench: %s, generating inputs" % w.name, file=sys.stderr, flush=True)
     lay = Layer(w, dev)
+    if args.designs_only:
+        # the three designs alone on the router's routing (they are also
+        # reported under the default run's modes)
+        lay.route()
+        print(json.dumps({"designs": ratios_at(lay, swimba, dev, args.steps)[0]}),
+              flush=True)
+        return
     K, W = args.steps, args.warmup
     print("bench: timing %d steps" % K, file=sys.stderr, flush=True)
     r = lay.timed_steps(K, W, phases=False)
