@@ -13,9 +13,10 @@ Cache.  Printed as one JSON line:
                  with 6 algorithmic bytes per token x channel (bf16 x and
                  dt_raw read, y written); `valu` beside it gives the same
                  kernel against the VALU issue ceiling that bounds it
-  modes        = the scan alone, the dense single-expert scan (E = 1) and
-                 the separate design at the same shape ("mixed vs separate");
-                 the same three and the step on the Mamba-1.4B-like layer; an
+  modes        = the scan alone, the dense single-expert scan (E = 1), the
+                 separate design ("mixed vs separate") and the scalar-transition
+                 (Mamba-2) form at the same shape; the same and the step on the
+                 Mamba-1.4B-like layer; an
                  expert-count sweep; the Mamba-130M-like layer (steady and
                  cache-flushed) with the stream-mixed, scalar-transition,
                  zero-order-hold, per-slot and all-experts forms, the
@@ -481,8 +482,9 @@ def layer_mode(lay, swimba, dev, reps, flush):
         "chunk_valu_frac": chunk_valu(w, chunk_ms)["frac"]}
     ms_flushed = time_events(lay.step, reps, flush=flush)
     res["step_flushed_ms"] = round(ms_flushed, 4)
-    rat, _ = ratios_at(lay, swimba, dev, reps)
+    rat, ms_mixed = ratios_at(lay, swimba, dev, reps)
     res.update(rat)
+    res["scalar_a"] = scalar_a_mode(swimba, w, lay, reps, ms_mixed)
     return res
 
 
@@ -497,8 +499,10 @@ def modes(args, lay, swimba, workloads, dev):
     res["step_flushed"] = {"ms": round(ms_fl, 4), "G_tc_per_s": round(lay.w.tc / ms_fl / 1e6, 3),
                            "note": "route + mixed scan after a 512 MB write, HIP events, median"}
     print("bench: modes at %s" % lay.w.name, file=sys.stderr, flush=True)
-    rat, _ = ratios_at(lay, swimba, dev, reps)
+    rat, ms_mixed = ratios_at(lay, swimba, dev, reps)
     res.update(rat)
+    # the Mamba-2 form (one transition per expert and channel) at this shape
+    res["scalar_a"] = scalar_a_mode(swimba, lay.w, lay, reps, ms_mixed)
     for name in ("mamba1p4b_layer", "long_context"):
         if name == lay.w.name:
             continue
