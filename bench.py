@@ -297,8 +297,9 @@ def main():
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--designs-only", action="store_true",
-                    help="time only the mixed, separate and dense scans at the "
-                         "workload's shape (for profiler runs of their kernels)")
+                    help="time only the mixed, separate, dense and scalar-transition "
+                         "scans at the workload's shape (for profiler runs of their "
+                         "kernels)")
     ap.add_argument("--no-modes", action="store_true",
                     help="time only the step (for profiler runs)")
     args = ap.parse_args()
@@ -326,8 +327,9 @@ def main():
         # the three designs alone on the router's routing (they are also
         # reported under the default run's modes)
         lay.route()
-        print(json.dumps({"designs": ratios_at(lay, swimba, dev, args.steps)[0]}),
-              flush=True)
+        res, ms_mixed = ratios_at(lay, swimba, dev, args.steps)
+        res["scalar_a"] = scalar_a_mode(swimba, w, lay, args.steps, ms_mixed)
+        print(json.dumps({"designs": res}), flush=True)
         return
     K, W = args.steps, args.warmup
     print("bench: timing %d steps" % K, file=sys.stderr, flush=True)
